@@ -1,0 +1,222 @@
+"""Benchmark: one paged decode step of an OPT-13B-shaped attention layer on one GPU.
+
+A step is the whole hot path over one batch: the host allocator reserves one
+slot per request (copy-on-write pairs, if any, are copied), the new tokens'
+K/V are written into their slots, block tables are uploaded, and decode
+attention runs over every request's context through its block table.  Inputs
+(pools, queries, new tokens) are resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is algorithmic KV bytes read by decode
+attention per step (logical tokens only: sum(L) * 2 * Hkv * D * 2 B) divided
+by the wall time per step; ``roofline`` is the same byte count per pa_decode
+launch divided by that launch's time measured with HIP events on the launch
+stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample of requests.
+
+    python bench.py [--steps K] [--warmup W] [--workload opt13b|gqa|long_context]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + µs/step, OPT-13B shape"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="opt13b", choices=["opt13b", "gqa", "long_context"])
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="rough budget for the CPU oracle baseline (0 disables it)")
+    return ap.parse_args()
+
+
+def kv_bytes(lengths, w):
+    return int(np.sum(lengths, dtype=np.int64)) * 2 * w.num_kv_heads * w.head_dim * 2
+
+
+def cpu_baseline(w, budget_s):
+    """Time the oracle's paged attention on a sample of requests, single-threaded BLAS."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import alloc_model, attention, cache
+
+    order = np.argsort(np.random.default_rng(0).random(w.num_seqs))
+    # Estimate the oracle's rate on a small request, then take requests until ~budget.
+    picked, tokens = [], 0
+    est_tok_per_s = 25_000.0 * (40 * 128) / (w.num_q_heads * w.head_dim)
+    for i in order:
+        picked.append(int(i))
+        tokens += int(w.lengths[i])
+        if tokens / est_tok_per_s >= budget_s:
+            break
+    lens = w.lengths[picked]
+    nb_need = int(sum(-(-int(L) // w.block_size) for L in lens))
+    m = alloc_model.AllocatorModel(nb_need, w.block_size)
+    shape = (nb_need, w.num_kv_heads, w.block_size, w.head_dim)
+    kp = np.zeros(shape, dtype=np.float16)
+    vp = np.zeros(shape, dtype=np.float16)
+    seqs = []
+    for i in picked:
+        s = m.create()
+        seqs.append(s)
+        k, v = w.tokens(i)
+        slots, _ = m.append(s, len(k))
+        cache.write_slots(kp, vp, k, v, slots, w.block_size)
+    max_blocks = max(len(m.table(s)) for s in seqs)
+    tables, lens_l = m.export(seqs, max_blocks, 0)
+    q = w.q[picked]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        attention.attend_paged(q, kp, vp, np.array(tables), lens_l, w.block_size, w.scale)
+        dt = time.perf_counter() - t0
+    nbytes = kv_bytes(lens, w)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(picked)} of {w.num_seqs} requests ({int(lens.sum())} tokens), "
+                      f"fp64 numpy attend_paged, attention only, {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path has no multi-GPU sharding in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_244_amd import workloads
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.workload == "long_context":
+        w = workloads.long_context(16)
+    else:
+        w = workloads.WORKLOADS[args.workload]()
+    total_steps = args.warmup + args.steps
+    # Room for the tokens appended during the run: one more block per request per B steps.
+    growth = w.num_seqs * (-(-total_steps // w.block_size) + 1)
+    num_blocks = w.num_blocks + growth
+    order = np.concatenate([w.initial_order, np.arange(w.num_blocks, num_blocks, dtype=np.int32)])
+    cache = PagedKVCache(num_blocks, w.num_kv_heads, w.head_dim, w.block_size, initial_order=order,
+                         device=dev, poison=False)
+    stream = cache.stream
+    seqs = [cache.new_sequence() for _ in range(w.num_seqs)]
+
+    # Prefill: the first L-1 tokens of every request.
+    prompt_idx = np.concatenate([np.arange(o, o + L - 1) for o, L in zip(w.offsets[:-1], w.lengths)])
+    slots = cache.reserve_many(seqs, [int(L) - 1 for L in w.lengths])
+    cache.write(slots, torch.from_numpy(w.k_tokens[prompt_idx]).to(dev),
+                torch.from_numpy(w.v_tokens[prompt_idx]).to(dev))
+    last_idx = w.offsets[:-1] + w.lengths - 1
+
+    # Per-step inputs, resident on the device before timing.
+    step_k, step_v, step_q = [], [], []
+    for t in range(total_steps):
+        if t == 0:
+            k, v, q = w.k_tokens[last_idx], w.v_tokens[last_idx], w.q
+        else:
+            k, v, q = workloads.step_inputs(w, t)
+        step_k.append(torch.from_numpy(np.ascontiguousarray(k)).to(dev))
+        step_v.append(torch.from_numpy(np.ascontiguousarray(v)).to(dev))
+        step_q.append(torch.from_numpy(np.ascontiguousarray(q)).to(dev))
+    max_len_final = int(w.lengths.max()) + total_steps
+    max_blocks = -(-max_len_final // w.block_size)
+    out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    cache.workspace(w.num_seqs, w.num_q_heads, max_len_final, args.partition)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    step_bytes = []
+
+    def step(t, timed_slot=None):
+        s = cache.reserve_step(seqs)
+        cache.write(s, step_k[t], step_v[t])
+        tables, lens, max_len = cache.block_tables(seqs, max_blocks)
+        if timed_slot is not None:
+            ev[timed_slot][0].record(stream)
+        cache.attend(step_q[t], tables, lens, max_len, w.scale, partition_size=args.partition,
+                     out=out)
+        if timed_slot is not None:
+            ev[timed_slot][1].record(stream)
+        return max_len
+
+    lengths = w.lengths.astype(np.int64) - 1
+    for t in range(args.warmup):
+        step(t)
+        lengths += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, timed_slot=i)
+        lengths += 1
+        step_bytes.append(kv_bytes(lengths, w))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    decode_ms = [a.elapsed_time(b) for a, b in ev]
+    decode_avg_s = float(np.mean(decode_ms)) / 1e3
+    bytes_avg = float(np.mean(step_bytes))
+    total_bytes = float(np.sum(step_bytes))
+    value = total_bytes / wall / 1e9
+    achieved = bytes_avg / decode_avg_s / 1e9
+
+    baseline = None
+    if args.cpu_seconds > 0:
+        baseline = cpu_baseline(w, args.cpu_seconds)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name} decode layer",
+            "num_seqs": w.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": "f16",
+            "q_dtype": np.dtype(w.q_dtype).name, "partition_size": args.partition,
+            "mean_context": round(float(np.mean(lengths)), 1),
+            "kv_bytes_per_step": int(bytes_avg),
+        },
+        "decode_us": round(decode_avg_s * 1e6, 2),
+        "decode_us_p10_p90": [round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
+                              round(float(np.percentile(decode_ms, 90)) * 1e3, 2)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_decode (partition + reduce launches)"},
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * pagedkv.h — C ABI of the paged KV-cache hot path for AMD MI355X (gfx950).
+ *
+ * The library (libpagedkv.so) implements PagedAttention's data-parallel path as
+ * described on three web pages about it:
+ *   [A] "800 kilobytes per token" (shashforge.dev log)
+ *   [B] "Only 20.4% of your KV cache held actual tokens: how PagedAttention put a
+ *       page table inside the attention kernel" (blog.teqners.com)
+ *   [C] "The KV cache is a systems problem" (rsw.lol notes)
+ *
+ * Every call returns an int: PKV_OK (0) on success, a negative PKV_ERR_* code on
+ * failure; pkv_last_error() then returns a message (thread-local, valid until the
+ * next failing call on that thread).  No call here allocates or frees device
+ * memory, and no device call synchronises: device work is enqueued on the
+ * caller's HIP stream (a hipStream_t passed as void*; NULL = the null stream).
+ *
+ * Cache pools.  One pool for keys and one for values, each
+ *     fp16 [num_blocks][num_kv_heads][block_size][head_dim], contiguous,
+ * so one (block, KV head) is one contiguous block_size*head_dim*2-byte tile.
+ * A slot number s names block s / block_size, offset s % block_size.  The
+ * caller owns every device buffer (pools, queries, outputs, tables, lengths,
+ * slot maps, block pairs, workspace); the library owns only allocator objects.
+ *
+ * Supported shapes: head_dim in {64, 128}; block_size in {8, 16, 32, 64, 128};
+ * num_q_heads a multiple of num_kv_heads.  Anything else is PKV_ERR_UNSUPPORTED.
+ *
+ * Device-resident indices (slots, block ids, lengths, pairs) cannot be checked
+ * on the host without a synchronisation.  The kernels guard them instead: a
+ * slot or block id outside the pool is skipped (never dereferenced), and a
+ * context length is clamped to [0, min(max_context_len, max_blocks_per_seq *
+ * block_size)].  These guards keep bad input from faulting; they are not a
+ * feature, and the results for such input are unspecified.
+ *
+ * Ordering: enqueue kv_copy_blocks, then kv_cache_write, then pa_decode for one
+ * step on one stream.  A block freed by the host allocator may be handed out at
+ * once because every later device use of it is enqueued later on the same
+ * stream, after the work that still reads it ([C], "Shared prefixes need
+ * ownership rules": a delayed device write must not land in reassigned
+ * storage).  Using several streams on one pool is unsafe unless the caller
+ * orders them.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,   /* null pointer, negative size, bad permutation ...  */
+  PKV_ERR_UNSUPPORTED = -2,   /* head_dim / block_size / grouping not built        */
+  PKV_ERR_OUT_OF_BLOCKS = -3, /* allocator: not enough free blocks; state unchanged */
+  PKV_ERR_BAD_SEQ = -4,       /* allocator: unknown or freed sequence id           */
+  PKV_ERR_HIP = -5,           /* a HIP launch or runtime call failed               */
+  PKV_ERR_WORKSPACE = -6      /* pa_decode workspace missing or too small          */
+};
+
+/* Element types of the query tensor. */
+enum { PKV_F32 = 0, PKV_F16 = 1 };
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Device operations                                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * kv_cache_write — store each new token's key and value in its slot.
+ * [B] "The page table, relocated into attention": a request's logical blocks
+ * fill left to right and each maps to a physical block anywhere in the pool.
+ *
+ *   k_cache, v_cache : device fp16 pools (layout above), num_blocks blocks.
+ *   k_new, v_new     : device fp16 [num_tokens][num_kv_heads][head_dim].
+ *   slot_mapping     : device int64 [num_tokens]; token j goes to slot
+ *                      slot_mapping[j]; a negative slot skips the token.
+ * A bit copy: the pools' bytes at the slot become the token's bytes.  Two
+ * tokens with the same slot race (the result is one of them).
+ * num_tokens == 0 is a no-op.
+ */
+int kv_cache_write(void* k_cache, void* v_cache, int32_t num_blocks,
+                   const void* k_new, const void* v_new,
+                   const int64_t* slot_mapping, int32_t num_tokens,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   void* stream);
+
+/*
+ * kv_copy_blocks — the copy of copy-on-write: for each pair (src, dst) and each
+ * layer, the whole dst block of K and of V becomes a copy of the src block (all
+ * heads, all block_size slots, filled or not).  [B] "The part everyone forgets:
+ * pages enable sharing, not just packing": a shared block about to diverge is
+ * copied one block's worth at a time; [A] "The old answer, imported honestly".
+ *
+ *   k_caches, v_caches : HOST arrays of num_layers device pool pointers.
+ *   block_pairs        : device int32 [num_pairs][2] = (src, dst).
+ * A pair with an id outside [0, num_blocks) is skipped.  dst blocks must be
+ * distinct and must not appear as a src in the same call (pairs run
+ * concurrently).  num_pairs == 0 is a no-op.
+ */
+int kv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                   const int32_t* block_pairs, int32_t num_pairs, int32_t num_blocks,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   void* stream);
+
+/*
+ * Workspace bytes pa_decode needs for a split-context launch (0 when a single
+ * partition covers max_context_len, or partition_size == 0).
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode — single-query decode attention through the block table.
+ * [A] "The old answer, imported honestly" and [B] "The page table, relocated
+ * into attention": the kernel walks each request's block table and gathers its
+ * keys and values from scattered physical blocks.  [B] "Why the KV cache is the
+ * thing that limits your batch": one query per request per step.  [C]
+ * "Calculate bytes per token before choosing a batch": groups of query heads
+ * may share one KV head.
+ *
+ * For request i, query head h, KV head g = h / (num_q_heads / num_kv_heads),
+ * L = context_lens[i], and logical token t < L stored in physical block
+ * block_tables[i][t / block_size] at offset t % block_size:
+ *     out[i][h][:] = sum_t softmax_t(scale * q[i][h] . K_t) * V_t
+ * computed in fp32 from fp16 keys/values.  L == 0 gives zeros.
+ *
+ *   out            : device fp32 [num_seqs][num_q_heads][head_dim] (written).
+ *   q              : device [num_seqs][num_q_heads][head_dim], q_dtype PKV_F32/F16.
+ *   block_tables   : device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                    ceil(L / block_size) are never read.
+ *   context_lens   : device int32 [num_seqs], tokens attended per request.
+ *   max_context_len: an upper bound on every context length (sizes the grid).
+ *   partition_size : 0 = one pass per request; otherwise a multiple of
+ *                    block_size: each request's context is split into
+ *                    partitions of that many tokens, processed in parallel and
+ *                    combined by a log-sum-exp reduce.
+ *   workspace      : device buffer of pa_decode_workspace_size(...) bytes, 256-B
+ *                    aligned (may be NULL when that size is 0).  Scratch only.
+ */
+int pa_decode(float* out, const void* q, int32_t q_dtype,
+              const void* k_cache, const void* v_cache, int32_t num_blocks,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              float scale, int32_t max_context_len, int32_t partition_size,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator                                                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * Host memory only, no HIP calls; not thread-safe (one owner per object).
+ * Rules ([B] "The page table, relocated into attention" and "The part everyone
+ * forgets: pages enable sharing, not just packing"; [C] "Shared prefixes need
+ * ownership rules"):
+ *  - A new physical block is taken only when the request's last block is full.
+ *  - Blocks carry reference counts; fork shares every block of the parent.
+ *  - Appending into a last block that is partly filled and shared (count > 1)
+ *    takes a fresh block, reports the pair (shared, fresh) to be copied with
+ *    kv_copy_blocks before the write, and drops one reference to the shared
+ *    block.  The last holder writes in place.  At most one pair per append.
+ *  - Freeing drops one reference per block, in logical order; a block reaching
+ *    zero returns to the free list, which is last-in first-out.  The first
+ *    allocations follow initial_order[0], [1], ...
+ *  - Running out of blocks (PKV_ERR_OUT_OF_BLOCKS) changes nothing.
+ *  - Sequence ids count up from 0 and are never reused.
+ */
+typedef struct kv_allocator kv_allocator;
+
+typedef struct {
+  int32_t num_blocks;     /* pool size                                   */
+  int32_t free_blocks;    /* on the free list                            */
+  int32_t used_blocks;    /* referenced by at least one sequence         */
+  int32_t shared_blocks;  /* referenced by more than one sequence        */
+  int64_t live_tokens;    /* sum of live sequences' lengths              */
+  int64_t sum_refcounts;  /* sum of all reference counts                 */
+} kv_stats;
+
+/* initial_order: host int32 [num_blocks], a permutation of 0..num_blocks-1, or
+ * NULL for 0, 1, 2, ...  The allocator copies it. */
+int kv_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order,
+                        kv_allocator** out);
+void kv_allocator_destroy(kv_allocator* a);
+
+int kv_seq_create(kv_allocator* a, int32_t* seq_out);
+/* New sequence sharing all of parent's blocks (each count + 1) and its length. */
+int kv_seq_fork(kv_allocator* a, int32_t parent, int32_t* child_out);
+/* Reserve n >= 0 more tokens.  slots_out: host int64 [n] (slot of each new
+ * token, in order).  cow_pair_out: host int32 [2]; *n_cow_out = 0 or 1. */
+int kv_seq_append(kv_allocator* a, int32_t seq, int32_t n, int64_t* slots_out,
+                  int32_t* cow_pair_out, int32_t* n_cow_out);
+/* One token for each of seqs[0..num_seqs-1] in that order (a decode step); all
+ * or nothing.  slots_out: host int64 [num_seqs]; cow_pairs_out: host int32
+ * [num_seqs][2], *n_cow_out pairs filled. */
+int kv_batch_append(kv_allocator* a, const int32_t* seqs, int32_t num_seqs, int64_t* slots_out,
+                    int32_t* cow_pairs_out, int32_t* n_cow_out);
+int kv_seq_free(kv_allocator* a, int32_t seq);
+int kv_seq_len(const kv_allocator* a, int32_t seq, int32_t* len_out);
+/* Host int32 tables_out [n][max_blocks_per_seq] (unused entries = pad_value) and
+ * lens_out [n].  PKV_ERR_INVALID_ARG if a sequence holds more blocks. */
+int kv_export_block_tables(const kv_allocator* a, const int32_t* seqs, int32_t n,
+                           int32_t max_blocks_per_seq, int32_t pad_value,
+                           int32_t* tables_out, int32_t* lens_out);
+int kv_allocator_stats(const kv_allocator* a, kv_stats* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

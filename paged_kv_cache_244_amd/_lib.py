@@ -1,0 +1,300 @@
+"""ctypes binding to libpagedkv.so: argument marshalling only.
+
+Every function here checks shapes and dtypes on the host, passes raw pointers
+and the current HIP stream to the C ABI declared in ``include/pagedkv.h``, and
+raises on a negative return code.  All computation happens in the library's
+HIP kernels (device ops) or its host C++ allocator.  If the library is missing
+the first call raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_OUT_OF_BLOCKS = -3
+PKV_ERR_BAD_SEQ = -4
+PKV_ERR_HIP = -5
+PKV_ERR_WORKSPACE = -6
+PKV_F32 = 0
+PKV_F16 = 1
+
+_ERR_NAMES = {
+    PKV_ERR_INVALID_ARG: "INVALID_ARG",
+    PKV_ERR_UNSUPPORTED: "UNSUPPORTED",
+    PKV_ERR_OUT_OF_BLOCKS: "OUT_OF_BLOCKS",
+    PKV_ERR_BAD_SEQ: "BAD_SEQ",
+    PKV_ERR_HIP: "HIP",
+    PKV_ERR_WORKSPACE: "WORKSPACE",
+}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"pagedkv error {code} ({_ERR_NAMES.get(code, '?')}): {message}")
+        self.code = code
+
+
+class OutOfBlocks(PagedKVError):
+    pass
+
+
+class BadSequence(PagedKVError):
+    pass
+
+
+class KVStats(ctypes.Structure):
+    _fields_ = [("num_blocks", c_int32), ("free_blocks", c_int32), ("used_blocks", c_int32),
+                ("shared_blocks", c_int32), ("live_tokens", c_int64), ("sum_refcounts", c_int64)]
+
+
+_SIGNATURES = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "kv_cache_write": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int32,
+                                 c_int32, c_int32, c_int32, c_void_p]),
+    "kv_copy_blocks": (c_int32, [POINTER(c_void_p), POINTER(c_void_p), c_int32, c_void_p, c_int32,
+                                 c_int32, c_int32, c_int32, c_int32, c_void_p]),
+    "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "pa_decode": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
+                            c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_float,
+                            c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
+    "kv_allocator_create": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_void_p)]),
+    "kv_allocator_destroy": (None, [c_void_p]),
+    "kv_seq_create": (c_int32, [c_void_p, POINTER(c_int32)]),
+    "kv_seq_fork": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
+    "kv_seq_append": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, POINTER(c_int32)]),
+    "kv_batch_append": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, POINTER(c_int32)]),
+    "kv_seq_free": (c_int32, [c_void_p, c_int32]),
+    "kv_seq_len": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
+    "kv_export_block_tables": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                         c_void_p]),
+    "kv_allocator_stats": (c_int32, [c_void_p, POINTER(KVStats)]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libpagedkv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_244_amd.build` (no fallback exists)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGNATURES)
+
+
+def _check(rc):
+    if rc != PKV_OK:
+        msg = lib().pkv_last_error().decode(errors="replace")
+        cls = {PKV_ERR_OUT_OF_BLOCKS: OutOfBlocks, PKV_ERR_BAD_SEQ: BadSequence}.get(rc, PagedKVError)
+        raise cls(rc, msg)
+
+
+# --------------------------------------------------------------------------- device ops
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return c_void_p(t.data_ptr())
+
+
+def _pool_geometry(k_cache, v_cache):
+    if k_cache.shape != v_cache.shape or k_cache.dim() != 4:
+        raise ValueError("k_cache and v_cache must both be [num_blocks, kv_heads, block_size, head_dim]")
+    return tuple(int(x) for x in k_cache.shape)
+
+
+def kv_cache_write(k_cache, v_cache, k_new, v_new, slot_mapping, stream=None):
+    """Store token j's K/V ([T, Hkv, D] fp16) in slot slot_mapping[j] (int64, <0 skips)."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_geometry(k_cache, v_cache)
+    if k_new.shape != v_new.shape or tuple(k_new.shape[1:]) != (hkv, d):
+        raise ValueError(f"k_new/v_new must be [T, {hkv}, {d}]")
+    t = int(k_new.shape[0])
+    if tuple(slot_mapping.shape) != (t,):
+        raise ValueError("slot_mapping must be [T]")
+    _check(lib().kv_cache_write(
+        _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"), nb,
+        _dev(k_new, torch.float16, "k_new"), _dev(v_new, torch.float16, "v_new"),
+        _dev(slot_mapping, torch.int64, "slot_mapping"), t, hkv, d, bs, _stream(stream)))
+
+
+def kv_copy_blocks(k_caches, v_caches, block_pairs, stream=None):
+    """For each (src, dst) row of block_pairs (device int32 [P, 2]) copy every layer's block."""
+    torch = _torch()
+    if len(k_caches) != len(v_caches) or not k_caches:
+        raise ValueError("need the same, non-zero number of K and V pools")
+    geo = _pool_geometry(k_caches[0], v_caches[0])
+    for k, v in zip(k_caches, v_caches):
+        if _pool_geometry(k, v) != geo:
+            raise ValueError("all layers' pools must share one geometry")
+    nb, hkv, bs, d = geo
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [P, 2]")
+    n = len(k_caches)
+    kp = (c_void_p * n)(*[_dev(k, torch.float16, "k_cache").value for k in k_caches])
+    vp = (c_void_p * n)(*[_dev(v, torch.float16, "v_cache").value for v in v_caches])
+    _check(lib().kv_copy_blocks(kp, vp, n, _dev(block_pairs, torch.int32, "block_pairs"),
+                                int(block_pairs.shape[0]), nb, hkv, d, bs, _stream(stream)))
+
+
+def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):
+    return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                              partition_size))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+              partition_size=512, workspace=None, stream=None):
+    """Decode attention: out[S, Hq, D] fp32 from q[S, Hq, D] (fp32 or fp16) via the block tables.
+
+    ``workspace`` is a device uint8 tensor of at least ``pa_decode_workspace_size`` bytes
+    (needed only when a request may span more than one partition).
+    """
+    torch = _torch()
+    nb, hkv, bs, d = _pool_geometry(k_cache, v_cache)
+    s, hq, dq = (int(x) for x in q.shape)
+    if dq != d or tuple(out.shape) != (s, hq, d):
+        raise ValueError("q and out must be [S, Hq, head_dim]")
+    if q.dtype == torch.float32:
+        qd = PKV_F32
+    elif q.dtype == torch.float16:
+        qd = PKV_F16
+    else:
+        raise TypeError("q must be float32 or float16")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or tuple(context_lens.shape) != (s,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    ws_ptr, ws_bytes = c_void_p(None), 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(lib().pa_decode(
+        _dev(out, torch.float32, "out"), _dev(q, q.dtype, "q"), qd,
+        _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"), nb,
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, bs, float(scale),
+        int(max_context_len), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+
+
+# --------------------------------------------------------------------------- host allocator
+
+class BlockAllocator:
+    """Owner of one host allocator object (refcounted blocks, tables, copy-on-write)."""
+
+    def __init__(self, num_blocks, block_size, initial_order=None):
+        self._h = c_void_p()
+        order = None
+        if initial_order is not None:
+            order = np.ascontiguousarray(initial_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise ValueError("initial_order must have num_blocks entries")
+        self._order = order
+        _check(lib().kv_allocator_create(num_blocks, block_size,
+                                         None if order is None else order.ctypes.data,
+                                         byref(self._h)))
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            lib().kv_allocator_destroy(self._h)
+            self._h = c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def create(self) -> int:
+        out = c_int32()
+        _check(lib().kv_seq_create(self._h, byref(out)))
+        return out.value
+
+    def fork(self, parent: int) -> int:
+        out = c_int32()
+        _check(lib().kv_seq_fork(self._h, parent, byref(out)))
+        return out.value
+
+    def append(self, seq: int, n: int):
+        """Returns (slots int64 [n], cow_pairs list of (src, dst))."""
+        slots = np.empty(max(n, 0), dtype=np.int64)
+        pair = np.empty(2, dtype=np.int32)
+        ncow = c_int32()
+        _check(lib().kv_seq_append(self._h, seq, n, slots.ctypes.data, pair.ctypes.data, byref(ncow)))
+        return slots, [tuple(int(x) for x in pair)] if ncow.value else []
+
+    def append_batch(self, seqs):
+        """One token per listed sequence; returns (slots int64 [n], pairs int32 [P, 2])."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = int(seqs.shape[0])
+        slots = np.empty(n, dtype=np.int64)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        ncow = c_int32()
+        _check(lib().kv_batch_append(self._h, seqs.ctypes.data, n, slots.ctypes.data,
+                                     pairs.ctypes.data, byref(ncow)))
+        return slots, pairs[: ncow.value]
+
+    def free(self, seq: int):
+        _check(lib().kv_seq_free(self._h, seq))
+
+    def length(self, seq: int) -> int:
+        out = c_int32()
+        _check(lib().kv_seq_len(self._h, seq, byref(out)))
+        return out.value
+
+    def export(self, seqs, max_blocks, pad_value=-1, tables_out=None, lens_out=None):
+        """Block tables int32 [n, max_blocks] and lengths int32 [n] (host arrays)."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = int(seqs.shape[0])
+        tables = tables_out if tables_out is not None else np.empty((n, max_blocks), dtype=np.int32)
+        lens = lens_out if lens_out is not None else np.empty(n, dtype=np.int32)
+        if tables.shape != (n, max_blocks) or tables.dtype != np.int32 or not tables.flags.c_contiguous:
+            raise ValueError("tables_out must be C-contiguous int32 [n, max_blocks]")
+        if lens.shape != (n,) or lens.dtype != np.int32:
+            raise ValueError("lens_out must be int32 [n]")
+        _check(lib().kv_export_block_tables(self._h, seqs.ctypes.data, n, max_blocks, pad_value,
+                                            tables.ctypes.data, lens.ctypes.data))
+        return tables, lens
+
+    def stats(self) -> dict:
+        st = KVStats()
+        _check(lib().kv_allocator_stats(self._h, byref(st)))
+        return {name: getattr(st, name) for name, _ in KVStats._fields_}

@@ -1,0 +1,78 @@
+"""Build libpagedkv.so (HIP kernels for gfx950 + host allocator) in-tree.
+
+Usage: ``python -m paged_kv_cache_244_amd.build`` or ``build()`` from Python.
+Every call recompiles.  Only gfx950 code objects are produced.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libpagedkv.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+
+HIP_SOURCES = ["pa_decode.hip", "kv_cache_ops.hip"]
+HOST_SOURCES = ["allocator.cpp", "errors.cpp"]
+
+# Device code: gfx950 only; packed-fp32 instructions disabled (the compiler
+# would otherwise form v_pk_* fp32 ops from scalar float code).
+DEVICE_FLAGS = [
+    "--offload-arch=gfx950",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
+                f"-I{CSRC}"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm toolchain required to build libpagedkv.so)")
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(jobs: int = 4) -> str:
+    """Compile every source to an object, then link the shared library."""
+    obj_dir = os.path.join(ROOT, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    cc = hipcc()
+    cmds, objs = [], []
+    for src in HIP_SOURCES:
+        obj = os.path.join(obj_dir, src + ".o")
+        cmds.append([cc, "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + DEVICE_FLAGS + COMMON_FLAGS)
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(obj_dir, src + ".o")
+        cmds.append([cc, "-c", "-x", "c++", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS)
+        objs.append(obj)
+    procs = []
+    for cmd in cmds:
+        print("+", " ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd))
+        if len(procs) >= jobs:
+            if procs.pop(0).wait() != 0:
+                raise RuntimeError("compilation failed")
+    for p in procs:
+        if p.wait() != 0:
+            raise RuntimeError("compilation failed")
+    tmp = LIB_PATH + ".tmp"
+    _run([cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

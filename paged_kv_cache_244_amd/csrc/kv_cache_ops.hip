@@ -1,0 +1,162 @@
+// Slot-mapped K/V write and copy-on-write block copy for the paged KV cache.
+//
+// kv_cache_write: "Only 20.4% of your KV cache held actual tokens"
+// (blog.teqners.com), section "The page table, relocated into attention" — each
+// new token lands in the next slot of its request's last logical block, which
+// lives in some physical block of the pool.
+// kv_copy_blocks: same page, section "The part everyone forgets: pages enable
+// sharing, not just packing" — a write into a shared, partly filled block is
+// preceded by copying one whole block into a fresh one.
+//
+// Both are bit copies of fp16 data moved as 16-byte vectors; they are bound by
+// HBM bandwidth (2 bytes moved per byte copied), not by arithmetic.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "errors.h"
+#include "pagedkv.h"
+
+namespace {
+
+using pkv::fail;
+
+constexpr int kThreads = 256;
+
+bool supported_geometry(int32_t head_dim, int32_t block_size) {
+  bool d_ok = head_dim == 64 || head_dim == 128;
+  bool b_ok = block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64 ||
+              block_size == 128;
+  return d_ok && b_ok;
+}
+
+// One thread moves one 16-byte chunk (8 halves) of one token's K and V.
+// chunk index = token * chunks_per_token + head * chunks_per_row + d8.
+__global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, const uint4* __restrict__ k_new,
+    const uint4* __restrict__ v_new, const int64_t* __restrict__ slot_mapping, int64_t total_chunks,
+    int32_t chunks_per_token, int32_t chunks_per_row, int32_t block_size, int64_t num_slots) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total_chunks;
+       idx += stride) {
+    const int64_t token = idx / chunks_per_token;
+    const int32_t c = static_cast<int32_t>(idx - token * chunks_per_token);
+    const int64_t slot = slot_mapping[token];
+    if (slot < 0 || slot >= num_slots) continue;   // skip marker / guard against bad slots
+    const int64_t block = slot / block_size;
+    const int32_t offset = static_cast<int32_t>(slot - block * block_size);
+    const int32_t head = c / chunks_per_row;
+    const int32_t d8 = c - head * chunks_per_row;
+    // [block][head][offset][d8] in 16-byte units; chunks_per_token = heads * chunks_per_row.
+    const int64_t dst =
+        ((block * (chunks_per_token / chunks_per_row) + head) * block_size + offset) * chunks_per_row + d8;
+    k_cache[dst] = k_new[idx];
+    v_cache[dst] = v_new[idx];
+  }
+}
+
+constexpr int kMaxLayersPerLaunch = 32;
+
+struct LayerPtrs {
+  uint4* k[kMaxLayersPerLaunch];
+  uint4* v[kMaxLayersPerLaunch];
+};
+
+constexpr int kCopyUnroll = 4;
+
+// grid: x = chunk groups within one block, y = pair, z = layer * 2 + (0: K, 1: V).
+// A block is contiguous: heads * block_size * head_dim halves = chunks_per_block
+// 16-byte chunks.  Each thread issues kCopyUnroll loads before its stores.
+__global__ __launch_bounds__(kThreads) void kv_copy_blocks_kernel(
+    LayerPtrs layers, const int32_t* __restrict__ pairs, int32_t num_blocks,
+    int64_t chunks_per_block) {
+  const int32_t src = pairs[2 * blockIdx.y];
+  const int32_t dst = pairs[2 * blockIdx.y + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int layer = blockIdx.z >> 1;
+  uint4* base = (blockIdx.z & 1) ? layers.v[layer] : layers.k[layer];
+  const uint4* s = base + static_cast<int64_t>(src) * chunks_per_block;
+  uint4* d = base + static_cast<int64_t>(dst) * chunks_per_block;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * kThreads * kCopyUnroll + threadIdx.x;
+  uint4 tmp[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = first + u * kThreads;
+    if (i < chunks_per_block) tmp[u] = s[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t i = first + u * kThreads;
+    if (i < chunks_per_block) d[i] = tmp[u];
+  }
+}
+
+int hip_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int kv_cache_write(void* k_cache, void* v_cache, int32_t num_blocks, const void* k_new,
+                              const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "kv_cache_write: bad sizes (tokens %d, blocks %d, heads %d)",
+                num_tokens, num_blocks, num_kv_heads);
+  if (!supported_geometry(head_dim, block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write: head_dim %d / block_size %d not built",
+                head_dim, block_size);
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "kv_cache_write: NULL pointer");
+  const int32_t chunks_per_row = head_dim / 8;
+  const int32_t chunks_per_token = num_kv_heads * chunks_per_row;
+  const int64_t total = static_cast<int64_t>(num_tokens) * chunks_per_token;
+  const int64_t want_blocks = (total + kThreads - 1) / kThreads;
+  const unsigned grid = static_cast<unsigned>(want_blocks < 65536 * 16 ? want_blocks : 65536 * 16);
+  hipLaunchKernelGGL(kv_cache_write_kernel, dim3(grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), static_cast<const uint4*>(k_new),
+                     static_cast<const uint4*>(v_new), slot_mapping, total, chunks_per_token,
+                     chunks_per_row, block_size, static_cast<int64_t>(num_blocks) * block_size);
+  return hip_status("kv_cache_write launch");
+}
+
+extern "C" int kv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                              const int32_t* block_pairs, int32_t num_pairs, int32_t num_blocks,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              void* stream) {
+  if (num_layers < 0 || num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: bad sizes");
+  if (!supported_geometry(head_dim, block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "kv_copy_blocks: head_dim %d / block_size %d not built",
+                head_dim, block_size);
+  if (num_pairs == 0 || num_layers == 0) return PKV_OK;
+  if (!k_caches || !v_caches || !block_pairs)
+    return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: NULL pointer");
+  if (num_pairs > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: at most 65535 pairs per call (got %d)",
+                num_pairs);
+  const int64_t chunks_per_block = static_cast<int64_t>(num_kv_heads) * block_size * head_dim / 8;
+  const int64_t per_wg = static_cast<int64_t>(kThreads) * kCopyUnroll;
+  const unsigned gx = static_cast<unsigned>((chunks_per_block + per_wg - 1) / per_wg);
+  for (int32_t first = 0; first < num_layers; first += kMaxLayersPerLaunch) {
+    const int32_t n = num_layers - first < kMaxLayersPerLaunch ? num_layers - first
+                                                               : kMaxLayersPerLaunch;
+    LayerPtrs ptrs{};
+    for (int32_t l = 0; l < n; ++l) {
+      if (!k_caches[first + l] || !v_caches[first + l])
+        return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: NULL pool for layer %d", first + l);
+      ptrs.k[l] = static_cast<uint4*>(k_caches[first + l]);
+      ptrs.v[l] = static_cast<uint4*>(v_caches[first + l]);
+    }
+    hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3(gx, num_pairs, 2 * n), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), ptrs, block_pairs, num_blocks,
+                       chunks_per_block);
+    if (int rc = hip_status("kv_copy_blocks launch")) return rc;
+  }
+  return PKV_OK;
+}

@@ -1,0 +1,460 @@
+// Paged decode attention for gfx950: one query per request attends over the
+// request's cached tokens, fetched block by block through its block table.
+//
+// What is computed: "800 kilobytes per token" (shashforge.dev), section "The old
+// answer, imported honestly", and "Only 20.4% of your KV cache held actual
+// tokens" (blog.teqners.com), section "The page table, relocated into
+// attention": attention whose kernel walks a per-request table of fixed-size
+// physical blocks instead of one contiguous tensor.  The decode step is a
+// matrix-vector product per request and is bound by memory (teqners, section
+// "Why the KV cache is the thing that limits your batch"), so this kernel is an
+// HBM-streaming kernel: no MFMA, fp32 VALU arithmetic on fp16 data.
+//
+// Work decomposition (one wave64 per work item):
+//   item = (request, head tile, partition).  A head tile is GT query heads that
+//   share one KV head ("The KV cache is a systems problem", section "Calculate
+//   bytes per token before choosing a batch"), so every K/V tile is read once
+//   per tile.  A partition is part_tokens consecutive logical tokens
+//   (block-aligned); long contexts split into several partitions that run in
+//   parallel and are merged by pa_decode_reduce with a log-sum-exp combine.
+//   Up to four waves (four head tiles of one request and partition) form a
+//   workgroup; they share nothing but the block-table lines in cache.
+//
+// Lane layout for one (block, KV head) tile of B tokens x D halves, which is
+// contiguous in the pool: the tile is read as 16-byte chunks, chunk c = it*64 +
+// lane, so one wave-wide load covers TPL = 64 / (D/8) consecutive tokens, and
+// lane holds dims [(lane % LPT)*8, +8) of token it*TPL + lane / LPT.  Loads are
+// fully coalesced 1 KiB wave transactions.  A score is the sum over the LPT
+// lanes of a token row, reduced with DPP row permutations (no LDS).
+//
+// Softmax: each token row (the LPT lanes that share lane / LPT) keeps its own
+// running max, sum and output for the tokens it sees; rows are merged once at
+// the end of the partition with cross-lane shuffles.  Scores are kept in the
+// log2 domain (q . k * scale * log2 e) so exp2 (v_exp_f32) is used directly.
+// Masked tokens (past the context length) get score -inf and their value
+// vectors are replaced by zeros with a select, so stale or NaN slots never leak.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cstdint>
+
+#include "errors.h"
+#include "pagedkv.h"
+
+namespace {
+
+using pkv::fail;
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+struct DecodeParams {
+  float* out;                 // [S][Hq][D]
+  float* ws_o;                // [S][Hq][max_parts][D]  unnormalised partial outputs
+  float* ws_ml;               // [S][Hq][max_parts][2]  (running max in log2 units, sum)
+  const void* q;              // [S][Hq][D], fp32 or fp16
+  const uint4* k_cache;       // [NB][Hkv][B][D] fp16 viewed as 16-byte chunks
+  const uint4* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;              // num_q_heads / num_kv_heads
+  int32_t num_head_tiles;     // num_q_heads / GT
+  float scale_log2;           // scale * log2(e)
+  int32_t len_clamp;          // min(max_context_len, max_blocks_per_seq * B)
+  int32_t part_tokens;        // tokens per partition, multiple of B
+  int32_t max_parts;
+};
+
+// ---- cross-lane helpers -------------------------------------------------------
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the LPT lanes of one token row; every lane of the row gets the same
+// bits (each step adds two equal-order partial sums).
+template <int LPT>
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: pairs
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: quads
+  v += dpp<0x141>(v);   // row_half_mirror: 8 lanes
+  if constexpr (LPT == 16) v += dpp<0x140>(v);   // row_mirror: 16 lanes
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- query load -------------------------------------------------------------------
+
+template <bool kQF32>
+__device__ __forceinline__ void load_q8(const void* q, int64_t elem_offset, float (&dst)[8]) {
+  if constexpr (kQF32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q) + elem_offset);
+    float4 a = p[0], b = p[1];
+    dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
+    dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const _Float16*>(q) + elem_offset);
+    half8 h = __builtin_bit_cast(half8, p[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = static_cast<float>(h[i]);
+  }
+}
+
+// ---- the partition kernel -------------------------------------------------------
+
+template <int D, int B, int GT, bool kQF32>
+__global__ __launch_bounds__(256) void pa_decode_partition_kernel(DecodeParams p) {
+  constexpr int LPT = D / 8;               // lanes per token row
+  constexpr int TPL = kWave / LPT;         // token rows per wave-wide load
+  constexpr int NLD = B * D / 8 / kWave;   // wave-wide loads per (block, head) tile
+  constexpr int CHUNKS = B * D / 8;        // 16-byte chunks per tile
+  static_assert(NLD >= 1 && NLD * TPL == B, "tile must be a whole number of wave loads");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int tile = blockIdx.y * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (tile >= p.num_head_tiles) return;
+  const int seq = blockIdx.z;
+  const int part = blockIdx.x;
+  const int h0 = tile * GT;
+  const int kvh = h0 / p.group;
+  const int row = lane / LPT;
+  const int dchunk = lane % LPT;
+
+  int len = p.context_lens[seq];
+  len = len < 0 ? 0 : (len > p.len_clamp ? p.len_clamp : len);
+  const int t_begin = part * p.part_tokens;
+  if (t_begin >= len) {
+    if (part == 0 && row == 0) {             // empty context: defined as zeros
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float4* o = reinterpret_cast<float4*>(
+            p.out + (static_cast<int64_t>(seq) * p.num_q_heads + h0 + g) * D + dchunk * 8);
+        o[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+        o[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    return;
+  }
+  const int t_end = min(len, t_begin + p.part_tokens);
+  const int nparts = (len + p.part_tokens - 1) / p.part_tokens;
+
+  float qf[GT][8];
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+    load_q8<kQF32>(p.q, (static_cast<int64_t>(seq) * p.num_q_heads + h0 + g) * D + dchunk * 8,
+                   qf[g]);
+
+  float m[GT], l[GT], o[GT][8];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    m[g] = -FLT_MAX;
+    l[g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[g][k] = 0.f;
+  }
+
+  const int32_t* table = p.block_tables + static_cast<int64_t>(seq) * p.max_blocks_per_seq;
+  const int blk_begin = t_begin / B;
+  const int nblk = (t_end - 1) / B - blk_begin + 1;
+  const int64_t head_stride = CHUNKS;                         // chunks per (block, head)
+  const int64_t block_stride = static_cast<int64_t>(p.num_kv_heads) * CHUNKS;
+  const uint4* kbase = p.k_cache + kvh * head_stride + lane;
+  const uint4* vbase = p.v_cache + kvh * head_stride + lane;
+
+  int staged = 0;   // block ids of this partition, 64 at a time, one per lane
+  for (int j = 0; j < nblk; ++j) {
+    if ((j & (kWave - 1)) == 0) {
+      const int idx = blk_begin + j + lane;
+      staged = (j + lane < nblk) ? table[idx] : -1;
+    }
+    const int phys = __builtin_amdgcn_readlane(staged, j & (kWave - 1));
+    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.num_blocks)) continue;
+
+    const uint4* kt = kbase + phys * block_stride;
+    const uint4* vt = vbase + phys * block_stride;
+    uint4 kc[NLD], vc[NLD];
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) kc[it] = kt[it * kWave];
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) vc[it] = vt[it * kWave];
+
+    const int tok0 = (blk_begin + j) * B + row;
+    float s[GT][NLD];
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+      const bool valid = tok0 + it * TPL < t_end;
+      half8 kh = __builtin_bit_cast(half8, kc[it]);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc = fmaf(qf[g][k], static_cast<float>(kh[k]), acc);
+        acc = row_sum<LPT>(acc) * p.scale_log2;
+        s[g][it] = valid ? acc : -INFINITY;
+      }
+      if (!valid) vc[it] = make_uint4(0u, 0u, 0u, 0u);
+    }
+
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float mb = s[g][0];
+#pragma unroll
+      for (int it = 1; it < NLD; ++it) mb = fmaxf(mb, s[g][it]);
+      const float m_new = fmaxf(m[g], mb);
+      const float alpha = fast_exp2(m[g] - m_new);
+      l[g] *= alpha;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[g][k] *= alpha;
+#pragma unroll
+      for (int it = 0; it < NLD; ++it) {
+        const float pr = fast_exp2(s[g][it] - m_new);
+        l[g] += pr;
+        half8 vh = __builtin_bit_cast(half8, vc[it]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[g][k] = fmaf(pr, static_cast<float>(vh[k]), o[g][k]);
+      }
+      m[g] = m_new;
+    }
+  }
+
+  // Merge the TPL token rows: lanes with equal dchunk differ by multiples of LPT.
+#pragma unroll
+  for (int mask = LPT; mask < kWave; mask <<= 1) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const float m2 = shfl_xor(m[g], mask);
+      const float l2 = shfl_xor(l[g], mask);
+      const float mm = fmaxf(m[g], m2);
+      const float a = fast_exp2(m[g] - mm);
+      const float b = fast_exp2(m2 - mm);
+      l[g] = l[g] * a + l2 * b;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[g][k] = o[g][k] * a + shfl_xor(o[g][k], mask) * b;
+      m[g] = mm;
+    }
+  }
+
+  if (row != 0) return;
+  if (nparts == 1) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const float inv = 1.f / l[g];
+      float4* dst = reinterpret_cast<float4*>(
+          p.out + (static_cast<int64_t>(seq) * p.num_q_heads + h0 + g) * D + dchunk * 8);
+      dst[0] = make_float4(o[g][0] * inv, o[g][1] * inv, o[g][2] * inv, o[g][3] * inv);
+      dst[1] = make_float4(o[g][4] * inv, o[g][5] * inv, o[g][6] * inv, o[g][7] * inv);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      const int64_t slot =
+          (static_cast<int64_t>(seq) * p.num_q_heads + h0 + g) * p.max_parts + part;
+      float4* dst = reinterpret_cast<float4*>(p.ws_o + slot * D + dchunk * 8);
+      dst[0] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
+      dst[1] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
+      if (dchunk == 0) {
+        p.ws_ml[2 * slot] = m[g];
+        p.ws_ml[2 * slot + 1] = l[g];
+      }
+    }
+  }
+}
+
+// ---- cross-partition reduce ---------------------------------------------------------
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
+// grid (Hq, S), D threads; only requests with more than one partition do work.
+template <int D>
+__global__ __launch_bounds__(D) void pa_decode_reduce_kernel(DecodeParams p) {
+  const int h = blockIdx.x;
+  const int seq = blockIdx.y;
+  const int d = threadIdx.x;
+  int len = p.context_lens[seq];
+  len = len < 0 ? 0 : (len > p.len_clamp ? p.len_clamp : len);
+  const int nparts = (len + p.part_tokens - 1) / p.part_tokens;
+  if (nparts <= 1) return;
+  const int64_t base = (static_cast<int64_t>(seq) * p.num_q_heads + h) * p.max_parts;
+  float mmax = -FLT_MAX;
+  for (int q = 0; q < nparts; ++q) mmax = fmaxf(mmax, p.ws_ml[2 * (base + q)]);
+  float num = 0.f, den = 0.f;
+  for (int q = 0; q < nparts; ++q) {
+    const float w = fast_exp2(p.ws_ml[2 * (base + q)] - mmax);
+    den = fmaf(w, p.ws_ml[2 * (base + q) + 1], den);
+    num = fmaf(w, p.ws_o[(base + q) * D + d], num);
+  }
+  p.out[(static_cast<int64_t>(seq) * p.num_q_heads + h) * D + d] = num / den;
+}
+
+// ---- host dispatch ---------------------------------------------------------------------
+
+using KernelFn = void (*)(DecodeParams);
+
+template <int D, int B, int GT>
+KernelFn pick_q(bool qf32) {
+  return qf32 ? pa_decode_partition_kernel<D, B, GT, true> : pa_decode_partition_kernel<D, B, GT, false>;
+}
+
+template <int D, int B>
+KernelFn pick_gt(int gt, bool qf32) {
+  switch (gt) {
+    case 1: return pick_q<D, B, 1>(qf32);
+    case 2: return pick_q<D, B, 2>(qf32);
+    case 4: return pick_q<D, B, 4>(qf32);
+    default: return nullptr;
+  }
+}
+
+template <int D>
+KernelFn pick_b(int b, int gt, bool qf32) {
+  switch (b) {
+    case 8: return pick_gt<D, 8>(gt, qf32);
+    case 16: return pick_gt<D, 16>(gt, qf32);
+    case 32: return pick_gt<D, 32>(gt, qf32);
+    case 64: return pick_gt<D, 64>(gt, qf32);
+    case 128: return pick_gt<D, 128>(gt, qf32);
+    default: return nullptr;
+  }
+}
+
+KernelFn pick_kernel(int d, int b, int gt, bool qf32) {
+  if (d == 64) return pick_b<64>(b, gt, qf32);
+  if (d == 128) return pick_b<128>(b, gt, qf32);
+  return nullptr;
+}
+
+int head_tile(int group) {
+  if (group % 4 == 0) return 4;
+  if (group % 2 == 0) return 2;
+  return 1;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int64_t parts_for(int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0 || max_context_len <= 0) return 1;
+  return (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+}
+
+size_t workspace_bytes_for(int32_t S, int32_t Hq, int32_t D, int64_t parts) {
+  if (parts <= 1) return 0;
+  const size_t n = static_cast<size_t>(S) * Hq * parts;
+  return align256(n * D * sizeof(float)) + align256(n * 2 * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                           int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return workspace_bytes_for(num_seqs, num_q_heads, head_dim,
+                             parts_for(max_context_len, partition_size));
+}
+
+extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                         const void* v_cache, int32_t num_blocks, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, float scale, int32_t max_context_len,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode: bad sizes");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "pa_decode: num_q_heads %d not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (q_dtype != PKV_F32 && q_dtype != PKV_F16)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode: q_dtype %d unknown", q_dtype);
+  if (partition_size % (block_size > 0 ? block_size : 1) != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode: partition_size %d not a multiple of block_size %d",
+                partition_size, block_size);
+  if (num_seqs > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode: at most 65535 sequences per call");
+  const int gt = head_tile(num_q_heads / num_kv_heads);
+  KernelFn fn = pick_kernel(head_dim, block_size, gt, q_dtype == PKV_F32);
+  if (!fn)
+    return fail(PKV_ERR_UNSUPPORTED, "pa_decode: head_dim %d / block_size %d not built", head_dim,
+                block_size);
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode: NULL pointer");
+
+  int64_t clamp64 = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  if (clamp64 > max_context_len) clamp64 = max_context_len;
+  const int32_t len_clamp = static_cast<int32_t>(clamp64);
+  int32_t part_tokens;
+  int64_t parts;
+  if (partition_size == 0) {
+    const int64_t whole = (static_cast<int64_t>(len_clamp > 0 ? len_clamp : 1) + block_size - 1) /
+                          block_size * block_size;
+    part_tokens = static_cast<int32_t>(whole);
+    parts = 1;
+  } else {
+    part_tokens = partition_size;
+    parts = parts_for(len_clamp, partition_size);
+  }
+  if (parts > 0x7fffffff) return fail(PKV_ERR_INVALID_ARG, "pa_decode: too many partitions");
+
+  DecodeParams prm{};
+  prm.out = out;
+  prm.q = q;
+  prm.k_cache = static_cast<const uint4*>(k_cache);
+  prm.v_cache = static_cast<const uint4*>(v_cache);
+  prm.block_tables = block_tables;
+  prm.context_lens = context_lens;
+  prm.num_blocks = num_blocks;
+  prm.max_blocks_per_seq = max_blocks_per_seq;
+  prm.num_q_heads = num_q_heads;
+  prm.num_kv_heads = num_kv_heads;
+  prm.group = num_q_heads / num_kv_heads;
+  prm.num_head_tiles = num_q_heads / gt;
+  prm.scale_log2 = scale * kLog2e;
+  prm.len_clamp = len_clamp;
+  prm.part_tokens = part_tokens;
+  prm.max_parts = static_cast<int32_t>(parts);
+
+  if (parts > 1) {
+    const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, parts);
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed (got %zu)", need,
+                  workspace ? workspace_bytes : static_cast<size_t>(0));
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(PKV_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
+    const size_t n = static_cast<size_t>(num_seqs) * num_q_heads * parts;
+    prm.ws_o = static_cast<float*>(workspace);
+    prm.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         align256(n * head_dim * sizeof(float)));
+  }
+
+  const int waves = prm.num_head_tiles >= 4 ? 4 : prm.num_head_tiles;
+  const unsigned gy = static_cast<unsigned>((prm.num_head_tiles + waves - 1) / waves);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(parts), gy, num_seqs), dim3(kWave * waves), 0,
+                     st, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode launch: %s", hipGetErrorString(e));
+  if (parts > 1) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL(pa_decode_reduce_kernel<64>, dim3(num_q_heads, num_seqs), dim3(64), 0, st, prm);
+    else
+      hipLaunchKernelGGL(pa_decode_reduce_kernel<128>, dim3(num_q_heads, num_seqs), dim3(128), 0, st,
+                         prm);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode reduce launch: %s", hipGetErrorString(e));
+  }
+  return PKV_OK;
+}

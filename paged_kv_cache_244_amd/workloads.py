@@ -38,6 +38,7 @@ already in the cache, token ``L - 1`` is written by the step and then attended.
 from __future__ import annotations
 
 import math
+import zlib
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
@@ -99,6 +100,18 @@ class DecodeWorkload:
     def tokens(self, i: int):
         lo, hi = self.offsets[i], self.offsets[i + 1]
         return self.k_tokens[lo:hi], self.v_tokens[lo:hi]
+
+
+def step_inputs(w: DecodeWorkload, step: int):
+    """New-token K, V ``[S, Hkv, D]`` and q ``[S, Hq, D]`` for decode step ``step`` >= 1
+    after the workload's own step (step 0 uses the workload's last tokens and q)."""
+    child = np.random.SeedSequence([zlib.crc32(w.name.encode()), step])
+    sk, sv, sq = child.spawn(3)
+    S = w.num_seqs
+    k = _normal(sk, (S, w.num_kv_heads, w.head_dim), np.float16)
+    v = _normal(sv, (S, w.num_kv_heads, w.head_dim), np.float16)
+    q = _normal(sq, (S, w.num_q_heads, w.head_dim), w.q_dtype)
+    return k, v, q
 
 
 def _pool_blocks(lengths, block_size, slack):
@@ -211,6 +224,17 @@ def parallel_sampling(seed: int = 3, num_prompts: int = 16, samples: int = 8, st
     v = _normal(s_v, (total, 40, 128), np.float16)
     return SamplingWorkload("parallel_sampling", 40, 40, 128, block_size, 1.0 / math.sqrt(128),
                             plen, samples, steps, num_blocks, order, k, v, s_steps)
+
+
+def with_block_size(w: DecodeWorkload, block_size: int, seed: int = 4) -> DecodeWorkload:
+    """The same requests and values stored with another block size: a new pool size
+    (1.2x the blocks needed) and a new free-list permutation drawn for that size."""
+    num_blocks = _pool_blocks(w.lengths, block_size, 1.2)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, block_size])))
+    order = g.permutation(num_blocks).astype(np.int32)
+    return DecodeWorkload(f"{w.name.split('_b')[0]}_b{block_size}", w.num_q_heads, w.num_kv_heads,
+                          w.head_dim, block_size, w.q_dtype, w.scale, w.lengths, num_blocks, order,
+                          w.k_tokens, w.v_tokens, w.q, w.offsets, w.partition_size)
 
 
 WORKLOADS = {
