@@ -151,16 +151,14 @@ def main():
     step_bytes = []
 
     def step(t, timed_slot=None):
-        s = cache.reserve_step(seqs)
+        s, batch = cache.decode_step(seqs, max_blocks)
         cache.write(s, step_k[t], step_v[t])
-        tables, lens, max_len = cache.block_tables(seqs, max_blocks)
         if timed_slot is not None:
             ev[timed_slot][0].record(stream)
-        cache.attend(step_q[t], tables, lens, max_len, w.scale, partition_size=args.partition,
-                     out=out)
+        cache.attend(step_q[t], batch, w.scale, partition_size=args.partition, out=out)
         if timed_slot is not None:
             ev[timed_slot][1].record(stream)
-        return max_len
+        return batch.max_len
 
     lengths = w.lengths.astype(np.int64) - 1
     for t in range(args.warmup):

@@ -133,6 +133,11 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *   block_tables   : device int32 [num_seqs][max_blocks_per_seq]; entries past
  *                    ceil(L / block_size) are never read.
  *   context_lens   : device int32 [num_seqs], tokens attended per request.
+ *   work_order     : device int32 [num_seqs], a permutation of 0..num_seqs-1
+ *                    giving the order in which requests are scheduled onto the
+ *                    GPU (longest context first balances the compute units
+ *                    best), or NULL for 0, 1, 2, ...  Only the timing depends
+ *                    on it; an entry outside [0, num_seqs) is skipped.
  *   max_context_len: an upper bound on every context length (sizes the grid).
  *   partition_size : 0 = one pass per request; otherwise a multiple of
  *                    block_size: each request's context is split into
@@ -144,7 +149,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
 int pa_decode(float* out, const void* q, int32_t q_dtype,
               const void* k_cache, const void* v_cache, int32_t num_blocks,
               const int32_t* block_tables, int32_t max_blocks_per_seq,
-              const int32_t* context_lens, int32_t num_seqs,
+              const int32_t* context_lens, const int32_t* work_order, int32_t num_seqs,
               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               float scale, int32_t max_context_len, int32_t partition_size,
               void* workspace, size_t workspace_bytes, void* stream);
@@ -200,6 +205,8 @@ int kv_batch_append(kv_allocator* a, const int32_t* seqs, int32_t num_seqs, int6
                     int32_t* cow_pairs_out, int32_t* n_cow_out);
 int kv_seq_free(kv_allocator* a, int32_t seq);
 int kv_seq_len(const kv_allocator* a, int32_t seq, int32_t* len_out);
+/* Lengths of n sequences in one call: host int32 lens_out [n]. */
+int kv_seq_lens(const kv_allocator* a, const int32_t* seqs, int32_t n, int32_t* lens_out);
 /* Host int32 tables_out [n][max_blocks_per_seq] (unused entries = pad_value) and
  * lens_out [n].  PKV_ERR_INVALID_ARG if a sequence holds more blocks. */
 int kv_export_block_tables(const kv_allocator* a, const int32_t* seqs, int32_t n,

@@ -64,8 +64,8 @@ _SIGNATURES = {
                                  c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
-                            c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_float,
-                            c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
+                            c_int32, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+                            c_float, c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
     "kv_allocator_create": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_void_p)]),
     "kv_allocator_destroy": (None, [c_void_p]),
     "kv_seq_create": (c_int32, [c_void_p, POINTER(c_int32)]),
@@ -74,6 +74,7 @@ _SIGNATURES = {
     "kv_batch_append": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, POINTER(c_int32)]),
     "kv_seq_free": (c_int32, [c_void_p, c_int32]),
     "kv_seq_len": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
+    "kv_seq_lens": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p]),
     "kv_export_block_tables": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
                                          c_void_p]),
     "kv_allocator_stats": (c_int32, [c_void_p, POINTER(KVStats)]),
@@ -176,17 +177,25 @@ def kv_copy_blocks(k_caches, v_caches, block_pairs, stream=None):
                                 int(block_pairs.shape[0]), nb, hkv, d, bs, _stream(stream)))
 
 
+def _order(work_order, s):
+    torch = _torch()
+    if tuple(work_order.shape) != (s,):
+        raise ValueError("work_order must be [S]")
+    return _dev(work_order, torch.int32, "work_order")
+
+
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):
     return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
                                               partition_size))
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-              partition_size=512, workspace=None, stream=None):
+              partition_size=512, workspace=None, stream=None, work_order=None):
     """Decode attention: out[S, Hq, D] fp32 from q[S, Hq, D] (fp32 or fp16) via the block tables.
 
     ``workspace`` is a device uint8 tensor of at least ``pa_decode_workspace_size`` bytes
-    (needed only when a request may span more than one partition).
+    (needed only when a request may span more than one partition).  ``work_order`` is an
+    optional device int32 [S] permutation: the order in which requests are scheduled.
     """
     torch = _torch()
     nb, hkv, bs, d = _pool_geometry(k_cache, v_cache)
@@ -209,7 +218,9 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _dev(out, torch.float32, "out"), _dev(q, q.dtype, "q"), qd,
         _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"), nb,
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
-        _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, bs, float(scale),
+        _dev(context_lens, torch.int32, "context_lens"),
+        c_void_p(None) if work_order is None else _order(work_order, s), s, hq, hkv, d, bs,
+        float(scale),
         int(max_context_len), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
 
 
@@ -279,6 +290,13 @@ class BlockAllocator:
         out = c_int32()
         _check(lib().kv_seq_len(self._h, seq, byref(out)))
         return out.value
+
+    def lengths(self, seqs):
+        """Lengths of the listed sequences (host int32 array), one library call."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        lens = np.empty(seqs.shape[0], dtype=np.int32)
+        _check(lib().kv_seq_lens(self._h, seqs.ctypes.data, int(seqs.shape[0]), lens.ctypes.data))
+        return lens
 
     def export(self, seqs, max_blocks, pad_value=-1, tables_out=None, lens_out=None):
         """Block tables int32 [n, max_blocks] and lengths int32 [n] (host arrays)."""

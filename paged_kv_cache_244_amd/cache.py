@@ -9,9 +9,10 @@ kernels.  The pattern of one decode step, all on one HIP stream:
     kv_cache_write(slots, k_new, v_new)  (per layer)
     pa_decode(q, block tables)           (per layer)
 
-Host-to-device uploads go through a small ring of pinned buffers so the host
-can run ahead of the device; a ring slot is reused only after the copy that
-last read it has completed (an event wait that normally returns at once).
+Host-to-device uploads of one step (slots, copy pairs, tables, lengths,
+schedule) are packed into one pinned buffer and sent with a single copy: each
+small copy is a serialised operation on the stream, so one copy instead of
+four or five shortens every step.
 """
 
 from __future__ import annotations
@@ -22,34 +23,53 @@ import torch
 from . import _lib
 
 
-class _PinnedRing:
-    """Pinned host staging buffers for asynchronous uploads."""
+class _Staging:
+    """Uploads several small host arrays with ONE host-to-device copy.
 
-    def __init__(self, nbytes: int, depth: int = 8):
-        self.bufs = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
+    The arrays are packed (16-byte aligned) into a pinned host buffer taken from a
+    ring, copied asynchronously into a device buffer, and returned as typed views
+    of that buffer.  A pinned ring slot is reused only after the copy that last
+    read it has completed; the device buffer is reused in stream order, so views
+    stay valid until the next ``upload`` on the same stream.
+    """
+
+    def __init__(self, device, depth: int = 4, nbytes: int = 1 << 20):
+        self.device = device
+        self.host = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
         self.events = [None] * depth
         self.next = 0
+        self.dev = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
-    def upload(self, array: np.ndarray, out: torch.Tensor, stream) -> torch.Tensor:
-        array = np.ascontiguousarray(array)
-        nbytes = array.nbytes
-        if nbytes == 0:
-            return out
+    def upload(self, arrays, stream):
+        arrays = [np.ascontiguousarray(a) for a in arrays]
+        offsets, total = [], 0
+        for a in arrays:
+            offsets.append(total)
+            total += (a.nbytes + 15) // 16 * 16
         i = self.next
-        self.next = (i + 1) % len(self.bufs)
-        if self.bufs[i].numel() < nbytes:
-            if self.events[i] is not None:
-                self.events[i].synchronize()
-            self.bufs[i] = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
-        elif self.events[i] is not None:
+        self.next = (i + 1) % len(self.host)
+        if self.events[i] is not None:
             self.events[i].synchronize()
-        host = self.bufs[i][:nbytes]
-        host.numpy()[:] = array.view(np.uint8).reshape(-1)
-        out.view(torch.uint8).view(-1)[:nbytes].copy_(host, non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        self.events[i] = ev
-        return out
+        if self.host[i].numel() < total:
+            self.host[i] = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+        if self.dev.numel() < total:
+            self.dev = torch.empty(total, dtype=torch.uint8, device=self.device)
+        buf = self.host[i].numpy()
+        for a, off in zip(arrays, offsets):
+            buf[off:off + a.nbytes] = a.reshape(-1).view(np.uint8)
+        if total:
+            self.dev[:total].copy_(self.host[i][:total], non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            self.events[i] = ev
+        views = []
+        for a, off in zip(arrays, offsets):
+            t = self.dev[off:off + a.nbytes].view(_TORCH_DTYPE[a.dtype.str[1:]])
+            views.append(t.view(a.shape))
+        return views
+
+
+_TORCH_DTYPE = {"i4": torch.int32, "i8": torch.int64, "f4": torch.float32, "f2": torch.float16}
 
 
 class PagedKVCache:
@@ -70,8 +90,7 @@ class PagedKVCache:
                   for _ in range(num_layers)]
         self.v = [torch.full(shape, fill, dtype=torch.float16, device=self.device)
                   for _ in range(num_layers)]
-        self._ring = _PinnedRing(1 << 20)
-        self._dev_bufs = {}
+        self._staging = _Staging(self.device)
         self._workspace = None
 
     # -- sequences -------------------------------------------------------------
@@ -88,28 +107,18 @@ class PagedKVCache:
         return self.alloc.length(seq)
 
     # -- device staging -------------------------------------------------------
-    def _buf(self, name, numel, dtype):
-        t = self._dev_bufs.get(name)
-        if t is None or t.numel() < numel or t.dtype != dtype:
-            t = torch.empty(max(numel, 1), dtype=dtype, device=self.device)
-            self._dev_bufs[name] = t
-        return t[:numel]
+    def upload(self, *arrays):
+        """Copy host arrays to the device in one transfer; returns device views."""
+        return self._staging.upload(arrays, self.stream)
 
-    def upload(self, name, array: np.ndarray, dtype) -> torch.Tensor:
-        out = self._buf(name, array.size, dtype)
-        return self._ring.upload(array, out, self.stream).view(array.shape)
-
-    def _copy_pairs(self, pairs: np.ndarray):
-        if len(pairs):
-            dev = self.upload("pairs", np.ascontiguousarray(pairs, dtype=np.int32), torch.int32)
-            _lib.kv_copy_blocks(self.k, self.v, dev, stream=self.stream)
+    def _copy_pairs_dev(self, pairs_dev):
+        if pairs_dev is not None and pairs_dev.shape[0]:
+            _lib.kv_copy_blocks(self.k, self.v, pairs_dev, stream=self.stream)
 
     # -- reserving slots (copy-on-write copies are issued here) -------------------
     def reserve(self, seq: int, n: int) -> torch.Tensor:
         """Slots for ``n`` more tokens of one sequence, as a device int64 tensor."""
-        slots, pairs = self.alloc.append(seq, n)
-        self._copy_pairs(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
-        return self.upload("slots", slots, torch.int64)
+        return self.reserve_many([seq], [n])
 
     def reserve_many(self, seqs, counts) -> torch.Tensor:
         """Slots for ``counts[i]`` more tokens of each ``seqs[i]`` (e.g. a batched prefill),
@@ -119,31 +128,61 @@ class PagedKVCache:
             slots, pairs = self.alloc.append(int(seq), int(n))
             all_slots.append(slots)
             all_pairs.extend(pairs)
-        self._copy_pairs(np.asarray(all_pairs, dtype=np.int32).reshape(-1, 2))
         flat = np.concatenate(all_slots) if all_slots else np.empty(0, dtype=np.int64)
-        return self.upload("many_slots", flat, torch.int64)
+        pairs = np.asarray(all_pairs, dtype=np.int32).reshape(-1, 2)
+        slots_dev, pairs_dev = self.upload(flat.astype(np.int64), pairs)
+        self._copy_pairs_dev(pairs_dev)
+        return slots_dev
 
     def reserve_step(self, seqs) -> torch.Tensor:
         """One slot per listed sequence (a decode step); device int64 [len(seqs)]."""
         slots, pairs = self.alloc.append_batch(seqs)
-        self._copy_pairs(pairs)
-        return self.upload("step_slots", slots, torch.int64)
+        slots_dev, pairs_dev = self.upload(slots, pairs)
+        self._copy_pairs_dev(pairs_dev)
+        return slots_dev
+
+    def decode_step(self, seqs, max_blocks=None, longest_first=True):
+        """One decode step's host work with a single upload: reserve one slot per
+        sequence (issuing copy-on-write copies), then export tables, lengths and the
+        schedule.  Returns (device slots, DecodeBatch)."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        slots, pairs = self.alloc.append_batch(seqs)
+        tables, lens, max_len, order = self._tables(seqs, max_blocks, None, longest_first)
+        arrays = [slots, pairs, tables, lens] + ([order] if order is not None else [])
+        views = self.upload(*arrays)
+        self._copy_pairs_dev(views[1])
+        batch = DecodeBatch(views[2], views[3], max_len, views[4] if order is not None else None,
+                            lens)
+        return views[0], batch
 
     def write(self, slots: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, layer: int = 0):
         _lib.kv_cache_write(self.k[layer], self.v[layer], k_new, v_new, slots, stream=self.stream)
 
     # -- attention ---------------------------------------------------------------
-    def block_tables(self, seqs, max_blocks=None, pad_value=None):
-        """Device int32 tables [n, max_blocks], device int32 lengths [n], host max length."""
-        seqs = np.asarray(seqs, dtype=np.int32)
-        lens_host = np.array([self.alloc.length(int(s)) for s in seqs], dtype=np.int32)
-        max_len = int(lens_host.max()) if len(lens_host) else 0
+    def _tables(self, seqs, max_blocks, pad_value, longest_first):
+        lens = self.alloc.lengths(seqs)
+        max_len = int(lens.max()) if len(lens) else 0
         if max_blocks is None:
             max_blocks = max(1, -(-max_len // self.block_size))
         pad = self.num_blocks if pad_value is None else pad_value
-        tables, lens = self.alloc.export(seqs, max_blocks, pad)
-        return (self.upload("tables", tables, torch.int32), self.upload("lens", lens, torch.int32),
-                max_len)
+        tables, _ = self.alloc.export(seqs, max_blocks, pad)
+        order = None
+        if longest_first and len(lens) > 1:
+            order = np.argsort(-lens, kind="stable").astype(np.int32)
+        return tables, lens, max_len, order
+
+    def batch(self, seqs, max_blocks=None, pad_value=None, longest_first=True) -> "DecodeBatch":
+        """Upload the block tables, lengths and schedule of ``seqs`` for one decode launch.
+
+        The returned device tensors stay valid until the next upload.
+        """
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        tables, lens, max_len, order = self._tables(seqs, max_blocks, pad_value, longest_first)
+        if order is None:
+            t, l_ = self.upload(tables, lens)
+            return DecodeBatch(t, l_, max_len, None, lens)
+        t, l_, o = self.upload(tables, lens, order)
+        return DecodeBatch(t, l_, max_len, o, lens)
 
     def workspace(self, num_seqs, num_q_heads, max_context_len, partition_size):
         need = _lib.pa_decode_workspace_size(num_seqs, num_q_heads, self.head_dim, max_context_len,
@@ -154,11 +193,25 @@ class PagedKVCache:
             self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._workspace
 
-    def attend(self, q, tables, lens, max_context_len, scale, partition_size=512, layer=0, out=None):
+    def attend(self, q, batch: "DecodeBatch", scale, partition_size=512, layer=0, out=None):
         s, hq, d = q.shape
         if out is None:
             out = torch.empty((s, hq, d), dtype=torch.float32, device=self.device)
-        ws = self.workspace(s, hq, max_context_len, partition_size)
-        _lib.pa_decode(out, q, self.k[layer], self.v[layer], tables, lens, scale, max_context_len,
-                       partition_size=partition_size, workspace=ws, stream=self.stream)
+        ws = self.workspace(s, hq, batch.max_len, partition_size)
+        _lib.pa_decode(out, q, self.k[layer], self.v[layer], batch.tables, batch.lens, scale,
+                       batch.max_len, partition_size=partition_size, workspace=ws,
+                       stream=self.stream, work_order=batch.order)
         return out
+
+
+class DecodeBatch:
+    """Device views of one decode launch: tables, lengths, schedule; host lengths."""
+
+    __slots__ = ("tables", "lens", "max_len", "order", "lens_host")
+
+    def __init__(self, tables, lens, max_len, order, lens_host):
+        self.tables = tables
+        self.lens = lens
+        self.max_len = max_len
+        self.order = order
+        self.lens_host = lens_host

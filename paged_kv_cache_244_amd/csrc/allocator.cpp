@@ -253,6 +253,18 @@ int kv_seq_len(const kv_allocator* a, int32_t seq, int32_t* len_out) {
   return PKV_OK;
 }
 
+int kv_seq_lens(const kv_allocator* a, const int32_t* seqs, int32_t n, int32_t* lens_out) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "allocator is NULL");
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (n > 0 && (!seqs || !lens_out)) return fail(PKV_ERR_INVALID_ARG, "NULL array");
+  for (int32_t i = 0; i < n; ++i) {
+    if (int rc = check_seq(a, seqs[i])) return rc;
+    if (a->seqs[seqs[i]].length > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "length overflows int32");
+  }
+  for (int32_t i = 0; i < n; ++i) lens_out[i] = static_cast<int32_t>(a->seqs[seqs[i]].length);
+  return PKV_OK;
+}
+
 int kv_export_block_tables(const kv_allocator* a, const int32_t* seqs, int32_t n,
                            int32_t max_blocks_per_seq, int32_t pad_value, int32_t* tables_out,
                            int32_t* lens_out) {

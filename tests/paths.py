@@ -56,7 +56,7 @@ def run_oracle(w, sample=None):
     return {"k": kp, "v": vp, "tables": tables, "lens": np.array(lens), "out": out}
 
 
-def run_gpu(w, partition_size, cache_obj=None, out_only=False):
+def run_gpu(w, partition_size, cache_obj=None, out_only=False, longest_first=True):
     """HIP path: returns pools, tables, lengths (host copies) and the fp32 output."""
     import torch
 
@@ -75,15 +75,15 @@ def run_gpu(w, partition_size, cache_obj=None, out_only=False):
     if len(step_idx):
         c.write(step_slots, torch.from_numpy(w.k_tokens[step_idx]).to(dev),
                 torch.from_numpy(w.v_tokens[step_idx]).to(dev))
-    tables, lens, max_len = c.block_tables(seqs, max_blocks_for(w))
+    batch = c.batch(seqs, max_blocks_for(w), longest_first=longest_first)
     q = torch.from_numpy(w.q).to(dev)
-    out = c.attend(q, tables, lens, max_len, w.scale, partition_size=partition_size)
+    out = c.attend(q, batch, w.scale, partition_size=partition_size)
     torch.cuda.synchronize()
-    res = {"out": out.cpu().numpy(), "cache": c, "seqs": seqs, "tables_dev": tables,
-           "lens_dev": lens, "max_len": max_len, "q_dev": q}
+    res = {"out": out.cpu().numpy(), "cache": c, "seqs": seqs, "batch": batch, "q_dev": q}
     if not out_only:
         res.update(k=c.k[0].cpu().numpy(), v=c.v[0].cpu().numpy(),
-                   tables=tables.cpu().numpy().astype(np.int64), lens=lens.cpu().numpy())
+                   tables=batch.tables.cpu().numpy().astype(np.int64),
+                   lens=batch.lens.cpu().numpy())
     return res
 
 

@@ -54,8 +54,8 @@ def test_host_argument_errors_without_gpu():
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
 
     def decode(d=128, hq=40, hkv=40, bs=16, part=0, maxlen=64, ptr=fake, ws=None, ws_bytes=0):
-        return lib.pa_decode(ptr, ptr, 1, ptr, ptr, 16, ptr, 4, ptr, 1, hq, hkv, d, bs, 1.0, maxlen,
-                             part, ws, ws_bytes, None)
+        return lib.pa_decode(ptr, ptr, 1, ptr, ptr, 16, ptr, 4, ptr, None, 1, hq, hkv, d, bs, 1.0,
+                             maxlen, part, ws, ws_bytes, None)
 
     assert decode(d=96) == _lib.PKV_ERR_UNSUPPORTED and b"head_dim" in lib.pkv_last_error()
     assert decode(bs=24) == _lib.PKV_ERR_INVALID_ARG or decode(bs=24) == _lib.PKV_ERR_UNSUPPORTED

@@ -76,6 +76,7 @@ class Pair:
             assert ct.tolist() == mt and cl.tolist() == ml
         for s in self.live:
             assert self.c.length(s) == self.m.length(s)
+        assert self.c.lengths(self.live).tolist() == [self.m.length(s) for s in self.live]
 
 
 def test_random_op_sequences_match_model():

@@ -87,6 +87,25 @@ def test_placement_does_not_change_bits():
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def test_work_order_does_not_change_bits():
+    """The schedule (natural, longest first, a random permutation) changes timing only."""
+    import torch
+
+    _announce("work order invariance")
+    w = workloads.custom("order", 6, [900, 3, 40, 2000, 129, 0, 600], 8, 2, 128, 16)
+    ref = paths.run_oracle(w)
+    for partition in (0, 256):
+        natural = paths.run_gpu(w, partition, longest_first=False)
+        longest = paths.run_gpu(w, partition, longest_first=True)
+        assert np.array_equal(natural["out"].view(np.uint32), longest["out"].view(np.uint32))
+        c, batch = longest["cache"], longest["batch"]
+        perm = torch.from_numpy(np.random.default_rng(3).permutation(w.num_seqs).astype(np.int32))
+        batch.order = perm.cuda()
+        again = c.attend(longest["q_dev"], batch, w.scale, partition_size=partition).cpu().numpy()
+        assert np.array_equal(again.view(np.uint32), natural["out"].view(np.uint32))
+        paths.assert_attention_close(natural["out"], ref["out"])
+
+
 def test_copy_blocks_multi_layer_bit_exact():
     import torch
 
