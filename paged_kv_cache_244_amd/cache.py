@@ -193,8 +193,13 @@ class PagedKVCache:
             self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._workspace
 
-    def attend(self, q, batch: "DecodeBatch", scale, partition_size=512, layer=0, out=None):
+    def attend(self, q, batch: "DecodeBatch", scale, partition_size="auto", layer=0, out=None):
+        """Decode attention for ``batch``; ``partition_size`` "auto" applies
+        ``choose_partition`` to the batch's host-side lengths."""
         s, hq, d = q.shape
+        if partition_size == "auto":
+            partition_size = choose_partition(batch.lens_host, hq, self.num_kv_heads,
+                                              self.block_size)
         if out is None:
             out = torch.empty((s, hq, d), dtype=torch.float32, device=self.device)
         ws = self.workspace(s, hq, batch.max_len, partition_size)
@@ -202,6 +207,30 @@ class PagedKVCache:
                        batch.max_len, partition_size=partition_size, workspace=ws,
                        stream=self.stream, work_order=batch.order)
         return out
+
+
+def head_tile(num_q_heads: int, num_kv_heads: int) -> int:
+    """Query heads one wave serves (the library's own choice for this grouping)."""
+    group = num_q_heads // num_kv_heads
+    return 4 if group % 4 == 0 else (2 if group % 2 == 0 else 1)
+
+
+def choose_partition(lens_host, num_q_heads, num_kv_heads, block_size, gpu_waves=2048) -> int:
+    """Split-context policy (measured on MI355X): one pass per request when there are
+    enough (request, head tile) work items to fill the GPU; otherwise the largest of
+    1024 / 512 tokens that yields at least half a GPU's worth of items."""
+    lens = np.asarray(lens_host, dtype=np.int64)
+    if lens.size == 0:
+        return 0
+    tiles = num_q_heads // head_tile(num_q_heads, num_kv_heads)
+    if lens.size * tiles >= gpu_waves and int(lens.max()) <= 8192:
+        return 0
+    for part in (1024, 512):
+        if part % block_size:
+            continue
+        if tiles * int(np.sum((lens + part - 1) // part)) >= gpu_waves // 2:
+            return part
+    return max(512, block_size)
 
 
 class DecodeBatch:

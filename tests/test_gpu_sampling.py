@@ -1,0 +1,119 @@
+"""Parallel sampling with shared prompt blocks, end to end on the GPU.
+
+16 prompts of 64..512 tokens are forked into 8 samples each; the prompt's own
+reference is dropped, so its blocks are shared 8 ways.  Each of 128 decode
+steps appends one token per sample (the first step copies the partly filled
+last prompt block for 7 of 8 samples of every prompt whose length is not a
+multiple of 16), writes it, and runs decode attention.  The HIP path (C++
+allocator + kv_copy_blocks + kv_cache_write + pa_decode) is checked against:
+
+* the oracle allocator model: identical slots, copy pairs and tables (bit-exact);
+* the oracle pools (oracle write + copy applied to the same inputs): identical
+  bytes over the whole pool at chosen steps;
+* each sample's logical view, gathered through its table, equals its prompt
+  followed by its own tokens (the other readers' view survives copy-on-write);
+* the fp64 oracle attention for sampled rows, within the stated tolerance.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import alloc_model, attention, cache as oc
+from paged_kv_cache_244_amd import workloads
+from tests import paths
+
+pytestmark = pytest.mark.gpu
+
+CHECK_POOLS = {0, 16, 127}
+CHECK_ATTN = {0, 1, 2, 15, 16, 17, 63, 127}
+
+
+def test_parallel_sampling_128_steps():
+    import torch
+
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    print("\n[case] parallel sampling: 16 prompts x 8 samples, 128 steps", flush=True)
+    w = workloads.parallel_sampling()
+    B, n = w.block_size, w.samples
+    offs = w.prompt_offsets
+    dev = torch.device("cuda")
+
+    # --- HIP path
+    c = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, B, initial_order=w.initial_order)
+    prompts = [c.new_sequence() for _ in range(w.num_prompts)]
+    slots = c.reserve_many(prompts, w.prompt_lengths)
+    c.write(slots, torch.from_numpy(w.prompt_k).to(dev), torch.from_numpy(w.prompt_v).to(dev))
+    samples = []
+    for p in prompts:
+        samples.extend(c.fork(p) for _ in range(n))
+        c.free(p)
+
+    # --- oracle
+    m = alloc_model.AllocatorModel(w.num_blocks, B, w.initial_order)
+    shape = (w.num_blocks, w.num_kv_heads, B, w.head_dim)
+    kp = np.full(shape, np.nan, dtype=np.float16)
+    vp = np.full(shape, np.nan, dtype=np.float16)
+    m_prompts = [m.create() for _ in range(w.num_prompts)]
+    m_slots = []
+    for s, L in zip(m_prompts, w.prompt_lengths):
+        m_slots.extend(m.append(s, int(L))[0])
+    oc.write_slots(kp, vp, w.prompt_k, w.prompt_v, m_slots, B)
+    m_samples = []
+    for p in m_prompts:
+        m_samples.extend(m.fork(p) for _ in range(n))
+        m.free_seq(p)
+    assert samples == m_samples
+
+    own_k = [[] for _ in samples]          # each sample's own tokens, for the logical check
+    own_v = [[] for _ in samples]
+    rng = np.random.default_rng(0)
+    for step in range(w.steps):
+        k_new, v_new, q = w.step_inputs(step)
+        # HIP path: one decode step (copy-on-write copies are issued inside).
+        slots_dev, batch = c.decode_step(samples)
+        c.write(slots_dev, torch.from_numpy(k_new).to(dev), torch.from_numpy(v_new).to(dev))
+        q_dev = torch.from_numpy(q).to(dev)
+        out = c.attend(q_dev, batch, w.scale)
+        # Oracle: the same step.
+        m_step_slots, m_pairs = m.append_batch(m_samples)
+        oc.copy_blocks([(kp, vp)], m_pairs)
+        oc.write_slots(kp, vp, k_new, v_new, m_step_slots, B)
+        for i in range(len(samples)):
+            own_k[i].append(k_new[i])
+            own_v[i].append(v_new[i])
+        if step == 0:
+            partial = int(np.sum(w.prompt_lengths % B != 0))
+            assert len(m_pairs) == (n - 1) * partial
+            assert m.stats()["shared_blocks"] == int(np.sum(w.prompt_lengths // B))
+        if step not in CHECK_ATTN and step not in CHECK_POOLS:
+            continue
+        print(f"[case] parallel sampling step {step}", flush=True)
+        torch.cuda.synchronize()
+        tables = batch.tables.cpu().numpy().astype(np.int64)
+        m_tables, m_lens = m.export(m_samples, tables.shape[1], c.num_blocks)
+        assert tables.tolist() == m_tables
+        assert batch.lens.cpu().numpy().tolist() == m_lens
+        gk = c.k[0].cpu().numpy()
+        gv = c.v[0].cpu().numpy()
+        if step in CHECK_POOLS:
+            paths.assert_pools_bit_exact({"k": gk, "v": gv}, {"k": kp, "v": vp})
+        rows = sorted(set(rng.choice(len(samples), size=6, replace=False).tolist()) | {0, 7})
+        got = out.cpu().numpy()
+        want = np.zeros_like(got, dtype=np.float64)
+        for i in rows:
+            p = i // n
+            lo, hi = offs[p], offs[p + 1]
+            keys = np.concatenate([w.prompt_k[lo:hi], np.array(own_k[i])])
+            vals = np.concatenate([w.prompt_v[lo:hi], np.array(own_v[i])])
+            # The sample's view through its table is its prompt then its own tokens.
+            L = int(m_lens[i])
+            assert np.array_equal(oc.gather_logical(gk, tables[i], L, B).view(np.uint16),
+                                  keys.view(np.uint16))
+            assert np.array_equal(oc.gather_logical(gv, tables[i], L, B).view(np.uint16),
+                                  vals.view(np.uint16))
+            want[i] = attention.attend_one(q[i], keys, vals, w.scale)
+        paths.assert_attention_close(got, want, rows=rows)
+    for s in samples:
+        c.free(s)
+    assert c.alloc.stats()["free_blocks"] == w.num_blocks, "all blocks reclaimed"
