@@ -52,6 +52,25 @@ def kv_bytes(lengths, w):
     return int(np.sum(lengths, dtype=np.int64)) * 2 * w.num_kv_heads * w.head_dim * 2
 
 
+def counter_traffic(workload_name):
+    """HBM bytes per pa_decode launch from the committed rocprofv3 counter summary,
+    or None when there is none for this workload or the kernel source changed since."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload_name}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\s*(\{.*?\})\s*```", open(path).read(), flags=re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    src = os.path.join(ROOT, rec["kernel_source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha256"]:
+        return None
+    return rec
+
+
 def cpu_baseline(w, budget_s):
     """Time the oracle's paged attention on a sample of requests, single-threaded BLAS."""
     from threadpoolctl import threadpool_limits
@@ -204,6 +223,7 @@ def main():
     value = total_bytes / wall / 1e9
     achieved = bytes_avg / decode_avg_s / 1e9
 
+    traffic = counter_traffic(args.workload)
     baseline = None
     if args.cpu_seconds > 0:
         baseline = cpu_baseline(w, args.cpu_seconds)
@@ -233,7 +253,11 @@ def main():
         "decode_us_p10_p90": [round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
                               round(float(np.percentile(decode_ms, 90)) * 1e3, 2)],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+                     "traffic_over_algorithmic": (round(traffic["traffic_bytes_per_launch"]
+                                                       / traffic["algorithmic_bytes_per_launch"], 4)
+                                                 if traffic else None),
                      "kernel": "pa_decode (partition + reduce launches)"},
         "cpu_baseline": baseline,
     }
