@@ -41,6 +41,8 @@ def parse_args():
     ap.add_argument("--workload", default="opt13b", choices=["opt13b", "gqa", "long_context"])
     ap.add_argument("--partition", default="auto",
                     help="tokens per split-context partition, 0 = one pass, or 'auto'")
+    ap.add_argument("--kernel-policy", default="default", choices=["default", "valu"],
+                    help="head-group kernel: MFMA (default for fp16 groups of >= 4) or VALU")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -149,6 +151,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    from paged_kv_cache_244_amd import _lib
+    _lib.set_kernel_policy(_lib.PKV_POLICY_VALU if args.kernel_policy == "valu"
+                           else _lib.PKV_POLICY_DEFAULT)
+
     if args.workload == "long_context":
         w = workloads.long_context(16)
     else:
@@ -246,6 +252,7 @@ def main():
             "num_seqs": w.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": "f16",
             "q_dtype": np.dtype(w.q_dtype).name, "partition_size": partition,
+            "kernel_policy": args.kernel_policy,
             "mean_context": round(float(np.mean(lengths)), 1),
             "kv_bytes_per_step": int(bytes_avg),
         },

@@ -143,9 +143,24 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *                    block_size: each request's context is split into
  *                    partitions of that many tokens, processed in parallel and
  *                    combined by a log-sum-exp reduce.
+ *   Kernels: one query head per wave on the vector ALUs; when query heads come in
+ *   groups of 4 or more per KV head and q is fp16, the group runs on the matrix
+ *   cores (scores and P.V as MFMA, P rounded to fp16), unless the kernel policy
+ *   (pa_decode_set_kernel_policy) says otherwise.
  *   workspace      : device buffer of pa_decode_workspace_size(...) bytes, 256-B
  *                    aligned (may be NULL when that size is 0).  Scratch only.
  */
+/*
+ * Kernel policy for query-head groups, process-wide, read at every pa_decode
+ * call: PKV_POLICY_DEFAULT (MFMA kernel for groups of >= 4 heads with fp16 q)
+ * or PKV_POLICY_VALU (vector-ALU kernel for every shape).  Its initial value is
+ * PKV_POLICY_VALU if the environment variable PKV_GQA_KERNEL is "valu".
+ * Returns the previous policy, or PKV_ERR_INVALID_ARG for an unknown value.
+ * Launches already enqueued are not affected.
+ */
+enum { PKV_POLICY_DEFAULT = 0, PKV_POLICY_VALU = 1 };
+int pa_decode_set_kernel_policy(int32_t policy);
+
 int pa_decode(float* out, const void* q, int32_t q_dtype,
               const void* k_cache, const void* v_cache, int32_t num_blocks,
               const int32_t* block_tables, int32_t max_blocks_per_seq,

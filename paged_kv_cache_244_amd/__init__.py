@@ -24,4 +24,5 @@ from ._lib import (  # noqa: F401
     lib,
     pa_decode,
     pa_decode_workspace_size,
+    set_kernel_policy,
 )

@@ -26,6 +26,8 @@ PKV_ERR_HIP = -5
 PKV_ERR_WORKSPACE = -6
 PKV_F32 = 0
 PKV_F16 = 1
+PKV_POLICY_DEFAULT = 0
+PKV_POLICY_VALU = 1
 
 _ERR_NAMES = {
     PKV_ERR_INVALID_ARG: "INVALID_ARG",
@@ -63,6 +65,7 @@ _SIGNATURES = {
     "kv_copy_blocks": (c_int32, [POINTER(c_void_p), POINTER(c_void_p), c_int32, c_void_p, c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "pa_decode_set_kernel_policy": (c_int32, [c_int32]),
     "pa_decode": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
                             c_int32, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                             c_float, c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
@@ -182,6 +185,15 @@ def _order(work_order, s):
     if tuple(work_order.shape) != (s,):
         raise ValueError("work_order must be [S]")
     return _dev(work_order, torch.int32, "work_order")
+
+
+def set_kernel_policy(policy: int) -> int:
+    """PKV_POLICY_DEFAULT (MFMA for fp16 head groups of >= 4) or PKV_POLICY_VALU.
+    Returns the previous policy."""
+    rc = lib().pa_decode_set_kernel_policy(int(policy))
+    if rc < 0:
+        _check(rc)
+    return rc
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):

@@ -210,15 +210,19 @@ class PagedKVCache:
 
 
 def head_tile(num_q_heads: int, num_kv_heads: int) -> int:
-    """Query heads one wave serves (the library's own choice for this grouping)."""
+    """Query heads one wave serves (the library's choice for fp16 queries: groups of
+    4 or more run 4, 8 or 16 heads per wave on the matrix cores)."""
     group = num_q_heads // num_kv_heads
-    return 4 if group % 4 == 0 else (2 if group % 2 == 0 else 1)
+    for gt in (16, 8, 4):
+        if group % gt == 0:
+            return gt
+    return 2 if group % 2 == 0 else 1
 
 
 def choose_partition(lens_host, num_q_heads, num_kv_heads, block_size, gpu_waves=2048) -> int:
     """Split-context policy (measured on MI355X): one pass per request when there are
     enough (request, head tile) work items to fill the GPU; otherwise the largest of
-    1024 / 512 tokens that yields at least half a GPU's worth of items."""
+    1024 / 512 tokens that yields a GPU's worth of items, else 512."""
     lens = np.asarray(lens_host, dtype=np.int64)
     if lens.size == 0:
         return 0
@@ -228,7 +232,7 @@ def choose_partition(lens_host, num_q_heads, num_kv_heads, block_size, gpu_waves
     for part in (1024, 512):
         if part % block_size:
             continue
-        if tiles * int(np.sum((lens + part - 1) // part)) >= gpu_waves // 2:
+        if tiles * int(np.sum((lens + part - 1) // part)) >= gpu_waves:
             return part
     return max(512, block_size)
 

@@ -37,79 +37,22 @@
 // vectors are replaced by zeros with a select, so stale or NaN slots never leak.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cfloat>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "errors.h"
+#include "pa_decode_common.h"
 #include "pagedkv.h"
 
 namespace {
 
 using pkv::fail;
+using namespace pkv_decode;
 
-constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// K/V tiles are read exactly once: non-temporal loads keep them from displacing
-// useful lines in L2 and the Infinity Cache (measured ~10% faster on MI355X).
-__device__ __forceinline__ uint4 load_stream(const uint4* ptr) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-struct DecodeParams {
-  float* out;                 // [S][Hq][D]
-  float* ws_o;                // [S][Hq][max_parts][D]  unnormalised partial outputs
-  float* ws_ml;               // [S][Hq][max_parts][2]  (running max in log2 units, sum)
-  const void* q;              // [S][Hq][D], fp32 or fp16
-  const uint4* k_cache;       // [NB][Hkv][B][D] fp16 viewed as 16-byte chunks
-  const uint4* v_cache;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  const int32_t* work_order;  // optional [S] permutation: grid z -> request (NULL = identity)
-  int32_t num_seqs;
-  int32_t num_blocks;
-  int32_t max_blocks_per_seq;
-  int32_t num_q_heads;
-  int32_t num_kv_heads;
-  int32_t group;              // num_q_heads / num_kv_heads
-  int32_t num_head_tiles;     // num_q_heads / GT
-  float scale_log2;           // scale * log2(e)
-  int32_t len_clamp;          // min(max_context_len, max_blocks_per_seq * B)
-  int32_t part_tokens;        // tokens per partition, multiple of B
-  int32_t max_parts;
-};
-
-// ---- cross-lane helpers -------------------------------------------------------
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
-}
-
-// Sum over the LPT lanes of one token row; every lane of the row gets the same
-// bits (each step adds two equal-order partial sums).
-template <int LPT>
-__device__ __forceinline__ float row_sum(float v) {
-  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: pairs
-  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: quads
-  v += dpp<0x141>(v);   // row_half_mirror: 8 lanes
-  if constexpr (LPT == 16) v += dpp<0x140>(v);   // row_mirror: 16 lanes
-  return v;
-}
-
-__device__ __forceinline__ float shfl_xor(float v, int mask) {
-  const int lane = __lane_id();
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, v)));
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- the partition kernel -------------------------------------------------------
 
@@ -174,10 +117,10 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
   static_assert(NLD >= 1 && NLD * TPL == TT && TPB * TT == B, "tile shape");
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int tile = blockIdx.y;
-  const int seq = p.work_order ? p.work_order[blockIdx.z] : static_cast<int>(blockIdx.z);
+  const int tile = blockIdx.x;
+  const int seq = scheduled_seq(p);
   if (static_cast<unsigned>(seq) >= static_cast<unsigned>(p.num_seqs)) return;
-  const int part = blockIdx.x;
+  const int part = blockIdx.z;
   const int h0 = tile * GT;
   const int kvh = h0 / p.group;
   const int row = lane / LPT;
@@ -190,8 +133,7 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
   const int staged_first = blk_begin + lane < p.max_blocks_per_seq ? table[blk_begin + lane] : 0;
   QueryRegs<GT, kQF32> qr;
   qr.load(p.q, (static_cast<int64_t>(seq) * p.num_q_heads + h0) * D + dchunk * 8, D);
-  int len = p.context_lens[seq];
-  len = len < 0 ? 0 : (len > p.len_clamp ? p.len_clamp : len);
+  const int len = clamped_len(p, seq);
   const int t_begin = part * p.part_tokens;
   if (t_begin >= len) {
     if (part == 0 && row == 0) {             // empty context: defined as zeros
@@ -362,8 +304,7 @@ __global__ __launch_bounds__(D) void pa_decode_reduce_kernel(DecodeParams p) {
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int d = threadIdx.x;
-  int len = p.context_lens[seq];
-  len = len < 0 ? 0 : (len > p.len_clamp ? p.len_clamp : len);
+  const int len = clamped_len(p, seq);
   const int nparts = (len + p.part_tokens - 1) / p.part_tokens;
   if (nparts <= 1) return;
   const int64_t base = (static_cast<int64_t>(seq) * p.num_q_heads + h) * p.max_parts;
@@ -380,7 +321,7 @@ __global__ __launch_bounds__(D) void pa_decode_reduce_kernel(DecodeParams p) {
 
 // ---- host dispatch ---------------------------------------------------------------------
 
-using KernelFn = void (*)(DecodeParams);
+
 
 template <int D, int B, int GT>
 KernelFn pick_q(bool qf32) {
@@ -421,6 +362,24 @@ int head_tile(int group) {
   return 1;
 }
 
+// Kernel policy for head groups (see pa_decode_set_kernel_policy).  The first
+// value comes from PKV_GQA_KERNEL=valu in the environment, if set.
+std::atomic<int> g_policy{-1};
+
+int kernel_policy() {
+  int v = g_policy.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* env = std::getenv("PKV_GQA_KERNEL");
+    const int init = (env != nullptr && std::strcmp(env, "valu") == 0) ? PKV_POLICY_VALU
+                                                                       : PKV_POLICY_DEFAULT;
+    g_policy.compare_exchange_strong(v, init);
+    v = g_policy.load(std::memory_order_relaxed);
+  }
+  return v;
+}
+
+bool gqa_valu_forced() { return kernel_policy() == PKV_POLICY_VALU; }
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 int64_t parts_for(int32_t max_context_len, int32_t partition_size) {
@@ -435,6 +394,14 @@ size_t workspace_bytes_for(int32_t S, int32_t Hq, int32_t D, int64_t parts) {
 }
 
 }  // namespace
+
+extern "C" int pa_decode_set_kernel_policy(int32_t policy) {
+  if (policy != PKV_POLICY_DEFAULT && policy != PKV_POLICY_VALU)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_set_kernel_policy: unknown policy %d", policy);
+  const int previous = kernel_policy();
+  g_policy.store(policy, std::memory_order_relaxed);
+  return previous;
+}
 
 extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                            int32_t max_context_len, int32_t partition_size) {
@@ -464,10 +431,13 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
                 partition_size, block_size);
   if (num_seqs > 65535)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: at most 65535 sequences per call");
-  if (num_q_heads / head_tile(num_q_heads / num_kv_heads) > 65535)
+  if (num_q_heads > 65535)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: too many query heads");
-  const int gt = head_tile(num_q_heads / num_kv_heads);
-  KernelFn fn = pick_kernel(head_dim, block_size, gt, q_dtype == PKV_F32);
+  const int group = num_q_heads / num_kv_heads;
+  const bool mfma = q_dtype == PKV_F16 && group % 4 == 0 && !gqa_valu_forced();
+  const int gt = mfma ? (group % 16 == 0 ? 16 : (group % 8 == 0 ? 8 : 4)) : head_tile(group);
+  KernelFn fn = mfma ? pick_mfma_kernel(head_dim, block_size, gt)
+                     : pick_kernel(head_dim, block_size, gt, q_dtype == PKV_F32);
   if (!fn)
     return fail(PKV_ERR_UNSUPPORTED, "pa_decode: head_dim %d / block_size %d not built", head_dim,
                 block_size);
@@ -489,7 +459,8 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
     part_tokens = partition_size;
     parts = parts_for(len_clamp, partition_size);
   }
-  if (parts > 0x7fffffff) return fail(PKV_ERR_INVALID_ARG, "pa_decode: too many partitions");
+  if (parts > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode: more than 65535 partitions per request");
 
   DecodeParams prm{};
   prm.out = out;
@@ -526,11 +497,16 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
 
   // One wave per workgroup: the dispatcher then places work at wave granularity,
   // which balances requests of unequal length across CUs far better than
-  // multi-wave groups.  Grid order: partitions fastest, then head tiles, then
-  // requests in work_order (longest first is the caller's best choice).
+  // multi-wave groups.  Grid: x = head tile (fastest), y = request in
+  // work_order (longest first is the caller's best choice), z = partition.
+  // Workgroups are dealt round-robin to the 8 XCDs and, inside an XCD, to its
+  // shader engines, so neighbours in dispatch order must carry similar work.
+  // With the partition varying fastest, a request's long first partitions and
+  // short last one alternated with a fixed period and whole XCDs / shader
+  // engines received only the long ones (measured: up to 2x slower on GQA).
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(parts), static_cast<unsigned>(prm.num_head_tiles),
-                              static_cast<unsigned>(num_seqs)),
+  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(prm.num_head_tiles), static_cast<unsigned>(num_seqs),
+                              static_cast<unsigned>(parts)),
                      dim3(kWave), 0, st, prm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode launch: %s", hipGetErrorString(e));

@@ -1,0 +1,97 @@
+// Definitions shared by the two pa_decode kernel families (VALU and MFMA):
+// launch parameters and cross-lane helpers.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cstdint>
+
+namespace pkv_decode {
+
+constexpr int kWave = 64;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+struct DecodeParams {
+  float* out;                 // [S][Hq][D]
+  float* ws_o;                // [S][Hq][max_parts][D]  unnormalised partial outputs
+  float* ws_ml;               // [S][Hq][max_parts][2]  (running max in log2 units, sum)
+  const void* q;              // [S][Hq][D], fp32 or fp16
+  const uint4* k_cache;       // [NB][Hkv][B][D] fp16 viewed as 16-byte chunks
+  const uint4* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* work_order;  // optional [S] permutation: grid z -> request (NULL = identity)
+  int32_t num_seqs;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;              // num_q_heads / num_kv_heads
+  int32_t num_head_tiles;     // num_q_heads / GT
+  float scale_log2;           // scale * log2(e)
+  int32_t len_clamp;          // min(max_context_len, max_blocks_per_seq * B)
+  int32_t part_tokens;        // tokens per partition, multiple of B
+  int32_t max_parts;
+};
+
+// K/V tiles are read exactly once: non-temporal loads keep them from displacing
+// useful lines in L2 and the Infinity Cache (measured ~10% faster on MI355X).
+__device__ __forceinline__ uint4 load_stream(const uint4* ptr) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the LPT lanes of one token row; every lane of the row gets the same
+// bits (each step adds two equal-order partial sums).
+template <int LPT>
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: pairs
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: quads
+  v += dpp<0x141>(v);   // row_half_mirror: 8 lanes
+  if constexpr (LPT == 16) v += dpp<0x140>(v);   // row_mirror: 16 lanes
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ float shfl(float v, int src_lane) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_bpermute(src_lane << 2, __builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Request handled by this workgroup (the schedule maps grid y to a request).
+__device__ __forceinline__ int scheduled_seq(const DecodeParams& p) {
+  return p.work_order ? p.work_order[blockIdx.y] : static_cast<int>(blockIdx.y);
+}
+
+__device__ __forceinline__ int clamped_len(const DecodeParams& p, int seq) {
+  const int len = p.context_lens[seq];
+  return len < 0 ? 0 : (len > p.len_clamp ? p.len_clamp : len);
+}
+
+// MFMA head-group kernel, defined in pa_decode_mfma.hip: 16-token tiles, scores
+// on v_mfma_f32_16x16x32_f16 and P.V on v_mfma_f32_16x16x16_f16, for head
+// groups of GT in {4, 8, 16} query heads and fp16 queries.
+using KernelFn = void (*)(DecodeParams);
+KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt);
+
+}  // namespace pkv_decode

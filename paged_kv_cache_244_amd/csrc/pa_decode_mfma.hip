@@ -1,0 +1,290 @@
+// Paged decode attention for query-head groups on the gfx950 matrix cores.
+//
+// When several query heads share one KV head ("The KV cache is a systems
+// problem", section "Calculate bytes per token before choosing a batch"), each
+// K/V byte read feeds GT query heads, and the VALU kernel becomes bound by its
+// own arithmetic (4 heads cost ~4.7x the instructions of one).  This kernel
+// moves both products of a 16-token tile onto MFMA:
+//
+//   S^T[t][h] = sum_d K[t][d] Q[h][d]      v_mfma_f32_16x16x32_f16, D/32 steps
+//   O[h][d]  += sum_t P[h][t] V[t][d]      v_mfma_f32_16x16x16_f16, D/16 blocks
+//
+// Rows of the 16-wide head dimension beyond GT are zero queries (unused).  The
+// output layout of S^T (lane (g, i) holds tokens 4g..4g+3 of head i) is exactly
+// the A-operand layout P needs, so P goes from the softmax straight into the
+// second MFMA after rounding to fp16 (P is in [0, 1]).  V must be consumed with
+// tokens along K, i.e. transposed relative to the pool: each V tile is written
+// to LDS (rows padded by 32 bytes so the reads below hit distinct banks) and
+// read back with ds_read_b64_tr_b16, which hands every lane the four tokens of
+// one column.  K is loaded directly in the MFMA A layout: lane (g, i) reads
+// 16 bytes of token row i at column chunk 4*kk + g.
+//
+// Softmax: S^T is scaled into log2 units and masked (tokens past the context
+// get -inf; their V rows are zeroed in LDS).  The running max of head i is kept
+// identical in its four lane groups (max exchanged with two shuffles per
+// tile); each lane accumulates its share of the denominator and the four
+// shares are summed once at the end.  O rows are rescaled by their head's
+// factor each tile.
+//
+// Work decomposition, masking, partitions and the workspace format are those of
+// the VALU kernel in pa_decode.hip, so both feed the same reduce kernel.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cstdint>
+
+#include "pa_decode_common.h"
+
+namespace pkv_decode {
+namespace {
+
+constexpr float kSlack = 8.f;
+
+template <int D, int B, int GT>
+__global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
+#ifndef PKV_MFMA_DEPTH
+#define PKV_MFMA_DEPTH 2
+#endif
+  constexpr int DEPTH = PKV_MFMA_DEPTH;      // tiles in flight per wave
+  constexpr int TT = 16;                     // tokens per tile
+  constexpr int KSTEPS = D / 32;             // score MFMAs per tile
+  constexpr int DBLK = D / 16;               // P.V MFMAs per tile
+  constexpr int CPR = D / 8;                 // 16-byte chunks per token row
+  constexpr int VLD = TT * CPR / kWave;      // wave-wide loads per V tile
+  constexpr int ROWB = D * 2 + 32;           // LDS bytes per V row (padded)
+  constexpr int BPT = B < TT ? TT / B : 1;   // blocks per tile
+  constexpr int TPB = B > TT ? B / TT : 1;   // tiles per block
+  constexpr int CHUNKS = B * D / 8;          // 16-byte chunks per (block, KV head)
+  static_assert(KSTEPS == VLD && (B < TT ? BPT * B == TT : TPB * TT == B), "tile shape");
+  static_assert(GT == 4 || GT == 8 || GT == 16, "head group");
+  __shared__ __align__(16) unsigned char vlds[DEPTH][TT * ROWB];
+
+  const int lane = threadIdx.x;
+  const int grp = lane >> 4;                 // lane group: tokens 4*grp..4*grp+3 of a tile
+  const int li = lane & 15;                  // head index (scores) / column (outputs)
+  const int seq = scheduled_seq(p);
+  if (static_cast<unsigned>(seq) >= static_cast<unsigned>(p.num_seqs)) return;
+  const int part = blockIdx.z;
+  const int h0 = blockIdx.x * GT;
+  const int kvh = h0 / p.group;
+
+  // Independent loads first: table ids, queries, length.
+  const int32_t* table = p.block_tables + static_cast<int64_t>(seq) * p.max_blocks_per_seq;
+  const int blk_begin = part * (p.part_tokens / B);
+  const int staged_first = blk_begin + lane < p.max_blocks_per_seq ? table[blk_begin + lane] : 0;
+  half8 qb[KSTEPS];                          // Q^T as the B operand: head li, dims kk*32 + 8*grp
+  {
+    const _Float16* qp = static_cast<const _Float16*>(p.q) +
+                         (static_cast<int64_t>(seq) * p.num_q_heads + h0 + (li < GT ? li : 0)) * D +
+                         8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const half8 v = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(qp + kk * 32));
+      qb[kk] = li < GT ? v : half8{};
+    }
+  }
+  const int len = clamped_len(p, seq);
+  const int t_begin = part * p.part_tokens;
+  float* const out_rows = p.out + (static_cast<int64_t>(seq) * p.num_q_heads + h0) * D;
+  if (t_begin >= len) {
+    if (part == 0) {                          // empty context: defined as zeros
+      for (int x = lane; x < GT * D / 4; x += kWave)
+        reinterpret_cast<float4*>(out_rows)[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  const int t_end = min(len, t_begin + p.part_tokens);
+  const int nparts = (len + p.part_tokens - 1) / p.part_tokens;
+  const int nblk = (t_end - 1) / B - blk_begin + 1;
+  const int ntiles = (t_end - t_begin + TT - 1) / TT;
+  const int64_t block_stride = static_cast<int64_t>(p.num_kv_heads) * CHUNKS;
+  const uint4* kbase = p.k_cache + kvh * static_cast<int64_t>(CHUNKS);
+  const uint4* vbase = p.v_cache + kvh * static_cast<int64_t>(CHUNKS);
+
+  float4_t o[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) o[db] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -FLT_MAX;     // running max of head li (log2 units), equal in all lane groups
+  float lsum = 0.f;       // this lane's share of head li's denominator
+
+  uint4 kbuf[DEPTH][KSTEPS], vbuf[DEPTH][VLD];
+
+  for (int c0 = 0; c0 < nblk; c0 += kWave) {
+    const int staged =
+        c0 == 0 ? staged_first : (lane < min(kWave, nblk - c0) ? table[blk_begin + c0 + lane] : 0);
+    const int tile0 = c0 * TPB / BPT;                         // first tile of this chunk
+    const int cn = min(kWave * TPB / BPT, ntiles - tile0);    // tiles in this chunk
+
+    // Physical block (raw table entry) and row inside it of token row r of tile jj.
+    auto locate = [&](int jj, int r, int& raw, int& row) {
+      if constexpr (BPT == 1) {
+        raw = __builtin_amdgcn_readlane(staged, jj / TPB);
+        row = (jj % TPB) * TT + r;
+      } else {
+        const int first = __builtin_amdgcn_readlane(staged, jj * BPT);
+        const int second = __builtin_amdgcn_readlane(staged, jj * BPT + 1);
+        raw = r < B ? first : second;
+        row = r % B;
+      }
+    };
+    auto safe = [&](int raw) {
+      return static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks) ? raw : 0;
+    };
+
+    auto issue = [&](uint4 (&kr)[KSTEPS], uint4 (&vr)[VLD], int jj) {
+      int raw, row;
+      locate(jj, li, raw, row);
+      const uint4* kt = kbase + safe(raw) * block_stride + row * CPR + grp;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) kr[kk] = load_stream(kt + 4 * kk);
+#pragma unroll
+      for (int it = 0; it < VLD; ++it) {
+        const int c = it * kWave + lane;
+        locate(jj, c / CPR, raw, row);
+        vr[it] = load_stream(vbase + safe(raw) * block_stride + row * CPR + c % CPR);
+      }
+    };
+
+    auto consume = [&](uint4 (&kr)[KSTEPS], uint4 (&vr)[VLD], int jj, unsigned char* vl) {
+      const int tok0 = t_begin + (tile0 + jj) * TT;
+      auto token_ok = [&](int r) {
+        int raw, row;
+        locate(jj, r, raw, row);
+        return tok0 + r < t_end && static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks);
+      };
+      // V tile into LDS first (its latency hides behind the score MFMAs).
+#pragma unroll
+      for (int it = 0; it < VLD; ++it) {
+        const int c = it * kWave + lane;
+        const int r = c / CPR;
+        const uint4 v = token_ok(r) ? vr[it] : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(vl + r * ROWB + (c % CPR) * 16) = v;
+      }
+      float4_t s = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, kr[kk]), qb[kk], s, 0,
+                                                  0, 0);
+      float sr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sr[r] = token_ok(4 * grp + r) ? s[r] * p.scale_log2 : -INFINITY;
+      float mt = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
+      mt = fmaxf(mt, shfl_xor(mt, 16));
+      mt = fmaxf(mt, shfl_xor(mt, 32));
+      // Lazy rescaling: the reference max of a head moves only when a score
+      // exceeds it by more than kSlack (log2 units), so P stays below 2^kSlack
+      // (exact enough in fp16) and the accumulators are rescaled rarely.
+      const bool moved = mt > m + kSlack;
+      const float m_new = moved ? mt : m;
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sr[r] - m_new);
+      if (__builtin_amdgcn_ballot_w64(moved)) {    // some head moved: rescale (wave-uniform)
+        const float alpha = fast_exp2(m - m_new);
+        lsum *= alpha;
+        // O rows are heads 4*grp + r; head h's factor lives in lane h.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = shfl(alpha, 4 * grp + r);
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db) o[db][r] *= ar;
+        }
+      }
+      lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      m = m_new;
+      const half4 pa = half4{static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1]),
+                             static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])};
+      __syncthreads();                        // V tile visible in LDS
+      const unsigned char* src = vl + (4 * grp + (li >> 2)) * ROWB + 8 * (li & 3);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        typedef __attribute__((address_space(3))) short4_t lds_short4;
+        const short4_t raw =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src + 32 * db));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4, raw), o[db], 0,
+                                                      0, 0);
+      }
+    };
+
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) issue(kbuf[u], vbuf[u], u < cn ? u : cn - 1);
+    int j = 0;
+    for (; j + 2 * DEPTH - 1 < cn; j += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        consume(kbuf[u], vbuf[u], j + u, vlds[u]);
+        issue(kbuf[u], vbuf[u], j + u + DEPTH);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      if (j + u < cn) consume(kbuf[u], vbuf[u], j + u, vlds[u]);
+      if (j + u + DEPTH < cn) issue(kbuf[u], vbuf[u], j + u + DEPTH);
+    }
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u)
+      if (j + u + DEPTH < cn) consume(kbuf[u], vbuf[u], j + u + DEPTH, vlds[u]);
+  }
+
+  // Denominator of head li: the four lane groups' shares.
+  float l = lsum + shfl_xor(lsum, 16);
+  l = l + shfl_xor(l, 32);
+  float lr[4], mr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {               // this lane's output rows: heads 4*grp + r
+    lr[r] = shfl(l, 4 * grp + r);
+    mr[r] = shfl(m, 4 * grp + r);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * grp + r;
+    if (h >= GT) continue;
+    if (nparts == 1) {
+      const float inv = 1.f / lr[r];
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) out_rows[h * D + db * 16 + li] = o[db][r] * inv;
+    } else {
+      const int64_t slot =
+          (static_cast<int64_t>(seq) * p.num_q_heads + h0 + h) * p.max_parts + part;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) p.ws_o[slot * D + db * 16 + li] = o[db][r];
+      if (li == 0) {
+        p.ws_ml[2 * slot] = mr[r];
+        p.ws_ml[2 * slot + 1] = lr[r];
+      }
+    }
+  }
+}
+
+template <int D, int B>
+KernelFn pick_gt(int gt) {
+  switch (gt) {
+    case 4: return pa_decode_mfma_kernel<D, B, 4>;
+    case 8: return pa_decode_mfma_kernel<D, B, 8>;
+    case 16: return pa_decode_mfma_kernel<D, B, 16>;
+    default: return nullptr;
+  }
+}
+
+template <int D>
+KernelFn pick_b(int b, int gt) {
+  switch (b) {
+    case 8: return pick_gt<D, 8>(gt);
+    case 16: return pick_gt<D, 16>(gt);
+    case 32: return pick_gt<D, 32>(gt);
+    case 64: return pick_gt<D, 64>(gt);
+    case 128: return pick_gt<D, 128>(gt);
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt) {
+  if (head_dim == 64) return pick_b<64>(block_size, gt);
+  if (head_dim == 128) return pick_b<128>(block_size, gt);
+  return nullptr;
+}
+
+}  // namespace pkv_decode

@@ -74,6 +74,30 @@ def test_head_grouping(hq, hkv, q_dtype):
         paths.assert_attention_close(got["out"], ref["out"])
 
 
+@pytest.mark.parametrize("hq,hkv,head_dim,block_size", [(8, 2, 128, 16), (32, 8, 128, 8),
+                                                         (16, 2, 64, 32), (16, 1, 128, 128),
+                                                         (32, 2, 128, 64)])
+def test_head_group_kernels_agree(hq, hkv, head_dim, block_size):
+    """Head groups run on MFMA by default; the VALU kernel is the alternative policy.
+    Both are checked against the oracle on ragged lengths, single pass and split."""
+    from paged_kv_cache_244_amd import _lib
+    _announce(f"group kernels hq={hq} hkv={hkv} D={head_dim} B={block_size}")
+    w = workloads.custom(f"groups_{hq}_{hkv}", 91 + hq, [0, 1, 15, 16, 17, 100, 513, 1500], hq, hkv,
+                         head_dim, block_size)
+    ref = paths.run_oracle(w)
+    outs = {}
+    try:
+        for policy in (_lib.PKV_POLICY_DEFAULT, _lib.PKV_POLICY_VALU):
+            _lib.set_kernel_policy(policy)
+            for partition in (0, 256):
+                got = paths.run_gpu(w, partition, out_only=True)["out"]
+                paths.assert_attention_close(got, ref["out"])
+                outs[(policy, partition)] = got
+    finally:
+        _lib.set_kernel_policy(_lib.PKV_POLICY_DEFAULT)
+    assert np.array_equal(outs[(0, 0)][0], np.zeros_like(outs[(0, 0)][0]))
+
+
 def test_placement_does_not_change_bits():
     """The reduction order depends on logical order only: two physical placements of
     the same data give bitwise-identical outputs."""
