@@ -38,7 +38,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="opt13b", choices=["opt13b", "gqa", "long_context"])
+    ap.add_argument("--workload", default="opt13b",
+                    choices=["opt13b", "gqa", "long_context", "parallel_sampling", "tiny"])
     ap.add_argument("--partition", default="auto",
                     help="tokens per split-context partition, 0 = one pass, or 'auto'")
     ap.add_argument("--kernel-policy", default="default", choices=["default", "valu"],
@@ -130,6 +131,110 @@ def copy_probe():
                       "kernel": "elementwise copy (torch copy_)"}), flush=True)
 
 
+class Scenario:
+    """Resident state of one benchmark: cache, requests and per-step device inputs."""
+
+    def __init__(self, w, cache, seqs, lengths, step_k, step_v, step_q, max_blocks, out,
+                 unique_bytes=None, extra=None):
+        self.w, self.cache, self.seqs, self.lengths = w, cache, seqs, lengths
+        self.step_k, self.step_v, self.step_q = step_k, step_v, step_q
+        self.max_blocks, self.out = max_blocks, out
+        self.unique_bytes = unique_bytes
+        self.extra = extra or {}
+
+    @property
+    def num_seqs(self):
+        return len(self.seqs)
+
+
+def _to_dev(arrays, dev):
+    import torch
+    return [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrays]
+
+
+def decode_scenario(w, total_steps, dev):
+    """Requests whose first L-1 tokens are cached; step t appends one token to each."""
+    import torch
+
+    from paged_kv_cache_244_amd import workloads
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    # Room for the tokens appended during the run: one more block per request per B steps.
+    growth = w.num_seqs * (-(-total_steps // w.block_size) + 1)
+    num_blocks = w.num_blocks + growth
+    order = np.concatenate([w.initial_order, np.arange(w.num_blocks, num_blocks, dtype=np.int32)])
+    cache = PagedKVCache(num_blocks, w.num_kv_heads, w.head_dim, w.block_size, initial_order=order,
+                         device=dev, poison=False)
+    seqs = [cache.new_sequence() for _ in range(w.num_seqs)]
+    prompt_idx = np.concatenate([np.arange(o, o + L - 1) for o, L in zip(w.offsets[:-1], w.lengths)])
+    slots = cache.reserve_many(seqs, [int(L) - 1 for L in w.lengths])
+    cache.write(slots, *_to_dev([w.k_tokens[prompt_idx], w.v_tokens[prompt_idx]], dev))
+    last_idx = w.offsets[:-1] + w.lengths - 1
+    step_k, step_v, step_q = [], [], []
+    for t in range(total_steps):
+        k, v, q = ((w.k_tokens[last_idx], w.v_tokens[last_idx], w.q) if t == 0
+                   else workloads.step_inputs(w, t))
+        dk, dv, dq = _to_dev([k, v, q], dev)
+        step_k.append(dk)
+        step_v.append(dv)
+        step_q.append(dq)
+    max_blocks = -(-(int(w.lengths.max()) + total_steps) // w.block_size)
+    out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    return Scenario(w, cache, seqs, w.lengths.astype(np.int64) - 1, step_k, step_v, step_q,
+                    max_blocks, out)
+
+
+def sampling_scenario(sw, total_steps, dev):
+    """Prompts forked into samples sharing their blocks; the first step copies the
+    partly filled last prompt block of every sample but one per prompt."""
+    import torch
+
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    if total_steps > sw.steps:
+        raise SystemExit(f"parallel_sampling has {sw.steps} steps; asked for {total_steps}")
+    cache = PagedKVCache(sw.num_blocks, sw.num_kv_heads, sw.head_dim, sw.block_size,
+                         initial_order=sw.initial_order, device=dev, poison=False)
+    prompts = [cache.new_sequence() for _ in range(sw.num_prompts)]
+    slots = cache.reserve_many(prompts, sw.prompt_lengths)
+    cache.write(slots, *_to_dev([sw.prompt_k, sw.prompt_v], dev))
+    seqs = []
+    for p in prompts:
+        seqs.extend(cache.fork(p) for _ in range(sw.samples))
+        cache.free(p)
+    step_k, step_v, step_q = [], [], []
+    for t in range(total_steps):
+        dk, dv, dq = _to_dev(list(sw.step_inputs(t)), dev)
+        step_k.append(dk)
+        step_v.append(dv)
+        step_q.append(dq)
+    lengths = np.repeat(sw.prompt_lengths.astype(np.int64), sw.samples)
+    max_blocks = -(-(int(lengths.max()) + total_steps) // sw.block_size)
+    out = torch.empty((len(seqs), sw.num_q_heads, sw.head_dim), dtype=torch.float32, device=dev)
+    tok_bytes = 2 * sw.num_kv_heads * sw.head_dim * 2
+    B = sw.block_size
+
+    def unique_bytes(lens):
+        # Shared full prompt blocks are stored (and read from HBM) once per prompt.
+        shared = sum(int(P) // B * B for P in sw.prompt_lengths)
+        own = int(np.sum(lens)) - sw.samples * shared
+        return (shared + own) * tok_bytes
+
+    w = SimpleWorkload(sw.name, sw.num_q_heads, sw.num_kv_heads, sw.head_dim, sw.block_size,
+                       np.float16, sw.scale)
+    return Scenario(w, cache, seqs, lengths, step_k, step_v, step_q, max_blocks, out,
+                    unique_bytes=unique_bytes,
+                    extra={"prompts": sw.num_prompts, "samples_per_prompt": sw.samples,
+                           "note": "value counts logical K/V bytes; shared prompt blocks are "
+                                   "read by every sample"})
+
+
+class SimpleWorkload:
+    def __init__(self, name, hq, hkv, d, b, q_dtype, scale):
+        self.name, self.num_q_heads, self.num_kv_heads = name, hq, hkv
+        self.head_dim, self.block_size, self.q_dtype, self.scale = d, b, q_dtype, scale
+
+
 def main():
     args = parse_args()
     if args.copy_probe:
@@ -143,7 +248,6 @@ def main():
     import torch
 
     from paged_kv_cache_244_amd import workloads
-    from paged_kv_cache_244_amd.cache import PagedKVCache
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -155,61 +259,38 @@ def main():
     _lib.set_kernel_policy(_lib.PKV_POLICY_VALU if args.kernel_policy == "valu"
                            else _lib.PKV_POLICY_DEFAULT)
 
-    if args.workload == "long_context":
-        w = workloads.long_context(16)
-    else:
-        w = workloads.WORKLOADS[args.workload]()
-    total_steps = args.warmup + args.steps
-    # Room for the tokens appended during the run: one more block per request per B steps.
-    growth = w.num_seqs * (-(-total_steps // w.block_size) + 1)
-    num_blocks = w.num_blocks + growth
-    order = np.concatenate([w.initial_order, np.arange(w.num_blocks, num_blocks, dtype=np.int32)])
-    cache = PagedKVCache(num_blocks, w.num_kv_heads, w.head_dim, w.block_size, initial_order=order,
-                         device=dev, poison=False)
-    stream = cache.stream
-    seqs = [cache.new_sequence() for _ in range(w.num_seqs)]
-
-    # Prefill: the first L-1 tokens of every request.
-    prompt_idx = np.concatenate([np.arange(o, o + L - 1) for o, L in zip(w.offsets[:-1], w.lengths)])
-    slots = cache.reserve_many(seqs, [int(L) - 1 for L in w.lengths])
-    cache.write(slots, torch.from_numpy(w.k_tokens[prompt_idx]).to(dev),
-                torch.from_numpy(w.v_tokens[prompt_idx]).to(dev))
-    last_idx = w.offsets[:-1] + w.lengths - 1
-
-    # Per-step inputs, resident on the device before timing.
-    step_k, step_v, step_q = [], [], []
-    for t in range(total_steps):
-        if t == 0:
-            k, v, q = w.k_tokens[last_idx], w.v_tokens[last_idx], w.q
-        else:
-            k, v, q = workloads.step_inputs(w, t)
-        step_k.append(torch.from_numpy(np.ascontiguousarray(k)).to(dev))
-        step_v.append(torch.from_numpy(np.ascontiguousarray(v)).to(dev))
-        step_q.append(torch.from_numpy(np.ascontiguousarray(q)).to(dev))
-    max_len_final = int(w.lengths.max()) + total_steps
-    max_blocks = -(-max_len_final // w.block_size)
-    out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     from paged_kv_cache_244_amd.cache import choose_partition
-    partition = (choose_partition(w.lengths, w.num_q_heads, w.num_kv_heads, w.block_size)
+
+    total_steps = args.warmup + args.steps
+    if args.workload == "parallel_sampling":
+        sc = sampling_scenario(workloads.parallel_sampling(), total_steps, dev)
+    else:
+        w = {"long_context": lambda: workloads.long_context(16),
+             "tiny": workloads.tiny}.get(args.workload, workloads.WORKLOADS.get(args.workload))()
+        sc = decode_scenario(w, total_steps, dev)
+    w = sc.w
+    cache = sc.cache
+    stream = cache.stream
+    partition = (choose_partition(sc.lengths + total_steps, w.num_q_heads, w.num_kv_heads,
+                                  w.block_size)
                  if args.partition == "auto" else int(args.partition))
-    cache.workspace(w.num_seqs, w.num_q_heads, max_len_final, partition)
+    cache.workspace(sc.num_seqs, w.num_q_heads, int(sc.lengths.max()) + total_steps, partition)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
-    step_bytes = []
+    step_bytes, unique_step_bytes = [], []
 
     def step(t, timed_slot=None):
-        s, batch = cache.decode_step(seqs, max_blocks)
-        cache.write(s, step_k[t], step_v[t])
+        s, batch = cache.decode_step(sc.seqs, sc.max_blocks)
+        cache.write(s, sc.step_k[t], sc.step_v[t])
         if timed_slot is not None:
             ev[timed_slot][0].record(stream)
-        cache.attend(step_q[t], batch, w.scale, partition_size=partition, out=out)
+        cache.attend(sc.step_q[t], batch, w.scale, partition_size=partition, out=sc.out)
         if timed_slot is not None:
             ev[timed_slot][1].record(stream)
-        return batch.max_len
 
-    lengths = w.lengths.astype(np.int64) - 1
+    lengths = sc.lengths.copy()
     for t in range(args.warmup):
         step(t)
         lengths += 1
@@ -219,6 +300,8 @@ def main():
         step(args.warmup + i, timed_slot=i)
         lengths += 1
         step_bytes.append(kv_bytes(lengths, w))
+        if sc.unique_bytes is not None:
+            unique_step_bytes.append(sc.unique_bytes(lengths))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -228,10 +311,14 @@ def main():
     total_bytes = float(np.sum(step_bytes))
     value = total_bytes / wall / 1e9
     achieved = bytes_avg / decode_avg_s / 1e9
+    if unique_step_bytes:
+        # Shared prompt blocks are read from HBM once; the roofline counts unique bytes.
+        sc.extra["unique_kv_bytes_per_step"] = int(np.mean(unique_step_bytes))
+        achieved = float(np.mean(unique_step_bytes)) / decode_avg_s / 1e9
 
     traffic = counter_traffic(args.workload)
     baseline = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and hasattr(w, "offsets"):
         baseline = cpu_baseline(w, args.cpu_seconds)
 
     result = {
@@ -249,12 +336,13 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name} decode layer",
-            "num_seqs": w.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "num_seqs": sc.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": "f16",
             "q_dtype": np.dtype(w.q_dtype).name, "partition_size": partition,
             "kernel_policy": args.kernel_policy,
             "mean_context": round(float(np.mean(lengths)), 1),
             "kv_bytes_per_step": int(bytes_avg),
+            **sc.extra,
         },
         "decode_us": round(decode_avg_s * 1e6, 2),
         "decode_us_p10_p90": [round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
