@@ -68,9 +68,10 @@ def counter_traffic(workload_name):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    src = os.path.join(ROOT, rec["kernel_source"])
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["kernel_source_sha256"]:
-        return None
+    for rel, digest in rec["kernel_sources_sha256"].items():
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path) or hashlib.sha256(open(path, "rb").read()).hexdigest() != digest:
+            return None
     return rec
 
 

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-HIP_SOURCES = ["pa_decode.hip", "pa_decode_mfma.hip", "kv_cache_ops.hip"]
+HIP_SOURCES = ["pa_decode.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip", "pa_decode_reduce.hip",
+               "kv_cache_ops.hip"]
 HOST_SOURCES = ["allocator.cpp", "errors.cpp"]
 
 # Device code: gfx950 only; packed-fp32 instructions disabled (the compiler

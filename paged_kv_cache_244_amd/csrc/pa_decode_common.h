@@ -94,4 +94,11 @@ __device__ __forceinline__ int clamped_len(const DecodeParams& p, int seq) {
 using KernelFn = void (*)(DecodeParams);
 KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt);
 
+// VALU kernel (pa_decode_valu.hip): one wave per (request, head tile,
+// partition), GT in {1, 2, 4} query heads per wave, fp32 or fp16 queries.
+KernelFn pick_valu_kernel(int head_dim, int block_size, int gt, bool qf32);
+
+// Cross-partition combine (pa_decode_reduce.hip), launched after a split pass.
+hipError_t launch_reduce(const DecodeParams& prm, int head_dim, hipStream_t stream);
+
 }  // namespace pkv_decode
