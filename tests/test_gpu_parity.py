@@ -189,29 +189,41 @@ def _sample_rows(w, n=8):
 
 @pytest.mark.parametrize("name", ["opt13b", "gqa"])
 def test_full_size_workload(name):
-    """Full-size inputs in the launch configuration the benchmark times (512-token
-    partitions); pools and tables compared whole, attention on sampled requests."""
+    """Full-size inputs in the launch configuration the benchmark times (the automatic
+    partition policy and longest-first order), plus a fixed 512-token split; pools and
+    tables compared whole, attention on sampled requests."""
+    from paged_kv_cache_244_amd.cache import choose_partition
     _announce(f"full size {name}")
     w = workloads.WORKLOADS[name]()
     rows = _sample_rows(w)
     ref = paths.run_oracle(w, sample=rows)
-    got = paths.run_gpu(w, 512)
+    auto = choose_partition(w.lengths, w.num_q_heads, w.num_kv_heads, w.block_size)
+    got = paths.run_gpu(w, auto)
     assert np.array_equal(got["tables"], ref["tables"])
     paths.assert_pools_bit_exact(got, ref)
     paths.assert_attention_close(got["out"], ref["out"], rows=rows)
+    c, batch, q = got["cache"], got["batch"], got["q_dev"]
+    other = 512 if auto != 512 else 0
+    out = c.attend(q, batch, w.scale, partition_size=other).cpu().numpy()
+    paths.assert_attention_close(out, ref["out"], rows=rows)
 
 
 @pytest.mark.parametrize("block_size", [8, 16, 32, 64, 128])
 def test_long_context_block_sweep(block_size):
     """16 requests of 8K-32K tokens, 32/8 heads; every block size against one oracle
     output (the logical data does not depend on the block size)."""
+    from paged_kv_cache_244_amd.cache import choose_partition
     _announce(f"long context B={block_size}")
     w = _long_context_base()
     if block_size != 16:
         w = workloads.with_block_size(w, block_size)
     rows = [0, 5, 11]
-    got = paths.run_gpu(w, 512, out_only=True)
+    auto = choose_partition(w.lengths, w.num_q_heads, w.num_kv_heads, w.block_size)
+    got = paths.run_gpu(w, auto, out_only=True)
     paths.assert_attention_close(got["out"], _long_context_ref(rows), rows=rows)
+    c, batch, q = got["cache"], got["batch"], got["q_dev"]
+    out = c.attend(q, batch, w.scale, partition_size=512).cpu().numpy()
+    paths.assert_attention_close(out, _long_context_ref(rows), rows=rows)
 
 
 _LC = {}
