@@ -165,7 +165,8 @@ def decode_scenario(w, total_steps, dev):
     num_blocks = w.num_blocks + growth
     order = np.concatenate([w.initial_order, np.arange(w.num_blocks, num_blocks, dtype=np.int32)])
     cache = PagedKVCache(num_blocks, w.num_kv_heads, w.head_dim, w.block_size, initial_order=order,
-                         device=dev, poison=False)
+                         device=dev, poison=False, num_q_heads=w.num_q_heads,
+                         q_dtype=torch.float16 if w.q.dtype == np.float16 else torch.float32)
     seqs = [cache.new_sequence() for _ in range(w.num_seqs)]
     prompt_idx = np.concatenate([np.arange(o, o + L - 1) for o, L in zip(w.offsets[:-1], w.lengths)])
     slots = cache.reserve_many(seqs, [int(L) - 1 for L in w.lengths])
@@ -195,7 +196,8 @@ def sampling_scenario(sw, total_steps, dev):
     if total_steps > sw.steps:
         raise SystemExit(f"parallel_sampling has {sw.steps} steps; asked for {total_steps}")
     cache = PagedKVCache(sw.num_blocks, sw.num_kv_heads, sw.head_dim, sw.block_size,
-                         initial_order=sw.initial_order, device=dev, poison=False)
+                         initial_order=sw.initial_order, device=dev, poison=False,
+                         num_q_heads=sw.num_q_heads)
     prompts = [cache.new_sequence() for _ in range(sw.num_prompts)]
     slots = cache.reserve_many(prompts, sw.prompt_lengths)
     cache.write(slots, *_to_dev([sw.prompt_k, sw.prompt_v], dev))
@@ -260,8 +262,6 @@ def main():
     _lib.set_kernel_policy(_lib.PKV_POLICY_VALU if args.kernel_policy == "valu"
                            else _lib.PKV_POLICY_DEFAULT)
 
-    from paged_kv_cache_244_amd.cache import choose_partition
-
     total_steps = args.warmup + args.steps
     if args.workload == "parallel_sampling":
         sc = sampling_scenario(workloads.parallel_sampling(), total_steps, dev)
@@ -272,8 +272,11 @@ def main():
     w = sc.w
     cache = sc.cache
     stream = cache.stream
-    partition = (choose_partition(sc.lengths + total_steps, w.num_q_heads, w.num_kv_heads,
-                                  w.block_size)
+    # The planner's automatic choice for the lengths the run ends at (they grow by
+    # total_steps tokens), then kept fixed so every timed step runs one schedule shape.
+    qd = _lib.PKV_F16 if w.q_dtype == np.float16 else _lib.PKV_F32
+    partition = (_lib.plan(sc.lengths + total_steps, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                           w.block_size, qd)[1]["partition_size"]
                  if args.partition == "auto" else int(args.partition))
     cache.workspace(sc.num_seqs, w.num_q_heads, int(sc.lengths.max()) + total_steps, partition)
     torch.cuda.synchronize()
@@ -281,13 +284,15 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     step_bytes, unique_step_bytes = [], []
+    plans = []
 
     def step(t, timed_slot=None):
-        s, batch = cache.decode_step(sc.seqs, sc.max_blocks)
+        s, batch = cache.decode_step(sc.seqs, sc.max_blocks, partition_size=partition)
+        plans.append(batch.plan)
         cache.write(s, sc.step_k[t], sc.step_v[t])
         if timed_slot is not None:
             ev[timed_slot][0].record(stream)
-        cache.attend(sc.step_q[t], batch, w.scale, partition_size=partition, out=sc.out)
+        cache.attend(sc.step_q[t], batch, w.scale, out=sc.out)
         if timed_slot is not None:
             ev[timed_slot][1].record(stream)
 
@@ -341,6 +346,8 @@ def main():
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": "f16",
             "q_dtype": np.dtype(w.q_dtype).name, "partition_size": partition,
             "kernel_policy": args.kernel_policy,
+            "schedule": "planner work list, largest piece first",
+            "work_items": plans[-1]["num_items"], "waves_per_cu": plans[-1]["waves_per_cu"],
             "mean_context": round(float(np.mean(lengths)), 1),
             "kv_bytes_per_step": int(bytes_avg),
             **sc.extra,

@@ -107,11 +107,100 @@ int kv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_lay
                    void* stream);
 
 /*
+ * pkv_upload — copy `bytes` from pinned host memory (allocated with
+ * hipHostMalloc, e.g. torch's pin_memory) into device memory with a kernel on
+ * `stream`.  [B] "The page table, relocated into attention": a step's tables
+ * are built on the host and must be in GPU memory before the kernel walks
+ * them.  The kernel reads the host memory directly over the bus, so the copy
+ * is ordered with the step's other kernels on one queue, without a hand-off to
+ * a copy engine.  The host must not change the source until the copy has run
+ * (an event recorded after it tells).
+ *   dst : device memory, 16-byte aligned.     src : pinned host memory, 16-byte aligned.
+ *   bytes : a multiple of 16; 0 is a no-op.
+ * Errors: PKV_ERR_INVALID_ARG (NULL, alignment, size), PKV_ERR_HIP.
+ */
+int pkv_upload(void* dst, const void* src, uint64_t bytes, void* stream);
+
+/*
  * Workspace bytes pa_decode needs for a split-context launch (0 when a single
  * partition covers max_context_len, or partition_size == 0).
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Kernel policy for query-head groups, process-wide, read at every pa_decode
+ * and pa_decode_plan call: PKV_POLICY_DEFAULT (MFMA kernel for groups of >= 4
+ * heads with fp16 q) or PKV_POLICY_VALU (vector-ALU kernel for every shape).
+ * Its initial value is PKV_POLICY_VALU if the environment variable
+ * PKV_GQA_KERNEL is "valu".  Returns the previous policy, or
+ * PKV_ERR_INVALID_ARG for an unknown value.  Launches already enqueued are not
+ * affected.
+ */
+enum { PKV_POLICY_DEFAULT = 0, PKV_POLICY_VALU = 1 };
+int pa_decode_set_kernel_policy(int32_t policy);
+
+/*
+ * Schedule of one pa_decode launch, filled by pa_decode_plan.
+ */
+typedef struct {
+  int32_t partition_size;   /* tokens per partition; 0 = one pass per request        */
+  int32_t max_parts;        /* partitions of the longest request (>= 1)              */
+  int32_t num_items;        /* work items written to items[]                         */
+  int32_t waves_per_cu;     /* residency limit to pass to pa_decode (0 = none)       */
+  uint64_t workspace_bytes; /* = pa_decode_workspace_size for this schedule          */
+} pkv_decode_plan;
+
+/* Packing of one work item: (request << 16) | partition. */
+#define PKV_ITEM(request, partition) (((uint32_t)(request) << 16) | (uint32_t)(partition))
+
+/*
+ * pa_decode_plan — host only (no HIP call): the schedule of one decode launch,
+ * computed from a host copy of the context lengths.  Decode reads every cached
+ * byte of every request once per step ([A] "The old answer, imported
+ * honestly"; [C] "Calculate bytes per token before choosing a batch"), so the
+ * time of a launch is set by how evenly that traffic is spread over the GPU.
+ * Requests of very different lengths ([B] "Why the KV cache is the thing that
+ * limits your batch": the batch mixes short and long contexts) are cut into
+ * partitions and the pieces are listed longest first, so that the GPU's
+ * dispatcher hands the long pieces out first and fills in with short ones.
+ *
+ *   context_lens   : HOST int32 [num_seqs], the lengths pa_decode will see
+ *                    (negative counts as 0).
+ *   partition_size : < 0 chooses one (below); 0 = no split; > 0 uses that
+ *                    value, which must be a multiple of block_size.
+ *   num_compute_units: the GPU's compute units; <= 0 means 256 (MI355X).
+ *   items          : HOST uint32 [items_capacity], written with PKV_ITEM
+ *                    entries: one per (request, partition) that holds tokens,
+ *                    plus partition 0 of each empty request (it writes zeros),
+ *                    ordered by tokens per item, largest first (ties: the
+ *                    longer request first, then the lower partition).
+ *   items_capacity : at least sum over requests of max(1, ceil(L / partition));
+ *                    num_seqs * max_parts always suffices, and
+ *                    pa_decode_plan_capacity gives a bound before the plan.
+ *   plan           : written on success.
+ * Chosen partition size: 0 when every request fits in one pass without
+ * leaving the GPU unbalanced (one item per (request, head tile) gives at
+ * least one wave per SIMD and no request is longer than 1.25x the tokens a
+ * SIMD would process), otherwise the largest of 2048, 1024, 512 and 256 tokens
+ * that is at most half a SIMD's share of the tokens (256 if none is), rounded
+ * up to a multiple of block_size.  The residency limit is 6 waves per compute
+ * unit for the MFMA kernel (it leaves the dispatcher room to balance) and none
+ * for the vector-ALU kernel.
+ * Errors: PKV_ERR_INVALID_ARG (bad sizes, capacity too small: plan->num_items
+ * then holds the number needed), PKV_ERR_UNSUPPORTED (shape not built).
+ */
+int pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t q_dtype,
+                   int32_t partition_size, int32_t num_compute_units, uint32_t* items,
+                   int32_t items_capacity, pkv_decode_plan* plan);
+
+/*
+ * Upper bound of the items pa_decode_plan writes for num_seqs requests of at
+ * most max_context_len tokens (any partition size it may choose or be given
+ * that is >= block_size).
+ */
+int32_t pa_decode_plan_capacity(int32_t num_seqs, int32_t max_context_len, int32_t block_size);
 
 /*
  * pa_decode — single-query decode attention through the block table.
@@ -133,16 +222,23 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *   block_tables   : device int32 [num_seqs][max_blocks_per_seq]; entries past
  *                    ceil(L / block_size) are never read.
  *   context_lens   : device int32 [num_seqs], tokens attended per request.
- *   work_order     : device int32 [num_seqs], a permutation of 0..num_seqs-1
- *                    giving the order in which requests are scheduled onto the
- *                    GPU (longest context first balances the compute units
- *                    best), or NULL for 0, 1, 2, ...  Only the timing depends
- *                    on it; an entry outside [0, num_seqs) is skipped.
  *   max_context_len: an upper bound on every context length (sizes the grid).
  *   partition_size : 0 = one pass per request; otherwise a multiple of
  *                    block_size: each request's context is split into
  *                    partitions of that many tokens, processed in parallel and
  *                    combined by a log-sum-exp reduce.
+ *   work_items     : device uint32 [num_work_items] of PKV_ITEM entries, the
+ *                    (request, partition) pieces to run in the order they are
+ *                    to be dispatched (pa_decode_plan's list), or NULL for
+ *                    every piece in index order.  Each piece that holds tokens,
+ *                    and partition 0 of each empty request, must be listed
+ *                    exactly once, or the outputs of the missing ones are not
+ *                    written.  Entries naming a request >= num_seqs or a
+ *                    partition past the launch's partition count are skipped;
+ *                    only the timing depends on the order.
+ *   waves_per_cu   : 0 = as many waves per compute unit as the kernel's
+ *                    registers allow; n > 0 reserves LDS so that at most about
+ *                    n waves share a compute unit (values below 4 act as 4).
  *   Kernels: one query head per wave on the vector ALUs; when query heads come in
  *   groups of 4 or more per KV head and q is fp16, the group runs on the matrix
  *   cores (scores and P.V as MFMA, P rounded to fp16), unless the kernel policy
@@ -150,23 +246,13 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *   workspace      : device buffer of pa_decode_workspace_size(...) bytes, 256-B
  *                    aligned (may be NULL when that size is 0).  Scratch only.
  */
-/*
- * Kernel policy for query-head groups, process-wide, read at every pa_decode
- * call: PKV_POLICY_DEFAULT (MFMA kernel for groups of >= 4 heads with fp16 q)
- * or PKV_POLICY_VALU (vector-ALU kernel for every shape).  Its initial value is
- * PKV_POLICY_VALU if the environment variable PKV_GQA_KERNEL is "valu".
- * Returns the previous policy, or PKV_ERR_INVALID_ARG for an unknown value.
- * Launches already enqueued are not affected.
- */
-enum { PKV_POLICY_DEFAULT = 0, PKV_POLICY_VALU = 1 };
-int pa_decode_set_kernel_policy(int32_t policy);
-
 int pa_decode(float* out, const void* q, int32_t q_dtype,
               const void* k_cache, const void* v_cache, int32_t num_blocks,
               const int32_t* block_tables, int32_t max_blocks_per_seq,
-              const int32_t* context_lens, const int32_t* work_order, int32_t num_seqs,
+              const int32_t* context_lens, int32_t num_seqs,
               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               float scale, int32_t max_context_len, int32_t partition_size,
+              const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
@@ -228,6 +314,53 @@ int kv_export_block_tables(const kv_allocator* a, const int32_t* seqs, int32_t n
                            int32_t max_blocks_per_seq, int32_t pad_value,
                            int32_t* tables_out, int32_t* lens_out);
 int kv_allocator_stats(const kv_allocator* a, kv_stats* out);
+
+/*
+ * Where kv_decode_step_host put each array in the caller's buffer: byte
+ * offsets from the buffer's start, each a multiple of 16.
+ */
+typedef struct {
+  uint64_t slots_offset;    /* int64 [num_seqs]: the appended token's slot, per entry    */
+  uint64_t pairs_offset;    /* int32 [num_pairs][2]: copy-on-write (src, dst) pairs      */
+  uint64_t tables_offset;   /* int32 [num_seqs][max_blocks]: block tables, padded        */
+  uint64_t lens_offset;     /* int32 [num_seqs]: lengths after the append                */
+  uint64_t items_offset;    /* uint32 [plan.num_items]: pa_decode work items             */
+  uint64_t total_bytes;     /* bytes used; on PKV_ERR_INVALID_ARG for a short buffer,
+                               the bytes needed                                         */
+  int32_t num_pairs;
+  int32_t max_blocks;       /* table width used                                         */
+  int32_t max_context_len;  /* longest length after the append                          */
+  int32_t reserved;
+  pkv_decode_plan plan;
+} kv_step_layout;
+
+/*
+ * kv_decode_step_host — the host side of one decode step in one call, laid out
+ * for a single host-to-device copy: append one token to each listed sequence
+ * (exactly as kv_batch_append: all or nothing, copy-on-write pairs reported),
+ * export the listed sequences' block tables and lengths (as
+ * kv_export_block_tables, after the append) and plan the attention launch for
+ * those lengths (as pa_decode_plan).  [B] "The page table, relocated into
+ * attention" (the table the kernel walks) and "The part everyone forgets"
+ * (copy-on-write before the write).
+ *
+ *   seqs, num_seqs     : sequences of the step (a sequence listed k times gets
+ *                        k tokens; its rows then show its final length).
+ *   max_blocks_per_seq : table width; <= 0 uses the smallest that fits.
+ *   pad_value          : table entries past a sequence's blocks.
+ *   num_q_heads ... num_compute_units : as pa_decode_plan (block size and
+ *                        partition rules included).
+ *   buffer, buffer_bytes: caller's host memory (pinned memory lets the copy
+ *                        run asynchronously); filled as *layout describes.
+ * Everything is checked, and the space needed computed, before anything
+ * changes: on any error (bad sequence, sizes, a buffer too small, too few free
+ * blocks, a table narrower than a sequence) the allocator is unchanged.
+ */
+int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
+                        int32_t max_blocks_per_seq, int32_t pad_value, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t q_dtype,
+                        int32_t partition_size, int32_t num_compute_units, void* buffer,
+                        uint64_t buffer_bytes, kv_step_layout* layout);
 
 #ifdef __cplusplus
 }

@@ -53,6 +53,19 @@ class BadSequence(PagedKVError):
     pass
 
 
+class DecodePlan(ctypes.Structure):
+    _fields_ = [("partition_size", c_int32), ("max_parts", c_int32), ("num_items", c_int32),
+                ("waves_per_cu", c_int32), ("workspace_bytes", ctypes.c_uint64)]
+
+
+class StepLayout(ctypes.Structure):
+    _fields_ = [("slots_offset", ctypes.c_uint64), ("pairs_offset", ctypes.c_uint64),
+                ("tables_offset", ctypes.c_uint64), ("lens_offset", ctypes.c_uint64),
+                ("items_offset", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
+                ("num_pairs", c_int32), ("max_blocks", c_int32), ("max_context_len", c_int32),
+                ("reserved", c_int32), ("plan", DecodePlan)]
+
+
 class KVStats(ctypes.Structure):
     _fields_ = [("num_blocks", c_int32), ("free_blocks", c_int32), ("used_blocks", c_int32),
                 ("shared_blocks", c_int32), ("live_tokens", c_int64), ("sum_refcounts", c_int64)]
@@ -64,11 +77,16 @@ _SIGNATURES = {
                                  c_int32, c_int32, c_int32, c_void_p]),
     "kv_copy_blocks": (c_int32, [POINTER(c_void_p), POINTER(c_void_p), c_int32, c_void_p, c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_void_p]),
+    "pkv_upload": (c_int32, [c_void_p, c_void_p, ctypes.c_uint64, c_void_p]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode_set_kernel_policy": (c_int32, [c_int32]),
+    "pa_decode_plan": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                 c_int32, c_int32, c_void_p, c_int32, POINTER(DecodePlan)]),
+    "pa_decode_plan_capacity": (c_int32, [c_int32, c_int32, c_int32]),
     "pa_decode": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_void_p,
-                            c_int32, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
-                            c_float, c_int32, c_int32, c_void_p, c_size_t, c_void_p]),
+                            c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+                            c_float, c_int32, c_int32, c_void_p, c_int32, c_int32,
+                            c_void_p, c_size_t, c_void_p]),
     "kv_allocator_create": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_void_p)]),
     "kv_allocator_destroy": (None, [c_void_p]),
     "kv_seq_create": (c_int32, [c_void_p, POINTER(c_int32)]),
@@ -81,6 +99,9 @@ _SIGNATURES = {
     "kv_export_block_tables": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
                                          c_void_p]),
     "kv_allocator_stats": (c_int32, [c_void_p, POINTER(KVStats)]),
+    "kv_decode_step_host": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                      c_int32, c_int32, c_int32, c_int32, c_void_p, ctypes.c_uint64,
+                                      POINTER(StepLayout)]),
 }
 
 _lib = None
@@ -180,11 +201,34 @@ def kv_copy_blocks(k_caches, v_caches, block_pairs, stream=None):
                                 int(block_pairs.shape[0]), nb, hkv, d, bs, _stream(stream)))
 
 
-def _order(work_order, s):
+def plan(context_lens, num_q_heads, num_kv_heads, head_dim, block_size, q_dtype=PKV_F16,
+         partition_size=-1, num_compute_units=0):
+    """Host schedule of one decode launch from host lengths (``pa_decode_plan``).
+
+    Returns (items, plan): items is a host uint32 array of (request << 16 | partition)
+    entries, longest piece first; plan a dict with partition_size, max_parts, num_items,
+    waves_per_cu and workspace_bytes.  ``partition_size`` < 0 lets the library choose.
+    """
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    n = int(lens.shape[0])
+    cap = int(lib().pa_decode_plan_capacity(n, int(lens.max()) if n else 0, int(block_size)))
+    items = np.empty(max(cap, 1), dtype=np.uint32)
+    pl = DecodePlan()
+    _check(lib().pa_decode_plan(lens.ctypes.data if n else None, n, int(num_q_heads),
+                                int(num_kv_heads), int(head_dim), int(block_size), int(q_dtype),
+                                int(partition_size), int(num_compute_units), items.ctypes.data,
+                                int(items.shape[0]), byref(pl)))
+    info = {name: int(getattr(pl, name)) for name, _ in DecodePlan._fields_}
+    return items[: info["num_items"]].copy(), info
+
+
+def _items(work_items):
     torch = _torch()
-    if tuple(work_order.shape) != (s,):
-        raise ValueError("work_order must be [S]")
-    return _dev(work_order, torch.int32, "work_order")
+    if work_items.dim() != 1:
+        raise ValueError("work_items must be 1-D")
+    if work_items.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("work_items must be int32 or uint32 (request << 16 | partition)")
+    return _dev(work_items, work_items.dtype, "work_items"), int(work_items.shape[0])
 
 
 def set_kernel_policy(policy: int) -> int:
@@ -202,12 +246,13 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, p
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-              partition_size=512, workspace=None, stream=None, work_order=None):
+              partition_size=512, workspace=None, stream=None, work_items=None, waves_per_cu=0):
     """Decode attention: out[S, Hq, D] fp32 from q[S, Hq, D] (fp32 or fp16) via the block tables.
 
     ``workspace`` is a device uint8 tensor of at least ``pa_decode_workspace_size`` bytes
-    (needed only when a request may span more than one partition).  ``work_order`` is an
-    optional device int32 [S] permutation: the order in which requests are scheduled.
+    (needed only when a request may span more than one partition).  ``work_items`` is an
+    optional device 1-D int32/uint32 tensor of (request << 16 | partition) pieces in
+    dispatch order (``plan``'s list); ``waves_per_cu`` limits residency (0 = none).
     """
     torch = _torch()
     nb, hkv, bs, d = _pool_geometry(k_cache, v_cache)
@@ -222,6 +267,9 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         raise TypeError("q must be float32 or float16")
     if block_tables.dim() != 2 or block_tables.shape[0] != s or tuple(context_lens.shape) != (s,):
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    items_ptr, n_items = c_void_p(None), 0
+    if work_items is not None:
+        items_ptr, n_items = _items(work_items)
     ws_ptr, ws_bytes = c_void_p(None), 0
     if workspace is not None:
         ws_ptr = _dev(workspace, torch.uint8, "workspace")
@@ -230,10 +278,9 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _dev(out, torch.float32, "out"), _dev(q, q.dtype, "q"), qd,
         _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"), nb,
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
-        _dev(context_lens, torch.int32, "context_lens"),
-        c_void_p(None) if work_order is None else _order(work_order, s), s, hq, hkv, d, bs,
-        float(scale),
-        int(max_context_len), int(partition_size), ws_ptr, ws_bytes, _stream(stream)))
+        _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, bs, float(scale),
+        int(max_context_len), int(partition_size), items_ptr, n_items, int(waves_per_cu),
+        ws_ptr, ws_bytes, _stream(stream)))
 
 
 # --------------------------------------------------------------------------- host allocator
@@ -323,6 +370,25 @@ class BlockAllocator:
         _check(lib().kv_export_block_tables(self._h, seqs.ctypes.data, n, max_blocks, pad_value,
                                             tables.ctypes.data, lens.ctypes.data))
         return tables, lens
+
+    def decode_step_host(self, seqs, max_blocks, pad_value, num_q_heads, num_kv_heads, head_dim,
+                         q_dtype, partition_size, buffer_ptr, buffer_bytes, num_compute_units=0):
+        """One decode step's host work into a caller buffer (``kv_decode_step_host``).
+
+        ``seqs`` must be a C-contiguous int32 array.  Returns the StepLayout, or None when
+        the buffer is too small (the allocator is then unchanged and the layout's
+        ``total_bytes`` -- see ``needed`` -- says how much is needed)."""
+        lay = StepLayout()
+        rc = lib().kv_decode_step_host(self._h, seqs.ctypes.data, int(seqs.shape[0]),
+                                       int(max_blocks), int(pad_value), int(num_q_heads),
+                                       int(num_kv_heads), int(head_dim), int(q_dtype),
+                                       int(partition_size), int(num_compute_units),
+                                       buffer_ptr, int(buffer_bytes), byref(lay))
+        if rc == PKV_ERR_INVALID_ARG and lay.total_bytes > buffer_bytes:
+            self.needed = int(lay.total_bytes)
+            return None
+        _check(rc)
+        return lay
 
     def stats(self) -> dict:
         st = KVStats()

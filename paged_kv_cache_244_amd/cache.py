@@ -9,10 +9,10 @@ kernels.  The pattern of one decode step, all on one HIP stream:
     kv_cache_write(slots, k_new, v_new)  (per layer)
     pa_decode(q, block tables)           (per layer)
 
-Host-to-device uploads of one step (slots, copy pairs, tables, lengths,
-schedule) are packed into one pinned buffer and sent with a single copy: each
-small copy is a serialised operation on the stream, so one copy instead of
-four or five shortens every step.
+Host-to-device uploads of one step (slots, copy pairs, tables, lengths, the
+launch's work items) are packed into one pinned buffer and sent with a single
+copy: each small copy is a serialised operation on the stream, so one copy
+instead of four or five shortens every step.
 """
 
 from __future__ import annotations
@@ -40,47 +40,108 @@ class _Staging:
         self.next = 0
         self.dev = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
+    def _slot(self, nbytes):
+        """Next pinned ring slot, once the copy that last read it is done."""
+        i = self.next
+        self.next = (i + 1) % len(self.host)
+        if self.events[i] is not None:
+            self.events[i].synchronize()
+        if self.host[i].numel() < nbytes:
+            self.host[i] = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        return i
+
+    def _send(self, i, total, stream):
+        if self.dev.numel() < total:
+            self.dev = torch.empty(total, dtype=torch.uint8, device=self.device)
+        if total:
+            # A library kernel reads the pinned buffer over the bus: no copy-engine
+            # hand-off between the step's kernels.
+            _lib._check(_lib.lib().pkv_upload(self.dev.data_ptr(), self.host[i].data_ptr(),
+                                              (total + 15) // 16 * 16, stream.cuda_stream))
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            self.events[i] = ev
+        return self.dev
+
     def upload(self, arrays, stream):
         arrays = [np.ascontiguousarray(a) for a in arrays]
         offsets, total = [], 0
         for a in arrays:
             offsets.append(total)
             total += (a.nbytes + 15) // 16 * 16
-        i = self.next
-        self.next = (i + 1) % len(self.host)
-        if self.events[i] is not None:
-            self.events[i].synchronize()
-        if self.host[i].numel() < total:
-            self.host[i] = torch.empty(total, dtype=torch.uint8, pin_memory=True)
-        if self.dev.numel() < total:
-            self.dev = torch.empty(total, dtype=torch.uint8, device=self.device)
+        i = self._slot(total)
         buf = self.host[i].numpy()
         for a, off in zip(arrays, offsets):
             buf[off:off + a.nbytes] = a.reshape(-1).view(np.uint8)
-        if total:
-            self.dev[:total].copy_(self.host[i][:total], non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(stream)
-            self.events[i] = ev
+        dev = self._send(i, total, stream)
         views = []
         for a, off in zip(arrays, offsets):
-            t = self.dev[off:off + a.nbytes].view(_TORCH_DTYPE[a.dtype.str[1:]])
+            t = dev[off:off + a.nbytes].view(_TORCH_DTYPE[a.dtype.str[1:]])
             views.append(t.view(a.shape))
         return views
+
+    def fill_and_upload(self, fill, stream):
+        """``fill(host_ptr, capacity)`` writes the host buffer in place and returns the
+        bytes used, or None with ``needed`` bytes to retry with.  Returns
+        (result of fill, device buffer, pinned host buffer) after one asynchronous copy."""
+        i = self._slot(0)
+        while True:
+            host = self.host[i]
+            res = fill(host.data_ptr(), host.numel())
+            if res is not None:
+                break
+            self.host[i] = torch.empty(max(fill.needed, 2 * host.numel()), dtype=torch.uint8,
+                                       pin_memory=True)
+        return res, self._send(i, int(res.total_bytes), stream), self.host[i]
 
 
 _TORCH_DTYPE = {"i4": torch.int32, "i8": torch.int64, "f4": torch.float32, "f2": torch.float16}
 
 
+class DeviceArray:
+    """A typed region of a device buffer: its address for the library, and a torch
+    view built only when asked for (``tensor()``)."""
+
+    __slots__ = ("base", "offset", "dtype", "shape", "ptr", "_t")
+
+    def __init__(self, base, offset, dtype, shape):
+        self.base, self.offset, self.dtype, self.shape = base, int(offset), dtype, tuple(shape)
+        self.ptr = base.data_ptr() + self.offset
+        self._t = None
+
+    @classmethod
+    def of(cls, t):
+        a = cls.__new__(cls)
+        a.base, a.offset, a.dtype, a.shape, a.ptr, a._t = t, 0, t.dtype, tuple(t.shape), t.data_ptr(), t
+        return a
+
+    def tensor(self):
+        if self._t is None:
+            n = int(np.prod(self.shape)) * torch.empty(0, dtype=self.dtype).element_size()
+            self._t = self.base[self.offset:self.offset + n].view(self.dtype).view(self.shape)
+        return self._t
+
+    def cpu(self):
+        return self.tensor().cpu()
+
+
 class PagedKVCache:
-    """K/V pools for ``num_layers`` layers sharing one block allocator."""
+    """K/V pools for ``num_layers`` layers sharing one block allocator.
+
+    ``num_q_heads`` and ``q_dtype`` describe the queries that will attend (they
+    decide the kernel and so the schedule that ``decode_step`` and ``batch``
+    prepare); defaults: one query head per KV head, fp16.
+    """
 
     def __init__(self, num_blocks, num_kv_heads, head_dim, block_size, num_layers=1,
-                 initial_order=None, device="cuda", poison=True, stream=None):
+                 initial_order=None, device="cuda", poison=True, stream=None,
+                 num_q_heads=None, q_dtype=None):
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
         self.block_size = block_size
+        self.num_q_heads = int(num_q_heads) if num_q_heads else num_kv_heads
+        self.q_dtype = q_dtype if q_dtype is not None else torch.float16
         self.device = torch.device(device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self.alloc = _lib.BlockAllocator(num_blocks, block_size, initial_order)
@@ -91,7 +152,9 @@ class PagedKVCache:
         self.v = [torch.full(shape, fill, dtype=torch.float16, device=self.device)
                   for _ in range(num_layers)]
         self._staging = _Staging(self.device)
+        self._plan_staging = _Staging(self.device, nbytes=1 << 16)   # re-plans in attend
         self._workspace = None
+        self._stream_ptr = self.stream.cuda_stream
 
     # -- sequences -------------------------------------------------------------
     def new_sequence(self) -> int:
@@ -141,48 +204,86 @@ class PagedKVCache:
         self._copy_pairs_dev(pairs_dev)
         return slots_dev
 
-    def decode_step(self, seqs, max_blocks=None, longest_first=True):
-        """One decode step's host work with a single upload: reserve one slot per
-        sequence (issuing copy-on-write copies), then export tables, lengths and the
-        schedule.  Returns (device slots, DecodeBatch)."""
+    def decode_step(self, seqs, max_blocks=None, partition_size="auto"):
+        """One decode step's host work in one library call and one upload: reserve one
+        slot per sequence (issuing copy-on-write copies), export tables and lengths and
+        plan the launch (``kv_decode_step_host``).  Returns (device slots, DecodeBatch)."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
-        slots, pairs = self.alloc.append_batch(seqs)
-        tables, lens, max_len, order = self._tables(seqs, max_blocks, None, longest_first)
-        arrays = [slots, pairs, tables, lens] + ([order] if order is not None else [])
-        views = self.upload(*arrays)
-        self._copy_pairs_dev(views[1])
-        batch = DecodeBatch(views[2], views[3], max_len, views[4] if order is not None else None,
-                            lens)
-        return views[0], batch
+        key = (self.num_q_heads, self.q_dtype, partition_size)
+        part = -1 if partition_size == "auto" else int(partition_size)
+        qd = _lib.PKV_F16 if self.q_dtype == torch.float16 else _lib.PKV_F32
+        alloc = self.alloc
 
-    def write(self, slots: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, layer: int = 0):
-        _lib.kv_cache_write(self.k[layer], self.v[layer], k_new, v_new, slots, stream=self.stream)
+        def fill(ptr, cap):
+            lay = alloc.decode_step_host(seqs, max_blocks or 0, self.num_blocks, self.num_q_heads,
+                                         self.num_kv_heads, self.head_dim, qd, part, ptr, cap)
+            if lay is None:
+                fill.needed = alloc.needed
+            return lay
+
+        lay, dev, host = self._staging.fill_and_upload(fill, self.stream)
+        n = int(seqs.shape[0])
+        lens_host = host[lay.lens_offset:lay.lens_offset + 4 * n].numpy().view(np.int32).copy()
+        if lay.num_pairs:
+            _lib.kv_copy_blocks(self.k, self.v, DeviceArray(dev, lay.pairs_offset, torch.int32,
+                                                            (lay.num_pairs, 2)).tensor(),
+                                stream=self.stream)
+        plan = {name: int(getattr(lay.plan, name)) for name, _ in _lib.DecodePlan._fields_}
+        slots = DeviceArray(dev, lay.slots_offset, torch.int64, (n,))
+        batch = DecodeBatch(DeviceArray(dev, lay.tables_offset, torch.int32, (n, lay.max_blocks)),
+                            DeviceArray(dev, lay.lens_offset, torch.int32, (n,)),
+                            int(lay.max_context_len), lens_host,
+                            DeviceArray(dev, lay.items_offset, torch.int32, (plan["num_items"],)),
+                            plan, key)
+        return slots, batch
+
+    def write(self, slots, k_new: torch.Tensor, v_new: torch.Tensor, layer: int = 0):
+        """Store k_new/v_new ([T, kv_heads, head_dim] fp16) at ``slots`` (int64 [T])."""
+        if not isinstance(slots, DeviceArray):
+            _lib.kv_cache_write(self.k[layer], self.v[layer], k_new, v_new, slots,
+                                stream=self.stream)
+            return
+        t = slots.shape[0]
+        want = (t, self.num_kv_heads, self.head_dim)
+        for x in (k_new, v_new):
+            if (tuple(x.shape) != want or x.dtype != torch.float16 or not x.is_cuda
+                    or not x.is_contiguous()):
+                raise ValueError(f"k_new/v_new must be contiguous device fp16 {want}")
+        _lib._check(_lib.lib().kv_cache_write(
+            self.k[layer].data_ptr(), self.v[layer].data_ptr(), self.num_blocks, k_new.data_ptr(),
+            v_new.data_ptr(), slots.ptr, t, self.num_kv_heads, self.head_dim, self.block_size,
+            self._stream_ptr))
 
     # -- attention ---------------------------------------------------------------
-    def _tables(self, seqs, max_blocks, pad_value, longest_first):
+    def _tables(self, seqs, max_blocks, pad_value):
         lens = self.alloc.lengths(seqs)
         max_len = int(lens.max()) if len(lens) else 0
         if max_blocks is None:
             max_blocks = max(1, -(-max_len // self.block_size))
         pad = self.num_blocks if pad_value is None else pad_value
         tables, _ = self.alloc.export(seqs, max_blocks, pad)
-        order = None
-        if longest_first and len(lens) > 1:
-            order = np.argsort(-lens, kind="stable").astype(np.int32)
-        return tables, lens, max_len, order
+        return tables, lens, max_len
 
-    def batch(self, seqs, max_blocks=None, pad_value=None, longest_first=True) -> "DecodeBatch":
-        """Upload the block tables, lengths and schedule of ``seqs`` for one decode launch.
+    def _plan(self, lens, num_q_heads, q_dtype, partition_size):
+        """Host schedule (library planner): work items as int32 bits, plan dict."""
+        part = -1 if partition_size == "auto" else int(partition_size)
+        qd = _lib.PKV_F16 if q_dtype == torch.float16 else _lib.PKV_F32
+        items, info = _lib.plan(lens, num_q_heads, self.num_kv_heads, self.head_dim,
+                                self.block_size, qd, part)
+        return items.view(np.int32), info
+
+    def batch(self, seqs, max_blocks=None, pad_value=None, partition_size="auto") -> "DecodeBatch":
+        """Upload the block tables, lengths and launch schedule of ``seqs`` for decode.
 
         The returned device tensors stay valid until the next upload.
         """
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
-        tables, lens, max_len, order = self._tables(seqs, max_blocks, pad_value, longest_first)
-        if order is None:
-            t, l_ = self.upload(tables, lens)
-            return DecodeBatch(t, l_, max_len, None, lens)
-        t, l_, o = self.upload(tables, lens, order)
-        return DecodeBatch(t, l_, max_len, o, lens)
+        tables, lens, max_len = self._tables(seqs, max_blocks, pad_value)
+        key = (self.num_q_heads, self.q_dtype, partition_size)
+        items, info = self._plan(lens, *key)
+        t, l_, it = self.upload(tables, lens, items)
+        return DecodeBatch(DeviceArray.of(t), DeviceArray.of(l_), max_len, lens,
+                           DeviceArray.of(it), info, key)
 
     def workspace(self, num_seqs, num_q_heads, max_context_len, partition_size):
         need = _lib.pa_decode_workspace_size(num_seqs, num_q_heads, self.head_dim, max_context_len,
@@ -193,58 +294,67 @@ class PagedKVCache:
             self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._workspace
 
-    def attend(self, q, batch: "DecodeBatch", scale, partition_size="auto", layer=0, out=None):
-        """Decode attention for ``batch``; ``partition_size`` "auto" applies
-        ``choose_partition`` to the batch's host-side lengths."""
+    def attend(self, q, batch: "DecodeBatch", scale, partition_size=None, layer=0, out=None):
+        """Decode attention for ``batch`` with the schedule planned for it.
+
+        ``partition_size`` None keeps the batch's plan; "auto" or a number plans
+        again (the library's policy, or that split), as does a query shape or dtype
+        other than the one the batch was planned for.
+        """
         s, hq, d = q.shape
-        if partition_size == "auto":
-            partition_size = choose_partition(batch.lens_host, hq, self.num_kv_heads,
-                                              self.block_size)
+        key = (hq, q.dtype, batch.plan_key[2] if partition_size is None else partition_size)
+        if key == batch.plan_key:
+            items, info = batch.items_dev, batch.plan
+        else:
+            items_h, info = self._plan(batch.lens_host, *key)
+            (items,) = self._plan_staging.upload([items_h], self.stream)
+            items = DeviceArray.of(items)
         if out is None:
             out = torch.empty((s, hq, d), dtype=torch.float32, device=self.device)
-        ws = self.workspace(s, hq, batch.max_len, partition_size)
-        _lib.pa_decode(out, q, self.k[layer], self.v[layer], batch.tables, batch.lens, scale,
-                       batch.max_len, partition_size=partition_size, workspace=ws,
-                       stream=self.stream, work_order=batch.order)
+        if (q.dtype not in (torch.float16, torch.float32) or not q.is_cuda or not q.is_contiguous()
+                or d != self.head_dim or s != batch.num_seqs):
+            raise ValueError("q must be a contiguous device fp16/fp32 [S, Hq, head_dim] tensor "
+                             "for the batch's S requests")
+        if (tuple(out.shape) != (s, hq, d) or out.dtype != torch.float32 or not out.is_cuda
+                or not out.is_contiguous()):
+            raise ValueError("out must be a contiguous device fp32 [S, Hq, head_dim] tensor")
+        part = info["partition_size"]
+        ws = self.workspace(s, hq, batch.max_len, part)
+        _lib._check(_lib.lib().pa_decode(
+            out.data_ptr(), q.data_ptr(), _lib.PKV_F16 if q.dtype == torch.float16 else _lib.PKV_F32,
+            self.k[layer].data_ptr(), self.v[layer].data_ptr(), self.num_blocks,
+            batch.tables_dev.ptr, batch.tables_dev.shape[1], batch.lens_dev.ptr, s, hq,
+            self.num_kv_heads, d, self.block_size, float(scale), batch.max_len, part, items.ptr,
+            items.shape[0], info["waves_per_cu"], ws.data_ptr() if ws is not None else None,
+            ws.numel() if ws is not None else 0, self._stream_ptr))
         return out
 
 
-def head_tile(num_q_heads: int, num_kv_heads: int) -> int:
-    """Query heads one wave serves (the library's choice for fp16 queries: groups of
-    4 or more run 4, 8 or 16 heads per wave on the matrix cores)."""
-    group = num_q_heads // num_kv_heads
-    for gt in (16, 8, 4):
-        if group % gt == 0:
-            return gt
-    return 2 if group % 2 == 0 else 1
-
-
-def choose_partition(lens_host, num_q_heads, num_kv_heads, block_size, gpu_waves=2048) -> int:
-    """Split-context policy (measured on MI355X): one pass per request when there are
-    enough (request, head tile) work items to fill the GPU; otherwise the largest of
-    1024 / 512 tokens that yields a GPU's worth of items, else 512."""
-    lens = np.asarray(lens_host, dtype=np.int64)
-    if lens.size == 0:
-        return 0
-    tiles = num_q_heads // head_tile(num_q_heads, num_kv_heads)
-    if lens.size * tiles >= gpu_waves and int(lens.max()) <= 8192:
-        return 0
-    for part in (1024, 512):
-        if part % block_size:
-            continue
-        if tiles * int(np.sum((lens + part - 1) // part)) >= gpu_waves:
-            return part
-    return max(512, block_size)
-
-
 class DecodeBatch:
-    """Device views of one decode launch: tables, lengths, schedule; host lengths."""
+    """One decode launch: device tables, lengths and work items (``*_dev``: addresses
+    for the library; ``tables``/``lens``/``items``: torch views, built on demand), the
+    host lengths, the plan and the (num_q_heads, q dtype, partition request) it was
+    made for."""
 
-    __slots__ = ("tables", "lens", "max_len", "order", "lens_host")
+    __slots__ = ("tables_dev", "lens_dev", "max_len", "lens_host", "items_dev", "plan",
+                 "plan_key", "num_seqs")
 
-    def __init__(self, tables, lens, max_len, order, lens_host):
-        self.tables = tables
-        self.lens = lens
+    def __init__(self, tables, lens, max_len, lens_host, items, plan, plan_key):
+        self.tables_dev, self.lens_dev, self.items_dev = tables, lens, items
         self.max_len = max_len
-        self.order = order
         self.lens_host = lens_host
+        self.plan = plan
+        self.plan_key = plan_key
+        self.num_seqs = tables.shape[0]
+
+    @property
+    def tables(self):
+        return self.tables_dev.tensor()
+
+    @property
+    def lens(self):
+        return self.lens_dev.tensor()
+
+    @property
+    def items(self):
+        return self.items_dev.tensor()

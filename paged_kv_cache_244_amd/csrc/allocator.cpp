@@ -13,7 +13,9 @@
 //
 // Plain host C++, no HIP.  Free list: a stack whose first pops follow the
 // caller's initial order; freed blocks are pushed and so handed out next.
+#include <algorithm>
 #include <cstdint>
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -28,6 +30,7 @@ struct kv_allocator {
   struct Seq {
     bool live = false;
     int64_t length = 0;
+    int32_t pending = 0;             // scratch of kv_decode_step_host, 0 between calls
     std::vector<int32_t> blocks;     // logical -> physical
   };
   std::vector<Seq> seqs;             // indexed by id; ids never reused
@@ -287,6 +290,87 @@ int kv_export_block_tables(const kv_allocator* a, const int32_t* seqs, int32_t n
     for (int32_t j = static_cast<int32_t>(nb); j < max_blocks_per_seq; ++j) row[j] = pad_value;
     lens_out[i] = static_cast<int32_t>(s.length);
   }
+  return PKV_OK;
+}
+
+int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
+                        int32_t max_blocks_per_seq, int32_t pad_value, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t q_dtype,
+                        int32_t partition_size, int32_t num_compute_units, void* buffer,
+                        uint64_t buffer_bytes, kv_step_layout* layout) {
+  if (!a || !layout) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  *layout = kv_step_layout{};
+  if (num_seqs < 0 || num_seqs > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs %d outside [0, 65535]", num_seqs);
+  if (num_seqs > 0 && !seqs) return fail(PKV_ERR_INVALID_ARG, "NULL seqs");
+  const int32_t B = a->block_size;
+  // Final lengths per entry (a sequence listed k times grows by k).
+  for (int32_t i = 0; i < num_seqs; ++i)
+    if (int rc = check_seq(a, seqs[i])) return rc;
+  for (int32_t i = 0; i < num_seqs; ++i) a->seqs[seqs[i]].pending += 1;
+  static thread_local std::vector<int32_t> lens;
+  lens.resize(static_cast<size_t>(num_seqs));
+  int64_t longest = 0, blocks_wanted = 0;
+  bool too_long = false;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const kv_allocator::Seq& s = a->seqs[seqs[i]];
+    const int64_t len = s.length + s.pending;
+    too_long |= len > INT32_MAX;
+    lens[i] = static_cast<int32_t>(len > INT32_MAX ? INT32_MAX : len);
+    longest = std::max(longest, len);
+    blocks_wanted = std::max(blocks_wanted, blocks_for(len, B));
+  }
+  for (int32_t i = 0; i < num_seqs; ++i) a->seqs[seqs[i]].pending = 0;
+  if (too_long) return fail(PKV_ERR_INVALID_ARG, "length overflows int32");
+  int32_t width = max_blocks_per_seq;
+  if (width <= 0) width = static_cast<int32_t>(std::max<int64_t>(1, blocks_wanted));
+  if (blocks_wanted > width)
+    return fail(PKV_ERR_INVALID_ARG, "a sequence needs %lld blocks > max_blocks_per_seq %d",
+                static_cast<long long>(blocks_wanted), width);
+  // The plan, into scratch first: its size decides the layout.
+  static thread_local std::vector<uint32_t> items;
+  items.resize(static_cast<size_t>(std::max(1, pa_decode_plan_capacity(num_seqs, static_cast<int32_t>(longest), B))));
+  pkv_decode_plan plan{};
+  if (int rc = pa_decode_plan(lens.data(), num_seqs, num_q_heads, num_kv_heads, head_dim, B, q_dtype,
+                              partition_size, num_compute_units, items.data(),
+                              static_cast<int32_t>(items.size()), &plan))
+    return rc;
+  auto up16 = [](uint64_t x) { return (x + 15) & ~static_cast<uint64_t>(15); };
+  kv_step_layout L{};
+  L.slots_offset = 0;
+  L.pairs_offset = up16(L.slots_offset + 8ull * num_seqs);
+  L.tables_offset = up16(L.pairs_offset + 8ull * num_seqs);
+  L.lens_offset = up16(L.tables_offset + 4ull * num_seqs * static_cast<uint64_t>(width));
+  L.items_offset = up16(L.lens_offset + 4ull * num_seqs);
+  L.total_bytes = up16(L.items_offset + 4ull * static_cast<uint64_t>(plan.num_items));
+  L.max_blocks = width;
+  L.max_context_len = static_cast<int32_t>(longest);
+  L.plan = plan;
+  if (!buffer || buffer_bytes < L.total_bytes) {
+    layout->total_bytes = L.total_bytes;
+    return fail(PKV_ERR_INVALID_ARG, "step buffer of %llu bytes needed (got %llu)",
+                static_cast<unsigned long long>(L.total_bytes),
+                static_cast<unsigned long long>(buffer ? buffer_bytes : 0));
+  }
+  char* base = static_cast<char*>(buffer);
+  int32_t n_pairs = 0;
+  if (int rc = kv_batch_append(a, seqs, num_seqs, reinterpret_cast<int64_t*>(base + L.slots_offset),
+                               reinterpret_cast<int32_t*>(base + L.pairs_offset), &n_pairs))
+    return rc;
+  L.num_pairs = n_pairs;
+  int32_t* tables = reinterpret_cast<int32_t*>(base + L.tables_offset);
+  int32_t* lens_out = reinterpret_cast<int32_t*>(base + L.lens_offset);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const kv_allocator::Seq& s = a->seqs[seqs[i]];
+    int32_t* row = tables + static_cast<int64_t>(i) * width;
+    const int32_t nb = static_cast<int32_t>(s.blocks.size());
+    if (nb > 0) std::memcpy(row, s.blocks.data(), sizeof(int32_t) * nb);
+    for (int32_t j = nb; j < width; ++j) row[j] = pad_value;
+    lens_out[i] = static_cast<int32_t>(s.length);
+  }
+  if (plan.num_items > 0)
+    std::memcpy(base + L.items_offset, items.data(), sizeof(uint32_t) * plan.num_items);
+  *layout = L;
   return PKV_OK;
 }
 

@@ -1,0 +1,197 @@
+// Host launch planning: kernel policy and choice, the planner pa_decode_plan
+// (partition size, work list longest piece first, residency limit) and its
+// size helpers.  Plain C++, no HIP.
+//
+// Why: decode reads every cached byte of every request once per step ("800
+// kilobytes per token" (shashforge.dev), section "The old answer, imported
+// honestly"; "The KV cache is a systems problem" (rsw.lol), section "Calculate
+// bytes per token before choosing a batch"), so a launch lasts as long as its
+// busiest compute unit; batches mix short and long contexts ("Only 20.4% of
+// your KV cache held actual tokens" (blog.teqners.com), section "Why the KV
+// cache is the thing that limits your batch").
+#include "decode_plan.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <utility>
+#include <vector>
+
+#include "errors.h"
+#include "pagedkv.h"
+
+namespace pkv_plan {
+namespace {
+
+using pkv::fail;
+
+int head_tile(int group) {
+  if (group % 4 == 0) return 4;
+  if (group % 2 == 0) return 2;
+  return 1;
+}
+
+// Kernel policy for head groups (see pa_decode_set_kernel_policy).  The first
+// value comes from PKV_GQA_KERNEL=valu in the environment, if set.
+std::atomic<int> g_policy{-1};
+
+int kernel_policy() {
+  int v = g_policy.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* env = std::getenv("PKV_GQA_KERNEL");
+    const int init = (env != nullptr && std::strcmp(env, "valu") == 0) ? PKV_POLICY_VALU
+                                                                       : PKV_POLICY_DEFAULT;
+    g_policy.compare_exchange_strong(v, init);
+    v = g_policy.load(std::memory_order_relaxed);
+  }
+  return v;
+}
+
+}  // namespace
+
+KernelChoice choose_kernel(int32_t q_dtype, int group) {
+  const bool mfma = q_dtype == PKV_F16 && group % 4 == 0 && kernel_policy() != PKV_POLICY_VALU;
+  if (mfma) return {true, group % 16 == 0 ? 16 : (group % 8 == 0 ? 8 : 4)};
+  return {false, head_tile(group)};
+}
+
+namespace {
+
+// Partition size chosen by pa_decode_plan (see pagedkv.h): lens already clamped >= 0.
+int32_t auto_partition(const int32_t* lens, int32_t n, int tiles, int cus, int32_t block_size) {
+  int64_t total = 0;
+  int32_t longest = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    total += lens[i];
+    longest = lens[i] > longest ? lens[i] : longest;
+  }
+  const int64_t simds = static_cast<int64_t>(cus) * 4;
+  const double share = static_cast<double>(total) * tiles / static_cast<double>(simds);
+  if (static_cast<int64_t>(n) * tiles >= simds && longest <= 1.25 * share) return 0;
+  int32_t part = 256;
+  for (int32_t cand : {2048, 1024, 512}) {
+    if (cand <= share / 2) {
+      part = cand;
+      break;
+    }
+  }
+  return (part + block_size - 1) / block_size * block_size;
+}
+
+}  // namespace
+}  // namespace pkv_plan
+
+using pkv::fail;
+using namespace pkv_plan;
+
+extern "C" int pa_decode_set_kernel_policy(int32_t policy) {
+  if (policy != PKV_POLICY_DEFAULT && policy != PKV_POLICY_VALU)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_set_kernel_policy: unknown policy %d", policy);
+  const int previous = kernel_policy();
+  g_policy.store(policy, std::memory_order_relaxed);
+  return previous;
+}
+
+extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                           int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return workspace_bytes_for(num_seqs, num_q_heads, head_dim,
+                             parts_for(max_context_len, partition_size));
+}
+
+extern "C" int32_t pa_decode_plan_capacity(int32_t num_seqs, int32_t max_context_len,
+                                           int32_t block_size) {
+  if (num_seqs <= 0) return 0;
+  const int64_t per = block_size > 0 && max_context_len > 0
+                          ? (static_cast<int64_t>(max_context_len) + block_size - 1) / block_size
+                          : 1;
+  const int64_t n = static_cast<int64_t>(num_seqs) * (per > 0 ? per : 1);
+  return n > INT32_MAX ? INT32_MAX : static_cast<int32_t>(n);
+}
+
+extern "C" int pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t q_dtype, int32_t partition_size, int32_t num_compute_units,
+                              uint32_t* items, int32_t items_capacity, pkv_decode_plan* plan) {
+  if (!plan) return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: NULL plan");
+  *plan = pkv_decode_plan{};
+  if (num_seqs < 0 || num_seqs > 65535 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      block_size <= 0 || items_capacity < 0)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: bad sizes");
+  if (num_seqs > 0 && !context_lens) return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: NULL lengths");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "pa_decode_plan: num_q_heads %d not a multiple of %d",
+                num_q_heads, num_kv_heads);
+  if (q_dtype != PKV_F32 && q_dtype != PKV_F16)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: q_dtype %d unknown", q_dtype);
+  if (partition_size > 0 && partition_size % block_size != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: partition_size %d not a multiple of %d",
+                partition_size, block_size);
+  const KernelChoice kc = choose_kernel(q_dtype, num_q_heads / num_kv_heads);
+  const int tiles = num_q_heads / kc.gt;
+  // Per-thread scratch: a plan is made every decode step.
+  static thread_local std::vector<int32_t> lens;
+  static thread_local std::vector<uint64_t> keys;
+  lens.resize(static_cast<size_t>(num_seqs));
+  int32_t longest = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    lens[i] = context_lens[i] > 0 ? context_lens[i] : 0;
+    longest = std::max(longest, lens[i]);
+  }
+  const int cus = num_compute_units > 0 ? num_compute_units : 256;
+  const int32_t part =
+      partition_size >= 0 ? partition_size : auto_partition(lens.data(), num_seqs, tiles, cus, block_size);
+  const int64_t parts = parts_for(longest, part);
+  if (parts > 65535) return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: more than 65535 partitions");
+
+  int64_t count = 0;
+  for (int32_t i = 0; i < num_seqs; ++i) count += part > 0 && lens[i] > 0 ? (lens[i] + part - 1) / part : 1;
+  plan->partition_size = part;
+  plan->max_parts = static_cast<int32_t>(parts);
+  plan->num_items = count > INT32_MAX ? INT32_MAX : static_cast<int32_t>(count);
+  plan->waves_per_cu = kc.mfma ? kMfmaWavesPerCu : 0;
+  plan->workspace_bytes = workspace_bytes_for(num_seqs, num_q_heads, head_dim, parts);
+  if (count > items_capacity)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: %lld items do not fit in %d",
+                static_cast<long long>(count), items_capacity);
+  if (count > 0 && !items) return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: NULL items");
+
+  // Item order.  Requests by length, longest first (ties: lower index), as
+  // ascending 64-bit keys (complemented length, index).  Full partitions (all
+  // of one size) come first, request by request; then the requests' shorter
+  // last pieces by size, largest first (ties: the request's rank above).
+  keys.resize(static_cast<size_t>(num_seqs));
+  for (int32_t i = 0; i < num_seqs; ++i)
+    keys[i] = (static_cast<uint64_t>(UINT32_MAX - static_cast<uint32_t>(lens[i])) << 32) |
+              static_cast<uint32_t>(i);
+  std::sort(keys.begin(), keys.end());
+  int64_t k = 0;
+  if (part > 0) {
+    for (int32_t r = 0; r < num_seqs; ++r) {
+      const int32_t s = static_cast<int32_t>(keys[r] & 0xFFFFFFFFu);
+      for (int32_t j = 0; j < lens[s] / part; ++j) items[k++] = PKV_ITEM(s, j);
+    }
+  }
+  // Tail keys replace the request keys in place: (complemented tail size, rank),
+  // with the request index recovered from the rank through a second array.
+  static thread_local std::vector<int32_t> by_rank;
+  by_rank.resize(static_cast<size_t>(num_seqs));
+  int32_t ntails = 0;
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    const int32_t s = static_cast<int32_t>(keys[r] & 0xFFFFFFFFu);
+    by_rank[r] = s;
+    const int32_t rest = part > 0 ? lens[s] % part : lens[s];
+    if (rest > 0 || lens[s] == 0)
+      keys[ntails++] = (static_cast<uint64_t>(UINT32_MAX - static_cast<uint32_t>(rest)) << 32) |
+                       static_cast<uint32_t>(r);
+  }
+  std::sort(keys.begin(), keys.begin() + ntails);
+  for (int32_t t = 0; t < ntails; ++t) {
+    const int32_t s = by_rank[keys[t] & 0xFFFFFFFFu];
+    items[k++] = PKV_ITEM(s, part > 0 ? lens[s] / part : 0);
+  }
+  if (k != count) return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: internal count mismatch");
+  return PKV_OK;
+}
+

@@ -10,6 +10,12 @@
 //
 // Both are bit copies of fp16 data moved as 16-byte vectors; they are bound by
 // HBM bandwidth (2 bytes moved per byte copied), not by arithmetic.
+//
+// pkv_upload: the per-step host data (slots, copy pairs, block tables, lengths,
+// work items) read by a kernel straight from pinned host memory and stored in
+// device memory, on the caller's stream.  Same page, section "The page table,
+// relocated into attention": the tables are made on the host and must be in
+// GPU memory before the kernel walks them.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -53,6 +59,17 @@ __global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(
     k_cache[dst] = k_new[idx];
     v_cache[dst] = v_new[idx];
   }
+}
+
+// Host-to-device copy as a kernel: 16 bytes per lane, grid-stride.  The loads
+// cross PCIe (the source is pinned host memory the GPU can address); running
+// on the compute queue keeps the step's kernels free of copy-engine handoffs.
+__global__ __launch_bounds__(kThreads) void upload_kernel(uint4* __restrict__ dst,
+                                                          const uint4* __restrict__ src,
+                                                          int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
 }
 
 constexpr int kMaxLayersPerLaunch = 32;
@@ -159,4 +176,37 @@ extern "C" int kv_copy_blocks(void* const* k_caches, void* const* v_caches, int3
     if (int rc = hip_status("kv_copy_blocks launch")) return rc;
   }
   return PKV_OK;
+}
+
+extern "C" int pkv_upload(void* dst, const void* src, uint64_t bytes, void* stream) {
+  if (bytes == 0) return PKV_OK;
+  if (!dst || !src) return fail(PKV_ERR_INVALID_ARG, "pkv_upload: NULL pointer");
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(src) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_upload: pointers and size must be multiples of 16");
+  // The kernel may only touch memory the GPU can address: the source must be
+  // pinned host memory (its device-side address is taken from the runtime) and
+  // the destination device memory.  Anything else is refused before a launch.
+  hipPointerAttribute_t sa{}, da{};
+  if (hipPointerGetAttributes(&sa, src) != hipSuccess || sa.type != hipMemoryTypeHost ||
+      sa.devicePointer == nullptr) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_INVALID_ARG, "pkv_upload: source is not pinned host memory");
+  }
+  if (hipPointerGetAttributes(&da, dst) != hipSuccess || da.type != hipMemoryTypeDevice) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_INVALID_ARG, "pkv_upload: destination is not device memory");
+  }
+  const char* dev_src = static_cast<const char*>(sa.devicePointer);
+  if (sa.hostPointer != nullptr && sa.hostPointer != src)   // attributes of the allocation base
+    dev_src += static_cast<const char*>(src) - static_cast<const char*>(sa.hostPointer);
+  if (reinterpret_cast<uintptr_t>(dev_src) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_upload: device address of the source is misaligned");
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  int64_t blocks = (n16 + kThreads - 1) / kThreads;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(upload_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
+                     reinterpret_cast<const uint4*>(dev_src), n16);
+  return hip_status("pkv_upload launch");
 }

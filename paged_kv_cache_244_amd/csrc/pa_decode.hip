@@ -1,5 +1,6 @@
-// pa_decode entry point: argument checks, kernel choice (VALU or MFMA),
-// split-context geometry and workspace, launch order.
+// pa_decode entry point: argument checks, split-context geometry and
+// workspace, residency limit, launch order.  The kernel choice and the launch
+// planner are host code in decode_plan.cpp.
 //
 // What is computed: "800 kilobytes per token" (shashforge.dev), section "The old
 // answer, imported honestly", and "Only 20.4% of your KV cache held actual
@@ -13,12 +14,12 @@
 // split-context partitions).
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cfloat>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
+#include <mutex>
+#include <vector>
 
+#include "decode_plan.h"
 #include "errors.h"
 #include "pa_decode_common.h"
 #include "pagedkv.h"
@@ -27,75 +28,74 @@ namespace {
 
 using pkv::fail;
 using namespace pkv_decode;
+using pkv_plan::KernelChoice;
+using pkv_plan::align256;
+using pkv_plan::choose_kernel;
+using pkv_plan::parts_for;
+using pkv_plan::workspace_bytes_for;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxGridY = 32768;      // work-list entries per grid row (y), then z
 
+// Dynamic LDS that limits a launch of fn to about waves_per_cu one-wave
+// workgroups per compute unit (0 = no limit).  Cached per kernel and device.
+struct LdsInfo {
+  const void* fn = nullptr;
+  int device = -1;
+  int static_bytes = 0;
+  int per_cu = 0;
+  int per_block = 0;
+};
+std::mutex g_lds_mu;
+std::vector<LdsInfo> g_lds_cache;
 
-
-int head_tile(int group) {
-  if (group % 4 == 0) return 4;
-  if (group % 2 == 0) return 2;
-  return 1;
-}
-
-// Kernel policy for head groups (see pa_decode_set_kernel_policy).  The first
-// value comes from PKV_GQA_KERNEL=valu in the environment, if set.
-std::atomic<int> g_policy{-1};
-
-int kernel_policy() {
-  int v = g_policy.load(std::memory_order_relaxed);
-  if (v < 0) {
-    const char* env = std::getenv("PKV_GQA_KERNEL");
-    const int init = (env != nullptr && std::strcmp(env, "valu") == 0) ? PKV_POLICY_VALU
-                                                                       : PKV_POLICY_DEFAULT;
-    g_policy.compare_exchange_strong(v, init);
-    v = g_policy.load(std::memory_order_relaxed);
+hipError_t reserve_lds_bytes(const void* fn, int waves_per_cu, unsigned* dyn) {
+  *dyn = 0;
+  if (waves_per_cu <= 0) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  LdsInfo info;
+  {
+    std::lock_guard<std::mutex> lock(g_lds_mu);
+    for (const LdsInfo& c : g_lds_cache)
+      if (c.fn == fn && c.device == dev) info = c;
   }
-  return v;
-}
-
-bool gqa_valu_forced() { return kernel_policy() == PKV_POLICY_VALU; }
-
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-int64_t parts_for(int32_t max_context_len, int32_t partition_size) {
-  if (partition_size <= 0 || max_context_len <= 0) return 1;
-  return (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
-}
-
-size_t workspace_bytes_for(int32_t S, int32_t Hq, int32_t D, int64_t parts) {
-  if (parts <= 1) return 0;
-  const size_t n = static_cast<size_t>(S) * Hq * parts;
-  return align256(n * D * sizeof(float)) + align256(n * 2 * sizeof(float));
+  if (info.fn == nullptr) {
+    hipFuncAttributes attr;
+    e = hipFuncGetAttributes(&attr, fn);
+    if (e != hipSuccess) return e;
+    info.fn = fn;
+    info.device = dev;
+    info.static_bytes = static_cast<int>(attr.sharedSizeBytes);
+    e = hipDeviceGetAttribute(&info.per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&info.per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_lds_mu);
+    g_lds_cache.push_back(info);
+  }
+  const int w = waves_per_cu < 4 ? 4 : waves_per_cu;
+  int bytes = info.per_cu / w - info.static_bytes;
+  if (bytes > info.per_block - info.static_bytes) bytes = info.per_block - info.static_bytes;
+  bytes &= ~255;
+  *dyn = bytes > 0 ? static_cast<unsigned>(bytes) : 0u;
+  return hipSuccess;
 }
 
 }  // namespace
 
-extern "C" int pa_decode_set_kernel_policy(int32_t policy) {
-  if (policy != PKV_POLICY_DEFAULT && policy != PKV_POLICY_VALU)
-    return fail(PKV_ERR_INVALID_ARG, "pa_decode_set_kernel_policy: unknown policy %d", policy);
-  const int previous = kernel_policy();
-  g_policy.store(policy, std::memory_order_relaxed);
-  return previous;
-}
-
-extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                           int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  return workspace_bytes_for(num_seqs, num_q_heads, head_dim,
-                             parts_for(max_context_len, partition_size));
-}
-
 extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                          const void* v_cache, int32_t num_blocks, const int32_t* block_tables,
                          int32_t max_blocks_per_seq, const int32_t* context_lens,
-                         const int32_t* work_order, int32_t num_seqs,
-                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                         int32_t block_size, float scale, int32_t max_context_len,
-                         int32_t partition_size, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, float scale,
+                         int32_t max_context_len, int32_t partition_size,
+                         const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
-      max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0)
+      max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0 || num_work_items < 0 ||
+      waves_per_cu < 0)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: bad sizes");
   if (num_q_heads % num_kv_heads != 0)
     return fail(PKV_ERR_UNSUPPORTED, "pa_decode: num_q_heads %d not a multiple of num_kv_heads %d",
@@ -109,17 +109,16 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: at most 65535 sequences per call");
   if (num_q_heads > 65535)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: too many query heads");
-  const int group = num_q_heads / num_kv_heads;
-  const bool mfma = q_dtype == PKV_F16 && group % 4 == 0 && !gqa_valu_forced();
-  const int gt = mfma ? (group % 16 == 0 ? 16 : (group % 8 == 0 ? 8 : 4)) : head_tile(group);
-  KernelFn fn = mfma ? pick_mfma_kernel(head_dim, block_size, gt)
-                     : pick_valu_kernel(head_dim, block_size, gt, q_dtype == PKV_F32);
+  const KernelChoice kc = choose_kernel(q_dtype, num_q_heads / num_kv_heads);
+  KernelFn fn = kc.mfma ? pick_mfma_kernel(head_dim, block_size, kc.gt)
+                        : pick_valu_kernel(head_dim, block_size, kc.gt, q_dtype == PKV_F32);
   if (!fn)
     return fail(PKV_ERR_UNSUPPORTED, "pa_decode: head_dim %d / block_size %d not built", head_dim,
                 block_size);
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: NULL pointer");
+  if (work_items && num_work_items == 0) return PKV_OK;
 
   int64_t clamp64 = static_cast<int64_t>(max_blocks_per_seq) * block_size;
   if (clamp64 > max_context_len) clamp64 = max_context_len;
@@ -145,14 +144,15 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
   prm.v_cache = static_cast<const uint4*>(v_cache);
   prm.block_tables = block_tables;
   prm.context_lens = context_lens;
-  prm.work_order = work_order;
+  prm.items = work_items;
+  prm.num_items = work_items ? num_work_items : 0;
   prm.num_seqs = num_seqs;
   prm.num_blocks = num_blocks;
   prm.max_blocks_per_seq = max_blocks_per_seq;
   prm.num_q_heads = num_q_heads;
   prm.num_kv_heads = num_kv_heads;
   prm.group = num_q_heads / num_kv_heads;
-  prm.num_head_tiles = num_q_heads / gt;
+  prm.num_head_tiles = num_q_heads / kc.gt;
   prm.scale_log2 = scale * kLog2e;
   prm.len_clamp = len_clamp;
   prm.part_tokens = part_tokens;
@@ -171,20 +171,27 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
                                          align256(n * head_dim * sizeof(float)));
   }
 
-  // One wave per workgroup: the dispatcher then places work at wave granularity,
-  // which balances requests of unequal length across CUs far better than
-  // multi-wave groups.  Grid: x = head tile (fastest), y = request in
-  // work_order (longest first is the caller's best choice), z = partition.
-  // Workgroups are dealt round-robin to the 8 XCDs and, inside an XCD, to its
-  // shader engines, so neighbours in dispatch order must carry similar work.
-  // With the partition varying fastest, a request's long first partitions and
-  // short last one alternated with a fixed period and whole XCDs / shader
-  // engines received only the long ones (measured: up to 2x slower on GQA).
+  unsigned dyn_lds = 0;
+  hipError_t e = reserve_lds_bytes(reinterpret_cast<const void*>(fn), waves_per_cu, &dyn_lds);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode: kernel attributes: %s", hipGetErrorString(e));
+
+  // One wave per workgroup: the dispatcher then places work at wave granularity.
+  // Grid x = head tile (fastest), then the pieces: with a work list, (y, z)
+  // enumerate its entries in order, so the dispatcher hands out the pieces in
+  // the list's order (longest first balances the compute units); without one,
+  // y = request and z = partition.  Workgroups are dealt round-robin to the 8
+  // XCDs and, inside an XCD, to its shader engines, so neighbours in dispatch
+  // order must carry similar work: the head tiles of one piece do.
+  dim3 grid(static_cast<unsigned>(prm.num_head_tiles), static_cast<unsigned>(num_seqs),
+            static_cast<unsigned>(parts));
+  if (work_items) {
+    const int ny = num_work_items < kMaxGridY ? num_work_items : kMaxGridY;
+    grid.y = static_cast<unsigned>(ny);
+    grid.z = static_cast<unsigned>((num_work_items + ny - 1) / ny);
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(prm.num_head_tiles), static_cast<unsigned>(num_seqs),
-                              static_cast<unsigned>(parts)),
-                     dim3(kWave), 0, st, prm);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL(fn, grid, dim3(kWave), dyn_lds, st, prm);
+  e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode launch: %s", hipGetErrorString(e));
   if (parts > 1) {
     e = launch_reduce(prm, head_dim, st);

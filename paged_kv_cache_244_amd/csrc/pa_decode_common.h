@@ -27,7 +27,7 @@ struct DecodeParams {
   const uint4* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  const int32_t* work_order;  // optional [S] permutation: grid z -> request (NULL = identity)
+  const uint32_t* items;      // optional [num_items] (request << 16 | partition), NULL = grid
   int32_t num_seqs;
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
@@ -39,6 +39,7 @@ struct DecodeParams {
   int32_t len_clamp;          // min(max_context_len, max_blocks_per_seq * B)
   int32_t part_tokens;        // tokens per partition, multiple of B
   int32_t max_parts;
+  int32_t num_items;
 };
 
 // K/V tiles are read exactly once: non-temporal loads keep them from displacing
@@ -78,9 +79,21 @@ __device__ __forceinline__ float shfl(float v, int src_lane) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Request handled by this workgroup (the schedule maps grid y to a request).
-__device__ __forceinline__ int scheduled_seq(const DecodeParams& p) {
-  return p.work_order ? p.work_order[blockIdx.y] : static_cast<int>(blockIdx.y);
+// The (request, partition) piece handled by this workgroup.  With a work list,
+// grid (y, z) enumerates its entries in order (y fastest); without one, grid y
+// is the request and z the partition.  Returns false for entries to skip.
+__device__ __forceinline__ bool scheduled_piece(const DecodeParams& p, int& seq, int& part) {
+  if (p.items) {
+    const unsigned k = blockIdx.y + blockIdx.z * gridDim.y;
+    if (k >= static_cast<unsigned>(p.num_items)) return false;
+    const uint32_t it = p.items[k];
+    seq = static_cast<int>(it >> 16);
+    part = static_cast<int>(it & 0xFFFFu);
+  } else {
+    seq = static_cast<int>(blockIdx.y);
+    part = static_cast<int>(blockIdx.z);
+  }
+  return seq < p.num_seqs && part < p.max_parts;
 }
 
 __device__ __forceinline__ int clamped_len(const DecodeParams& p, int seq) {

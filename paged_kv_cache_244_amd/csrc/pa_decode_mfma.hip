@@ -62,9 +62,8 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
   const int lane = threadIdx.x;
   const int grp = lane >> 4;                 // lane group: tokens 4*grp..4*grp+3 of a tile
   const int li = lane & 15;                  // head index (scores) / column (outputs)
-  const int seq = scheduled_seq(p);
-  if (static_cast<unsigned>(seq) >= static_cast<unsigned>(p.num_seqs)) return;
-  const int part = blockIdx.z;
+  int seq, part;
+  if (!scheduled_piece(p, seq, part)) return;
   const int h0 = blockIdx.x * GT;
   const int kvh = h0 / p.group;
 

@@ -110,9 +110,8 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
 
   const int lane = threadIdx.x & (kWave - 1);
   const int tile = blockIdx.x;
-  const int seq = scheduled_seq(p);
-  if (static_cast<unsigned>(seq) >= static_cast<unsigned>(p.num_seqs)) return;
-  const int part = blockIdx.z;
+  int seq, part;
+  if (!scheduled_piece(p, seq, part)) return;
   const int h0 = tile * GT;
   const int kvh = h0 / p.group;
   const int row = lane / LPT;

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <random>
+#include <map>
 #include <set>
 #include <vector>
 
@@ -71,8 +72,30 @@ int main(int argc, char** argv) {
         const size_t k = 1 + rng() % (2 * live.size());
         for (size_t i = 0; i < k && i < 4096; ++i) batch.push_back(live[rng() % live.size()]);
         int32_t ncow = 0;
-        rc = kv_batch_append(a, batch.data(), static_cast<int32_t>(batch.size()), slots.data(),
-                             pairs.data(), &ncow);
+        if (rng() % 2) {
+          rc = kv_batch_append(a, batch.data(), static_cast<int32_t>(batch.size()), slots.data(),
+                               pairs.data(), &ncow);
+        } else {
+          // The fused step call into a heap buffer of exactly the size it asks for,
+          // so a write past its end is caught by the sanitizer.
+          kv_step_layout lay{};
+          const int32_t n = static_cast<int32_t>(batch.size());
+          const int32_t part = static_cast<int32_t>(rng() % 3) == 0 ? -1 : bs * (1 + rng() % 4);
+          rc = kv_decode_step_host(a, batch.data(), n, 0, -1, 8, 2, 64, PKV_F16, part, 0, nullptr,
+                                   0, &lay);
+          CHECK(rc == PKV_ERR_INVALID_ARG && lay.total_bytes > 0);
+          std::vector<char> buf(lay.total_bytes);
+          rc = kv_decode_step_host(a, batch.data(), n, 0, -1, 8, 2, 64, PKV_F16, part, 0,
+                                   buf.data(), buf.size(), &lay);
+          if (rc == PKV_OK) {
+            ncow = lay.num_pairs;
+            const int32_t* lens_out = reinterpret_cast<const int32_t*>(buf.data() + lay.lens_offset);
+            std::map<int32_t, int64_t> want;
+            for (int32_t s : batch) want[s] = (want.count(s) ? want[s] : len[s]) + 1;
+            for (int32_t i = 0; i < n; ++i) CHECK(lens_out[i] == want[batch[i]]);
+            CHECK(lay.plan.num_items >= 1 && lay.items_offset + 4ull * lay.plan.num_items <= buf.size());
+          }
+        }
         if (rc == PKV_OK) {
           for (int32_t s : batch) len[s] += 1;
           CHECK(ncow >= 0 && ncow <= static_cast<int32_t>(batch.size()));

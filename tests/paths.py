@@ -56,14 +56,21 @@ def run_oracle(w, sample=None):
     return {"k": kp, "v": vp, "tables": tables, "lens": np.array(lens), "out": out}
 
 
-def run_gpu(w, partition_size, cache_obj=None, out_only=False, longest_first=True):
-    """HIP path: returns pools, tables, lengths (host copies) and the fp32 output."""
+def run_gpu(w, partition_size, cache_obj=None, out_only=False, schedule="plan"):
+    """HIP path: returns pools, tables, lengths (host copies) and the fp32 output.
+
+    ``partition_size`` is a number or "auto" (the library's planner chooses).
+    ``schedule`` "plan" runs the planner's work list (longest piece first);
+    "grid" runs pa_decode without a work list (pieces in index order).
+    """
     import torch
 
     from paged_kv_cache_244_amd.cache import PagedKVCache
 
+    q_dtype = torch.float16 if w.q.dtype == np.float16 else torch.float32
     c = cache_obj or PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
-                                  initial_order=w.initial_order)
+                                  initial_order=w.initial_order, num_q_heads=w.num_q_heads,
+                                  q_dtype=q_dtype)
     seqs = [c.new_sequence() for _ in range(w.num_seqs)]
     prompt_idx, step_idx, step_rows = split_tokens(w)
     dev = c.device
@@ -75,11 +82,21 @@ def run_gpu(w, partition_size, cache_obj=None, out_only=False, longest_first=Tru
     if len(step_idx):
         c.write(step_slots, torch.from_numpy(w.k_tokens[step_idx]).to(dev),
                 torch.from_numpy(w.v_tokens[step_idx]).to(dev))
-    batch = c.batch(seqs, max_blocks_for(w), longest_first=longest_first)
+    batch = c.batch(seqs, max_blocks_for(w), partition_size=partition_size)
     q = torch.from_numpy(w.q).to(dev)
-    out = c.attend(q, batch, w.scale, partition_size=partition_size)
+    if schedule == "plan":
+        out = c.attend(q, batch, w.scale)
+    else:
+        from paged_kv_cache_244_amd import _lib
+
+        part = batch.plan["partition_size"]
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        _lib.pa_decode(out, q, c.k[0], c.v[0], batch.tables, batch.lens, w.scale, batch.max_len,
+                       partition_size=part, stream=c.stream,
+                       workspace=c.workspace(q.shape[0], q.shape[1], batch.max_len, part))
     torch.cuda.synchronize()
-    res = {"out": out.cpu().numpy(), "cache": c, "seqs": seqs, "batch": batch, "q_dev": q}
+    res = {"out": out.cpu().numpy(), "cache": c, "seqs": seqs, "batch": batch, "q_dev": q,
+           "plan": batch.plan}
     if not out_only:
         res.update(k=c.k[0].cpu().numpy(), v=c.v[0].cpu().numpy(),
                    tables=batch.tables.cpu().numpy().astype(np.int64),

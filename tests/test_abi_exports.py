@@ -20,15 +20,16 @@ def declared_functions():
         text = open(path).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
-        for m in re.finditer(r"\b(?:int|void|size_t|char\s*\*)\s*\**\s*(\w+)\s*\(", text):
+        for m in re.finditer(r"\b(?:int|int32_t|void|size_t|char\s*\*)\s*\**\s*(\w+)\s*\(", text):
             names.add(m.group(1))
     return sorted(names)
 
 
 def test_header_declares_the_hot_path():
     names = declared_functions()
-    for required in ("pa_decode", "kv_cache_write", "kv_copy_blocks", "kv_allocator_create",
-                     "kv_seq_append", "kv_export_block_tables", "pkv_last_error"):
+    for required in ("pa_decode", "pa_decode_plan", "pa_decode_plan_capacity", "kv_cache_write",
+                     "kv_copy_blocks", "kv_allocator_create", "kv_seq_append",
+                     "kv_export_block_tables", "pkv_last_error"):
         assert required in names
 
 
@@ -53,9 +54,10 @@ def test_host_argument_errors_without_gpu():
     lib = _lib.lib()
     fake = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
 
-    def decode(d=128, hq=40, hkv=40, bs=16, part=0, maxlen=64, ptr=fake, ws=None, ws_bytes=0):
-        return lib.pa_decode(ptr, ptr, 1, ptr, ptr, 16, ptr, 4, ptr, None, 1, hq, hkv, d, bs, 1.0,
-                             maxlen, part, ws, ws_bytes, None)
+    def decode(d=128, hq=40, hkv=40, bs=16, part=0, maxlen=64, ptr=fake, ws=None, ws_bytes=0,
+               n_items=0, wpc=0):
+        return lib.pa_decode(ptr, ptr, 1, ptr, ptr, 16, ptr, 4, ptr, 1, hq, hkv, d, bs, 1.0,
+                             maxlen, part, None, n_items, wpc, ws, ws_bytes, None)
 
     assert decode(d=96) == _lib.PKV_ERR_UNSUPPORTED and b"head_dim" in lib.pkv_last_error()
     assert decode(bs=24) == _lib.PKV_ERR_INVALID_ARG or decode(bs=24) == _lib.PKV_ERR_UNSUPPORTED
@@ -63,6 +65,8 @@ def test_host_argument_errors_without_gpu():
     assert decode(part=100) == _lib.PKV_ERR_INVALID_ARG        # not a multiple of 16
     assert decode(ptr=None) == _lib.PKV_ERR_INVALID_ARG
     assert decode(part=16, maxlen=64) == _lib.PKV_ERR_WORKSPACE
+    assert decode(n_items=-1) == _lib.PKV_ERR_INVALID_ARG
+    assert decode(wpc=-2) == _lib.PKV_ERR_INVALID_ARG
     assert lib.pa_decode_workspace_size(1, 40, 128, 64, 16) > 0
     assert lib.pa_decode_workspace_size(1, 40, 128, 64, 0) == 0
     assert lib.pa_decode_workspace_size(1, 40, 128, 64, 64) == 0
@@ -71,3 +75,7 @@ def test_host_argument_errors_without_gpu():
     assert lib.kv_cache_write(fake, fake, 4, fake, fake, fake, 0, 2, 64, 16, None) == _lib.PKV_OK
     assert lib.kv_copy_blocks(None, None, 1, fake, 0, 4, 2, 64, 16, None) == _lib.PKV_OK
     assert lib.kv_copy_blocks(None, None, 1, fake, 1, 4, 2, 64, 16, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_upload(fake, fake, 0, None) == _lib.PKV_OK
+    assert lib.pkv_upload(None, fake, 16, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_upload(fake, fake, 24, None) == _lib.PKV_ERR_INVALID_ARG       # size
+    assert lib.pkv_upload(ctypes.c_void_p(0x1008), fake, 16, None) == _lib.PKV_ERR_INVALID_ARG

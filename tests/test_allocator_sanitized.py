@@ -25,7 +25,8 @@ def test_allocator_under_asan_ubsan(tmp_path):
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
            os.path.join(ROOT, "tests", "alloc_stress.cpp"),
-           os.path.join(CSRC, "allocator.cpp"), os.path.join(CSRC, "errors.cpp"), "-o", exe]
+           os.path.join(CSRC, "allocator.cpp"), os.path.join(CSRC, "decode_plan.cpp"),
+           os.path.join(CSRC, "errors.cpp"), "-o", exe]
     build = subprocess.run(cmd, capture_output=True, text=True)
     if build.returncode != 0 and "asan" in build.stderr.lower():
         pytest.skip("sanitizer runtime not available: " + build.stderr[-300:])

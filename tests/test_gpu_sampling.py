@@ -40,7 +40,8 @@ def test_parallel_sampling_128_steps():
     dev = torch.device("cuda")
 
     # --- HIP path
-    c = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, B, initial_order=w.initial_order)
+    c = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, B, initial_order=w.initial_order,
+                     num_q_heads=w.num_q_heads)
     prompts = [c.new_sequence() for _ in range(w.num_prompts)]
     slots = c.reserve_many(prompts, w.prompt_lengths)
     c.write(slots, torch.from_numpy(w.prompt_k).to(dev), torch.from_numpy(w.prompt_v).to(dev))
