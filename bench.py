@@ -48,6 +48,13 @@ def parse_args():
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough budget for the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
+                    help="K/V layout: the paged pool (the product path) or one contiguous row "
+                         "per (request, KV head) without a block table, for comparison")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="pool replicas rotated over the steps, as a model's layers would be "
+                         "(0 = enough for 2 GiB of K/V pools, so no step finds its pool in the "
+                         "256 MiB last-level cache)")
     return ap.parse_args()
 
 
@@ -132,6 +139,17 @@ def copy_probe():
                       "kernel": "elementwise copy (torch copy_)"}), flush=True)
 
 
+REPLICA_TARGET_BYTES = 2 << 30
+
+
+def replicas_for(num_blocks, w, requested):
+    """Pool replicas so that the rotated K/V pools total at least 2 GiB (at most 16)."""
+    if requested > 0:
+        return requested
+    pool = num_blocks * w.num_kv_heads * w.block_size * w.head_dim * 2 * 2
+    return int(min(16, max(1, -(-REPLICA_TARGET_BYTES // pool))))
+
+
 class Scenario:
     """Resident state of one benchmark: cache, requests and per-step device inputs."""
 
@@ -147,14 +165,30 @@ class Scenario:
     def num_seqs(self):
         return len(self.seqs)
 
+    def workspace(self, part, max_len):
+        return self.cache.workspace(self.num_seqs, self.w.num_q_heads, max_len, part)
+
+    def step(self, t, partition, ev_pair, plans):
+        cache = self.cache
+        layer = t % len(cache.k)            # the pool replica this step writes and reads
+        s, batch = cache.decode_step(self.seqs, self.max_blocks, partition_size=partition)
+        plans.append(batch.plan)
+        cache.write(s, self.step_k[t], self.step_v[t], layer=layer)
+        if ev_pair is not None:
+            ev_pair[0].record(cache.stream)
+        cache.attend(self.step_q[t], batch, self.w.scale, layer=layer, out=self.out)
+        if ev_pair is not None:
+            ev_pair[1].record(cache.stream)
+
 
 def _to_dev(arrays, dev):
     import torch
     return [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrays]
 
 
-def decode_scenario(w, total_steps, dev):
-    """Requests whose first L-1 tokens are cached; step t appends one token to each."""
+def decode_scenario(w, total_steps, dev, replicas=0):
+    """Requests whose first L-1 tokens are cached; step t appends one token to each.
+    The pool exists in ``replicas`` copies with identical contents and tables."""
     import torch
 
     from paged_kv_cache_244_amd import workloads
@@ -164,13 +198,17 @@ def decode_scenario(w, total_steps, dev):
     growth = w.num_seqs * (-(-total_steps // w.block_size) + 1)
     num_blocks = w.num_blocks + growth
     order = np.concatenate([w.initial_order, np.arange(w.num_blocks, num_blocks, dtype=np.int32)])
-    cache = PagedKVCache(num_blocks, w.num_kv_heads, w.head_dim, w.block_size, initial_order=order,
-                         device=dev, poison=False, num_q_heads=w.num_q_heads,
+    nrep = replicas_for(num_blocks, w, replicas)
+    cache = PagedKVCache(num_blocks, w.num_kv_heads, w.head_dim, w.block_size, num_layers=nrep,
+                         initial_order=order, device=dev, poison=False, num_q_heads=w.num_q_heads,
                          q_dtype=torch.float16 if w.q.dtype == np.float16 else torch.float32)
     seqs = [cache.new_sequence() for _ in range(w.num_seqs)]
     prompt_idx = np.concatenate([np.arange(o, o + L - 1) for o, L in zip(w.offsets[:-1], w.lengths)])
     slots = cache.reserve_many(seqs, [int(L) - 1 for L in w.lengths])
-    cache.write(slots, *_to_dev([w.k_tokens[prompt_idx], w.v_tokens[prompt_idx]], dev))
+    pk, pv = _to_dev([w.k_tokens[prompt_idx], w.v_tokens[prompt_idx]], dev)
+    for layer in range(nrep):
+        cache.write(slots, pk, pv, layer=layer)
+    del pk, pv
     last_idx = w.offsets[:-1] + w.lengths - 1
     step_k, step_v, step_q = [], [], []
     for t in range(total_steps):
@@ -183,10 +221,10 @@ def decode_scenario(w, total_steps, dev):
     max_blocks = -(-(int(w.lengths.max()) + total_steps) // w.block_size)
     out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     return Scenario(w, cache, seqs, w.lengths.astype(np.int64) - 1, step_k, step_v, step_q,
-                    max_blocks, out)
+                    max_blocks, out, extra={"pool_replicas": nrep})
 
 
-def sampling_scenario(sw, total_steps, dev):
+def sampling_scenario(sw, total_steps, dev, replicas=0):
     """Prompts forked into samples sharing their blocks; the first step copies the
     partly filled last prompt block of every sample but one per prompt."""
     import torch
@@ -195,12 +233,16 @@ def sampling_scenario(sw, total_steps, dev):
 
     if total_steps > sw.steps:
         raise SystemExit(f"parallel_sampling has {sw.steps} steps; asked for {total_steps}")
+    nrep = replicas_for(sw.num_blocks, sw, replicas)
     cache = PagedKVCache(sw.num_blocks, sw.num_kv_heads, sw.head_dim, sw.block_size,
-                         initial_order=sw.initial_order, device=dev, poison=False,
+                         num_layers=nrep, initial_order=sw.initial_order, device=dev, poison=False,
                          num_q_heads=sw.num_q_heads)
     prompts = [cache.new_sequence() for _ in range(sw.num_prompts)]
     slots = cache.reserve_many(prompts, sw.prompt_lengths)
-    cache.write(slots, *_to_dev([sw.prompt_k, sw.prompt_v], dev))
+    pk, pv = _to_dev([sw.prompt_k, sw.prompt_v], dev)
+    for layer in range(nrep):
+        cache.write(slots, pk, pv, layer=layer)
+    del pk, pv
     seqs = []
     for p in prompts:
         seqs.extend(cache.fork(p) for _ in range(sw.samples))
@@ -227,9 +269,92 @@ def sampling_scenario(sw, total_steps, dev):
                        np.float16, sw.scale)
     return Scenario(w, cache, seqs, lengths, step_k, step_v, step_q, max_blocks, out,
                     unique_bytes=unique_bytes,
-                    extra={"prompts": sw.num_prompts, "samples_per_prompt": sw.samples,
+                    extra={"pool_replicas": nrep,
+                           "prompts": sw.num_prompts, "samples_per_prompt": sw.samples,
                            "note": "value counts logical K/V bytes; shared prompt blocks are "
                                    "read by every sample"})
+
+
+class ContiguousScenario:
+    """The same requests, data and per-step inputs in the layout without a block
+    table: K and V rows [S, Hkv, Lmax, D] per replica.  The new token of each step
+    is stored with a torch index (plumbing of this comparison layout, outside the
+    timed decode launch); the launch schedule comes from the same planner."""
+
+    def __init__(self, base, total_steps, dev, replicas):
+        import torch
+
+        from paged_kv_cache_244_amd.cache import _Staging
+
+        w = base.w
+        self.w, self.seqs, self.lengths = w, base.seqs, base.lengths
+        self.step_k, self.step_v, self.step_q, self.out = base.step_k, base.step_v, base.step_q, base.out
+        self.unique_bytes, self.extra = None, {}
+        S, hkv, d = len(base.seqs), w.num_kv_heads, w.head_dim
+        self.lmax = -(-(int(base.lengths.max()) + total_steps) // 16) * 16
+        row_bytes = S * hkv * self.lmax * d * 2 * 2
+        nrep = replicas if replicas > 0 else int(min(16, max(1, -(-REPLICA_TARGET_BYTES // row_bytes))))
+        self.k = [torch.zeros((S, hkv, self.lmax, d), dtype=torch.float16, device=dev)
+                  for _ in range(nrep)]
+        self.v = [torch.zeros_like(self.k[0]) for _ in range(nrep)]
+        # Prompt tokens: request i's first L_i - 1 tokens, in logical order.
+        lens0 = base.lengths.astype(np.int64)
+        seq_idx = np.repeat(np.arange(S), lens0)
+        pos_idx = np.concatenate([np.arange(L) for L in lens0]) if S else np.zeros(0, np.int64)
+        tok_idx = np.concatenate([np.arange(o, o + L) for o, L in zip(w.offsets[:-1], lens0)])
+        si, pi = (torch.from_numpy(a).to(dev) for a in (seq_idx, pos_idx))
+        kt, vt = _to_dev([w.k_tokens[tok_idx], w.v_tokens[tok_idx]], dev)
+        for r in range(nrep):
+            self.k[r][si, :, pi, :] = kt
+            self.v[r][si, :, pi, :] = vt
+        del kt, vt
+        self.lens = lens0.astype(np.int32)          # cached tokens per request
+        self.staging = _Staging(dev)
+        self.arange = torch.arange(S, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.ws = None
+        self.extra = {"pool_replicas": nrep, "layout": "contiguous", "row_tokens": self.lmax}
+
+    @property
+    def num_seqs(self):
+        return len(self.seqs)
+
+    def workspace(self, part, max_len):
+        import torch
+        need = _lib_mod().pa_decode_workspace_size(self.num_seqs, self.w.num_q_heads,
+                                                   self.w.head_dim, max_len, part)
+        if need and (self.ws is None or self.ws.numel() < need):
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.out.device)
+        return self.ws if need else None
+
+    def step(self, t, partition, ev_pair, plans):
+        _lib = _lib_mod()
+        w, r = self.w, t % len(self.k)
+        pos = self.lens.copy()
+        self.lens += 1
+        qd = _lib.PKV_F16 if self.step_q[t].dtype.itemsize == 2 else _lib.PKV_F32
+        items, plan = _lib.plan(self.lens, w.num_q_heads, w.num_kv_heads, w.head_dim, 16, qd,
+                                partition_size=partition)
+        plans.append(plan)
+        lens_d, pos_d, items_d = self.staging.upload([self.lens, pos.astype(np.int64),
+                                                      items.view(np.int32)], self.stream)
+        self.k[r][self.arange, :, pos_d, :] = self.step_k[t]
+        self.v[r][self.arange, :, pos_d, :] = self.step_v[t]
+        max_len = int(self.lens.max())
+        ws = self.workspace(plan["partition_size"], max_len)
+        if ev_pair is not None:
+            ev_pair[0].record(self.stream)
+        _lib.pa_decode_contiguous(self.out, self.step_q[t], self.k[r], self.v[r], lens_d, w.scale,
+                                  max_len, partition_size=plan["partition_size"], workspace=ws,
+                                  stream=self.stream, work_items=items_d,
+                                  waves_per_cu=plan["waves_per_cu"])
+        if ev_pair is not None:
+            ev_pair[1].record(self.stream)
+
+
+def _lib_mod():
+    from paged_kv_cache_244_amd import _lib
+    return _lib
 
 
 class SimpleWorkload:
@@ -264,21 +389,26 @@ def main():
 
     total_steps = args.warmup + args.steps
     if args.workload == "parallel_sampling":
-        sc = sampling_scenario(workloads.parallel_sampling(), total_steps, dev)
+        sc = sampling_scenario(workloads.parallel_sampling(), total_steps, dev, args.replicas)
     else:
         w = {"long_context": lambda: workloads.long_context(16),
              "tiny": workloads.tiny}.get(args.workload, workloads.WORKLOADS.get(args.workload))()
-        sc = decode_scenario(w, total_steps, dev)
+        sc = decode_scenario(w, total_steps, dev, args.replicas)
+        if args.layout == "contiguous":
+            base = sc
+            sc = ContiguousScenario(base, total_steps, dev, args.replicas)
+            del base
+            torch.cuda.empty_cache()
+    if args.layout == "contiguous" and args.workload == "parallel_sampling":
+        raise SystemExit("the contiguous layout is measured on the decode workloads only")
     w = sc.w
-    cache = sc.cache
-    stream = cache.stream
     # The planner's automatic choice for the lengths the run ends at (they grow by
     # total_steps tokens), then kept fixed so every timed step runs one schedule shape.
     qd = _lib.PKV_F16 if w.q_dtype == np.float16 else _lib.PKV_F32
     partition = (_lib.plan(sc.lengths + total_steps, w.num_q_heads, w.num_kv_heads, w.head_dim,
                            w.block_size, qd)[1]["partition_size"]
                  if args.partition == "auto" else int(args.partition))
-    cache.workspace(sc.num_seqs, w.num_q_heads, int(sc.lengths.max()) + total_steps, partition)
+    sc.workspace(partition, int(sc.lengths.max()) + total_steps)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -287,14 +417,7 @@ def main():
     plans = []
 
     def step(t, timed_slot=None):
-        s, batch = cache.decode_step(sc.seqs, sc.max_blocks, partition_size=partition)
-        plans.append(batch.plan)
-        cache.write(s, sc.step_k[t], sc.step_v[t])
-        if timed_slot is not None:
-            ev[timed_slot][0].record(stream)
-        cache.attend(sc.step_q[t], batch, w.scale, out=sc.out)
-        if timed_slot is not None:
-            ev[timed_slot][1].record(stream)
+        sc.step(t, partition, ev[timed_slot] if timed_slot is not None else None, plans)
 
     lengths = sc.lengths.copy()
     for t in range(args.warmup):
@@ -322,9 +445,10 @@ def main():
         sc.extra["unique_kv_bytes_per_step"] = int(np.mean(unique_step_bytes))
         achieved = float(np.mean(unique_step_bytes)) / decode_avg_s / 1e9
 
-    traffic = counter_traffic(args.workload)
+    # The committed counter summaries describe the paged kernels only.
+    traffic = counter_traffic(args.workload) if args.layout == "paged" else None
     baseline = None
-    if args.cpu_seconds > 0 and hasattr(w, "offsets"):
+    if args.cpu_seconds > 0 and hasattr(w, "offsets") and args.layout == "paged":
         baseline = cpu_baseline(w, args.cpu_seconds)
 
     result = {
@@ -345,7 +469,7 @@ def main():
             "num_seqs": sc.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": "f16",
             "q_dtype": np.dtype(w.q_dtype).name, "partition_size": partition,
-            "kernel_policy": args.kernel_policy,
+            "kernel_policy": args.kernel_policy, "layout": args.layout,
             "schedule": "planner work list, largest piece first",
             "work_items": plans[-1]["num_items"], "waves_per_cu": plans[-1]["waves_per_cu"],
             "mean_context": round(float(np.mean(lengths)), 1),

@@ -184,9 +184,10 @@ typedef struct {
  * least one wave per SIMD and no request is longer than 1.25x the tokens a
  * SIMD would process), otherwise the largest of 2048, 1024, 512 and 256 tokens
  * that is at most half a SIMD's share of the tokens (256 if none is), rounded
- * up to a multiple of block_size.  The residency limit is 6 waves per compute
- * unit for the MFMA kernel (it leaves the dispatcher room to balance) and none
- * for the vector-ALU kernel.
+ * up to a multiple of block_size.  Residency limit (waves per compute unit,
+ * measured on MI355X; it leaves the dispatcher pieces to balance): 6 for the
+ * MFMA kernel; 4 for the vector-ALU kernel when requests run in one pass and
+ * the longest is more than 1.5x the mean non-empty length; otherwise none.
  * Errors: PKV_ERR_INVALID_ARG (bad sizes, capacity too small: plan->num_items
  * then holds the number needed), PKV_ERR_UNSUPPORTED (shape not built).
  */
@@ -254,6 +255,29 @@ int pa_decode(float* out, const void* q, int32_t q_dtype,
               float scale, int32_t max_context_len, int32_t partition_size,
               const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_contiguous — the same decode attention over the layout without a
+ * block table, for measuring what the table costs: [A] "The old answer,
+ * imported honestly" (one contiguous region per request, sized for its
+ * maximum length) against [B] "The page table, relocated into attention"
+ * (the table walk and scattered blocks).  Same kernels, tiles, order of
+ * arithmetic and schedule as pa_decode with block_size 16, so for equal data
+ * the outputs are bitwise equal to pa_decode's.
+ *   k_cache, v_cache : device fp16 [num_seqs][num_kv_heads][row_tokens][head_dim]:
+ *                      request i's logical token t of KV head g at [i][g][t].
+ *   row_tokens       : a positive multiple of 16, >= max_context_len.
+ * Every other argument as pa_decode (work items from pa_decode_plan with
+ * block_size 16).  Errors as pa_decode, plus PKV_ERR_INVALID_ARG for a bad
+ * row_tokens.
+ */
+int pa_decode_contiguous(float* out, const void* q, int32_t q_dtype,
+                         const void* k_cache, const void* v_cache, int32_t row_tokens,
+                         const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         float scale, int32_t max_context_len, int32_t partition_size,
+                         const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Host block allocator                                                      */

@@ -73,3 +73,24 @@ def attend_paged(q, k_pool, v_pool, block_tables, context_lens, block_size, scal
         values = gather_logical(v_pool, block_tables[i], length, block_size)
         out[i] = attend_one(q[i], keys, values, scale)
     return out
+
+
+def attend_contiguous(q, k_rows, v_rows, context_lens, scale, seqs=None):
+    """Decode attention over the layout without a block table (float64).
+
+    The pre-paging arrangement the pages compare against ("800 kilobytes per
+    token", section "The old answer, imported honestly"): request i's keys for
+    KV head g are one contiguous row ``k_rows[i, g, :L_i, :]``.  ``k_rows,
+    v_rows``: ``[S, Hkv, Lmax, D]`` float16; q ``[S, Hq, D]``.  Returns
+    ``[S, Hq, D]`` float64 (rows not in ``seqs`` are left zero).
+    """
+    q = np.asarray(q)
+    num_seqs, num_q_heads, head_dim = q.shape
+    out = np.zeros((num_seqs, num_q_heads, head_dim), dtype=np.float64)
+    rows = range(num_seqs) if seqs is None else seqs
+    for i in rows:
+        length = int(context_lens[i])
+        keys = np.swapaxes(k_rows[i, :, :length, :], 0, 1)     # [L, Hkv, D]
+        values = np.swapaxes(v_rows[i, :, :length, :], 0, 1)
+        out[i] = attend_one(q[i], keys, values, scale)
+    return out

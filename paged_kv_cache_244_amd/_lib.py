@@ -87,6 +87,10 @@ _SIGNATURES = {
                             c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                             c_float, c_int32, c_int32, c_void_p, c_int32, c_int32,
                             c_void_p, c_size_t, c_void_p]),
+    "pa_decode_contiguous": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                       c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
+                                       c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p,
+                                       c_size_t, c_void_p]),
     "kv_allocator_create": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_void_p)]),
     "kv_allocator_destroy": (None, [c_void_p]),
     "kv_seq_create": (c_int32, [c_void_p, POINTER(c_int32)]),
@@ -279,6 +283,43 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"), nb,
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
         _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, bs, float(scale),
+        int(max_context_len), int(partition_size), items_ptr, n_items, int(waves_per_cu),
+        ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_decode_contiguous(out, q, k_rows, v_rows, context_lens, scale, max_context_len,
+                         partition_size=0, workspace=None, stream=None, work_items=None,
+                         waves_per_cu=0):
+    """Decode attention over the layout without a block table: ``k_rows, v_rows`` are
+    device fp16 [S, Hkv, Lmax, D], request i's token t of KV head g at [i, g, t]
+    (Lmax a multiple of 16).  Otherwise as ``pa_decode``; the workspace size is
+    ``pa_decode_workspace_size`` of the same arguments."""
+    torch = _torch()
+    if k_rows.shape != v_rows.shape or k_rows.dim() != 4:
+        raise ValueError("k_rows and v_rows must both be [S, Hkv, Lmax, D]")
+    s, hkv, lmax, d = (int(x) for x in k_rows.shape)
+    sq, hq, dq = (int(x) for x in q.shape)
+    if sq != s or dq != d or tuple(out.shape) != (s, hq, d):
+        raise ValueError("q and out must be [S, Hq, D] matching the rows")
+    if q.dtype == torch.float32:
+        qd = PKV_F32
+    elif q.dtype == torch.float16:
+        qd = PKV_F16
+    else:
+        raise TypeError("q must be float32 or float16")
+    if tuple(context_lens.shape) != (s,):
+        raise ValueError("context_lens must be [S]")
+    items_ptr, n_items = c_void_p(None), 0
+    if work_items is not None:
+        items_ptr, n_items = _items(work_items)
+    ws_ptr, ws_bytes = c_void_p(None), 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(lib().pa_decode_contiguous(
+        _dev(out, torch.float32, "out"), _dev(q, q.dtype, "q"), qd,
+        _dev(k_rows, torch.float16, "k_rows"), _dev(v_rows, torch.float16, "v_rows"), lmax,
+        _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, float(scale),
         int(max_context_len), int(partition_size), items_ptr, n_items, int(waves_per_cu),
         ws_ptr, ws_bytes, _stream(stream)))
 

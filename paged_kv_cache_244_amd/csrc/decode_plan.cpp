@@ -79,6 +79,25 @@ int32_t auto_partition(const int32_t* lens, int32_t n, int tiles, int cus, int32
   return (part + block_size - 1) / block_size * block_size;
 }
 
+// Residency limit (waves per CU) for a launch, measured on MI355X: the MFMA
+// kernel runs best with 6 for every length mix; the VALU kernel gains from 4
+// only when requests run in one pass and their lengths are skewed (all pieces
+// are resident at once otherwise, so the dispatcher cannot balance them),
+// and loses a few percent with any limit on even lengths.
+int residency_limit(bool mfma, int32_t part, const int32_t* lens, int32_t n) {
+  if (mfma) return kMfmaWavesPerCu;
+  if (part != 0 || n == 0) return 0;
+  int64_t total = 0, nonempty = 0;
+  int32_t longest = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    total += lens[i];
+    nonempty += lens[i] > 0;
+    longest = std::max(longest, lens[i]);
+  }
+  if (nonempty == 0) return 0;
+  return longest * nonempty > 1.5 * static_cast<double>(total) ? kValuSkewedWavesPerCu : 0;
+}
+
 }  // namespace
 }  // namespace pkv_plan
 
@@ -150,7 +169,7 @@ extern "C" int pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int
   plan->partition_size = part;
   plan->max_parts = static_cast<int32_t>(parts);
   plan->num_items = count > INT32_MAX ? INT32_MAX : static_cast<int32_t>(count);
-  plan->waves_per_cu = kc.mfma ? kMfmaWavesPerCu : 0;
+  plan->waves_per_cu = residency_limit(kc.mfma, part, lens.data(), num_seqs);
   plan->workspace_bytes = workspace_bytes_for(num_seqs, num_q_heads, head_dim, parts);
   if (count > items_capacity)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan: %lld items do not fit in %d",

@@ -34,7 +34,9 @@ inline size_t workspace_bytes_for(int32_t S, int32_t Hq, int32_t D, int64_t part
   return align256(n * D * sizeof(float)) + align256(n * 2 * sizeof(float));
 }
 
-// Residency limit the planner sets for the MFMA kernel (waves per CU).
+// Residency limits the planner sets (waves per CU): the MFMA kernel always,
+// the VALU kernel for one-pass launches over skewed lengths.
 constexpr int kMfmaWavesPerCu = 6;
+constexpr int kValuSkewedWavesPerCu = 4;
 
 }  // namespace pkv_plan

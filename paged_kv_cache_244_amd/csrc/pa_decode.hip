@@ -85,14 +85,19 @@ hipError_t reserve_lds_bytes(const void* fn, int waves_per_cu, unsigned* dyn) {
 
 }  // namespace
 
-extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
-                         const void* v_cache, int32_t num_blocks, const int32_t* block_tables,
-                         int32_t max_blocks_per_seq, const int32_t* context_lens,
-                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t head_dim, int32_t block_size, float scale,
-                         int32_t max_context_len, int32_t partition_size,
-                         const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared by both layouts.  Paged: block_tables / num_blocks / max_blocks_per_seq
+// describe the table and pool.  Contiguous (row_chunks > 0): no table; num_blocks
+// = max_blocks_per_seq = 16-token blocks per (request, KV head) row.
+int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                const void* v_cache, int32_t num_blocks, const int32_t* block_tables,
+                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                float scale, int32_t max_context_len, int32_t partition_size,
+                const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
+                void* workspace, size_t workspace_bytes, void* stream, int64_t row_chunks) {
+  const bool contig = row_chunks > 0;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0 || num_work_items < 0 ||
       waves_per_cu < 0)
@@ -110,13 +115,13 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
   if (num_q_heads > 65535)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: too many query heads");
   const KernelChoice kc = choose_kernel(q_dtype, num_q_heads / num_kv_heads);
-  KernelFn fn = kc.mfma ? pick_mfma_kernel(head_dim, block_size, kc.gt)
-                        : pick_valu_kernel(head_dim, block_size, kc.gt, q_dtype == PKV_F32);
+  KernelFn fn = kc.mfma ? pick_mfma_kernel(head_dim, block_size, kc.gt, contig)
+                        : pick_valu_kernel(head_dim, block_size, kc.gt, q_dtype == PKV_F32, contig);
   if (!fn)
     return fail(PKV_ERR_UNSUPPORTED, "pa_decode: head_dim %d / block_size %d not built", head_dim,
                 block_size);
   if (num_seqs == 0) return PKV_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+  if (!out || !q || !k_cache || !v_cache || (!contig && !block_tables) || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: NULL pointer");
   if (work_items && num_work_items == 0) return PKV_OK;
 
@@ -157,6 +162,7 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
   prm.len_clamp = len_clamp;
   prm.part_tokens = part_tokens;
   prm.max_parts = static_cast<int32_t>(parts);
+  prm.row_chunks = row_chunks;
 
   if (parts > 1) {
     const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, parts);
@@ -199,3 +205,44 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
   }
   return PKV_OK;
 }
+
+}  // namespace
+
+extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                         const void* v_cache, int32_t num_blocks, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, float scale,
+                         int32_t max_context_len, int32_t partition_size,
+                         const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, q_dtype, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, scale, max_context_len, partition_size, work_items,
+                     num_work_items, waves_per_cu, workspace, workspace_bytes, stream, 0);
+}
+
+extern "C" int pa_decode_contiguous(float* out, const void* q, int32_t q_dtype,
+                                    const void* k_cache, const void* v_cache, int32_t row_tokens,
+                                    const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    float scale, int32_t max_context_len, int32_t partition_size,
+                                    const uint32_t* work_items, int32_t num_work_items,
+                                    int32_t waves_per_cu, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  constexpr int32_t kTile = 16;
+  if (row_tokens <= 0 || row_tokens % kTile != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_contiguous: row_tokens %d not a positive multiple of 16",
+                row_tokens);
+  if (max_context_len > row_tokens)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_contiguous: max_context_len %d > row_tokens %d",
+                max_context_len, row_tokens);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "pa_decode_contiguous: head_dim %d not built", head_dim);
+  const int32_t blocks = row_tokens / kTile;
+  return decode_impl(out, q, q_dtype, k_cache, v_cache, blocks, nullptr, blocks, context_lens,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, kTile, scale, max_context_len,
+                     partition_size, work_items, num_work_items, waves_per_cu, workspace,
+                     workspace_bytes, stream, static_cast<int64_t>(row_tokens) * head_dim / 8);
+}
+

@@ -40,7 +40,36 @@ struct DecodeParams {
   int32_t part_tokens;        // tokens per partition, multiple of B
   int32_t max_parts;
   int32_t num_items;
+  int64_t row_chunks;         // contiguous layout only: 16-byte chunks per (request, KV head) row
 };
+
+// Where the tiles of one (request, KV head) live.  Paged: block id b (from the
+// table) of KV head g starts at chunk (b * Hkv + g) * CHUNKS.  Contiguous
+// ([S][Hkv][Lmax][D], the layout without a block table): logical block b of
+// (request s, KV head g) starts at chunk (s * Hkv + g) * row_chunks + b * CHUNKS,
+// so the "block id" is the logical block number itself.
+template <bool kContig, int CHUNKS>
+struct TileAddressing {
+  int64_t head_base;      // chunk offset of block 0 of this (request, KV head)
+  int64_t block_stride;   // chunks between consecutive block ids
+  __device__ TileAddressing(const DecodeParams& p, int seq, int kvh) {
+    if constexpr (kContig) {
+      head_base = (static_cast<int64_t>(seq) * p.num_kv_heads + kvh) * p.row_chunks;
+      block_stride = CHUNKS;
+    } else {
+      head_base = static_cast<int64_t>(kvh) * CHUNKS;
+      block_stride = static_cast<int64_t>(p.num_kv_heads) * CHUNKS;
+    }
+  }
+};
+
+// Block id of logical block `blk` of the request: its table entry (paged), or
+// blk itself (contiguous); ids past the table read as 0 (never used unguarded).
+template <bool kContig>
+__device__ __forceinline__ int block_id(const int32_t* table, int blk, int max_blocks) {
+  if constexpr (kContig) return blk;
+  return blk < max_blocks ? table[blk] : 0;
+}
 
 // K/V tiles are read exactly once: non-temporal loads keep them from displacing
 // useful lines in L2 and the Infinity Cache (measured ~10% faster on MI355X).
@@ -105,11 +134,12 @@ __device__ __forceinline__ int clamped_len(const DecodeParams& p, int seq) {
 // on v_mfma_f32_16x16x32_f16 and P.V on v_mfma_f32_16x16x16_f16, for head
 // groups of GT in {4, 8, 16} query heads and fp16 queries.
 using KernelFn = void (*)(DecodeParams);
-KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt);
+KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt, bool contiguous);
 
 // VALU kernel (pa_decode_valu.hip): one wave per (request, head tile,
 // partition), GT in {1, 2, 4} query heads per wave, fp32 or fp16 queries.
-KernelFn pick_valu_kernel(int head_dim, int block_size, int gt, bool qf32);
+// `contiguous` selects the layout without a block table (block size 16 only).
+KernelFn pick_valu_kernel(int head_dim, int block_size, int gt, bool qf32, bool contiguous);
 
 // Cross-partition combine (pa_decode_reduce.hip), launched after a split pass.
 hipError_t launch_reduce(const DecodeParams& prm, int head_dim, hipStream_t stream);

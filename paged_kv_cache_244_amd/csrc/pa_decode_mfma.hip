@@ -27,7 +27,7 @@
 // factor each tile.
 //
 // Work decomposition, masking, partitions and the workspace format are those of
-// the VALU kernel in pa_decode.hip, so both feed the same reduce kernel.
+// the VALU kernel in pa_decode_valu.hip, so both feed the same reduce kernel.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -40,7 +40,7 @@ namespace {
 
 constexpr float kSlack = 8.f;
 
-template <int D, int B, int GT>
+template <int D, int B, int GT, bool kContig>
 __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
 #ifndef PKV_MFMA_DEPTH
 #define PKV_MFMA_DEPTH 2
@@ -68,9 +68,10 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
   const int kvh = h0 / p.group;
 
   // Independent loads first: table ids, queries, length.
-  const int32_t* table = p.block_tables + static_cast<int64_t>(seq) * p.max_blocks_per_seq;
+  const int32_t* table =
+      kContig ? nullptr : p.block_tables + static_cast<int64_t>(seq) * p.max_blocks_per_seq;
   const int blk_begin = part * (p.part_tokens / B);
-  const int staged_first = blk_begin + lane < p.max_blocks_per_seq ? table[blk_begin + lane] : 0;
+  const int staged_first = block_id<kContig>(table, blk_begin + lane, p.max_blocks_per_seq);
   half8 qb[KSTEPS];                          // Q^T as the B operand: head li, dims kk*32 + 8*grp
   {
     const _Float16* qp = static_cast<const _Float16*>(p.q) +
@@ -96,9 +97,10 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
   const int nparts = (len + p.part_tokens - 1) / p.part_tokens;
   const int nblk = (t_end - 1) / B - blk_begin + 1;
   const int ntiles = (t_end - t_begin + TT - 1) / TT;
-  const int64_t block_stride = static_cast<int64_t>(p.num_kv_heads) * CHUNKS;
-  const uint4* kbase = p.k_cache + kvh * static_cast<int64_t>(CHUNKS);
-  const uint4* vbase = p.v_cache + kvh * static_cast<int64_t>(CHUNKS);
+  const TileAddressing<kContig, CHUNKS> at(p, seq, kvh);
+  const int64_t block_stride = at.block_stride;
+  const uint4* kbase = p.k_cache + at.head_base;
+  const uint4* vbase = p.v_cache + at.head_base;
 
   float4_t o[DBLK];
 #pragma unroll
@@ -110,7 +112,10 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
 
   for (int c0 = 0; c0 < nblk; c0 += kWave) {
     const int staged =
-        c0 == 0 ? staged_first : (lane < min(kWave, nblk - c0) ? table[blk_begin + c0 + lane] : 0);
+        c0 == 0 ? staged_first
+                : (lane < min(kWave, nblk - c0)
+                       ? block_id<kContig>(table, blk_begin + c0 + lane, p.max_blocks_per_seq)
+                       : 0);
     const int tile0 = c0 * TPB / BPT;                         // first tile of this chunk
     const int cn = min(kWave * TPB / BPT, ntiles - tile0);    // tiles in this chunk
 
@@ -256,12 +261,12 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int B>
+template <int D, int B, bool kContig>
 KernelFn pick_gt(int gt) {
   switch (gt) {
-    case 4: return pa_decode_mfma_kernel<D, B, 4>;
-    case 8: return pa_decode_mfma_kernel<D, B, 8>;
-    case 16: return pa_decode_mfma_kernel<D, B, 16>;
+    case 4: return pa_decode_mfma_kernel<D, B, 4, kContig>;
+    case 8: return pa_decode_mfma_kernel<D, B, 8, kContig>;
+    case 16: return pa_decode_mfma_kernel<D, B, 16, kContig>;
     default: return nullptr;
   }
 }
@@ -269,18 +274,24 @@ KernelFn pick_gt(int gt) {
 template <int D>
 KernelFn pick_b(int b, int gt) {
   switch (b) {
-    case 8: return pick_gt<D, 8>(gt);
-    case 16: return pick_gt<D, 16>(gt);
-    case 32: return pick_gt<D, 32>(gt);
-    case 64: return pick_gt<D, 64>(gt);
-    case 128: return pick_gt<D, 128>(gt);
+    case 8: return pick_gt<D, 8, false>(gt);
+    case 16: return pick_gt<D, 16, false>(gt);
+    case 32: return pick_gt<D, 32, false>(gt);
+    case 64: return pick_gt<D, 64, false>(gt);
+    case 128: return pick_gt<D, 128, false>(gt);
     default: return nullptr;
   }
 }
 
 }  // namespace
 
-KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt) {
+KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt, bool contiguous) {
+  if (contiguous) {
+    if (block_size != 16) return nullptr;
+    if (head_dim == 64) return pick_gt<64, 16, true>(gt);
+    if (head_dim == 128) return pick_gt<128, 16, true>(gt);
+    return nullptr;
+  }
   if (head_dim == 64) return pick_b<64>(block_size, gt);
   if (head_dim == 128) return pick_b<128>(block_size, gt);
   return nullptr;

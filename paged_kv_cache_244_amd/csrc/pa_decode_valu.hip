@@ -96,7 +96,7 @@ struct QueryRegs<GT, false> {       // fp16 queries: v_dot2_f32_f16 (products ex
   }
 };
 
-template <int D, int B, int GT, bool kQF32>
+template <int D, int B, int GT, bool kQF32, bool kContig>
 __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams p) {
   constexpr int LPT = D / 8;               // lanes per token row
   constexpr int TPL = kWave / LPT;         // token rows per wave-wide load
@@ -119,9 +119,10 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
 
   // The first 64 block ids of this partition, the query and the length do not
   // depend on one another: issue all three loads before waiting on any.
-  const int32_t* table = p.block_tables + static_cast<int64_t>(seq) * p.max_blocks_per_seq;
+  const int32_t* table =
+      kContig ? nullptr : p.block_tables + static_cast<int64_t>(seq) * p.max_blocks_per_seq;
   const int blk_begin = part * (p.part_tokens / B);
-  const int staged_first = blk_begin + lane < p.max_blocks_per_seq ? table[blk_begin + lane] : 0;
+  const int staged_first = block_id<kContig>(table, blk_begin + lane, p.max_blocks_per_seq);
   QueryRegs<GT, kQF32> qr;
   qr.load(p.q, (static_cast<int64_t>(seq) * p.num_q_heads + h0) * D + dchunk * 8, D);
   const int len = clamped_len(p, seq);
@@ -152,9 +153,10 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
 
   const int nblk = (t_end - 1) / B - blk_begin + 1;
   const int ntiles = (t_end - t_begin + TT - 1) / TT;
-  const int64_t block_stride = static_cast<int64_t>(p.num_kv_heads) * CHUNKS;
-  const uint4* kbase = p.k_cache + kvh * static_cast<int64_t>(CHUNKS) + lane;
-  const uint4* vbase = p.v_cache + kvh * static_cast<int64_t>(CHUNKS) + lane;
+  const TileAddressing<kContig, CHUNKS> at(p, seq, kvh);
+  const int64_t block_stride = at.block_stride;
+  const uint4* kbase = p.k_cache + at.head_base + lane;
+  const uint4* vbase = p.v_cache + at.head_base + lane;
 
   // DEPTH tiles in flight per wave: while one tile of K and V is consumed, the
   // loads of the next DEPTH-1 are outstanding.  Three for one head per wave; two
@@ -165,8 +167,11 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
   // Blocks are taken 64 at a time (one id per lane); tiles are numbered from the
   // start of the partition.
   for (int c0 = 0; c0 < nblk; c0 += kWave) {
-    const int staged = c0 == 0 ? staged_first
-                               : (lane < min(kWave, nblk - c0) ? table[blk_begin + c0 + lane] : 0);
+    const int staged =
+        c0 == 0 ? staged_first
+                : (lane < min(kWave, nblk - c0)
+                       ? block_id<kContig>(table, blk_begin + c0 + lane, p.max_blocks_per_seq)
+                       : 0);
     const int tile0 = c0 * TPB;                               // first tile of this chunk
     const int cn = min(kWave * TPB, ntiles - tile0);          // tiles in this chunk
 
@@ -287,17 +292,18 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
   }
 }
 
-template <int D, int B, int GT>
+template <int D, int B, int GT, bool kContig>
 KernelFn pick_q(bool qf32) {
-  return qf32 ? pa_decode_partition_kernel<D, B, GT, true> : pa_decode_partition_kernel<D, B, GT, false>;
+  return qf32 ? pa_decode_partition_kernel<D, B, GT, true, kContig>
+              : pa_decode_partition_kernel<D, B, GT, false, kContig>;
 }
 
-template <int D, int B>
+template <int D, int B, bool kContig>
 KernelFn pick_gt(int gt, bool qf32) {
   switch (gt) {
-    case 1: return pick_q<D, B, 1>(qf32);
-    case 2: return pick_q<D, B, 2>(qf32);
-    case 4: return pick_q<D, B, 4>(qf32);
+    case 1: return pick_q<D, B, 1, kContig>(qf32);
+    case 2: return pick_q<D, B, 2, kContig>(qf32);
+    case 4: return pick_q<D, B, 4, kContig>(qf32);
     default: return nullptr;
   }
 }
@@ -305,18 +311,24 @@ KernelFn pick_gt(int gt, bool qf32) {
 template <int D>
 KernelFn pick_b(int b, int gt, bool qf32) {
   switch (b) {
-    case 8: return pick_gt<D, 8>(gt, qf32);
-    case 16: return pick_gt<D, 16>(gt, qf32);
-    case 32: return pick_gt<D, 32>(gt, qf32);
-    case 64: return pick_gt<D, 64>(gt, qf32);
-    case 128: return pick_gt<D, 128>(gt, qf32);
+    case 8: return pick_gt<D, 8, false>(gt, qf32);
+    case 16: return pick_gt<D, 16, false>(gt, qf32);
+    case 32: return pick_gt<D, 32, false>(gt, qf32);
+    case 64: return pick_gt<D, 64, false>(gt, qf32);
+    case 128: return pick_gt<D, 128, false>(gt, qf32);
     default: return nullptr;
   }
 }
 
 }  // namespace
 
-KernelFn pick_valu_kernel(int head_dim, int block_size, int gt, bool qf32) {
+KernelFn pick_valu_kernel(int head_dim, int block_size, int gt, bool qf32, bool contiguous) {
+  if (contiguous) {
+    if (block_size != 16) return nullptr;
+    if (head_dim == 64) return pick_gt<64, 16, true>(gt, qf32);
+    if (head_dim == 128) return pick_gt<128, 16, true>(gt, qf32);
+    return nullptr;
+  }
   if (head_dim == 64) return pick_b<64>(block_size, gt, qf32);
   if (head_dim == 128) return pick_b<128>(block_size, gt, qf32);
   return nullptr;

@@ -203,6 +203,28 @@ def pin_paged_equals_contiguous(impl, rng):
             assert np.array_equal(got[0], want), f"paged != contiguous at L={L}"
 
 
+def pin_contiguous_rows(impl, rng):
+    """The layout without a block table: rows built from the logical tokens by a
+    library transpose, padded with NaN past each length (never read), give bitwise
+    the output of attend_one on the logical tokens, request by request."""
+    S, Hq, Hkv, D, Lmax = 4, 6, 3, 8, 48
+    lens = [1, 17, 48, 0]
+    q = rng.standard_normal((S, Hq, D)).astype(np.float32)
+    k_rows = np.full((S, Hkv, Lmax, D), np.nan, dtype=np.float16)
+    v_rows = np.full((S, Hkv, Lmax, D), np.nan, dtype=np.float16)
+    toks = []
+    for i, L in enumerate(lens):
+        k = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        v = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        k_rows[i, :, :L, :] = k.transpose(1, 0, 2)
+        v_rows[i, :, :L, :] = v.transpose(1, 0, 2)
+        toks.append((k, v))
+    got = impl.attend_contiguous(q, k_rows, v_rows, lens, 0.25)
+    for i, (k, v) in enumerate(toks):
+        assert np.array_equal(got[i], impl.attend_one(q[i], k, v, 0.25)), f"row {i}"
+    assert np.array_equal(got[3], np.zeros((Hq, D)))
+
+
 def pin_zero_length(impl, rng):
     q = rng.standard_normal((1, 2, 8))
     kp = np.full((2, 2, 4, 8), np.nan, dtype=np.float16)

@@ -136,6 +136,17 @@ def test_residency_limit_follows_the_kernel():
     mha = _lib.plan(lens, 8, 8, 128, 16, _lib.PKV_F16)[1]
     assert mfma["waves_per_cu"] == 6
     assert valu_f32["waves_per_cu"] == 0 and mha["waves_per_cu"] == 0
+    # VALU, one pass, skewed: longest > 1.5 x mean of the non-empty lengths.
+    def valu(lens, part=0):
+        return _lib.plan(np.asarray(lens, dtype=np.int32), 8, 8, 128, 16, _lib.PKV_F16,
+                         partition_size=part)[1]["waves_per_cu"]
+    assert valu([100, 100, 151, 0, 0]) == 0          # mean 117, 151 < 175.5
+    assert valu([100, 100, 200, 0]) == 0             # mean 133.3: 200 is not > 200
+    assert valu([100, 100, 201, 0]) == 4             # mean 133.7: 201 > 200.5
+    assert valu([10, 10, 100]) == 4
+    assert valu([10, 10, 100], part=64) == 0         # split launches: no limit
+    assert valu([0, 0]) == 0
+    assert _lib.plan(workloads.opt13b().lengths, 40, 40, 128, 16, _lib.PKV_F16)[1]["waves_per_cu"] == 4
     prev = _lib.set_kernel_policy(_lib.PKV_POLICY_VALU)
     try:
         assert _lib.plan(lens, 32, 8, 128, 16, _lib.PKV_F16)[1]["waves_per_cu"] == 0

@@ -85,6 +85,7 @@ def _impl(**over):
     base = dict(
         attend_one=oracle.attention.attend_one,
         attend_paged=oracle.attention.attend_paged,
+        attend_contiguous=oracle.attention.attend_contiguous,
         gather_logical=oracle.cache.gather_logical,
         write_slots=oracle.cache.write_slots,
         copy_blocks=oracle.cache.copy_blocks,
@@ -97,7 +98,23 @@ def _impl(**over):
     return types.SimpleNamespace(**base)
 
 
+def _contiguous_factory(extra_token=0, swap=True):
+    def attend_contiguous(q, k_rows, v_rows, context_lens, scale, seqs=None):
+        q = np.asarray(q)
+        out = np.zeros(q.shape, dtype=np.float64)
+        for i in range(q.shape[0]):
+            n = int(context_lens[i]) + extra_token
+            k, v = k_rows[i, :, :n, :], v_rows[i, :, :n, :]
+            if swap:
+                k, v = np.swapaxes(k, 0, 1), np.swapaxes(v, 0, 1)
+            out[i] = oracle.attention.attend_one(q[i], k, v, scale)
+        return out
+    return attend_contiguous
+
+
 MUTANTS = {
+    "rows_read_one_past_length": _impl(attend_contiguous=_contiguous_factory(extra_token=1)),
+    "rows_axes_not_swapped": _impl(attend_contiguous=_contiguous_factory(swap=False)),
     "head_map_modulo": _impl(attend_one=_attend_factory(head_map=lambda h, Hq, Hkv: h % Hkv)),
     "no_max_subtraction_overflow": _impl(attend_one=_attend_factory(subtract_max=False)),
     "scale_dropped": _impl(attend_one=_attend_factory(use_scale=False)),
@@ -118,7 +135,7 @@ def _caught(impl):
         try:
             with np.errstate(all="ignore"):
                 pin(impl, np.random.default_rng(7))
-        except (AssertionError, FloatingPointError, IndexError, ValueError):
+        except (AssertionError, FloatingPointError, IndexError, ValueError, ZeroDivisionError):
             return pin.__name__
     return None
 
