@@ -308,6 +308,8 @@ typedef struct {
   int32_t shared_blocks;  /* referenced by more than one sequence        */
   int64_t live_tokens;    /* sum of live sequences' lengths              */
   int64_t sum_refcounts;  /* sum of all reference counts                 */
+  int32_t pending_blocks; /* freed with kv_seq_free_deferred, not yet retired */
+  int32_t reserved;
 } kv_stats;
 
 /* initial_order: host int32 [num_blocks], a permutation of 0..num_blocks-1, or
@@ -329,6 +331,20 @@ int kv_seq_append(kv_allocator* a, int32_t seq, int32_t n, int64_t* slots_out,
 int kv_batch_append(kv_allocator* a, const int32_t* seqs, int32_t num_seqs, int64_t* slots_out,
                     int32_t* cow_pairs_out, int32_t* n_cow_out);
 int kv_seq_free(kv_allocator* a, int32_t seq);
+/*
+ * Stream-ordered free.  [C] "Shared prefixes need ownership rules": a device
+ * operation still queued must not find its storage reassigned.  Like
+ * kv_seq_free (the sequence is gone at once, references drop now), but a block
+ * whose count reaches zero is parked with the caller's `epoch` tag instead of
+ * going to the free list.  kv_allocator_retire(a, done) then returns every
+ * parked block whose tag is <= done to the free list, in the order they were
+ * freed (so the last freed is handed out first, as with kv_seq_free).  The
+ * caller picks the epochs, e.g. a step counter with an event recorded after
+ * each step's last use of its blocks: once that event has completed, the step's
+ * epoch may be retired.  *released_out (may be NULL) = blocks returned.
+ */
+int kv_seq_free_deferred(kv_allocator* a, int32_t seq, int64_t epoch);
+int kv_allocator_retire(kv_allocator* a, int64_t done, int32_t* released_out);
 int kv_seq_len(const kv_allocator* a, int32_t seq, int32_t* len_out);
 /* Lengths of n sequences in one call: host int32 lens_out [n]. */
 int kv_seq_lens(const kv_allocator* a, const int32_t* seqs, int32_t n, int32_t* lens_out);

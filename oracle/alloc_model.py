@@ -18,6 +18,9 @@ Plain Python lists and dicts.  The rules, each from the pages:
   be preserved).
 * Freeing drops one reference per block; a block whose count reaches zero goes
   back to the pool (teqners explainer, sharing section).
+* A block may be held back from reuse until device work still queued against
+  it has finished (rsw.lol, section "Shared prefixes need ownership rules":
+  storage must not be reassigned under a delayed device operation).
 
 Readings where the pages are silent:
 
@@ -30,6 +33,9 @@ Readings where the pages are silent:
   in place.  At most one copy per append.
 * Running out of blocks changes nothing (the whole call fails).
 * Request ids count up from 0 and are never reused.
+* Deferred free: references drop at once, but a block reaching zero is parked
+  with the caller's epoch; ``retire(done)`` returns every parked block with
+  epoch <= done to the free list in the order they were freed.
 """
 
 import copy
@@ -54,6 +60,7 @@ class AllocatorModel:
         self.block_size = block_size
         self.free = list(reversed(order))      # top of stack = end of list
         self.refcount = [0] * num_blocks
+        self.parked = []                        # (block, epoch) in free order
         self.tables = {}                        # seq id -> list of physical blocks
         self.lengths = {}                       # seq id -> tokens stored
         self.next_id = 0
@@ -137,6 +144,21 @@ class AllocatorModel:
         del self.tables[seq]
         del self.lengths[seq]
 
+    def free_seq_deferred(self, seq, epoch):
+        self._check(seq)
+        for b in self.tables[seq]:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.parked.append((b, int(epoch)))
+        del self.tables[seq]
+        del self.lengths[seq]
+
+    def retire(self, done):
+        released = [b for b, e in self.parked if e <= done]
+        self.parked = [(b, e) for b, e in self.parked if e > done]
+        self.free.extend(released)
+        return len(released)
+
     # -- views ------------------------------------------------------------
     def length(self, seq):
         self._check(seq)
@@ -166,4 +188,5 @@ class AllocatorModel:
             "shared_blocks": sum(1 for r in self.refcount if r > 1),
             "live_tokens": sum(self.lengths.values()),
             "sum_refcounts": sum(self.refcount),
+            "pending_blocks": len(self.parked),
         }

@@ -68,7 +68,8 @@ class StepLayout(ctypes.Structure):
 
 class KVStats(ctypes.Structure):
     _fields_ = [("num_blocks", c_int32), ("free_blocks", c_int32), ("used_blocks", c_int32),
-                ("shared_blocks", c_int32), ("live_tokens", c_int64), ("sum_refcounts", c_int64)]
+                ("shared_blocks", c_int32), ("live_tokens", c_int64), ("sum_refcounts", c_int64),
+                ("pending_blocks", c_int32), ("reserved", c_int32)]
 
 
 _SIGNATURES = {
@@ -98,6 +99,8 @@ _SIGNATURES = {
     "kv_seq_append": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, POINTER(c_int32)]),
     "kv_batch_append": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, POINTER(c_int32)]),
     "kv_seq_free": (c_int32, [c_void_p, c_int32]),
+    "kv_seq_free_deferred": (c_int32, [c_void_p, c_int32, c_int64]),
+    "kv_allocator_retire": (c_int32, [c_void_p, c_int64, POINTER(c_int32)]),
     "kv_seq_len": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
     "kv_seq_lens": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p]),
     "kv_export_block_tables": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
@@ -386,6 +389,16 @@ class BlockAllocator:
     def free(self, seq: int):
         _check(lib().kv_seq_free(self._h, seq))
 
+    def free_deferred(self, seq: int, epoch: int):
+        """Free now, but park blocks that reach zero until ``retire(>= epoch)``."""
+        _check(lib().kv_seq_free_deferred(self._h, seq, int(epoch)))
+
+    def retire(self, done: int) -> int:
+        """Return parked blocks with epoch <= ``done`` to the free list; how many."""
+        out = c_int32()
+        _check(lib().kv_allocator_retire(self._h, int(done), byref(out)))
+        return out.value
+
     def length(self, seq: int) -> int:
         out = c_int32()
         _check(lib().kv_seq_len(self._h, seq, byref(out)))
@@ -434,4 +447,4 @@ class BlockAllocator:
     def stats(self) -> dict:
         st = KVStats()
         _check(lib().kv_allocator_stats(self._h, byref(st)))
-        return {name: getattr(st, name) for name, _ in KVStats._fields_}
+        return {name: getattr(st, name) for name, _ in KVStats._fields_ if name != "reserved"}

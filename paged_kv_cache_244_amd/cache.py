@@ -155,6 +155,8 @@ class PagedKVCache:
         self._plan_staging = _Staging(self.device, nbytes=1 << 16)   # re-plans in attend
         self._workspace = None
         self._stream_ptr = self.stream.cuda_stream
+        self._epoch = 0
+        self._pending = []            # (epoch, event) of deferred frees, oldest first
 
     # -- sequences -------------------------------------------------------------
     def new_sequence(self) -> int:
@@ -163,8 +165,29 @@ class PagedKVCache:
     def fork(self, seq: int) -> int:
         return self.alloc.fork(seq)
 
-    def free(self, seq: int):
-        self.alloc.free(seq)
+    def free(self, seq: int, deferred: bool = False):
+        """Release a sequence.  Immediate reuse is safe for work on this cache's stream
+        (it runs in order).  ``deferred=True`` keeps its blocks out of circulation until
+        the device work enqueued on the stream so far has finished (an event marks it),
+        so that work on other streams, or a host running ahead, cannot reuse them early."""
+        if not deferred:
+            self.alloc.free(seq)
+            return
+        self._epoch += 1
+        ev = torch.cuda.Event()
+        ev.record(self.stream)
+        self._pending.append((self._epoch, ev))
+        self.alloc.free_deferred(seq, self._epoch)
+
+    def retire(self, wait: bool = False) -> int:
+        """Return the blocks of deferred frees whose device work has finished (all of
+        them, waiting, with ``wait=True``) to the free list; how many came back."""
+        done = None
+        while self._pending and (wait or self._pending[0][1].query()):
+            if wait:
+                self._pending[0][1].synchronize()
+            done = self._pending.pop(0)[0]
+        return self.alloc.retire(done) if done is not None else 0
 
     def length(self, seq: int) -> int:
         return self.alloc.length(seq)
@@ -186,6 +209,8 @@ class PagedKVCache:
     def reserve_many(self, seqs, counts) -> torch.Tensor:
         """Slots for ``counts[i]`` more tokens of each ``seqs[i]`` (e.g. a batched prefill),
         concatenated in order, as one device int64 tensor; copies are issued first."""
+        if self._pending:
+            self.retire()
         all_slots, all_pairs = [], []
         for seq, n in zip(seqs, counts):
             slots, pairs = self.alloc.append(int(seq), int(n))
@@ -199,6 +224,8 @@ class PagedKVCache:
 
     def reserve_step(self, seqs) -> torch.Tensor:
         """One slot per listed sequence (a decode step); device int64 [len(seqs)]."""
+        if self._pending:
+            self.retire()
         slots, pairs = self.alloc.append_batch(seqs)
         slots_dev, pairs_dev = self.upload(slots, pairs)
         self._copy_pairs_dev(pairs_dev)
@@ -209,6 +236,8 @@ class PagedKVCache:
         slot per sequence (issuing copy-on-write copies), export tables and lengths and
         plan the launch (``kv_decode_step_host``).  Returns (device slots, DecodeBatch)."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        if self._pending:
+            self.retire()
         key = (self.num_q_heads, self.q_dtype, partition_size)
         part = -1 if partition_size == "auto" else int(partition_size)
         qd = _lib.PKV_F16 if self.q_dtype == torch.float16 else _lib.PKV_F32

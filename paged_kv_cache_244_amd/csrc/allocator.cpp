@@ -34,6 +34,11 @@ struct kv_allocator {
     std::vector<int32_t> blocks;     // logical -> physical
   };
   std::vector<Seq> seqs;             // indexed by id; ids never reused
+  struct Parked {
+    int32_t block;
+    int64_t epoch;
+  };
+  std::vector<Parked> parked;        // freed with an epoch tag, in free order
 };
 
 namespace {
@@ -248,6 +253,37 @@ int kv_seq_free(kv_allocator* a, int32_t seq) {
   return PKV_OK;
 }
 
+int kv_seq_free_deferred(kv_allocator* a, int32_t seq, int64_t epoch) {
+  if (int rc = check_seq(a, seq)) return rc;
+  kv_allocator::Seq& s = a->seqs[seq];
+  for (int32_t b : s.blocks) {
+    if (--a->refcount[b] == 0) a->parked.push_back({b, epoch});
+  }
+  s.blocks.clear();
+  s.blocks.shrink_to_fit();
+  s.length = 0;
+  s.live = false;
+  return PKV_OK;
+}
+
+int kv_allocator_retire(kv_allocator* a, int64_t done, int32_t* released_out) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "allocator is NULL");
+  int32_t released = 0;
+  size_t keep = 0;
+  for (size_t i = 0; i < a->parked.size(); ++i) {
+    const kv_allocator::Parked p = a->parked[i];
+    if (p.epoch <= done) {
+      a->free_stack.push_back(p.block);
+      ++released;
+    } else {
+      a->parked[keep++] = p;
+    }
+  }
+  a->parked.resize(keep);
+  if (released_out) *released_out = released;
+  return PKV_OK;
+}
+
 int kv_seq_len(const kv_allocator* a, int32_t seq, int32_t* len_out) {
   if (int rc = check_seq(a, seq)) return rc;
   if (!len_out) return fail(PKV_ERR_INVALID_ARG, "len_out is NULL");
@@ -386,6 +422,7 @@ int kv_allocator_stats(const kv_allocator* a, kv_stats* out) {
   }
   for (const kv_allocator::Seq& s : a->seqs)
     if (s.live) st.live_tokens += s.length;
+  st.pending_blocks = static_cast<int32_t>(a->parked.size());
   *out = st;
   return PKV_OK;
 }

@@ -41,6 +41,7 @@ int main(int argc, char** argv) {
     std::vector<int64_t> len;          // by id
     std::vector<int64_t> slots(4096);
     std::vector<int32_t> pairs(2 * 4096);
+    int64_t epoch = 0;
     for (int it = 0; it < iters / 8; ++it) {
       kv_stats before{};
       CHECK(kv_allocator_stats(a, &before) == PKV_OK);
@@ -102,7 +103,15 @@ int main(int argc, char** argv) {
         }
       } else if (op == 4) {
         const size_t i = rng() % live.size();
-        CHECK(kv_seq_free(a, live[i]) == PKV_OK);
+        if (rng() % 2) {
+          CHECK(kv_seq_free(a, live[i]) == PKV_OK);
+        } else {
+          epoch += static_cast<int64_t>(rng() % 2);
+          CHECK(kv_seq_free_deferred(a, live[i], epoch) == PKV_OK);
+          int32_t released = -1;
+          CHECK(kv_allocator_retire(a, epoch - static_cast<int64_t>(rng() % 3), &released) == PKV_OK);
+          CHECK(released >= 0);
+        }
         live.erase(live.begin() + static_cast<long>(i));
       } else if (op == 5) {
         int32_t l = 0, pair[2], ncow = 0;
@@ -123,7 +132,7 @@ int main(int argc, char** argv) {
         CHECK(st.free_blocks == before.free_blocks && st.sum_refcounts == before.sum_refcounts &&
               st.live_tokens == before.live_tokens);
       }
-      CHECK(st.free_blocks + st.used_blocks == nb);
+      CHECK(st.free_blocks + st.used_blocks + st.pending_blocks == nb);
       CHECK(st.shared_blocks <= st.used_blocks);
       if (!live.empty()) {
         const int32_t maxb = nb;
@@ -152,6 +161,7 @@ int main(int argc, char** argv) {
       }
     }
     for (int32_t s : live) CHECK(kv_seq_free(a, s) == PKV_OK);
+    CHECK(kv_allocator_retire(a, epoch, nullptr) == PKV_OK);
     kv_stats st{};
     CHECK(kv_allocator_stats(a, &st) == PKV_OK);
     CHECK(st.free_blocks == nb && st.sum_refcounts == 0);

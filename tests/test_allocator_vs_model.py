@@ -68,6 +68,14 @@ class Pair:
         if seq in self.live:
             self.live.remove(seq)
 
+    def free_deferred(self, seq, epoch):
+        self._both(lambda: self.c.free_deferred(seq, epoch), lambda: self.m.free_seq_deferred(seq, epoch))
+        if seq in self.live:
+            self.live.remove(seq)
+
+    def retire(self, done):
+        assert self.c.retire(done) == self.m.retire(done)
+
     def compare_state(self):
         assert self.c.stats() == self.m.stats()
         if self.live:
@@ -85,9 +93,15 @@ def test_random_op_sequences_match_model():
         nb = int(rng.integers(4, 40))
         bs = int(rng.choice([1, 2, 4, 8, 16]))
         p = Pair(nb, bs, rng.permutation(nb))
+        epoch = 0
         for _ in range(120):
-            op = rng.integers(6)
-            if op == 0 or not p.live:
+            op = rng.integers(8)
+            if op == 6 and p.live:
+                epoch += int(rng.integers(0, 2))
+                p.free_deferred(p.live[rng.integers(len(p.live))], epoch)
+            elif op == 7:
+                p.retire(int(rng.integers(-1, epoch + 1)))
+            elif op == 0 or not p.live:
                 p.create()
             elif op == 1:
                 p.fork(p.live[rng.integers(len(p.live))])
@@ -103,6 +117,7 @@ def test_random_op_sequences_match_model():
             p.compare_state()
         for s in list(p.live):
             p.free(s)
+        p.retire(epoch)
         p.compare_state()
         assert p.c.stats()["free_blocks"] == nb
 

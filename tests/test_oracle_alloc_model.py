@@ -30,11 +30,13 @@ def check_invariants(m: AllocatorModel):
         for b in table:
             counts[b] += 1
     assert counts == m.refcount, "refcount = number of tables holding the block"
-    assert len(set(m.free)) == len(m.free)
-    for b in m.free:
-        assert m.refcount[b] == 0, "a free block is referenced by nobody"
+    parked = [b for b, _ in m.parked]
+    assert len(set(m.free + parked)) == len(m.free) + len(parked), "free and parked are disjoint"
+    for b in m.free + parked:
+        assert m.refcount[b] == 0, "a free or parked block is referenced by nobody"
     used = sum(1 for r in m.refcount if r > 0)
-    assert used + len(m.free) == m.num_blocks, "no block is lost (no external fragmentation)"
+    assert used + len(m.free) + len(parked) == m.num_blocks, \
+        "no block is lost (no external fragmentation)"
 
 
 def test_demand_allocation_and_block_count():
@@ -203,8 +205,9 @@ def test_bad_ids():
 
 def _random_ops(m, rng, steps):
     live = []
+    epoch = 0
     for _ in range(steps):
-        op = rng.integers(5)
+        op = rng.integers(7)
         try:
             if op == 0 or not live:
                 live.append(m.create())
@@ -214,11 +217,17 @@ def _random_ops(m, rng, steps):
                 m.append(live[rng.integers(len(live))], int(rng.integers(0, 7)))
             elif op == 3:
                 m.append_batch([live[i] for i in rng.integers(len(live), size=3)])
-            else:
+            elif op == 4:
                 m.free_seq(live.pop(rng.integers(len(live))))
+            elif op == 5:
+                epoch += 1
+                m.free_seq_deferred(live.pop(rng.integers(len(live))), epoch)
+            else:
+                m.retire(int(rng.integers(0, epoch + 1)))
         except OutOfBlocks:
             pass
         check_invariants(m)
+    m.retire(epoch)
     return live
 
 
@@ -263,3 +272,35 @@ def test_exhaustive_short_sequences():
             for s in live:
                 m.free_seq(s)
             assert len(m.free) == 4
+
+
+def test_deferred_free_parks_blocks_until_retired():
+    """A block freed at epoch e is not handed out before retire(>= e); then the last
+    freed comes back first, as with an immediate free."""
+    m = AllocatorModel(6, 4, [0, 1, 2, 3, 4, 5])
+    a, b = m.create(), m.create()
+    m.append(a, 8)                      # blocks 0, 1
+    m.append(b, 4)                      # block 2
+    m.free_seq_deferred(a, epoch=1)
+    m.free_seq_deferred(b, epoch=2)
+    assert m.stats()["pending_blocks"] == 3 and m.stats()["free_blocks"] == 3
+    c = m.create()
+    m.append(c, 12)                     # must not get 0, 1 or 2
+    assert sorted(m.table(c)) == [3, 4, 5]
+    with pytest.raises(OutOfBlocks):
+        m.append(c, 1)
+    assert m.retire(0) == 0
+    assert m.retire(1) == 2             # a's blocks, in free order 0 then 1
+    assert m.free == [0, 1]
+    m.append(c, 1)                      # a fresh block: the last freed, 1
+    assert m.table(c)[-1] == 1
+    assert m.retire(5) == 1 and m.stats()["pending_blocks"] == 0
+    check_invariants(m)
+    # a shared block parks only when its last reference goes
+    d = m.create()
+    m.append(d, 1)
+    e = m.fork(d)
+    m.free_seq_deferred(d, epoch=9)
+    assert m.stats()["pending_blocks"] == 0
+    m.free_seq_deferred(e, epoch=10)
+    assert m.stats()["pending_blocks"] == 1 and m.parked[0][1] == 10
