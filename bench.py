@@ -39,7 +39,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="opt13b",
-                    choices=["opt13b", "gqa", "long_context", "parallel_sampling", "tiny"])
+                    choices=["opt13b", "gqa", "long_context", "parallel_sampling", "tiny", "prefill"])
     ap.add_argument("--partition", default="auto",
                     help="tokens per split-context partition, 0 = one pass, or 'auto'")
     ap.add_argument("--kernel-policy", default="default", choices=["default", "valu"],
@@ -363,6 +363,103 @@ class SimpleWorkload:
         self.head_dim, self.block_size, self.q_dtype, self.scale = d, b, q_dtype, scale
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
+
+
+def prefill_bench(args):
+    """Prompt phase: each step admits the 16 prompts (host allocator, one upload), writes
+    their K/V, runs pa_prefill over the block tables, then frees them.  Metric: causal
+    attention FLOP/s (roofline: the fp16 matrix cores)."""
+    import torch
+
+    from paged_kv_cache_244_amd import workloads
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    dev = torch.device("cuda:0")
+    w = workloads.prefill()
+    cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                         initial_order=w.initial_order, device=dev, poison=False,
+                         num_q_heads=w.num_q_heads)
+    kd, vd, qd = _to_dev([w.k_tokens, w.v_tokens, w.q], dev)
+    out = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+    lens = [int(L) for L in w.lengths]
+    stream = cache.stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(slot=None):
+        seqs = [cache.new_sequence() for _ in lens]
+        slots = cache.reserve_many(seqs, lens)
+        cache.write(slots, kd, vd)
+        if slot is not None:
+            ev[slot][0].record(stream)
+        cache.prefill(qd, seqs, lens, w.scale, out=out)
+        if slot is not None:
+            ev[slot][1].record(stream)
+        for sq in seqs:
+            cache.free(sq)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in ev]
+    flops = float(w.flops())
+    achieved = flops / (float(np.mean(ms)) / 1e3) / 1e12
+    baseline = None
+    if args.cpu_seconds > 0:
+        baseline = prefill_cpu_baseline(w)
+    result = {
+        "metric": "paged prefill attention TFLOP/s (% of fp16 matrix peak)",
+        "value": round(flops * args.steps / wall / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "prefill: 16 prompts of U{512..4096} tokens", "num_seqs": w.num_seqs,
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "prompt_tokens": int(w.lengths.sum()),
+                   "flops_per_step": int(flops)},
+        "prefill_us": round(float(np.mean(ms)) * 1e3, 2),
+        "prefill_us_p10_p90": [round(float(np.percentile(ms, 10)) * 1e3, 2),
+                               round(float(np.percentile(ms, 90)) * 1e3, 2)],
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "pa_prefill"},
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def prefill_cpu_baseline(w, prompt=1024):
+    """The oracle's attend_prefill_paged on one request's first ``prompt`` tokens."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention, cache
+
+    nb = -(-prompt // w.block_size)
+    shape = (nb, w.num_kv_heads, w.block_size, w.head_dim)
+    kp, vp = np.zeros(shape, np.float16), np.zeros(shape, np.float16)
+    cache.write_slots(kp, vp, w.k_tokens[:prompt], w.v_tokens[:prompt], list(range(prompt)),
+                      w.block_size)
+    tables = np.arange(nb, dtype=np.int64)[None]
+    starts = np.array([0, prompt], dtype=np.int64)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        attention.attend_prefill_paged(w.q[:prompt], kp, vp, tables, [prompt], starts,
+                                       w.block_size, w.scale)
+        dt = time.perf_counter() - t0
+    flops = 4 * w.num_q_heads * w.head_dim * prompt * (prompt + 1) // 2
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"one prompt of {prompt} tokens, fp64 numpy attend_prefill_paged",
+            "seconds": round(dt, 2)}
+
+
 def main():
     args = parse_args()
     if args.copy_probe:
@@ -372,6 +469,14 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path has no multi-GPU sharding in this build)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "prefill":
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        torch.cuda.set_device(0)
+        prefill_bench(args)
+        return
 
     import torch
 

@@ -279,6 +279,57 @@ int pa_decode_contiguous(float* out, const void* q, int32_t q_dtype,
                          const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_prefill — causal attention of each request's new tokens (the prompt, or
+ * the next chunk of one) over its block table.  [C] "Prompt processing and
+ * incremental decoding impose different shapes of work": many queries per
+ * request at once, bound by arithmetic rather than bytes; [B] "The page table,
+ * relocated into attention": keys and values come through the table, after
+ * kv_cache_write stored the new tokens.
+ *
+ * Request i holds L = context_lens[i] tokens; its Q = q_starts[i+1] -
+ * q_starts[i] new queries are the last Q positions, query j at position
+ * L - Q + j.  For query head h, KV head g = h / (num_q_heads / num_kv_heads):
+ *     out[q_starts[i] + j][h][:] = sum_{t <= L-Q+j} softmax_t(scale q.K_t) V_t
+ * in fp32 from fp16 q, K, V (P rounded to fp16 for the matrix cores, as in
+ * pa_decode's MFMA kernel).  Requires Q <= L; a query at a negative position
+ * gets zeros.
+ *   out      : device fp32 [total_q][num_q_heads][head_dim] (rows of listed
+ *              blocks written).
+ *   q        : device fp16 [total_q][num_q_heads][head_dim].
+ *   q_starts : device int32 [num_seqs + 1], non-decreasing, q_starts[S] <= total_q
+ *              (a request whose offsets leave [0, total_q] is skipped).
+ *   block_tables, context_lens, k_cache, v_cache, num_blocks: as pa_decode.
+ *   work_items: device uint32 [num_work_items] of (request << 16 | query
+ *              block) entries, a block being pa_prefill_queries_per_item
+ *              queries; pa_prefill_plan lists every block once, most tokens
+ *              to read first.  Missing blocks leave their rows unwritten.
+ * Supported: head_dim 64/128, block_size 8..128, groups of 1, 2, 4, 8, 16 or a
+ * multiple of 16 query heads per KV head.  Errors as pa_decode.
+ */
+int pa_prefill(float* out, const void* q, const int32_t* q_starts, int32_t total_q,
+               const void* k_cache, const void* v_cache, int32_t num_blocks,
+               const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+               const uint32_t* work_items, int32_t num_work_items, void* stream);
+
+/* Queries per pa_prefill work item (16 / query heads per wave); 0 = unsupported. */
+int32_t pa_prefill_queries_per_item(int32_t num_q_heads, int32_t num_kv_heads);
+
+/*
+ * pa_prefill_plan — host only: the work items of a pa_prefill launch from
+ * host copies of each request's query count and context length, one per block
+ * of pa_prefill_queries_per_item queries, ordered by the tokens the block
+ * reads (its last query's position + 1), most first; ties by request, then
+ * block.  items_capacity >= the total query count always suffices;
+ * *num_items_out is set even when the capacity is too small
+ * (PKV_ERR_INVALID_ARG).
+ */
+int pa_prefill_plan(const int32_t* q_lens, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, uint32_t* items,
+                    int32_t items_capacity, int32_t* num_items_out);
+
 /* ------------------------------------------------------------------------ */
 /* Host block allocator                                                      */
 /* ------------------------------------------------------------------------ */

@@ -94,3 +94,32 @@ def attend_contiguous(q, k_rows, v_rows, context_lens, scale, seqs=None):
         values = np.swapaxes(v_rows[i, :, :length, :], 0, 1)
         out[i] = attend_one(q[i], keys, values, scale)
     return out
+
+
+def attend_prefill_paged(q, k_pool, v_pool, block_tables, context_lens, q_starts, block_size,
+                         scale):
+    """Causal attention of each request's new tokens over its block table (float64).
+
+    The prompt phase ("The KV cache is a systems problem", section "Prompt
+    processing and incremental decoding impose different shapes of work"):
+    request i holds L_i tokens, the last Q_i = q_starts[i+1] - q_starts[i] of
+    which are its new queries; query j sits at position L_i - Q_i + j and sees
+    tokens 0..that position, gathered through the table as in ``attend_paged``.
+    q: ``[T, Hq, D]``; returns ``[T, Hq, D]`` float64 (a query at a negative
+    position, or rows outside every request, stay zero).
+    """
+    q = np.asarray(q)
+    total, num_q_heads, head_dim = q.shape
+    out = np.zeros((total, num_q_heads, head_dim), dtype=np.float64)
+    for i in range(len(context_lens)):
+        length = int(context_lens[i])
+        first, last = int(q_starts[i]), int(q_starts[i + 1])
+        count = last - first
+        keys = gather_logical(k_pool, block_tables[i], length, block_size)
+        values = gather_logical(v_pool, block_tables[i], length, block_size)
+        for j in range(count):
+            pos = length - count + j
+            if pos < 0:
+                continue
+            out[first + j] = attend_one(q[first + j], keys[:pos + 1], values[:pos + 1], scale)
+    return out

@@ -92,6 +92,12 @@ _SIGNATURES = {
                                        c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
                                        c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p,
                                        c_size_t, c_void_p]),
+    "pa_prefill": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                             c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                             c_int32, c_float, c_void_p, c_int32, c_void_p]),
+    "pa_prefill_queries_per_item": (c_int32, [c_int32, c_int32]),
+    "pa_prefill_plan": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_int32,
+                                  POINTER(c_int32)]),
     "kv_allocator_create": (c_int32, [c_int32, c_int32, c_void_p, POINTER(c_void_p)]),
     "kv_allocator_destroy": (None, [c_void_p]),
     "kv_seq_create": (c_int32, [c_void_p, POINTER(c_int32)]),
@@ -325,6 +331,44 @@ def pa_decode_contiguous(out, q, k_rows, v_rows, context_lens, scale, max_contex
         _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, float(scale),
         int(max_context_len), int(partition_size), items_ptr, n_items, int(waves_per_cu),
         ws_ptr, ws_bytes, _stream(stream)))
+
+
+def prefill_plan(q_lens, context_lens, num_q_heads, num_kv_heads):
+    """Work items of a pa_prefill launch (host uint32, most tokens to read first)."""
+    ql = np.ascontiguousarray(q_lens, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if ql.shape != cl.shape or ql.ndim != 1:
+        raise ValueError("q_lens and context_lens must be 1-D and of one length")
+    n = int(ql.shape[0])
+    cap = max(int(np.maximum(ql, 0).sum()), 1)
+    items = np.empty(cap, dtype=np.uint32)
+    count = c_int32()
+    _check(lib().pa_prefill_plan(ql.ctypes.data if n else None, cl.ctypes.data if n else None, n,
+                                 int(num_q_heads), int(num_kv_heads), items.ctypes.data, cap,
+                                 byref(count)))
+    return items[: count.value].copy()
+
+
+def pa_prefill(out, q, q_starts, k_cache, v_cache, block_tables, context_lens, scale,
+               work_items, stream=None):
+    """Causal prefill attention: out[T, Hq, D] fp32 from q[T, Hq, D] fp16 (T queries of
+    all requests, request i's rows q_starts[i]..q_starts[i+1]) through the block tables;
+    ``work_items`` from ``prefill_plan`` (device int32/uint32)."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_geometry(k_cache, v_cache)
+    t, hq, dq = (int(x) for x in q.shape)
+    if dq != d or tuple(out.shape) != (t, hq, d):
+        raise ValueError("q and out must be [T, Hq, head_dim]")
+    s = int(context_lens.shape[0])
+    if tuple(q_starts.shape) != (s + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError("q_starts must be [S+1], block_tables [S, max_blocks], context_lens [S]")
+    items_ptr, n_items = _items(work_items)
+    _check(lib().pa_prefill(
+        _dev(out, torch.float32, "out"), _dev(q, torch.float16, "q"),
+        _dev(q_starts, torch.int32, "q_starts"), t, _dev(k_cache, torch.float16, "k_cache"),
+        _dev(v_cache, torch.float16, "v_cache"), nb, _dev(block_tables, torch.int32, "block_tables"),
+        int(block_tables.shape[1]), _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d,
+        bs, float(scale), items_ptr, n_items, _stream(stream)))
 
 
 # --------------------------------------------------------------------------- host allocator

@@ -323,6 +323,22 @@ class PagedKVCache:
             self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._workspace
 
+    def prefill(self, q, seqs, q_lens, scale, layer=0, out=None):
+        """Causal attention of new tokens (``pa_prefill``): ``q`` [T, Hq, D] fp16 holds
+        the last ``q_lens[i]`` tokens of each ``seqs[i]`` in order, whose K/V are
+        already written.  Tables, lengths, query offsets and the work list go up in
+        one upload.  Returns out [T, Hq, D] fp32."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        tables, lens, _ = self._tables(seqs, None, None)
+        starts = _prefill_starts(q_lens)
+        items = _lib.prefill_plan(np.diff(starts), lens, q.shape[1], self.num_kv_heads)
+        t_d, l_d, s_d, i_d = self.upload(tables, lens, starts, items.view(np.int32))
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        _lib.pa_prefill(out, q, s_d, self.k[layer], self.v[layer], t_d, l_d, scale, i_d,
+                        stream=self.stream)
+        return out
+
     def attend(self, q, batch: "DecodeBatch", scale, partition_size=None, layer=0, out=None):
         """Decode attention for ``batch`` with the schedule planned for it.
 
@@ -357,6 +373,10 @@ class PagedKVCache:
             items.shape[0], info["waves_per_cu"], ws.data_ptr() if ws is not None else None,
             ws.numel() if ws is not None else 0, self._stream_ptr))
         return out
+
+
+def _prefill_starts(q_lens):
+    return np.concatenate([[0], np.cumsum(np.asarray(q_lens, dtype=np.int64))]).astype(np.int32)
 
 
 class DecodeBatch:

@@ -21,21 +21,12 @@
 
 #include "decode_plan.h"
 #include "errors.h"
+#include "launch.h"
 #include "pa_decode_common.h"
 #include "pagedkv.h"
 
+namespace pkv_decode {
 namespace {
-
-using pkv::fail;
-using namespace pkv_decode;
-using pkv_plan::KernelChoice;
-using pkv_plan::align256;
-using pkv_plan::choose_kernel;
-using pkv_plan::parts_for;
-using pkv_plan::workspace_bytes_for;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMaxGridY = 32768;      // work-list entries per grid row (y), then z
 
 // Dynamic LDS that limits a launch of fn to about waves_per_cu one-wave
 // workgroups per compute unit (0 = no limit).  Cached per kernel and device.
@@ -48,6 +39,8 @@ struct LdsInfo {
 };
 std::mutex g_lds_mu;
 std::vector<LdsInfo> g_lds_cache;
+
+}  // namespace
 
 hipError_t reserve_lds_bytes(const void* fn, int waves_per_cu, unsigned* dyn) {
   *dyn = 0;
@@ -82,6 +75,21 @@ hipError_t reserve_lds_bytes(const void* fn, int waves_per_cu, unsigned* dyn) {
   *dyn = bytes > 0 ? static_cast<unsigned>(bytes) : 0u;
   return hipSuccess;
 }
+
+}  // namespace pkv_decode
+
+namespace {
+
+using pkv::fail;
+using namespace pkv_decode;
+using pkv_plan::KernelChoice;
+using pkv_plan::align256;
+using pkv_plan::choose_kernel;
+using pkv_plan::parts_for;
+using pkv_plan::workspace_bytes_for;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxGridY = 32768;      // work-list entries per grid row (y), then z
 
 }  // namespace
 

@@ -237,6 +237,50 @@ def with_block_size(w: DecodeWorkload, block_size: int, seed: int = 4) -> Decode
                           w.k_tokens, w.v_tokens, w.q, w.offsets, w.partition_size)
 
 
+@dataclass
+class PrefillWorkload:
+    """A batch of prompts processed at once: every prompt token is a query."""
+
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    scale: float
+    lengths: np.ndarray          # int32 [S] prompt tokens
+    num_blocks: int
+    initial_order: np.ndarray
+    k_tokens: np.ndarray         # float16 [sum(L), Hkv, D]
+    v_tokens: np.ndarray
+    q: np.ndarray                # float16 [sum(L), Hq, D], the prompt tokens' queries
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.lengths.shape[0])
+
+    def flops(self) -> int:
+        """Causal attention work: a query at position p meets p + 1 keys; each
+        (query, key, head) costs 2*D for the score and 2*D for the value sum."""
+        pairs = sum(int(L) * (int(L) + 1) // 2 for L in self.lengths)
+        return 4 * self.num_q_heads * self.head_dim * pairs
+
+
+def prefill(seed: int = 6, batch: int = 16) -> PrefillWorkload:
+    """16 prompts of U{512..4096} tokens, 32 query / 8 KV heads x 128, B = 16."""
+    root = np.random.SeedSequence(seed)
+    s_len, s_perm, s_k, s_v, s_q = root.spawn(5)
+    lengths = np.random.Generator(np.random.PCG64(s_len)).integers(512, 4096 + 1, size=batch)
+    lengths = lengths.astype(np.int32)
+    hq, hkv, d, bs = 32, 8, 128, 16
+    num_blocks = _pool_blocks(lengths, bs, 1.2)
+    order = np.random.Generator(np.random.PCG64(s_perm)).permutation(num_blocks).astype(np.int32)
+    total = int(lengths.sum())
+    return PrefillWorkload("prefill", hq, hkv, d, bs, 1.0 / math.sqrt(d), lengths, num_blocks,
+                           order, _normal(s_k, (total, hkv, d), np.float16),
+                           _normal(s_v, (total, hkv, d), np.float16),
+                           _normal(s_q, (total, hq, d), np.float16))
+
+
 WORKLOADS = {
     "tiny": tiny,
     "opt13b": opt13b,

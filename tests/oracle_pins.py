@@ -225,6 +225,65 @@ def pin_contiguous_rows(impl, rng):
     assert np.array_equal(got[3], np.zeros((Hq, D)))
 
 
+def _prefill_case(impl, rng, lens, qlens, Hq, Hkv, D, B):
+    """Requests scattered through random placements; q rows are each request's
+    last qlens[i] positions."""
+    NB = sum(-(-L // B) for L in lens) + 3
+    kp = np.full((NB, Hkv, B, D), np.nan, dtype=np.float16)
+    vp = np.full((NB, Hkv, B, D), np.nan, dtype=np.float16)
+    perm = rng.permutation(NB)
+    tables = np.full((len(lens), NB), 10 ** 6, dtype=np.int64)
+    toks, used = [], 0
+    for i, L in enumerate(lens):
+        k = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        v = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        nb = -(-L // B)
+        place = perm[used:used + nb]
+        used += nb
+        tables[i, :nb] = place
+        slots = [int(place[t // B]) * B + t % B for t in range(L)]
+        impl.write_slots(kp, vp, k, v, slots, B)
+        toks.append((k, v))
+    starts = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int64)
+    q = rng.standard_normal((int(starts[-1]), Hq, D)).astype(np.float16)
+    return kp, vp, tables, starts, q, toks
+
+
+def pin_prefill_torch_causal_sdpa(impl, rng):
+    """Library routine: torch fp64 SDPA with is_causal over the logical tokens (a full
+    prompt, Q = L), GQA by the library."""
+    for (L, Hq, Hkv, D, B) in [(1, 2, 2, 8, 4), (37, 8, 2, 16, 8), (50, 4, 4, 32, 16)]:
+        kp, vp, tables, starts, q, toks = _prefill_case(impl, rng, [L], [L], Hq, Hkv, D, B)
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+        out = impl.attend_prefill_paged(q, kp, vp, tables, [L], starts, B, scale)
+        k, v = toks[0]
+        tq = torch.from_numpy(np.ascontiguousarray(q.astype(np.float64).transpose(1, 0, 2)))[None]
+        tk = torch.from_numpy(np.ascontiguousarray(k.astype(np.float64).transpose(1, 0, 2)))[None]
+        tv = torch.from_numpy(np.ascontiguousarray(v.astype(np.float64).transpose(1, 0, 2)))[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, scale=scale, is_causal=True, enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def pin_prefill_rows_are_decodes(impl, rng):
+    """A query at position p sees exactly tokens 0..p: it equals a decode over the
+    first p + 1 tokens (bitwise), and a continued chunk (Q < L) equals the matching
+    rows of the full prompt's prefill."""
+    lens, Hq, Hkv, D, B = [9, 33, 1], 4, 2, 8, 8
+    kp, vp, tables, starts, q, toks = _prefill_case(impl, rng, lens, lens, Hq, Hkv, D, B)
+    full = impl.attend_prefill_paged(q, kp, vp, tables, lens, starts, B, 0.3)
+    for i, L in enumerate(lens):
+        for j in range(L):
+            row = int(starts[i]) + j
+            want = impl.attend_paged(q[row][None], kp, vp, tables[i:i + 1], [j + 1], B, 0.3)[0]
+            assert np.array_equal(full[row], want), f"request {i} query {j}"
+    # continued prefill of the last 5 tokens of request 1
+    chunk = np.array([0, 5], dtype=np.int64)
+    part = impl.attend_prefill_paged(q[int(starts[1]) + 28:int(starts[1]) + 33], kp, vp,
+                                     tables[1:2], [33], chunk, B, 0.3)
+    assert np.array_equal(part, full[int(starts[1]) + 28:int(starts[1]) + 33])
+
+
 def pin_zero_length(impl, rng):
     q = rng.standard_normal((1, 2, 8))
     kp = np.full((2, 2, 4, 8), np.nan, dtype=np.float16)

@@ -86,6 +86,7 @@ def _impl(**over):
         attend_one=oracle.attention.attend_one,
         attend_paged=oracle.attention.attend_paged,
         attend_contiguous=oracle.attention.attend_contiguous,
+        attend_prefill_paged=oracle.attention.attend_prefill_paged,
         gather_logical=oracle.cache.gather_logical,
         write_slots=oracle.cache.write_slots,
         copy_blocks=oracle.cache.copy_blocks,
@@ -112,7 +113,27 @@ def _contiguous_factory(extra_token=0, swap=True):
     return attend_contiguous
 
 
+def _prefill_factory(see_ahead=0, from_start=False):
+    def attend_prefill_paged(q, k_pool, v_pool, block_tables, context_lens, q_starts, block_size,
+                             scale):
+        q = np.asarray(q)
+        out = np.zeros(q.shape, dtype=np.float64)
+        for i in range(len(context_lens)):
+            L = int(context_lens[i])
+            first, last = int(q_starts[i]), int(q_starts[i + 1])
+            keys = oracle.cache.gather_logical(k_pool, block_tables[i], L, block_size)
+            vals = oracle.cache.gather_logical(v_pool, block_tables[i], L, block_size)
+            for j in range(last - first):
+                pos = j if from_start else L - (last - first) + j
+                n = min(L, pos + 1 + see_ahead)
+                out[first + j] = oracle.attention.attend_one(q[first + j], keys[:n], vals[:n], scale)
+        return out
+    return attend_prefill_paged
+
+
 MUTANTS = {
+    "prefill_sees_next_token": _impl(attend_prefill_paged=_prefill_factory(see_ahead=1)),
+    "prefill_positions_from_zero": _impl(attend_prefill_paged=_prefill_factory(from_start=True)),
     "rows_read_one_past_length": _impl(attend_contiguous=_contiguous_factory(extra_token=1)),
     "rows_axes_not_swapped": _impl(attend_contiguous=_contiguous_factory(swap=False)),
     "head_map_modulo": _impl(attend_one=_attend_factory(head_map=lambda h, Hq, Hkv: h % Hkv)),

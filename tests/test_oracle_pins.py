@@ -13,6 +13,7 @@ IMPL = types.SimpleNamespace(
     attend_one=oracle.attention.attend_one,
     attend_paged=oracle.attention.attend_paged,
     attend_contiguous=oracle.attention.attend_contiguous,
+    attend_prefill_paged=oracle.attention.attend_prefill_paged,
     gather_logical=oracle.cache.gather_logical,
     write_slots=oracle.cache.write_slots,
     copy_blocks=oracle.cache.copy_blocks,
