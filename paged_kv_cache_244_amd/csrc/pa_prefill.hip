@@ -14,18 +14,23 @@
 // 0..that position (Q_i = L_i is a plain prefill; Q_i < L_i continues a cached
 // prefix).
 //
-// One wave per work item (request, block of 16/HT queries, tile of HT query
-// heads of one KV head).  The wave's 16 "columns" are (query, head) pairs,
-// column c = (query j0 + c / HT, head h0 + c % HT).  Per 16-token tile:
+// One workgroup of 8 waves per work item (request, block of 8 * 16/HT queries,
+// tile of HT query heads of one KV head).  The waves load each 32-token K/V
+// tile once, together, into LDS (double-buffered, one barrier per tile), so the
+// L2 traffic per flop is an eighth of one wave working alone (measured best
+// of 4, 8, 16 waves and 16, 32, 64-token tiles on MI355X).  Each wave's 16
+// "columns" are (query, head) pairs, column c = (query wj0 + c / HT, head
+// h0 + c % HT).  Per 16 tokens:
 //
 //   S^T[t][c] = sum_d K[t][d] Q[c][d]     v_mfma_f32_16x16x32_f16, D/32 steps
 //   O[c][d]  += sum_t P[c][t] V[t][d]     v_mfma_f32_16x16x16_f16, D/16 blocks
 //
-// exactly as in the decode kernel for head groups (pa_decode_mfma.hip), whose
-// operand layouts this reuses: K straight from memory in the A layout, V through
-// LDS and ds_read_b64_tr_b16, P from the S^T output layout rounded to fp16.
-// Column c masks every token past its own position.  One pass, no split: a
-// wave walks tokens [0, last position of its block + 1).
+// with the operand layouts of the decode kernel for head groups
+// (pa_decode_mfma.hip): K read from LDS in the A layout, V through
+// ds_read_b64_tr_b16, P from the S^T output layout rounded to fp16.  Column c
+// masks every token past its own position, and a wave skips 16-token steps
+// that lie wholly past its queries.  One pass, no split: the group walks
+// tokens [0, last position of its block + 1).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -69,48 +74,64 @@ constexpr float kSlack = 8.f;
 // loads here are ordinary (cached in L2), not streaming.
 __device__ __forceinline__ uint4 load_shared(const uint4* ptr) { return *ptr; }
 
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 8
+#endif
+#ifndef PKV_PREFILL_TILE
+#define PKV_PREFILL_TILE 32
+#endif
+constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // waves per workgroup, sharing K/V tiles
+
 template <int D, int B, int HT>
-__global__ __launch_bounds__(kWave) void pa_prefill_kernel(PrefillParams p) {
-  constexpr int DEPTH = 2;                   // tiles in flight per wave
-  constexpr int TT = 16;                     // tokens per tile
+__global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(PrefillParams p) {
+  constexpr int NW = kPrefillWaves;
+  constexpr int NT = kWave * NW;             // threads
+  constexpr int KT = PKV_PREFILL_TILE;       // tokens per tile (KT/16 MFMA steps)
+  constexpr int SUB = KT / 16;
   constexpr int QB = 16 / HT;                // queries per wave
   constexpr int KSTEPS = D / 32;
   constexpr int DBLK = D / 16;
-  constexpr int CPR = D / 8;
-  constexpr int VLD = TT * CPR / kWave;
-  constexpr int ROWB = D * 2 + 32;
-  constexpr int BPT = B < TT ? TT / B : 1;
-  constexpr int TPB = B > TT ? B / TT : 1;
-  constexpr int CHUNKS = B * D / 8;
-  static_assert(KSTEPS == VLD && (B < TT ? BPT * B == TT : TPB * TT == B), "tile shape");
+  constexpr int CPR = D / 8;                 // 16-byte chunks per token row
+  constexpr int KROWB = D * 2 + 16;          // LDS bytes per K row (padded against conflicts)
+  constexpr int VROWB = D * 2 + 32;          // LDS bytes per V row (transposed reads)
+  constexpr int LPT = (KT * CPR + NT - 1) / NT;   // chunks of K (and V) a thread moves per tile
+  constexpr int CHUNKS = B * D / 8;          // 16-byte chunks per (block, KV head)
+  constexpr int TPC = kWave * B / KT;        // tiles covered by 64 staged block ids
+  static_assert(LPT * NT == KT * CPR || (LPT == 1 && NT % (KT * CPR) == 0), "tile shape");
+  static_assert(TPC >= 1 && TPC * KT == kWave * B, "chunk shape");
   static_assert(HT == 1 || HT == 2 || HT == 4 || HT == 8 || HT == 16, "head tile");
-  __shared__ __align__(16) unsigned char vlds[DEPTH][TT * ROWB];
+  __shared__ __align__(16) unsigned char klds[2][KT * KROWB];
+  __shared__ __align__(16) unsigned char vlds[2][KT * VROWB];
+  __shared__ __align__(4) unsigned char rowok[2][KT];
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
   const int grp = lane >> 4;
   const int li = lane & 15;                  // column of S^T (scores) / of O (outputs)
   const unsigned k = blockIdx.y + blockIdx.z * gridDim.y;
   if (k >= static_cast<unsigned>(p.num_items)) return;
   const uint32_t item = p.items[k];
   const int seq = static_cast<int>(item >> 16);
-  const int qblk = static_cast<int>(item & 0xFFFFu);
+  const int sblk = static_cast<int>(item & 0xFFFFu);
   if (seq >= p.num_seqs) return;
   const int h0 = blockIdx.x * HT;
   const int kvh = h0 / p.group;
 
   const int32_t* table = p.block_tables + static_cast<int64_t>(seq) * p.max_blocks_per_seq;
-  const int staged_first = lane < p.max_blocks_per_seq ? table[lane] : 0;
   const int q_first = p.q_starts[seq];
   const int nq = p.q_starts[seq + 1] - q_first;
   if (q_first < 0 || nq < 0 || q_first + nq > p.total_q) return;   // guard: bad offsets
   int len = p.context_lens[seq];
   const int cap = p.max_blocks_per_seq * B;
   len = len < 0 ? 0 : (len > cap ? cap : len);
-  const int j0 = qblk * QB;
+  const int j0 = sblk * NW * QB;
   if (j0 >= nq) return;
   const int base_pos = len - nq;             // position of query 0
-  // This lane's column: query cj, head ch; its last visible token is pos.
-  const int cj = j0 + li / HT;
+  // This wave's queries and this lane's column (query cj, head ch, last visible token pos).
+  const int wj0 = j0 + wave * QB;
+  const int wave_pos_max = wj0 < nq ? base_pos + min(wj0 + QB, nq) - 1 : -1;
+  const int cj = wj0 + li / HT;
   const int ch = h0 + li % HT;
   const bool col_ok = cj < nq;
   const int pos = col_ok ? base_pos + cj : -1;
@@ -125,8 +146,7 @@ __global__ __launch_bounds__(kWave) void pa_prefill_kernel(PrefillParams p) {
       qb[kk] = col_ok ? v : half8{};
     }
   }
-  const int j_last = min(j0 + QB, nq) - 1;
-  const int t_end = min(len, base_pos + j_last + 1);   // tokens this wave reads
+  const int t_end = min(len, base_pos + min(j0 + NW * QB, nq));   // tokens the group reads
 
   float4_t o[DBLK];
 #pragma unroll
@@ -135,100 +155,120 @@ __global__ __launch_bounds__(kWave) void pa_prefill_kernel(PrefillParams p) {
   float lsum = 0.f;
 
   if (t_end > 0) {
-    const int nblk = (t_end - 1) / B + 1;
-    const int ntiles = (t_end + TT - 1) / TT;
+    const int ntiles = (t_end + KT - 1) / KT;
     const int64_t block_stride = static_cast<int64_t>(p.num_kv_heads) * CHUNKS;
     const uint4* kbase = p.k_cache + kvh * static_cast<int64_t>(CHUNKS);
     const uint4* vbase = p.v_cache + kvh * static_cast<int64_t>(CHUNKS);
-    uint4 kbuf[DEPTH][KSTEPS], vbuf[DEPTH][VLD];
+    struct TileRegs {
+      uint4 k[LPT], v[LPT];
+      bool ok[LPT];
+    };
+    TileRegs ra, rb;                         // two tiles in flight, in separate registers
+    int staged = 0;                          // block ids of chunk `staged_chunk`, one per lane
+    int staged_chunk = -1;
 
-    for (int c0 = 0; c0 < nblk; c0 += kWave) {
-      const int staged =
-          c0 == 0 ? staged_first
-                  : (lane < min(kWave, nblk - c0) && c0 + lane < p.max_blocks_per_seq
-                         ? table[c0 + lane]
-                         : 0);
-      const int tile0 = c0 * TPB / BPT;
-      const int cn = min(kWave * TPB / BPT, ntiles - tile0);
-
-      auto locate = [&](int jj, int r, int& raw, int& row) {
-        if constexpr (BPT == 1) {
-          raw = __builtin_amdgcn_readlane(staged, jj / TPB);
-          row = (jj % TPB) * TT + r;
-        } else {
-          const int first = __builtin_amdgcn_readlane(staged, jj * BPT);
-          const int second = __builtin_amdgcn_readlane(staged, jj * BPT + 1);
-          raw = r < B ? first : second;
-          row = r % B;
+    // Global -> registers for tile jt: thread tid moves chunks tid, tid + NT, ...
+    auto issue = [&](TileRegs& rg, int jt) __attribute__((always_inline)) {
+      const int chunk = jt / TPC;
+      if (chunk != staged_chunk) {           // wave-uniform: every wave stages the same ids
+        const int b = chunk * kWave + lane;
+        staged = b < p.max_blocks_per_seq ? table[b] : 0;
+        staged_chunk = chunk;
+      }
+#pragma unroll
+      for (int it = 0; it < LPT; ++it) {
+        const int c = (it * NT + tid) % (KT * CPR);   // threads beyond the tile repeat a chunk
+        const int r = c / CPR;
+        const int t = jt * KT + r;
+        const int raw = __builtin_bit_cast(int, shfl(__builtin_bit_cast(float, staged),
+                                                     (t - chunk * kWave * B) / B));
+        const bool ok = t < t_end && static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks);
+        const int64_t off = (ok ? raw : 0) * block_stride + (t % B) * CPR + c % CPR;
+        rg.k[it] = load_shared(kbase + off);
+        rg.v[it] = load_shared(vbase + off);
+        rg.ok[it] = ok;
+      }
+    };
+    // Registers -> LDS buffer; invalid rows become zeros and are flagged.
+    auto store = [&](const TileRegs& rg, int u) __attribute__((always_inline)) {
+#pragma unroll
+      for (int it = 0; it < LPT; ++it) {
+        const int c = it * NT + tid;
+        if (c >= KT * CPR) break;            // (only when the group has more threads than chunks)
+        const int r = c / CPR;
+        const unsigned mask = rg.ok[it] ? 0xFFFFFFFFu : 0u;   // component-wise: no aggregate select
+        const uint4 kv = rg.k[it], vv = rg.v[it];
+        *reinterpret_cast<uint4*>(&klds[u][r * KROWB + (c % CPR) * 16]) =
+            make_uint4(kv.x & mask, kv.y & mask, kv.z & mask, kv.w & mask);
+        *reinterpret_cast<uint4*>(&vlds[u][r * VROWB + (c % CPR) * 16]) =
+            make_uint4(vv.x & mask, vv.y & mask, vv.z & mask, vv.w & mask);
+        if (c % CPR == 0) rowok[u][r] = rg.ok[it] ? 1 : 0;
+      }
+    };
+    // One wave's 16 columns against the KT-token tile in buffer u: every 16-token
+    // score step first, then one max exchange and one softmax update for the tile.
+    auto compute = [&](int u, int jt) __attribute__((always_inline)) {
+      const int tok0 = jt * KT;
+      if (tok0 > wave_pos_max) return;       // every column of this wave is past here
+      float4_t s[SUB];
+#pragma unroll
+      for (int sub = 0; sub < SUB; ++sub) {
+        s[sub] = float4_t{0.f, 0.f, 0.f, 0.f};
+        if (sub > 0 && tok0 + sub * 16 > wave_pos_max) continue;   // step wholly masked
+        const unsigned char* krow = &klds[u][(sub * 16 + li) * KROWB + grp * 16];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(krow + kk * 64);
+          s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, kv), qb[kk],
+                                                         s[sub], 0, 0, 0);
         }
-      };
-      auto safe = [&](int raw) {
-        return static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks) ? raw : 0;
-      };
-
-      auto issue = [&](uint4 (&kr)[KSTEPS], uint4 (&vr)[VLD], int jj) {
-        int raw, row;
-        locate(jj, li, raw, row);
-        const uint4* kt = kbase + safe(raw) * block_stride + row * CPR + grp;
+      }
+      float sr[SUB][4];
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) kr[kk] = load_shared(kt + 4 * kk);
-#pragma unroll
-        for (int it = 0; it < VLD; ++it) {
-          const int c = it * kWave + lane;
-          locate(jj, c / CPR, raw, row);
-          vr[it] = load_shared(vbase + safe(raw) * block_stride + row * CPR + c % CPR);
-        }
-      };
-
-      auto consume = [&](uint4 (&kr)[KSTEPS], uint4 (&vr)[VLD], int jj, unsigned char* vl) {
-        const int tok0 = (tile0 + jj) * TT;
-        auto token_ok = [&](int r) {
-          int raw, row;
-          locate(jj, r, raw, row);
-          return tok0 + r < t_end && static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks);
-        };
-#pragma unroll
-        for (int it = 0; it < VLD; ++it) {
-          const int c = it * kWave + lane;
-          const int r = c / CPR;
-          const uint4 v = token_ok(r) ? vr[it] : make_uint4(0u, 0u, 0u, 0u);
-          *reinterpret_cast<uint4*>(vl + r * ROWB + (c % CPR) * 16) = v;
-        }
-        float4_t s = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, kr[kk]), qb[kk], s, 0,
-                                                    0, 0);
-        float sr[4];
+      for (int sub = 0; sub < SUB; ++sub) {
+        // rows 4*grp .. 4*grp+3 of this step: their validity flags as one word
+        const unsigned ok4 = *reinterpret_cast<const unsigned*>(&rowok[u][sub * 16 + 4 * grp]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = tok0 + 4 * grp + r;
-          sr[r] = token_ok(4 * grp + r) && t <= pos ? s[r] * p.scale_log2 : -INFINITY;
+          const int t = tok0 + sub * 16 + 4 * grp + r;
+          const bool vis = ((ok4 >> (8 * r)) & 0xFFu) != 0 && t <= pos;
+          sr[sub][r] = vis ? s[sub][r] * p.scale_log2 : -INFINITY;
         }
-        float mt = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-        mt = fmaxf(mt, shfl_xor(mt, 16));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
-        const bool moved = mt > m + kSlack;
-        const float m_new = moved ? mt : m;
-        float pr[4];
+      }
+      float mt = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sr[r] - m_new);
-        if (__builtin_amdgcn_ballot_w64(moved)) {
-          const float alpha = fast_exp2(m - m_new);
-          lsum *= alpha;
+      for (int sub = 0; sub < SUB; ++sub)
+        mt = fmaxf(mt, fmaxf(fmaxf(sr[sub][0], sr[sub][1]), fmaxf(sr[sub][2], sr[sub][3])));
+      mt = fmaxf(mt, shfl_xor(mt, 16));
+      mt = fmaxf(mt, shfl_xor(mt, 32));
+      const bool moved = mt > m + kSlack;
+      const float m_new = moved ? mt : m;
+      float pr[SUB][4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float ar = shfl(alpha, 4 * grp + r);
+      for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
-            for (int db = 0; db < DBLK; ++db) o[db][r] *= ar;
-          }
+        for (int r = 0; r < 4; ++r) pr[sub][r] = fast_exp2(sr[sub][r] - m_new);
+      if (__builtin_amdgcn_ballot_w64(moved)) {
+        const float alpha = fast_exp2(m - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = shfl(alpha, 4 * grp + r);
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db) o[db][r] *= ar;
         }
-        lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        m = m_new;
-        const half4 pa = half4{static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1]),
-                               static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])};
-        __syncthreads();
-        const unsigned char* src = vl + (4 * grp + (li >> 2)) * ROWB + 8 * (li & 3);
+      }
+#pragma unroll
+      for (int sub = 0; sub < SUB; ++sub)
+        lsum += (pr[sub][0] + pr[sub][1]) + (pr[sub][2] + pr[sub][3]);
+      m = m_new;
+#pragma unroll
+      for (int sub = 0; sub < SUB; ++sub) {
+        if (sub > 0 && tok0 + sub * 16 > wave_pos_max) continue;
+        const half4 pa = half4{static_cast<_Float16>(pr[sub][0]), static_cast<_Float16>(pr[sub][1]),
+                               static_cast<_Float16>(pr[sub][2]), static_cast<_Float16>(pr[sub][3])};
+        const unsigned char* src =
+            &vlds[u][(sub * 16 + 4 * grp + (li >> 2)) * VROWB + 8 * (li & 3)];
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
           typedef __attribute__((address_space(3))) short4_t lds_short4;
@@ -237,28 +277,24 @@ __global__ __launch_bounds__(kWave) void pa_prefill_kernel(PrefillParams p) {
           o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4, raw), o[db],
                                                         0, 0, 0);
         }
-      };
+      }
+    };
 
-#pragma unroll
-      for (int u = 0; u < DEPTH; ++u) issue(kbuf[u], vbuf[u], u < cn ? u : cn - 1);
-      int j = 0;
-      for (; j + 2 * DEPTH - 1 < cn; j += DEPTH) {
-#pragma unroll
-        for (int u = 0; u < DEPTH; ++u) {
-          consume(kbuf[u], vbuf[u], j + u, vlds[u]);
-          issue(kbuf[u], vbuf[u], j + u + DEPTH);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < DEPTH; ++u) {
-        if (j + u < cn) consume(kbuf[u], vbuf[u], j + u, vlds[u]);
-        if (j + u + DEPTH < cn) issue(kbuf[u], vbuf[u], j + u + DEPTH);
-      }
-#pragma unroll
-      for (int u = 0; u < DEPTH; ++u)
-        if (j + u + DEPTH < cn) consume(kbuf[u], vbuf[u], j + u + DEPTH, vlds[u]);
+    // Tile jt is in register set ra (even jt) or rb (odd jt) and LDS buffer jt % 2.
+    auto step = [&](TileRegs& rg, int u, int jt) __attribute__((always_inline)) {
+      store(rg, u);
+      if (jt + 2 < ntiles) issue(rg, jt + 2);
+      __syncthreads();                       // tile jt visible; the other buffer free again
+      compute(u, jt);
+    };
+    issue(ra, 0);
+    if (ntiles > 1) issue(rb, 1);
+    int jt = 0;
+    for (; jt + 1 < ntiles; jt += 2) {
+      step(ra, 0, jt);
+      step(rb, 1, jt + 1);
     }
+    if (jt < ntiles) step(ra, 0, jt);
   }
 
   // Denominator of column li, then each lane's output rows: columns 4*grp + r.
@@ -270,7 +306,7 @@ __global__ __launch_bounds__(kWave) void pa_prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int c = 4 * grp + r;
-    const int qj = j0 + c / HT;
+    const int qj = wj0 + c / HT;
     if (qj >= nq) continue;
     const float inv = lr[r] > 0.f ? 1.f / lr[r] : 0.f;   // a query with no token: zeros
     float* dst = p.out + (static_cast<int64_t>(q_first + qj) * p.num_q_heads + h0 + c % HT) * D;
@@ -324,7 +360,7 @@ using namespace pkv_decode;
 extern "C" int32_t pa_prefill_queries_per_item(int32_t num_q_heads, int32_t num_kv_heads) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
   const int ht = head_tile_for(num_q_heads / num_kv_heads);
-  return ht > 0 ? 16 / ht : 0;
+  return ht > 0 ? kPrefillWaves * 16 / ht : 0;
 }
 
 extern "C" int pa_prefill_plan(const int32_t* q_lens, const int32_t* context_lens,
@@ -417,7 +453,8 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_starts, in
   const int ny = num_work_items < kMaxGridY ? num_work_items : kMaxGridY;
   const dim3 grid(static_cast<unsigned>(num_q_heads / ht), static_cast<unsigned>(ny),
                   static_cast<unsigned>((num_work_items + ny - 1) / ny));
-  hipLaunchKernelGGL(fn, grid, dim3(kWave), dyn, static_cast<hipStream_t>(stream), prm);
+  hipLaunchKernelGGL(fn, grid, dim3(kWave * kPrefillWaves), dyn, static_cast<hipStream_t>(stream),
+                     prm);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_prefill launch: %s", hipGetErrorString(e));
   return PKV_OK;
