@@ -56,7 +56,9 @@ enum {
   PKV_ERR_OUT_OF_BLOCKS = -3, /* allocator: not enough free blocks; state unchanged */
   PKV_ERR_BAD_SEQ = -4,       /* allocator: unknown or freed sequence id           */
   PKV_ERR_HIP = -5,           /* a HIP launch or runtime call failed               */
-  PKV_ERR_WORKSPACE = -6      /* pa_decode workspace missing or too small          */
+  PKV_ERR_WORKSPACE = -6,     /* pa_decode workspace missing or too small          */
+  PKV_ERR_SWAPPED = -7        /* allocator: the sequence is in the host tier (or, for
+                                 a swap-in, is not); state unchanged               */
 };
 
 /* Element types of the query tensor. */
@@ -360,7 +362,13 @@ typedef struct {
   int64_t live_tokens;    /* sum of live sequences' lengths              */
   int64_t sum_refcounts;  /* sum of all reference counts                 */
   int32_t pending_blocks; /* freed with kv_seq_free_deferred, not yet retired */
-  int32_t reserved;
+  int32_t host_blocks;         /* size of the host tier (0 without one)        */
+  int32_t host_free_blocks;
+  int32_t host_used_blocks;    /* referenced by at least one swapped sequence  */
+  int32_t host_pending_blocks; /* parked host blocks, not yet retired          */
+  int32_t swapped_seqs;        /* live sequences now in the host tier          */
+  int64_t swapped_out_blocks;  /* blocks copied device -> host so far           */
+  int64_t swapped_in_blocks;   /* blocks copied host -> device so far           */
 } kv_stats;
 
 /* initial_order: host int32 [num_blocks], a permutation of 0..num_blocks-1, or
@@ -395,7 +403,51 @@ int kv_seq_free(kv_allocator* a, int32_t seq);
  * epoch may be retired.  *released_out (may be NULL) = blocks returned.
  */
 int kv_seq_free_deferred(kv_allocator* a, int32_t seq, int64_t epoch);
+/* Frees parked blocks of both tiers; *released_out counts both. */
 int kv_allocator_retire(kv_allocator* a, int64_t done, int32_t* released_out);
+
+/*
+ * The host tier.  [C] "Eviction and reuse can move costs elsewhere": evicted
+ * state can move to another memory tier instead of being recomputed, paying
+ * in transfer time and bandwidth.  Here the tier is a second pool of blocks,
+ * num_host_blocks of them, with the device pool's block geometry, in memory
+ * the caller allocates (pinned host memory, for kv_swap_blocks).  Its free list
+ * follows the device pool's rules (initial order, last in first out).
+ * PKV_ERR_INVALID_ARG if the tier exists already or the order is not a
+ * permutation.
+ */
+int kv_allocator_add_host_tier(kv_allocator* a, int32_t num_host_blocks,
+                               const int32_t* initial_order);
+/*
+ * kv_swap_out / kv_swap_in — move a set of live sequences' blocks to the host
+ * tier / back to the device pool.  Each distinct block the set references
+ * (in the order of seqs, then logical order) gets one fresh block of the other
+ * tier, so blocks shared inside the set stay shared and are copied once.  The
+ * new block's count is the set's references to the old one.  The old block
+ * loses exactly those references (a holder outside the set keeps it).  A block
+ * left with no references goes to its free list, or, when `deferred` is
+ * non-zero, is parked with `epoch` as in kv_seq_free_deferred: the copy that
+ * reads it may still be queued.
+ *   seqs        : host int32 [num_seqs], distinct (PKV_ERR_INVALID_ARG if not);
+ *                 each resident for a swap-out and swapped out for a swap-in
+ *                 (PKV_ERR_SWAPPED if not).
+ *   pairs_out   : host int32 [pairs_capacity][2] = (old block, new block), in
+ *                 the order above, for kv_swap_blocks.  If the capacity is too
+ *                 small: PKV_ERR_INVALID_ARG and *num_pairs_out = pairs needed.
+ *                 The sum of the sequences' block counts always suffices.
+ * Too few free blocks in the target tier: PKV_ERR_OUT_OF_BLOCKS.  On any error
+ * the allocator is unchanged.  A swapped-out sequence keeps its length and can
+ * be freed (its host blocks are released), but append, fork, export and
+ * kv_decode_step_host refuse it with PKV_ERR_SWAPPED until it is swapped in.
+ */
+int kv_swap_out(kv_allocator* a, const int32_t* seqs, int32_t num_seqs, int32_t deferred,
+                int64_t epoch, int32_t* pairs_out, int32_t pairs_capacity,
+                int32_t* num_pairs_out);
+int kv_swap_in(kv_allocator* a, const int32_t* seqs, int32_t num_seqs, int32_t deferred,
+               int64_t epoch, int32_t* pairs_out, int32_t pairs_capacity,
+               int32_t* num_pairs_out);
+/* *swapped_out = 1 if the sequence's blocks are in the host tier, else 0. */
+int kv_seq_is_swapped(const kv_allocator* a, int32_t seq, int32_t* swapped_out);
 int kv_seq_len(const kv_allocator* a, int32_t seq, int32_t* len_out);
 /* Lengths of n sequences in one call: host int32 lens_out [n]. */
 int kv_seq_lens(const kv_allocator* a, const int32_t* seqs, int32_t n, int32_t* lens_out);

@@ -17,15 +17,19 @@ Sources (the three web pages on PagedAttention, cited by title and section):
   forgets: pages enable sharing, not just packing".
 * "The KV cache is a systems problem" (rsw.lol notes) — sections "Calculate
   bytes per token before choosing a batch", "Use blocks to bound waste, then
-  price the boundary", "Shared prefixes need ownership rules".
+  price the boundary", "Shared prefixes need ownership rules", "Eviction and
+  reuse can move costs elsewhere".
 
 Modules:
 
 * ``closed_forms`` — bytes per token, blocks per sequence, tail waste.
-* ``cache``        — slot-mapped K/V write, block copy, logical gather.
-* ``attention``    — single-query decode attention over a block table, fp64.
+* ``cache``        — slot-mapped K/V write, block copy (within a pool and
+  between the device and host pools), logical gather.
+* ``attention``    — decode and causal prefill attention over a block table,
+  and over contiguous rows, fp64.
 * ``alloc_model``  — reference model of the block allocator (refcounts,
-  demand allocation, fork, copy-on-write, free).
+  demand allocation, fork, copy-on-write, free, deferred free, swap to and
+  from a host tier).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against values
 printed on the pages, closed forms, library routines or brute force; none is

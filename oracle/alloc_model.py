@@ -21,6 +21,10 @@ Plain Python lists and dicts.  The rules, each from the pages:
 * A block may be held back from reuse until device work still queued against
   it has finished (rsw.lol, section "Shared prefixes need ownership rules":
   storage must not be reassigned under a delayed device operation).
+* Eviction may move a request's state to another memory tier instead of
+  dropping it, at the price of the transfer (rsw.lol, section "Eviction and
+  reuse can move costs elsewhere").  Here the other tier is a pool of blocks in
+  host memory with the same block geometry; a request's state is its blocks.
 
 Readings where the pages are silent:
 
@@ -36,6 +40,17 @@ Readings where the pages are silent:
 * Deferred free: references drop at once, but a block reaching zero is parked
   with the caller's epoch; ``retire(done)`` returns every parked block with
   epoch <= done to the free list in the order they were freed.
+* Swap moves a set of requests between the tiers together.  Each distinct
+  block they reference (taken in request order, then logical order) is copied
+  once into a fresh block of the other tier, so blocks shared inside the set
+  stay shared; the new block's count is the number of the set's references,
+  and the old block loses exactly those references (a block also held outside
+  the set stays where it is for its other holders).  An old block left with no
+  references is freed, or parked with an epoch as in a deferred free, since the
+  queued copy still reads it.  All or nothing: too few free blocks in the
+  target tier changes nothing.  A swapped-out request keeps its length and can
+  be freed, but cannot grow, fork or be attended to until swapped back in.
+  The host tier has its own free list with the same ordering rules.
 """
 
 import copy
@@ -47,6 +62,10 @@ class OutOfBlocks(Exception):
 
 class BadSequence(Exception):
     """Unknown or already freed request id."""
+
+
+class Swapped(Exception):
+    """The request's blocks are in the host tier (or, for swap-in, are not)."""
 
 
 class AllocatorModel:
@@ -64,11 +83,37 @@ class AllocatorModel:
         self.tables = {}                        # seq id -> list of physical blocks
         self.lengths = {}                       # seq id -> tokens stored
         self.next_id = 0
+        # host tier (empty until add_host_tier)
+        self.host_blocks = 0
+        self.host_free = []
+        self.host_refcount = []
+        self.host_parked = []
+        self.swapped = set()                    # ids whose tables name host blocks
+        self.swapped_out_blocks = 0             # blocks copied device -> host, ever
+        self.swapped_in_blocks = 0              # blocks copied host -> device, ever
+
+    def add_host_tier(self, num_host_blocks, initial_order=None):
+        if self.host_blocks:
+            raise ValueError("the host tier exists already")
+        if num_host_blocks <= 0:
+            raise ValueError("num_host_blocks must be positive")
+        order = (list(range(num_host_blocks)) if initial_order is None
+                 else [int(b) for b in initial_order])
+        if sorted(order) != list(range(num_host_blocks)):
+            raise ValueError("initial_order must be a permutation of 0..num_host_blocks-1")
+        self.host_blocks = num_host_blocks
+        self.host_free = list(reversed(order))
+        self.host_refcount = [0] * num_host_blocks
 
     # -- requests ---------------------------------------------------------
     def _check(self, seq):
         if seq not in self.tables:
             raise BadSequence(seq)
+
+    def _check_resident(self, seq):
+        self._check(seq)
+        if seq in self.swapped:
+            raise Swapped(seq)
 
     def create(self):
         seq = self.next_id
@@ -78,7 +123,7 @@ class AllocatorModel:
         return seq
 
     def fork(self, parent):
-        self._check(parent)
+        self._check_resident(parent)
         child = self.create()
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
@@ -93,7 +138,7 @@ class AllocatorModel:
 
     def append(self, seq, n):
         """Reserve slots for ``n`` more tokens.  Returns ``(slots, cow_pairs)``."""
-        self._check(seq)
+        self._check_resident(seq)
         if n < 0:
             raise ValueError("n must be >= 0")
         if n == 0:
@@ -130,34 +175,125 @@ class AllocatorModel:
                 s, p = self.append(seq, 1)
                 slots.extend(s)
                 pairs.extend(p)
-        except (OutOfBlocks, BadSequence):
+        except (OutOfBlocks, BadSequence, Swapped):
             self.free, self.refcount, self.tables, self.lengths = saved
             raise
         return slots, pairs
 
+    def _tier(self, seq):
+        """(reference counts, free list, parked list) of the tier holding ``seq``."""
+        if seq in self.swapped:
+            return self.host_refcount, self.host_free, self.host_parked
+        return self.refcount, self.free, self.parked
+
     def free_seq(self, seq):
         self._check(seq)
+        refcount, free, _ = self._tier(seq)
         for b in self.tables[seq]:
-            self.refcount[b] -= 1
-            if self.refcount[b] == 0:
-                self.free.append(b)
+            refcount[b] -= 1
+            if refcount[b] == 0:
+                free.append(b)
         del self.tables[seq]
         del self.lengths[seq]
+        self.swapped.discard(seq)
 
     def free_seq_deferred(self, seq, epoch):
         self._check(seq)
+        refcount, _, parked = self._tier(seq)
         for b in self.tables[seq]:
-            self.refcount[b] -= 1
-            if self.refcount[b] == 0:
-                self.parked.append((b, int(epoch)))
+            refcount[b] -= 1
+            if refcount[b] == 0:
+                parked.append((b, int(epoch)))
         del self.tables[seq]
         del self.lengths[seq]
+        self.swapped.discard(seq)
 
     def retire(self, done):
+        """Free every parked block (both tiers) with epoch <= done; how many."""
         released = [b for b, e in self.parked if e <= done]
         self.parked = [(b, e) for b, e in self.parked if e > done]
         self.free.extend(released)
-        return len(released)
+        host_released = [b for b, e in self.host_parked if e <= done]
+        self.host_parked = [(b, e) for b, e in self.host_parked if e > done]
+        self.host_free.extend(host_released)
+        return len(released) + len(host_released)
+
+    # -- the host tier ------------------------------------------------------
+    def _distinct_blocks(self, seqs):
+        """The blocks the set references, first appearance first, with the set's
+        reference count of each."""
+        order, refs = [], {}
+        for seq in seqs:
+            for b in self.tables[seq]:
+                if b not in refs:
+                    order.append(b)
+                    refs[b] = 0
+                refs[b] += 1
+        return order, refs
+
+    def _check_set(self, seqs, want_swapped):
+        if len(set(seqs)) != len(seqs):
+            raise ValueError("a request is listed twice")
+        for seq in seqs:
+            self._check(seq)
+            if (seq in self.swapped) != want_swapped:
+                raise Swapped(seq)
+
+    def swap_out(self, seqs, deferred=False, epoch=0):
+        """Move the requests' blocks to the host tier.  Returns the copies to make,
+        ``[(device block, host block), ...]``."""
+        seqs = [int(s) for s in seqs]
+        self._check_set(seqs, want_swapped=False)
+        order, refs = self._distinct_blocks(seqs)
+        if len(order) > len(self.host_free):
+            raise OutOfBlocks(len(order))
+        new_of, pairs = {}, []
+        for b in order:
+            h = self.host_free.pop()
+            self.host_refcount[h] = refs[b]
+            new_of[b] = h
+            pairs.append((b, h))
+            self.refcount[b] -= refs[b]
+            if self.refcount[b] == 0:
+                if deferred:
+                    self.parked.append((b, int(epoch)))
+                else:
+                    self.free.append(b)
+        for seq in seqs:
+            self.tables[seq] = [new_of[b] for b in self.tables[seq]]
+            self.swapped.add(seq)
+        self.swapped_out_blocks += len(pairs)
+        return pairs
+
+    def swap_in(self, seqs, deferred=False, epoch=0):
+        """Move swapped-out requests' blocks back to the device pool.  Returns the
+        copies to make, ``[(host block, device block), ...]``."""
+        seqs = [int(s) for s in seqs]
+        self._check_set(seqs, want_swapped=True)
+        order, refs = self._distinct_blocks(seqs)
+        if len(order) > len(self.free):
+            raise OutOfBlocks(len(order))
+        new_of, pairs = {}, []
+        for h in order:
+            b = self.free.pop()
+            self.refcount[b] = refs[h]
+            new_of[h] = b
+            pairs.append((h, b))
+            self.host_refcount[h] -= refs[h]
+            if self.host_refcount[h] == 0:
+                if deferred:
+                    self.host_parked.append((h, int(epoch)))
+                else:
+                    self.host_free.append(h)
+        for seq in seqs:
+            self.tables[seq] = [new_of[h] for h in self.tables[seq]]
+            self.swapped.discard(seq)
+        self.swapped_in_blocks += len(pairs)
+        return pairs
+
+    def is_swapped(self, seq):
+        self._check(seq)
+        return seq in self.swapped
 
     # -- views ------------------------------------------------------------
     def length(self, seq):
@@ -172,7 +308,7 @@ class AllocatorModel:
         """Block tables ``[n][max_blocks]`` padded with ``pad_value``, and lengths."""
         rows, lens = [], []
         for seq in seqs:
-            self._check(seq)
+            self._check_resident(seq)
             t = self.tables[seq]
             if len(t) > max_blocks:
                 raise ValueError("sequence holds more blocks than max_blocks")
@@ -189,4 +325,11 @@ class AllocatorModel:
             "live_tokens": sum(self.lengths.values()),
             "sum_refcounts": sum(self.refcount),
             "pending_blocks": len(self.parked),
+            "host_blocks": self.host_blocks,
+            "host_free_blocks": len(self.host_free),
+            "host_used_blocks": sum(1 for r in self.host_refcount if r > 0),
+            "host_pending_blocks": len(self.host_parked),
+            "swapped_seqs": len(self.swapped),
+            "swapped_out_blocks": self.swapped_out_blocks,
+            "swapped_in_blocks": self.swapped_in_blocks,
         }

@@ -14,6 +14,12 @@ block ``b`` holds, for every KV head, ``block_size`` token slots.
   sharing, not just packing"; "800 kilobytes per token", "The old answer,
   imported honestly").
 
+* Swap copies whole blocks between two pools of the same geometry (the
+  device pool and a pool in host memory): block ``src`` of the source becomes
+  block ``dst`` of the destination, for K and V and every layer (rsw.lol,
+  section "Eviction and reuse can move costs elsewhere": evicted state moved
+  to another memory tier).
+
 Every function copies bytes; nothing is rounded or converted.
 """
 
@@ -50,6 +56,19 @@ def copy_blocks(layer_pools, block_pairs):
             k_pool[dst] = k_pool[src]
             v_pool[dst] = v_pool[src]
     return layer_pools
+
+
+def copy_blocks_between(src_layers, dst_layers, block_pairs):
+    """For each (src, dst) pair and each layer: dst_pool[dst] = src_pool[src].
+
+    ``src_layers`` and ``dst_layers`` are lists of ``(k_pool, v_pool)``, one per
+    layer, of the same block geometry.  The whole block is copied.
+    """
+    for src, dst in np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2):
+        for (sk, sv), (dk, dv) in zip(src_layers, dst_layers):
+            dk[dst] = sk[src]
+            dv[dst] = sv[src]
+    return dst_layers
 
 
 def gather_logical(pool, table_row, num_tokens, block_size):

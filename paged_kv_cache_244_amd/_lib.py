@@ -24,6 +24,7 @@ PKV_ERR_OUT_OF_BLOCKS = -3
 PKV_ERR_BAD_SEQ = -4
 PKV_ERR_HIP = -5
 PKV_ERR_WORKSPACE = -6
+PKV_ERR_SWAPPED = -7
 PKV_F32 = 0
 PKV_F16 = 1
 PKV_POLICY_DEFAULT = 0
@@ -36,6 +37,7 @@ _ERR_NAMES = {
     PKV_ERR_BAD_SEQ: "BAD_SEQ",
     PKV_ERR_HIP: "HIP",
     PKV_ERR_WORKSPACE: "WORKSPACE",
+    PKV_ERR_SWAPPED: "SWAPPED",
 }
 
 
@@ -50,6 +52,10 @@ class OutOfBlocks(PagedKVError):
 
 
 class BadSequence(PagedKVError):
+    pass
+
+
+class Swapped(PagedKVError):
     pass
 
 
@@ -69,7 +75,10 @@ class StepLayout(ctypes.Structure):
 class KVStats(ctypes.Structure):
     _fields_ = [("num_blocks", c_int32), ("free_blocks", c_int32), ("used_blocks", c_int32),
                 ("shared_blocks", c_int32), ("live_tokens", c_int64), ("sum_refcounts", c_int64),
-                ("pending_blocks", c_int32), ("reserved", c_int32)]
+                ("pending_blocks", c_int32), ("host_blocks", c_int32),
+                ("host_free_blocks", c_int32), ("host_used_blocks", c_int32),
+                ("host_pending_blocks", c_int32), ("swapped_seqs", c_int32),
+                ("swapped_out_blocks", c_int64), ("swapped_in_blocks", c_int64)]
 
 
 _SIGNATURES = {
@@ -107,6 +116,12 @@ _SIGNATURES = {
     "kv_seq_free": (c_int32, [c_void_p, c_int32]),
     "kv_seq_free_deferred": (c_int32, [c_void_p, c_int32, c_int64]),
     "kv_allocator_retire": (c_int32, [c_void_p, c_int64, POINTER(c_int32)]),
+    "kv_allocator_add_host_tier": (c_int32, [c_void_p, c_int32, c_void_p]),
+    "kv_swap_out": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int64, c_void_p, c_int32,
+                              POINTER(c_int32)]),
+    "kv_swap_in": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int64, c_void_p, c_int32,
+                             POINTER(c_int32)]),
+    "kv_seq_is_swapped": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
     "kv_seq_len": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
     "kv_seq_lens": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p]),
     "kv_export_block_tables": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
@@ -143,7 +158,8 @@ def exported_symbols():
 def _check(rc):
     if rc != PKV_OK:
         msg = lib().pkv_last_error().decode(errors="replace")
-        cls = {PKV_ERR_OUT_OF_BLOCKS: OutOfBlocks, PKV_ERR_BAD_SEQ: BadSequence}.get(rc, PagedKVError)
+        cls = {PKV_ERR_OUT_OF_BLOCKS: OutOfBlocks, PKV_ERR_BAD_SEQ: BadSequence,
+               PKV_ERR_SWAPPED: Swapped}.get(rc, PagedKVError)
         raise cls(rc, msg)
 
 
@@ -389,6 +405,7 @@ class BlockAllocator:
                                          byref(self._h)))
         self.num_blocks = num_blocks
         self.block_size = block_size
+        self._swap_pairs = np.empty((256, 2), dtype=np.int32)
 
     def close(self):
         if self._h:
@@ -443,6 +460,43 @@ class BlockAllocator:
         _check(lib().kv_allocator_retire(self._h, int(done), byref(out)))
         return out.value
 
+    def add_host_tier(self, num_host_blocks, initial_order=None):
+        order = None
+        if initial_order is not None:
+            order = np.ascontiguousarray(initial_order, dtype=np.int32)
+            if order.shape != (num_host_blocks,):
+                raise ValueError("initial_order must have num_host_blocks entries")
+        _check(lib().kv_allocator_add_host_tier(self._h, int(num_host_blocks),
+                                                None if order is None else order.ctypes.data))
+        self.num_host_blocks = int(num_host_blocks)
+
+    def _swap(self, fn, seqs, deferred, epoch):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = int(seqs.shape[0])
+        pairs = self._swap_pairs
+        got = c_int32()
+        while True:
+            rc = fn(self._h, seqs.ctypes.data, n, int(bool(deferred)), int(epoch),
+                    pairs.ctypes.data, int(pairs.shape[0]), byref(got))
+            if rc == PKV_ERR_INVALID_ARG and got.value > pairs.shape[0]:
+                pairs = self._swap_pairs = np.empty((got.value, 2), dtype=np.int32)
+                continue
+            _check(rc)
+            return pairs[: got.value].copy()
+
+    def swap_out(self, seqs, deferred=False, epoch=0):
+        """Move the sequences' blocks to the host tier; int32 [P, 2] (device, host) pairs."""
+        return self._swap(lib().kv_swap_out, seqs, deferred, epoch)
+
+    def swap_in(self, seqs, deferred=False, epoch=0):
+        """Move swapped-out sequences back; int32 [P, 2] (host, device) pairs."""
+        return self._swap(lib().kv_swap_in, seqs, deferred, epoch)
+
+    def is_swapped(self, seq: int) -> bool:
+        out = c_int32()
+        _check(lib().kv_seq_is_swapped(self._h, seq, byref(out)))
+        return bool(out.value)
+
     def length(self, seq: int) -> int:
         out = c_int32()
         _check(lib().kv_seq_len(self._h, seq, byref(out)))
@@ -491,4 +545,4 @@ class BlockAllocator:
     def stats(self) -> dict:
         st = KVStats()
         _check(lib().kv_allocator_stats(self._h, byref(st)))
-        return {name: getattr(st, name) for name, _ in KVStats._fields_ if name != "reserved"}
+        return {name: getattr(st, name) for name, _ in KVStats._fields_}

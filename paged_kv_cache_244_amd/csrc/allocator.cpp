@@ -9,7 +9,9 @@
 // filled block takes a fresh block that receives a copy; freed blocks at zero
 // references return to the pool).  "The KV cache is a systems problem"
 // (rsw.lol), section "Shared prefixes need ownership rules": other readers keep
-// their view.
+// their view.  Same notes, section "Eviction and reuse can move costs
+// elsewhere": an evicted request's state may move to another memory tier; here
+// a pool of blocks in host memory (the host tier) with its own free list.
 //
 // Plain host C++, no HIP.  Free list: a stack whose first pops follow the
 // caller's initial order; freed blocks are pushed and so handed out next.
@@ -25,20 +27,30 @@
 struct kv_allocator {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::vector<int32_t> free_stack;   // back() is handed out next
-  std::vector<int32_t> refcount;     // per physical block
-  struct Seq {
-    bool live = false;
-    int64_t length = 0;
-    int32_t pending = 0;             // scratch of kv_decode_step_host, 0 between calls
-    std::vector<int32_t> blocks;     // logical -> physical
-  };
-  std::vector<Seq> seqs;             // indexed by id; ids never reused
   struct Parked {
     int32_t block;
     int64_t epoch;
   };
-  std::vector<Parked> parked;        // freed with an epoch tag, in free order
+  // One tier of blocks: the device pool, or the host pool swapped requests use.
+  struct Tier {
+    std::vector<int32_t> free_stack;   // back() is handed out next
+    std::vector<int32_t> refcount;     // per physical block
+    std::vector<Parked> parked;        // freed with an epoch tag, in free order
+    std::vector<int32_t> set_refs;     // scratch of a swap, all zero between calls
+  };
+  Tier dev;
+  Tier host;                           // empty until kv_allocator_add_host_tier
+  struct Seq {
+    bool live = false;
+    bool swapped = false;              // blocks name host-tier blocks
+    int64_t length = 0;
+    int32_t pending = 0;               // scratch of kv_decode_step_host, 0 between calls
+    std::vector<int32_t> blocks;       // logical -> physical
+  };
+  std::vector<Seq> seqs;               // indexed by id; ids never reused
+  int32_t swapped_seqs = 0;
+  int64_t swapped_out_blocks = 0;      // copies device -> host, ever
+  int64_t swapped_in_blocks = 0;       // copies host -> device, ever
 };
 
 namespace {
@@ -54,6 +66,31 @@ int check_seq(const kv_allocator* a, int32_t seq) {
   return PKV_OK;
 }
 
+// Live and with its blocks on the device (not swapped out).
+int check_resident(const kv_allocator* a, int32_t seq) {
+  if (int rc = check_seq(a, seq)) return rc;
+  if (a->seqs[seq].swapped)
+    return fail(PKV_ERR_SWAPPED, "sequence %d is swapped out to the host tier", seq);
+  return PKV_OK;
+}
+
+// Fills a tier's free stack so that the first pop is initial_order[0].
+int init_tier(kv_allocator::Tier& t, int32_t n, const int32_t* initial_order) {
+  t.refcount.assign(n, 0);
+  t.set_refs.assign(n, 0);
+  t.free_stack.resize(n);
+  t.parked.clear();
+  std::vector<char> seen(n, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t b = initial_order ? initial_order[i] : i;
+    if (b < 0 || b >= n || seen[b])
+      return fail(PKV_ERR_INVALID_ARG, "initial_order is not a permutation of 0..%d", n - 1);
+    seen[b] = 1;
+    t.free_stack[n - 1 - i] = b;   // initial_order[0] on top
+  }
+  return PKV_OK;
+}
+
 // What one append did, enough to undo it exactly (for all-or-nothing batches).
 struct AppendRecord {
   int32_t seq;
@@ -64,16 +101,16 @@ struct AppendRecord {
 };
 
 int32_t pop_block(kv_allocator* a) {
-  int32_t b = a->free_stack.back();
-  a->free_stack.pop_back();
-  a->refcount[b] = 1;
+  int32_t b = a->dev.free_stack.back();
+  a->dev.free_stack.pop_back();
+  a->dev.refcount[b] = 1;
   return b;
 }
 
 // Blocks an append of n tokens to `s` needs, copy-on-write included.
 int64_t blocks_needed(const kv_allocator* a, const kv_allocator::Seq& s, int64_t n, bool* cow) {
   const int32_t B = a->block_size;
-  *cow = n > 0 && (s.length % B) != 0 && a->refcount[s.blocks.back()] > 1;
+  *cow = n > 0 && (s.length % B) != 0 && a->dev.refcount[s.blocks.back()] > 1;
   int64_t fresh = blocks_for(s.length + n, B) - static_cast<int64_t>(s.blocks.size());
   return fresh + (*cow ? 1 : 0);
 }
@@ -88,7 +125,7 @@ AppendRecord do_append(kv_allocator* a, int32_t seq, int64_t n, int64_t* slots_o
   if (cow) {
     int32_t src = s.blocks.back();
     int32_t dst = pop_block(a);
-    a->refcount[src] -= 1;
+    a->dev.refcount[src] -= 1;
     s.blocks.back() = dst;
     rec.cow_src = src;
     rec.cow_dst = dst;
@@ -110,13 +147,13 @@ void undo_append(kv_allocator* a, const AppendRecord& rec) {
   for (int32_t i = 0; i < rec.new_blocks; ++i) {
     int32_t b = s.blocks.back();
     s.blocks.pop_back();
-    a->refcount[b] = 0;
-    a->free_stack.push_back(b);
+    a->dev.refcount[b] = 0;
+    a->dev.free_stack.push_back(b);
   }
   if (rec.cow_src >= 0) {
-    a->refcount[rec.cow_dst] = 0;
-    a->free_stack.push_back(rec.cow_dst);
-    a->refcount[rec.cow_src] += 1;
+    a->dev.refcount[rec.cow_dst] = 0;
+    a->dev.free_stack.push_back(rec.cow_dst);
+    a->dev.refcount[rec.cow_src] += 1;
     s.blocks.back() = rec.cow_src;
   }
   s.length = rec.old_length;
@@ -137,20 +174,24 @@ int kv_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* i
   if (!a) return fail(PKV_ERR_INVALID_ARG, "out of host memory");
   a->num_blocks = num_blocks;
   a->block_size = block_size;
-  a->refcount.assign(num_blocks, 0);
-  a->free_stack.resize(num_blocks);
-  std::vector<char> seen(num_blocks, 0);
-  for (int32_t i = 0; i < num_blocks; ++i) {
-    int32_t b = initial_order ? initial_order[i] : i;
-    if (b < 0 || b >= num_blocks || seen[b]) {
-      delete a;
-      return fail(PKV_ERR_INVALID_ARG, "initial_order is not a permutation of 0..%d",
-                  num_blocks - 1);
-    }
-    seen[b] = 1;
-    a->free_stack[num_blocks - 1 - i] = b;   // initial_order[0] on top
+  if (int rc = init_tier(a->dev, num_blocks, initial_order)) {
+    delete a;
+    return rc;
   }
   *out = a;
+  return PKV_OK;
+}
+
+int kv_allocator_add_host_tier(kv_allocator* a, int32_t num_host_blocks,
+                               const int32_t* initial_order) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "allocator is NULL");
+  if (!a->host.refcount.empty()) return fail(PKV_ERR_INVALID_ARG, "the host tier exists already");
+  if (num_host_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_host_blocks must be positive (got %d)", num_host_blocks);
+  if (int rc = init_tier(a->host, num_host_blocks, initial_order)) {
+    a->host = kv_allocator::Tier{};
+    return rc;
+  }
   return PKV_OK;
 }
 
@@ -167,7 +208,7 @@ int kv_seq_create(kv_allocator* a, int32_t* seq_out) {
 }
 
 int kv_seq_fork(kv_allocator* a, int32_t parent, int32_t* child_out) {
-  if (int rc = check_seq(a, parent)) return rc;
+  if (int rc = check_resident(a, parent)) return rc;
   if (!child_out) return fail(PKV_ERR_INVALID_ARG, "child_out is NULL");
   int32_t child = 0;
   if (int rc = kv_seq_create(a, &child)) return rc;
@@ -175,14 +216,14 @@ int kv_seq_fork(kv_allocator* a, int32_t parent, int32_t* child_out) {
   const kv_allocator::Seq& p = a->seqs[parent];   // after emplace_back: no dangling ref
   c.blocks = p.blocks;
   c.length = p.length;
-  for (int32_t b : c.blocks) a->refcount[b] += 1;
+  for (int32_t b : c.blocks) a->dev.refcount[b] += 1;
   *child_out = child;
   return PKV_OK;
 }
 
 int kv_seq_append(kv_allocator* a, int32_t seq, int32_t n, int64_t* slots_out,
                   int32_t* cow_pair_out, int32_t* n_cow_out) {
-  if (int rc = check_seq(a, seq)) return rc;
+  if (int rc = check_resident(a, seq)) return rc;
   if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n must be >= 0 (got %d)", n);
   if ((n > 0 && !slots_out) || !cow_pair_out || !n_cow_out)
     return fail(PKV_ERR_INVALID_ARG, "NULL output pointer");
@@ -190,9 +231,9 @@ int kv_seq_append(kv_allocator* a, int32_t seq, int32_t n, int64_t* slots_out,
   if (n == 0) return PKV_OK;
   bool cow = false;
   int64_t need = blocks_needed(a, a->seqs[seq], n, &cow);
-  if (need > static_cast<int64_t>(a->free_stack.size()))
+  if (need > static_cast<int64_t>(a->dev.free_stack.size()))
     return fail(PKV_ERR_OUT_OF_BLOCKS, "append of %d tokens needs %lld blocks, %zu free", n,
-                static_cast<long long>(need), a->free_stack.size());
+                static_cast<long long>(need), a->dev.free_stack.size());
   AppendRecord rec = do_append(a, seq, n, slots_out);
   if (rec.cow_src >= 0) {
     cow_pair_out[0] = rec.cow_src;
@@ -214,10 +255,10 @@ int kv_batch_append(kv_allocator* a, const int32_t* seqs, int32_t num_seqs, int6
   int status = PKV_OK;
   for (int32_t i = 0; i < num_seqs; ++i) {
     int32_t seq = seqs[i];
-    if ((status = check_seq(a, seq))) break;
+    if ((status = check_resident(a, seq))) break;
     bool cow = false;
     int64_t need = blocks_needed(a, a->seqs[seq], 1, &cow);
-    if (need > static_cast<int64_t>(a->free_stack.size())) {
+    if (need > static_cast<int64_t>(a->dev.free_stack.size())) {
       status = fail(PKV_ERR_OUT_OF_BLOCKS, "decode step for %d sequences ran out of blocks at #%d",
                     num_seqs, i);
       break;
@@ -240,47 +281,152 @@ int kv_batch_append(kv_allocator* a, const int32_t* seqs, int32_t num_seqs, int6
   return PKV_OK;
 }
 
-int kv_seq_free(kv_allocator* a, int32_t seq) {
+namespace {
+
+// Drops the sequence's references in logical order; a block reaching zero goes
+// to its tier's free list, or is parked with `epoch` when `deferred`.
+int release_seq(kv_allocator* a, int32_t seq, bool deferred, int64_t epoch) {
   if (int rc = check_seq(a, seq)) return rc;
   kv_allocator::Seq& s = a->seqs[seq];
+  kv_allocator::Tier& t = s.swapped ? a->host : a->dev;
   for (int32_t b : s.blocks) {
-    if (--a->refcount[b] == 0) a->free_stack.push_back(b);
+    if (--t.refcount[b] == 0) {
+      if (deferred)
+        t.parked.push_back({b, epoch});
+      else
+        t.free_stack.push_back(b);
+    }
   }
   s.blocks.clear();
   s.blocks.shrink_to_fit();
   s.length = 0;
   s.live = false;
+  if (s.swapped) --a->swapped_seqs;
+  s.swapped = false;
   return PKV_OK;
 }
 
-int kv_seq_free_deferred(kv_allocator* a, int32_t seq, int64_t epoch) {
-  if (int rc = check_seq(a, seq)) return rc;
-  kv_allocator::Seq& s = a->seqs[seq];
-  for (int32_t b : s.blocks) {
-    if (--a->refcount[b] == 0) a->parked.push_back({b, epoch});
+int32_t retire_tier(kv_allocator::Tier& t, int64_t done) {
+  int32_t released = 0;
+  size_t keep = 0;
+  for (size_t i = 0; i < t.parked.size(); ++i) {
+    const kv_allocator::Parked p = t.parked[i];
+    if (p.epoch <= done) {
+      t.free_stack.push_back(p.block);
+      ++released;
+    } else {
+      t.parked[keep++] = p;
+    }
   }
-  s.blocks.clear();
-  s.blocks.shrink_to_fit();
-  s.length = 0;
-  s.live = false;
+  t.parked.resize(keep);
+  return released;
+}
+
+// Moves every block the listed sequences reference from tier `from` to tier
+// `to`: each distinct block (request order, then logical order) gets one fresh
+// block of `to` whose count is the set's references; the old block loses those
+// references and, at zero, is freed or parked.  Checks everything first; on
+// any error nothing changes.
+int swap_set(kv_allocator* a, const int32_t* seqs, int32_t n, bool to_host, int32_t deferred,
+             int64_t epoch, int32_t* pairs_out, int32_t pairs_capacity, int32_t* num_pairs_out) {
+  if (!a || !num_pairs_out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  *num_pairs_out = 0;
+  if (n < 0 || pairs_capacity < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
+  if (n > 0 && !seqs) return fail(PKV_ERR_INVALID_ARG, "NULL seqs");
+  std::vector<int32_t> sorted(seqs, seqs + n);
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+    return fail(PKV_ERR_INVALID_ARG, "a sequence is listed twice");
+  for (int32_t i = 0; i < n; ++i) {
+    if (int rc = check_seq(a, seqs[i])) return rc;
+    if (a->seqs[seqs[i]].swapped == to_host)
+      return fail(PKV_ERR_SWAPPED, "sequence %d is %s", seqs[i],
+                  to_host ? "swapped out already" : "not swapped out");
+  }
+  kv_allocator::Tier& from = to_host ? a->dev : a->host;
+  kv_allocator::Tier& to = to_host ? a->host : a->dev;
+  // Distinct blocks, first appearance first; set_refs counts the set's references.
+  std::vector<int32_t> order;
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t b : a->seqs[seqs[i]].blocks)
+      if (from.set_refs[b]++ == 0) order.push_back(b);
+  const int32_t distinct = static_cast<int32_t>(order.size());
+  int status = PKV_OK;
+  if (distinct > 0 && !pairs_out)
+    status = fail(PKV_ERR_INVALID_ARG, "NULL pairs_out");
+  else if (distinct > pairs_capacity)
+    status = fail(PKV_ERR_INVALID_ARG, "%d pairs needed, capacity %d", distinct, pairs_capacity);
+  else if (distinct > static_cast<int32_t>(to.free_stack.size()))
+    status = fail(PKV_ERR_OUT_OF_BLOCKS, "swap %s needs %d blocks, %zu free",
+                  to_host ? "out" : "in", distinct, to.free_stack.size());
+  if (status != PKV_OK) {
+    for (int32_t b : order) from.set_refs[b] = 0;
+    if (distinct > pairs_capacity) *num_pairs_out = distinct;
+    return status;
+  }
+  // new_of: reuse set_refs as old block -> new block after taking the counts.
+  for (int32_t j = 0; j < distinct; ++j) {
+    const int32_t b = order[j];
+    const int32_t refs = from.set_refs[b];
+    const int32_t nb = to.free_stack.back();
+    to.free_stack.pop_back();
+    to.refcount[nb] = refs;
+    from.refcount[b] -= refs;
+    if (from.refcount[b] == 0) {
+      if (deferred)
+        from.parked.push_back({b, epoch});
+      else
+        from.free_stack.push_back(b);
+    }
+    from.set_refs[b] = nb;
+    pairs_out[2 * j] = b;
+    pairs_out[2 * j + 1] = nb;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    kv_allocator::Seq& s = a->seqs[seqs[i]];
+    for (int32_t& b : s.blocks) b = from.set_refs[b];
+    s.swapped = to_host;
+  }
+  for (int32_t b : order) from.set_refs[b] = 0;
+  a->swapped_seqs += to_host ? n : -n;
+  (to_host ? a->swapped_out_blocks : a->swapped_in_blocks) += distinct;
+  *num_pairs_out = distinct;
   return PKV_OK;
+}
+
+}  // namespace
+
+int kv_seq_free(kv_allocator* a, int32_t seq) { return release_seq(a, seq, false, 0); }
+
+int kv_seq_free_deferred(kv_allocator* a, int32_t seq, int64_t epoch) {
+  return release_seq(a, seq, true, epoch);
 }
 
 int kv_allocator_retire(kv_allocator* a, int64_t done, int32_t* released_out) {
   if (!a) return fail(PKV_ERR_INVALID_ARG, "allocator is NULL");
-  int32_t released = 0;
-  size_t keep = 0;
-  for (size_t i = 0; i < a->parked.size(); ++i) {
-    const kv_allocator::Parked p = a->parked[i];
-    if (p.epoch <= done) {
-      a->free_stack.push_back(p.block);
-      ++released;
-    } else {
-      a->parked[keep++] = p;
-    }
-  }
-  a->parked.resize(keep);
+  const int32_t released = retire_tier(a->dev, done) + retire_tier(a->host, done);
   if (released_out) *released_out = released;
+  return PKV_OK;
+}
+
+int kv_swap_out(kv_allocator* a, const int32_t* seqs, int32_t num_seqs, int32_t deferred,
+                int64_t epoch, int32_t* pairs_out, int32_t pairs_capacity,
+                int32_t* num_pairs_out) {
+  return swap_set(a, seqs, num_seqs, true, deferred, epoch, pairs_out, pairs_capacity,
+                  num_pairs_out);
+}
+
+int kv_swap_in(kv_allocator* a, const int32_t* seqs, int32_t num_seqs, int32_t deferred,
+               int64_t epoch, int32_t* pairs_out, int32_t pairs_capacity,
+               int32_t* num_pairs_out) {
+  return swap_set(a, seqs, num_seqs, false, deferred, epoch, pairs_out, pairs_capacity,
+                  num_pairs_out);
+}
+
+int kv_seq_is_swapped(const kv_allocator* a, int32_t seq, int32_t* swapped_out) {
+  if (int rc = check_seq(a, seq)) return rc;
+  if (!swapped_out) return fail(PKV_ERR_INVALID_ARG, "swapped_out is NULL");
+  *swapped_out = a->seqs[seq].swapped ? 1 : 0;
   return PKV_OK;
 }
 
@@ -311,7 +457,7 @@ int kv_export_block_tables(const kv_allocator* a, const int32_t* seqs, int32_t n
   if (n < 0 || max_blocks_per_seq < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
   if (n > 0 && (!seqs || !tables_out || !lens_out)) return fail(PKV_ERR_INVALID_ARG, "NULL array");
   for (int32_t i = 0; i < n; ++i) {
-    if (int rc = check_seq(a, seqs[i])) return rc;
+    if (int rc = check_resident(a, seqs[i])) return rc;
     const kv_allocator::Seq& s = a->seqs[seqs[i]];
     if (static_cast<int64_t>(s.blocks.size()) > max_blocks_per_seq)
       return fail(PKV_ERR_INVALID_ARG, "sequence %d holds %zu blocks > max_blocks_per_seq %d",
@@ -342,7 +488,7 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
   const int32_t B = a->block_size;
   // Final lengths per entry (a sequence listed k times grows by k).
   for (int32_t i = 0; i < num_seqs; ++i)
-    if (int rc = check_seq(a, seqs[i])) return rc;
+    if (int rc = check_resident(a, seqs[i])) return rc;
   for (int32_t i = 0; i < num_seqs; ++i) a->seqs[seqs[i]].pending += 1;
   static thread_local std::vector<int32_t> lens;
   lens.resize(static_cast<size_t>(num_seqs));
@@ -414,15 +560,22 @@ int kv_allocator_stats(const kv_allocator* a, kv_stats* out) {
   if (!a || !out) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
   kv_stats st{};
   st.num_blocks = a->num_blocks;
-  st.free_blocks = static_cast<int32_t>(a->free_stack.size());
-  for (int32_t r : a->refcount) {
+  st.free_blocks = static_cast<int32_t>(a->dev.free_stack.size());
+  for (int32_t r : a->dev.refcount) {
     st.used_blocks += r > 0;
     st.shared_blocks += r > 1;
     st.sum_refcounts += r;
   }
   for (const kv_allocator::Seq& s : a->seqs)
     if (s.live) st.live_tokens += s.length;
-  st.pending_blocks = static_cast<int32_t>(a->parked.size());
+  st.pending_blocks = static_cast<int32_t>(a->dev.parked.size());
+  st.host_blocks = static_cast<int32_t>(a->host.refcount.size());
+  st.host_free_blocks = static_cast<int32_t>(a->host.free_stack.size());
+  for (int32_t r : a->host.refcount) st.host_used_blocks += r > 0;
+  st.host_pending_blocks = static_cast<int32_t>(a->host.parked.size());
+  st.swapped_seqs = a->swapped_seqs;
+  st.swapped_out_blocks = a->swapped_out_blocks;
+  st.swapped_in_blocks = a->swapped_in_blocks;
   *out = st;
   return PKV_OK;
 }

@@ -1,12 +1,15 @@
 // Stress driver for the host block allocator, built with AddressSanitizer and
 // UndefinedBehaviorSanitizer by tests/test_allocator_sanitized.py (host code
 // only; no device code is involved).  Random create / fork / append / batch
-// append / free / bad-id operations; after every operation the invariants that
-// the C ABI exposes are checked:
-//   free + used == num_blocks; sum of table lengths == sum of refcounts;
-//   distinct blocks over all tables == used; each table holds ceil(len/B)
-//   blocks; lengths match the driver's own count; a failed call changes
-//   nothing; after freeing everything all blocks are free again.
+// append / free / swap-out / swap-in / bad-id operations; after every
+// operation the invariants that the C ABI exposes are checked:
+//   free + used + parked == blocks, for the device pool and the host tier;
+//   sum of resident table lengths == sum of refcounts; distinct blocks over the
+//   resident tables == used; each table holds ceil(len/B) blocks; lengths match
+//   the driver's own count; swapped sequences are refused by append, fork and
+//   export; a failed call changes nothing; after freeing everything all blocks
+//   of both tiers are free again.  Swap pair lists go into heap buffers of
+//   exactly the size the call asks for, so a write past the end is caught.
 #include <algorithm>
 #include <cstdint>
 #include <cstdio>
@@ -37,7 +40,11 @@ int main(int argc, char** argv) {
     std::shuffle(order.begin(), order.end(), rng);
     kv_allocator* a = nullptr;
     CHECK(kv_allocator_create(nb, bs, order.data(), &a) == PKV_OK);
+    const int32_t nh = 4 + static_cast<int32_t>(rng() % 100);
+    CHECK(kv_allocator_add_host_tier(a, nh, nullptr) == PKV_OK);
+    CHECK(kv_allocator_add_host_tier(a, nh, nullptr) == PKV_ERR_INVALID_ARG);
     std::vector<int32_t> live;
+    std::set<int32_t> swapped;
     std::vector<int64_t> len;          // by id
     std::vector<int64_t> slots(4096);
     std::vector<int32_t> pairs(2 * 4096);
@@ -45,22 +52,25 @@ int main(int argc, char** argv) {
     for (int it = 0; it < iters / 8; ++it) {
       kv_stats before{};
       CHECK(kv_allocator_stats(a, &before) == PKV_OK);
-      const int op = static_cast<int>(rng() % 7);
+      const int op = static_cast<int>(rng() % 9);
       int rc = PKV_OK;
-      if (op == 0 || live.empty()) {
+      std::vector<int32_t> resident;
+      for (int32_t s : live)
+        if (!swapped.count(s)) resident.push_back(s);
+      if (op == 0 || live.empty() || (op <= 3 && resident.empty())) {
         int32_t s = -1;
         CHECK(kv_seq_create(a, &s) == PKV_OK);
         if (static_cast<size_t>(s) >= len.size()) len.resize(s + 1, 0);
         len[s] = 0;
         live.push_back(s);
       } else if (op == 1) {
-        int32_t p = live[rng() % live.size()], c = -1;
+        int32_t p = resident[rng() % resident.size()], c = -1;
         CHECK(kv_seq_fork(a, p, &c) == PKV_OK);
         if (static_cast<size_t>(c) >= len.size()) len.resize(c + 1, 0);
         len[c] = len[p];
         live.push_back(c);
       } else if (op == 2) {
-        int32_t s = live[rng() % live.size()];
+        int32_t s = resident[rng() % resident.size()];
         int32_t n = static_cast<int32_t>(rng() % (3 * bs + 1));
         int32_t pair[2], ncow = 0;
         rc = kv_seq_append(a, s, n, slots.data(), pair, &ncow);
@@ -70,8 +80,8 @@ int main(int argc, char** argv) {
         }
       } else if (op == 3) {
         std::vector<int32_t> batch;
-        const size_t k = 1 + rng() % (2 * live.size());
-        for (size_t i = 0; i < k && i < 4096; ++i) batch.push_back(live[rng() % live.size()]);
+        const size_t k = 1 + rng() % (2 * resident.size());
+        for (size_t i = 0; i < k && i < 4096; ++i) batch.push_back(resident[rng() % resident.size()]);
         int32_t ncow = 0;
         if (rng() % 2) {
           rc = kv_batch_append(a, batch.data(), static_cast<int32_t>(batch.size()), slots.data(),
@@ -103,6 +113,7 @@ int main(int argc, char** argv) {
         }
       } else if (op == 4) {
         const size_t i = rng() % live.size();
+        swapped.erase(live[i]);
         if (rng() % 2) {
           CHECK(kv_seq_free(a, live[i]) == PKV_OK);
         } else {
@@ -119,32 +130,105 @@ int main(int argc, char** argv) {
         CHECK(kv_seq_len(a, bad, &l) == PKV_ERR_BAD_SEQ);
         CHECK(kv_seq_append(a, bad, 1, slots.data(), pair, &ncow) == PKV_ERR_BAD_SEQ);
         CHECK(kv_seq_free(a, bad) == PKV_ERR_BAD_SEQ);
-      } else {
-        int32_t s = live[rng() % live.size()];
+      } else if (op == 6) {
+        if (resident.empty()) continue;
+        int32_t s = resident[rng() % resident.size()];
         int32_t pair[2], ncow = 0;
         rc = kv_seq_append(a, s, nb * bs + 1, slots.data(), pair, &ncow);   // never fits
         CHECK(rc == PKV_ERR_OUT_OF_BLOCKS);
+      } else if (op == 7) {
+        // Swap a random distinct subset out (of the resident) or in (of the swapped).
+        const bool out = swapped.empty() || (!resident.empty() && rng() % 2);
+        std::vector<int32_t> from = out ? resident : std::vector<int32_t>(swapped.begin(), swapped.end());
+        std::shuffle(from.begin(), from.end(), rng);
+        from.resize(1 + rng() % from.size());
+        const int32_t n = static_cast<int32_t>(from.size());
+        const int32_t deferred = static_cast<int32_t>(rng() % 2);
+        epoch += deferred;
+        auto call = out ? kv_swap_out : kv_swap_in;
+        int32_t need = 0;
+        rc = call(a, from.data(), n, deferred, epoch, nullptr, 0, &need);
+        if (rc == PKV_ERR_INVALID_ARG) {
+          CHECK(need > 0);
+          std::vector<int32_t> exact(2 * static_cast<size_t>(need));
+          int32_t got = 0;
+          if (need > 1) {
+            CHECK(call(a, from.data(), n, deferred, epoch, exact.data(), need - 1, &got) ==
+                  PKV_ERR_INVALID_ARG && got == need);
+          }
+          rc = call(a, from.data(), n, deferred, epoch, exact.data(), need, &got);
+          if (rc == PKV_OK) {
+            CHECK(got == need);
+            std::set<int32_t> news;
+            for (int32_t j = 0; j < got; ++j) {
+              CHECK(exact[2 * j] >= 0 && exact[2 * j] < (out ? nb : nh));
+              CHECK(exact[2 * j + 1] >= 0 && exact[2 * j + 1] < (out ? nh : nb));
+              news.insert(exact[2 * j + 1]);
+            }
+            CHECK(static_cast<int32_t>(news.size()) == got);
+          }
+        } else {
+          CHECK(rc == PKV_OK && need == 0);   // nothing to copy (empty sequences)
+        }
+        if (rc == PKV_OK) {
+          for (int32_t s : from) {
+            if (out) swapped.insert(s); else swapped.erase(s);
+          }
+          int32_t released = -1;
+          CHECK(kv_allocator_retire(a, epoch - static_cast<int64_t>(rng() % 2), &released) == PKV_OK);
+          CHECK(released >= 0);
+        } else {
+          CHECK(rc == PKV_ERR_OUT_OF_BLOCKS);
+        }
+      } else {
+        // Refusals: a swapped sequence cannot grow, fork or be exported; a resident
+        // one cannot be swapped in; a set may not list a sequence twice.
+        if (!swapped.empty()) {
+          const int32_t s = *swapped.begin();
+          int32_t pair[2], ncow = 0, c = -1, flag = 0, np = 0;
+          CHECK(kv_seq_append(a, s, 1, slots.data(), pair, &ncow) == PKV_ERR_SWAPPED);
+          CHECK(kv_seq_fork(a, s, &c) == PKV_ERR_SWAPPED);
+          std::vector<int32_t> t(nb);
+          int32_t l = 0;
+          CHECK(kv_export_block_tables(a, &s, 1, nb, -1, t.data(), &l) == PKV_ERR_SWAPPED);
+          CHECK(kv_seq_is_swapped(a, s, &flag) == PKV_OK && flag == 1);
+          CHECK(kv_swap_out(a, &s, 1, 0, 0, pairs.data(), 4096, &np) == PKV_ERR_SWAPPED);
+        }
+        if (!resident.empty()) {
+          int32_t two[2] = {resident[0], resident[0]}, np = 0;
+          CHECK(kv_swap_in(a, two, 1, 0, 0, pairs.data(), 4096, &np) == PKV_ERR_SWAPPED);
+          CHECK(kv_swap_out(a, two, 2, 0, 0, pairs.data(), 4096, &np) == PKV_ERR_INVALID_ARG);
+        }
       }
       kv_stats st{};
       CHECK(kv_allocator_stats(a, &st) == PKV_OK);
       if (rc != PKV_OK) {                     // all or nothing
         CHECK(rc == PKV_ERR_OUT_OF_BLOCKS);
         CHECK(st.free_blocks == before.free_blocks && st.sum_refcounts == before.sum_refcounts &&
-              st.live_tokens == before.live_tokens);
+              st.live_tokens == before.live_tokens &&
+              st.host_free_blocks == before.host_free_blocks &&
+              st.swapped_seqs == before.swapped_seqs);
       }
       CHECK(st.free_blocks + st.used_blocks + st.pending_blocks == nb);
+      CHECK(st.host_free_blocks + st.host_used_blocks + st.host_pending_blocks == nh);
+      CHECK(st.host_blocks == nh && st.swapped_seqs == static_cast<int32_t>(swapped.size()));
       CHECK(st.shared_blocks <= st.used_blocks);
-      if (!live.empty()) {
+      resident.clear();
+      for (int32_t s : live)
+        if (!swapped.count(s)) resident.push_back(s);
+      if (!resident.empty()) {
         const int32_t maxb = nb;
-        std::vector<int32_t> tables(static_cast<size_t>(live.size()) * maxb), lens(live.size());
-        CHECK(kv_export_block_tables(a, live.data(), static_cast<int32_t>(live.size()), maxb, -1,
-                                     tables.data(), lens.data()) == PKV_OK);
-        std::vector<int32_t> lens2(live.size());
-        CHECK(kv_seq_lens(a, live.data(), static_cast<int32_t>(live.size()), lens2.data()) == PKV_OK);
+        std::vector<int32_t> tables(static_cast<size_t>(resident.size()) * maxb),
+            lens(resident.size());
+        CHECK(kv_export_block_tables(a, resident.data(), static_cast<int32_t>(resident.size()),
+                                     maxb, -1, tables.data(), lens.data()) == PKV_OK);
+        std::vector<int32_t> lens2(resident.size());
+        CHECK(kv_seq_lens(a, resident.data(), static_cast<int32_t>(resident.size()),
+                          lens2.data()) == PKV_OK);
         int64_t total = 0;
         std::set<int32_t> distinct;
-        for (size_t i = 0; i < live.size(); ++i) {
-          CHECK(lens[i] == len[live[i]] && lens2[i] == lens[i]);
+        for (size_t i = 0; i < resident.size(); ++i) {
+          CHECK(lens[i] == len[resident[i]] && lens2[i] == lens[i]);
           int64_t held = 0;
           for (int32_t j = 0; j < maxb; ++j) {
             const int32_t b = tables[i * maxb + j];
@@ -165,6 +249,7 @@ int main(int argc, char** argv) {
     kv_stats st{};
     CHECK(kv_allocator_stats(a, &st) == PKV_OK);
     CHECK(st.free_blocks == nb && st.sum_refcounts == 0);
+    CHECK(st.host_free_blocks == nh && st.swapped_seqs == 0);
     kv_allocator_destroy(a);
   }
   std::printf("ok\n");
