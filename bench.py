@@ -13,6 +13,10 @@ launch divided by that launch's time measured with HIP events on the launch
 stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample of requests.
 
     python bench.py [--steps K] [--warmup W] [--workload opt13b|gqa|long_context]
+
+Other workloads: ``prefill`` (prompt-phase attention, FLOP/s against the fp16
+matrix peak) and ``swap`` (requests moved to the pinned host tier and back,
+GB/s against the host link).
 """
 
 from __future__ import annotations
@@ -39,7 +43,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="opt13b",
-                    choices=["opt13b", "gqa", "long_context", "parallel_sampling", "tiny", "prefill"])
+                    choices=["opt13b", "gqa", "long_context", "parallel_sampling", "tiny", "prefill",
+                             "swap"])
     ap.add_argument("--partition", default="auto",
                     help="tokens per split-context partition, 0 = one pass, or 'auto'")
     ap.add_argument("--kernel-policy", default="default", choices=["default", "valu"],
@@ -436,6 +441,121 @@ def prefill_bench(args):
     print(json.dumps(result), flush=True)
 
 
+PCIE_PEAK_GBS = 63.0   # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
+
+
+def swap_bench(args):
+    """Eviction to the host tier: each step swaps every other request of the OPT-13B
+    decode batch out to pinned host memory and back in (the allocator picks the
+    blocks, one upload of the pairs, kv_swap_blocks per direction on one stream).
+    Metric: K/V bytes moved per second; roofline: the copy kernel against one
+    direction of the host link.  The copy engine's rate for one contiguous
+    transfer of the same size, each way, is reported beside it."""
+    import torch
+
+    from paged_kv_cache_244_amd import workloads
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    dev = torch.device("cuda:0")
+    w = workloads.opt13b()
+    lens = [int(L) for L in w.lengths]
+    bs = w.block_size
+    block_bytes = 2 * w.num_kv_heads * bs * w.head_dim * 2          # K and V of one block
+    moved_idx = list(range(0, len(lens), 2))
+    moved_blocks = sum(-(-lens[i] // bs) for i in moved_idx)
+    cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, bs,
+                         initial_order=w.initial_order, device=dev, poison=False,
+                         num_q_heads=w.num_q_heads, host_blocks=moved_blocks)
+    kd, vd = _to_dev([w.k_tokens, w.v_tokens], dev)
+    seqs = [cache.new_sequence() for _ in lens]
+    cache.write(cache.reserve_many(seqs, lens), kd, vd)
+    moved = [seqs[i] for i in moved_idx]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(slot=None):
+        e = ev[slot] if slot is not None else None
+        n_out = cache.swap_out(moved, events=None if e is None else (e[0], e[1]))
+        n_in = cache.swap_in(moved, events=None if e is None else (e[2], e[3]))
+        assert n_out == n_in == moved_blocks
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    out_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    in_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    nbytes = moved_blocks * block_bytes
+    gbs = lambda ms: nbytes / (ms / 1e3) / 1e9  # noqa: E731
+    achieved = gbs(float(np.mean(out_ms + in_ms)))
+    engine = copy_engine_rates(nbytes, dev)
+    baseline = swap_cpu_baseline(w) if args.cpu_seconds > 0 else None
+    result = {
+        "metric": "swap to host tier: K/V GB/s moved (% of one direction of PCIe 5.0 x16)",
+        "value": round(2 * nbytes * args.steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "swap: every other request of the OPT-13B decode batch out and in",
+                   "requests_moved": len(moved), "blocks_moved": moved_blocks,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": bs,
+                   "bytes_per_direction": nbytes},
+        "swap_out_us": round(float(np.mean(out_ms)) * 1e3, 1),
+        "swap_in_us": round(float(np.mean(in_ms)) * 1e3, 1),
+        "swap_out_gbs": round(gbs(float(np.mean(out_ms))), 2),
+        "swap_in_gbs": round(gbs(float(np.mean(in_ms))), 2),
+        "copy_engine_gbs": engine,
+        "roofline": {"bound": "pcie", "achieved": round(achieved, 2), "peak": PCIE_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kv_copy_blocks_kernel (kv_swap_blocks)"},
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def copy_engine_rates(nbytes, dev, reps=5):
+    """One contiguous device <-> pinned host transfer of ``nbytes`` through the runtime's
+    copy path (torch copy_), each direction: the link's rate without block gathering."""
+    import torch
+
+    d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    rates = {}
+    for name, dst, src in (("d2h", h, d), ("h2d", d, h)):
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dst.copy_(src, non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        rates[name] = round(nbytes * reps / (a.elapsed_time(b) / 1e3) / 1e9, 2)
+    return rates
+
+
+def swap_cpu_baseline(w, blocks=512):
+    """The oracle's copy_blocks_between moving ``blocks`` blocks between two host pools."""
+    from oracle import cache
+
+    shape = (blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    src = [(np.ones(shape, np.float16), np.ones(shape, np.float16))]
+    dst = [(np.zeros(shape, np.float16), np.zeros(shape, np.float16))]
+    pairs = np.stack([np.arange(blocks), np.random.default_rng(0).permutation(blocks)], 1)
+    t0 = time.perf_counter()
+    cache.copy_blocks_between(src, dst, pairs)
+    dt = time.perf_counter() - t0
+    nbytes = blocks * 2 * int(np.prod(shape[1:])) * 2
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{blocks} OPT-13B blocks (K and V) between two host pools, numpy",
+            "seconds": round(dt, 3)}
+
+
 def prefill_cpu_baseline(w, prompt=1024):
     """The oracle's attend_prefill_paged on one request's first ``prompt`` tokens."""
     from threadpoolctl import threadpool_limits
@@ -469,13 +589,13 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path has no multi-GPU sharding in this build)", file=sys.stderr)
         sys.exit(2)
-    if args.workload == "prefill":
+    if args.workload in ("prefill", "swap"):
         import torch
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(1)
         torch.cuda.set_device(0)
-        prefill_bench(args)
+        (prefill_bench if args.workload == "prefill" else swap_bench)(args)
         return
 
     import torch

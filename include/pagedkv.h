@@ -109,6 +109,36 @@ int kv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_lay
                    void* stream);
 
 /*
+ * kv_swap_blocks — move whole blocks between two pools of the same block
+ * geometry, typically the device pool and a host-tier pool in pinned host
+ * memory (kv_swap_out / kv_swap_in name the blocks).  [C] "Eviction and reuse
+ * can move costs elsewhere": evicted state moved to another memory tier costs
+ * transfer time and bandwidth, here one block's K and V per pair and layer
+ * over the host link.  For each pair (src, dst) and each layer, block dst of
+ * the destination pools becomes a copy of block src of the source pools (all
+ * heads, all block_size slots).  The copy is a kernel on `stream` that
+ * addresses pinned host memory directly, so it is ordered with the stream's
+ * other kernels (no copy-engine hand-off).
+ *
+ *   dst_k, dst_v, src_k, src_v : HOST arrays of num_layers pool pointers; each
+ *                        pool is device memory or pinned host memory (from
+ *                        hipHostMalloc, e.g. torch's pin_memory), 16-byte
+ *                        aligned.  Any other memory (pageable host memory) is
+ *                        refused with PKV_ERR_INVALID_ARG before a launch.
+ *   dst_num_blocks, src_num_blocks : blocks in each destination / source pool.
+ *   block_pairs        : device int32 [num_pairs][2] = (src, dst).  A pair with
+ *                        an id outside its pool is skipped.  dst ids must be
+ *                        distinct (pairs run concurrently); the source and
+ *                        destination pools must not overlap.
+ * num_pairs == 0 is a no-op; at most 65535 pairs per call.  The host must not
+ * touch a host pool's blocks until the copy has run (an event tells).
+ */
+int kv_swap_blocks(void* const* dst_k, void* const* dst_v, int32_t dst_num_blocks,
+                   void* const* src_k, void* const* src_v, int32_t src_num_blocks,
+                   int32_t num_layers, const int32_t* block_pairs, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, void* stream);
+
+/*
  * pkv_upload — copy `bytes` from pinned host memory (allocated with
  * hipHostMalloc, e.g. torch's pin_memory) into device memory with a kernel on
  * `stream`.  [B] "The page table, relocated into attention": a step's tables

@@ -88,6 +88,9 @@ _SIGNATURES = {
     "kv_copy_blocks": (c_int32, [POINTER(c_void_p), POINTER(c_void_p), c_int32, c_void_p, c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "pkv_upload": (c_int32, [c_void_p, c_void_p, ctypes.c_uint64, c_void_p]),
+    "kv_swap_blocks": (c_int32, [POINTER(c_void_p), POINTER(c_void_p), c_int32, POINTER(c_void_p),
+                                 POINTER(c_void_p), c_int32, c_int32, c_void_p, c_int32, c_int32,
+                                 c_int32, c_int32, c_void_p]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode_set_kernel_policy": (c_int32, [c_int32]),
     "pa_decode_plan": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
@@ -228,6 +231,46 @@ def kv_copy_blocks(k_caches, v_caches, block_pairs, stream=None):
     vp = (c_void_p * n)(*[_dev(v, torch.float16, "v_cache").value for v in v_caches])
     _check(lib().kv_copy_blocks(kp, vp, n, _dev(block_pairs, torch.int32, "block_pairs"),
                                 int(block_pairs.shape[0]), nb, hkv, d, bs, _stream(stream)))
+
+
+def _pool_ptr(t, name):
+    """Address of a pool that is a device tensor or a pinned host tensor (the library
+    checks which and refuses anything else)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous fp16 tensor")
+    if not (t.is_cuda or t.is_pinned()):
+        raise TypeError(f"{name} must be device memory or pinned host memory")
+    return t.data_ptr()
+
+
+def kv_swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, stream=None):
+    """For each (src, dst) row of block_pairs (device int32 [P, 2]) and each layer,
+    block dst of the destination pools becomes block src of the source pools.  Pools
+    are lists (one per layer) of fp16 [blocks, kv_heads, block_size, head_dim] tensors
+    on the device or in pinned host memory."""
+    torch = _torch()
+    n = len(dst_k)
+    if not n or not (len(dst_v) == len(src_k) == len(src_v) == n):
+        raise ValueError("need the same, non-zero number of pools on every side")
+    dgeo = _pool_geometry(dst_k[0], dst_v[0])
+    sgeo = _pool_geometry(src_k[0], src_v[0])
+    for a, b in zip(dst_k, dst_v):
+        if _pool_geometry(a, b) != dgeo:
+            raise ValueError("all destination pools must share one geometry")
+    for a, b in zip(src_k, src_v):
+        if _pool_geometry(a, b) != sgeo:
+            raise ValueError("all source pools must share one geometry")
+    if dgeo[1:] != sgeo[1:]:
+        raise ValueError("source and destination blocks must have the same geometry")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [P, 2]")
+    _, hkv, bs, d = dgeo
+    arr = [(c_void_p * n)(*[_pool_ptr(t, name) for t in ts])
+           for ts, name in ((dst_k, "dst_k"), (dst_v, "dst_v"), (src_k, "src_k"), (src_v, "src_v"))]
+    _check(lib().kv_swap_blocks(arr[0], arr[1], dgeo[0], arr[2], arr[3], sgeo[0], n,
+                                _dev(block_pairs, torch.int32, "block_pairs"),
+                                int(block_pairs.shape[0]), hkv, d, bs, _stream(stream)))
 
 
 def plan(context_lens, num_q_heads, num_kv_heads, head_dim, block_size, q_dtype=PKV_F16,

@@ -13,6 +13,11 @@ Host-to-device uploads of one step (slots, copy pairs, tables, lengths, the
 launch's work items) are packed into one pinned buffer and sent with a single
 copy: each small copy is a serialised operation on the stream, so one copy
 instead of four or five shortens every step.
+
+With ``host_blocks`` > 0 the cache also has a host tier: K/V pools in pinned
+host memory to which whole requests can be swapped out and back in
+(``swap_out`` / ``swap_in``); the allocator picks the blocks and a library
+kernel on the cache's stream moves them over the host link.
 """
 
 from __future__ import annotations
@@ -135,7 +140,7 @@ class PagedKVCache:
 
     def __init__(self, num_blocks, num_kv_heads, head_dim, block_size, num_layers=1,
                  initial_order=None, device="cuda", poison=True, stream=None,
-                 num_q_heads=None, q_dtype=None):
+                 num_q_heads=None, q_dtype=None, host_blocks=0, host_order=None):
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
@@ -151,6 +156,17 @@ class PagedKVCache:
                   for _ in range(num_layers)]
         self.v = [torch.full(shape, fill, dtype=torch.float16, device=self.device)
                   for _ in range(num_layers)]
+        self.host_blocks = int(host_blocks)
+        self.host_k, self.host_v = [], []
+        if self.host_blocks:
+            self.alloc.add_host_tier(self.host_blocks, host_order)
+            hshape = (self.host_blocks, num_kv_heads, block_size, head_dim)
+            for pools in (self.host_k, self.host_v):
+                for _ in range(num_layers):
+                    t = torch.empty(hshape, dtype=torch.float16, pin_memory=True)
+                    if poison:
+                        t.fill_(float("nan"))
+                    pools.append(t)
         self._staging = _Staging(self.device)
         self._plan_staging = _Staging(self.device, nbytes=1 << 16)   # re-plans in attend
         self._workspace = None
@@ -191,6 +207,59 @@ class PagedKVCache:
 
     def length(self, seq: int) -> int:
         return self.alloc.length(seq)
+
+    # -- the host tier -----------------------------------------------------------
+    def _epoch_for(self, deferred):
+        if not deferred:
+            return 0
+        self._epoch += 1
+        return self._epoch
+
+    def _after_copy(self, deferred, epoch):
+        if deferred:
+            ev = torch.cuda.Event()
+            ev.record(self.stream)
+            self._pending.append((epoch, ev))
+
+    def swap_out(self, seqs, deferred: bool = False, events=None) -> int:
+        """Move the requests' blocks to the host tier (each distinct block once, blocks
+        shared inside the set stay shared) and free their device blocks.  The copy runs
+        on the cache's stream, so work queued later on it may reuse the blocks at once;
+        ``deferred=True`` keeps them out of circulation until the copy has finished
+        (for work on other streams).  ``events`` (start, end), if given, are recorded
+        on the stream around the copy kernels.  Returns the number of blocks copied."""
+        if self._pending:
+            self.retire()
+        epoch = self._epoch_for(deferred)
+        pairs = self.alloc.swap_out(np.asarray(seqs, dtype=np.int32), deferred, epoch)
+        self._move(pairs, self.host_k, self.host_v, self.k, self.v, events)
+        self._after_copy(deferred, epoch)
+        return int(pairs.shape[0])
+
+    def swap_in(self, seqs, deferred: bool = False, events=None) -> int:
+        """Move swapped-out requests back to device blocks (the inverse of ``swap_out``;
+        the new blocks are whatever the free list gives).  Returns the blocks copied."""
+        if self._pending:
+            self.retire()
+        epoch = self._epoch_for(deferred)
+        pairs = self.alloc.swap_in(np.asarray(seqs, dtype=np.int32), deferred, epoch)
+        self._move(pairs, self.k, self.v, self.host_k, self.host_v, events)
+        self._after_copy(deferred, epoch)
+        return int(pairs.shape[0])
+
+    def _move(self, pairs, dst_k, dst_v, src_k, src_v, events=None):
+        if pairs.shape[0] == 0:
+            return
+        for first in range(0, pairs.shape[0], 65535):       # the kernel's per-call limit
+            (pairs_dev,) = self.upload(pairs[first:first + 65535])
+            if events is not None and first == 0:
+                events[0].record(self.stream)
+            _lib.kv_swap_blocks(dst_k, dst_v, src_k, src_v, pairs_dev, stream=self.stream)
+        if events is not None:
+            events[1].record(self.stream)
+
+    def is_swapped(self, seq: int) -> bool:
+        return self.alloc.is_swapped(seq)
 
     # -- device staging -------------------------------------------------------
     def upload(self, *arrays):

@@ -16,6 +16,12 @@
 // device memory, on the caller's stream.  Same page, section "The page table,
 // relocated into attention": the tables are made on the host and must be in
 // GPU memory before the kernel walks them.
+// kv_swap_blocks: "The KV cache is a systems problem" (rsw.lol), section
+// "Eviction and reuse can move costs elsewhere" — evicted blocks moved to a
+// pool in pinned host memory and back, block by block, by the same copy kernel
+// as copy-on-write: the host pool is addressed over the bus, so both
+// directions run on the caller's compute stream without a copy-engine hand-off,
+// bound by the host link rather than by HBM.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -74,9 +80,13 @@ __global__ __launch_bounds__(kThreads) void upload_kernel(uint4* __restrict__ ds
 
 constexpr int kMaxLayersPerLaunch = 32;
 
-struct LayerPtrs {
-  uint4* k[kMaxLayersPerLaunch];
-  uint4* v[kMaxLayersPerLaunch];
+// Source and destination pools of each layer: the same pools for copy-on-write,
+// a device pool and a pinned host pool (device-side addresses) for a swap.
+struct LayerPools {
+  const uint4* src_k[kMaxLayersPerLaunch];
+  const uint4* src_v[kMaxLayersPerLaunch];
+  uint4* dst_k[kMaxLayersPerLaunch];
+  uint4* dst_v[kMaxLayersPerLaunch];
 };
 
 constexpr int kCopyUnroll = 4;
@@ -85,15 +95,16 @@ constexpr int kCopyUnroll = 4;
 // A block is contiguous: heads * block_size * head_dim halves = chunks_per_block
 // 16-byte chunks.  Each thread issues kCopyUnroll loads before its stores.
 __global__ __launch_bounds__(kThreads) void kv_copy_blocks_kernel(
-    LayerPtrs layers, const int32_t* __restrict__ pairs, int32_t num_blocks,
+    LayerPools pools, const int32_t* __restrict__ pairs, int32_t src_blocks, int32_t dst_blocks,
     int64_t chunks_per_block) {
   const int32_t src = pairs[2 * blockIdx.y];
   const int32_t dst = pairs[2 * blockIdx.y + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
   const int layer = blockIdx.z >> 1;
-  uint4* base = (blockIdx.z & 1) ? layers.v[layer] : layers.k[layer];
-  const uint4* s = base + static_cast<int64_t>(src) * chunks_per_block;
-  uint4* d = base + static_cast<int64_t>(dst) * chunks_per_block;
+  const uint4* s = ((blockIdx.z & 1) ? pools.src_v[layer] : pools.src_k[layer]) +
+                   static_cast<int64_t>(src) * chunks_per_block;
+  uint4* d = ((blockIdx.z & 1) ? pools.dst_v[layer] : pools.dst_k[layer]) +
+             static_cast<int64_t>(dst) * chunks_per_block;
   const int64_t first = static_cast<int64_t>(blockIdx.x) * kThreads * kCopyUnroll + threadIdx.x;
   uint4 tmp[kCopyUnroll];
 #pragma unroll
@@ -111,6 +122,72 @@ __global__ __launch_bounds__(kThreads) void kv_copy_blocks_kernel(
 int hip_status(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+// The address a kernel uses for `p`, which must be device memory or pinned host
+// memory (the runtime knows both; anything else, e.g. pageable host memory, is
+// refused, since a kernel touching it would fault).  nullptr on refusal.
+const void* kernel_address(const void* p, bool* is_host) {
+  hipPointerAttribute_t at{};
+  if (p == nullptr || hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (at.type == hipMemoryTypeDevice) {
+    *is_host = false;
+    return p;
+  }
+  if (at.type != hipMemoryTypeHost || at.devicePointer == nullptr) return nullptr;
+  *is_host = true;
+  const char* dev = static_cast<const char*>(at.devicePointer);
+  if (at.hostPointer != nullptr && at.hostPointer != p)   // attributes of the allocation base
+    dev += static_cast<const char*>(p) - static_cast<const char*>(at.hostPointer);
+  return dev;
+}
+
+// Launches the block copy for every layer, kMaxLayersPerLaunch layers at a time.
+int launch_block_copy(const void* const* src_k, const void* const* src_v, void* const* dst_k,
+                      void* const* dst_v, int32_t num_layers, const int32_t* block_pairs,
+                      int32_t num_pairs, int32_t src_blocks, int32_t dst_blocks,
+                      int64_t chunks_per_block, bool translate, hipStream_t stream,
+                      const char* what) {
+  const int64_t per_wg = static_cast<int64_t>(kThreads) * kCopyUnroll;
+  const unsigned gx = static_cast<unsigned>((chunks_per_block + per_wg - 1) / per_wg);
+  for (int32_t first = 0; first < num_layers; first += kMaxLayersPerLaunch) {
+    const int32_t n = num_layers - first < kMaxLayersPerLaunch ? num_layers - first
+                                                               : kMaxLayersPerLaunch;
+    LayerPools pools{};
+    for (int32_t l = 0; l < n; ++l) {
+      const void* sk = src_k[first + l];
+      const void* sv = src_v[first + l];
+      void* dk = dst_k[first + l];
+      void* dv = dst_v[first + l];
+      if (!sk || !sv || !dk || !dv)
+        return fail(PKV_ERR_INVALID_ARG, "%s: NULL pool for layer %d", what, first + l);
+      if (translate) {
+        bool host[4];
+        sk = kernel_address(sk, &host[0]);
+        sv = kernel_address(sv, &host[1]);
+        dk = const_cast<void*>(kernel_address(dk, &host[2]));
+        dv = const_cast<void*>(kernel_address(dv, &host[3]));
+        if (!sk || !sv || !dk || !dv)
+          return fail(PKV_ERR_INVALID_ARG,
+                      "%s: a pool of layer %d is neither device memory nor pinned host memory",
+                      what, first + l);
+      }
+      if ((reinterpret_cast<uintptr_t>(sk) | reinterpret_cast<uintptr_t>(sv) |
+           reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv)) % 16 != 0)
+        return fail(PKV_ERR_INVALID_ARG, "%s: pools must be 16-byte aligned", what);
+      pools.src_k[l] = static_cast<const uint4*>(sk);
+      pools.src_v[l] = static_cast<const uint4*>(sv);
+      pools.dst_k[l] = static_cast<uint4*>(dk);
+      pools.dst_v[l] = static_cast<uint4*>(dv);
+    }
+    hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3(gx, num_pairs, 2 * n), dim3(kThreads), 0,
+                       stream, pools, block_pairs, src_blocks, dst_blocks, chunks_per_block);
+    if (int rc = hip_status(what)) return rc;
+  }
   return PKV_OK;
 }
 
@@ -158,24 +235,33 @@ extern "C" int kv_copy_blocks(void* const* k_caches, void* const* v_caches, int3
     return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: at most 65535 pairs per call (got %d)",
                 num_pairs);
   const int64_t chunks_per_block = static_cast<int64_t>(num_kv_heads) * block_size * head_dim / 8;
-  const int64_t per_wg = static_cast<int64_t>(kThreads) * kCopyUnroll;
-  const unsigned gx = static_cast<unsigned>((chunks_per_block + per_wg - 1) / per_wg);
-  for (int32_t first = 0; first < num_layers; first += kMaxLayersPerLaunch) {
-    const int32_t n = num_layers - first < kMaxLayersPerLaunch ? num_layers - first
-                                                               : kMaxLayersPerLaunch;
-    LayerPtrs ptrs{};
-    for (int32_t l = 0; l < n; ++l) {
-      if (!k_caches[first + l] || !v_caches[first + l])
-        return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: NULL pool for layer %d", first + l);
-      ptrs.k[l] = static_cast<uint4*>(k_caches[first + l]);
-      ptrs.v[l] = static_cast<uint4*>(v_caches[first + l]);
-    }
-    hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3(gx, num_pairs, 2 * n), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), ptrs, block_pairs, num_blocks,
-                       chunks_per_block);
-    if (int rc = hip_status("kv_copy_blocks launch")) return rc;
-  }
-  return PKV_OK;
+  return launch_block_copy(k_caches, v_caches, k_caches, v_caches, num_layers, block_pairs,
+                           num_pairs, num_blocks, num_blocks, chunks_per_block, false,
+                           static_cast<hipStream_t>(stream), "kv_copy_blocks launch");
+}
+
+extern "C" int kv_swap_blocks(void* const* dst_k, void* const* dst_v, int32_t dst_num_blocks,
+                              void* const* src_k, void* const* src_v, int32_t src_num_blocks,
+                              int32_t num_layers, const int32_t* block_pairs, int32_t num_pairs,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              void* stream) {
+  if (num_layers < 0 || num_pairs < 0 || dst_num_blocks <= 0 || src_num_blocks <= 0 ||
+      num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "kv_swap_blocks: bad sizes");
+  if (!supported_geometry(head_dim, block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "kv_swap_blocks: head_dim %d / block_size %d not built",
+                head_dim, block_size);
+  if (num_pairs == 0 || num_layers == 0) return PKV_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !block_pairs)
+    return fail(PKV_ERR_INVALID_ARG, "kv_swap_blocks: NULL pointer");
+  if (num_pairs > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "kv_swap_blocks: at most 65535 pairs per call (got %d)",
+                num_pairs);
+  const int64_t chunks_per_block = static_cast<int64_t>(num_kv_heads) * block_size * head_dim / 8;
+  return launch_block_copy(src_k, src_v, dst_k, dst_v, num_layers, block_pairs, num_pairs,
+                           src_num_blocks,
+                           dst_num_blocks, chunks_per_block, true,
+                           static_cast<hipStream_t>(stream), "kv_swap_blocks launch");
 }
 
 extern "C" int pkv_upload(void* dst, const void* src, uint64_t bytes, void* stream) {
@@ -185,21 +271,14 @@ extern "C" int pkv_upload(void* dst, const void* src, uint64_t bytes, void* stre
       reinterpret_cast<uintptr_t>(src) % 16 != 0)
     return fail(PKV_ERR_INVALID_ARG, "pkv_upload: pointers and size must be multiples of 16");
   // The kernel may only touch memory the GPU can address: the source must be
-  // pinned host memory (its device-side address is taken from the runtime) and
-  // the destination device memory.  Anything else is refused before a launch.
-  hipPointerAttribute_t sa{}, da{};
-  if (hipPointerGetAttributes(&sa, src) != hipSuccess || sa.type != hipMemoryTypeHost ||
-      sa.devicePointer == nullptr) {
-    (void)hipGetLastError();
+  // pinned host memory and the destination device memory.  Anything else is
+  // refused before a launch.
+  bool src_host = false, dst_host = true;
+  const char* dev_src = static_cast<const char*>(kernel_address(src, &src_host));
+  if (!dev_src || !src_host)
     return fail(PKV_ERR_INVALID_ARG, "pkv_upload: source is not pinned host memory");
-  }
-  if (hipPointerGetAttributes(&da, dst) != hipSuccess || da.type != hipMemoryTypeDevice) {
-    (void)hipGetLastError();
+  if (!kernel_address(dst, &dst_host) || dst_host)
     return fail(PKV_ERR_INVALID_ARG, "pkv_upload: destination is not device memory");
-  }
-  const char* dev_src = static_cast<const char*>(sa.devicePointer);
-  if (sa.hostPointer != nullptr && sa.hostPointer != src)   // attributes of the allocation base
-    dev_src += static_cast<const char*>(src) - static_cast<const char*>(sa.hostPointer);
   if (reinterpret_cast<uintptr_t>(dev_src) % 16 != 0)
     return fail(PKV_ERR_INVALID_ARG, "pkv_upload: device address of the source is misaligned");
   const int64_t n16 = static_cast<int64_t>(bytes / 16);
