@@ -449,8 +449,9 @@ def swap_bench(args):
     decode batch out to pinned host memory and back in (the allocator picks the
     blocks, one upload of the pairs, kv_swap_blocks per direction on one stream).
     Metric: K/V bytes moved per second; roofline: the copy kernel against one
-    direction of the host link.  The copy engine's rate for one contiguous
-    transfer of the same size, each way, is reported beside it."""
+    direction of the host link.  The runtime's own copy (hipMemcpyAsync through
+    torch) of one contiguous buffer of the same size, each way, is reported
+    beside it as the rate of the link without block gathering."""
     import torch
 
     from paged_kv_cache_244_amd import workloads
@@ -491,7 +492,7 @@ def swap_bench(args):
     nbytes = moved_blocks * block_bytes
     gbs = lambda ms: nbytes / (ms / 1e3) / 1e9  # noqa: E731
     achieved = gbs(float(np.mean(out_ms + in_ms)))
-    engine = copy_engine_rates(nbytes, dev)
+    runtime_copy = runtime_copy_rates(nbytes, dev)
     baseline = swap_cpu_baseline(w) if args.cpu_seconds > 0 else None
     result = {
         "metric": "swap to host tier: K/V GB/s moved (% of one direction of PCIe 5.0 x16)",
@@ -509,7 +510,7 @@ def swap_bench(args):
         "swap_in_us": round(float(np.mean(in_ms)) * 1e3, 1),
         "swap_out_gbs": round(gbs(float(np.mean(out_ms))), 2),
         "swap_in_gbs": round(gbs(float(np.mean(in_ms))), 2),
-        "copy_engine_gbs": engine,
+        "runtime_copy_gbs": runtime_copy,
         "roofline": {"bound": "pcie", "achieved": round(achieved, 2), "peak": PCIE_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PCIE_PEAK_GBS, 4), "traffic": None,
                      "kernel": "kv_copy_blocks_kernel (kv_swap_blocks)"},
@@ -518,9 +519,10 @@ def swap_bench(args):
     print(json.dumps(result), flush=True)
 
 
-def copy_engine_rates(nbytes, dev, reps=5):
+def runtime_copy_rates(nbytes, dev, reps=5):
     """One contiguous device <-> pinned host transfer of ``nbytes`` through the runtime's
-    copy path (torch copy_), each direction: the link's rate without block gathering."""
+    copy path (torch copy_ -> hipMemcpyAsync; the runtime picks a blit kernel or a copy
+    engine), each direction: the link's rate without block gathering."""
     import torch
 
     d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
