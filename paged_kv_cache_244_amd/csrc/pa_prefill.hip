@@ -14,20 +14,28 @@
 // 0..that position (Q_i = L_i is a plain prefill; Q_i < L_i continues a cached
 // prefix).
 //
-// One workgroup of 8 waves per work item (request, block of 8 * 16/HT queries,
-// tile of HT query heads of one KV head).  The waves load each 32-token K/V
-// tile once, together, into LDS (double-buffered, one barrier per tile), so the
-// L2 traffic per flop is an eighth of one wave working alone (measured best
-// of 4, 8, 16 waves and 16, 32, 64-token tiles on MI355X).  Each wave's 16
-// "columns" are (query, head) pairs, column c = (query wj0 + c / HT, head
-// h0 + c % HT).  Per 16 tokens:
+// One workgroup of 8 waves per work item (request, block of 8 * 2 * 16/HT
+// queries, tile of HT query heads of one KV head).  The waves load each
+// 64-token K/V tile once, together, into LDS (double-buffered, one barrier per
+// tile), so the L2 traffic per flop is an eighth of one wave working alone.
+// Measured on MI355X: 8 waves beat 4 and 16, and 64-token tiles beat 32 (half
+// the barriers; every wave of the workgroup reaches each barrier).
+// Each wave holds two sets of 16 "columns", (query, head) pairs: column c of
+// set cs = (query wj0 + cs * 16/HT + c / HT, head h0 + c % HT).  Every K or V
+// fragment a wave reads from LDS feeds one MFMA per set, which halves the LDS
+// bytes per flop (LDS bandwidth, not the matrix cores, bounded one set).  Per
+// 16 tokens and set:
 //
 //   S^T[t][c] = sum_d K[t][d] Q[c][d]     v_mfma_f32_16x16x32_f16, D/32 steps
-//   O[c][d]  += sum_t P[c][t] V[t][d]     v_mfma_f32_16x16x16_f16, D/16 blocks
+//
+// and per 32 tokens and set
+//
+//   O[c][d]  += sum_t P[c][t] V[t][d]     v_mfma_f32_16x16x32_f16, D/16 blocks
 //
 // with the operand layouts of the decode kernel for head groups
 // (pa_decode_mfma.hip): K read from LDS in the A layout, V through
-// ds_read_b64_tr_b16, P from the S^T output layout rounded to fp16.  Column c
+// ds_read_b64_tr_b16 (two 4-token reads per operand), P from the S^T output
+// layout rounded to fp16.  Column c
 // masks every token past its own position, and a wave skips 16-token steps
 // that lie wholly past its queries.  One pass, no split: the group walks
 // tokens [0, last position of its block + 1).
@@ -78,17 +86,23 @@ __device__ __forceinline__ uint4 load_shared(const uint4* ptr) { return *ptr; }
 #define PKV_PREFILL_WAVES 8
 #endif
 #ifndef PKV_PREFILL_TILE
-#define PKV_PREFILL_TILE 32
+#define PKV_PREFILL_TILE 64
+#endif
+#ifndef PKV_PREFILL_SETS
+#define PKV_PREFILL_SETS 2
 #endif
 constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // waves per workgroup, sharing K/V tiles
+constexpr int kPrefillSets = PKV_PREFILL_SETS;     // 16-column sets per wave, sharing LDS reads
 
 template <int D, int B, int HT>
 __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(PrefillParams p) {
   constexpr int NW = kPrefillWaves;
+  constexpr int NS = kPrefillSets;
   constexpr int NT = kWave * NW;             // threads
   constexpr int KT = PKV_PREFILL_TILE;       // tokens per tile (KT/16 MFMA steps)
   constexpr int SUB = KT / 16;
-  constexpr int QB = 16 / HT;                // queries per wave
+  constexpr int QB = 16 / HT;                // queries per set
+  constexpr int QW = NS * QB;                // queries per wave
   constexpr int KSTEPS = D / 32;
   constexpr int DBLK = D / 16;
   constexpr int CPR = D / 8;                 // 16-byte chunks per token row
@@ -100,6 +114,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
   static_assert(LPT * NT == KT * CPR || (LPT == 1 && NT % (KT * CPR) == 0), "tile shape");
   static_assert(TPC >= 1 && TPC * KT == kWave * B, "chunk shape");
   static_assert(HT == 1 || HT == 2 || HT == 4 || HT == 8 || HT == 16, "head tile");
+  static_assert(SUB % 2 == 0, "P.V takes 32 tokens per MFMA: tiles of a multiple of 32 tokens");
   __shared__ __align__(16) unsigned char klds[2][KT * KROWB];
   __shared__ __align__(16) unsigned char vlds[2][KT * VROWB];
   __shared__ __align__(4) unsigned char rowok[2][KT];
@@ -125,34 +140,40 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
   int len = p.context_lens[seq];
   const int cap = p.max_blocks_per_seq * B;
   len = len < 0 ? 0 : (len > cap ? cap : len);
-  const int j0 = sblk * NW * QB;
+  const int j0 = sblk * NW * QW;
   if (j0 >= nq) return;
   const int base_pos = len - nq;             // position of query 0
-  // This wave's queries and this lane's column (query cj, head ch, last visible token pos).
-  const int wj0 = j0 + wave * QB;
-  const int wave_pos_max = wj0 < nq ? base_pos + min(wj0 + QB, nq) - 1 : -1;
-  const int cj = wj0 + li / HT;
+  // This wave's queries; per set, this lane's column (query cj, head ch, last visible token pos).
+  const int wj0 = j0 + wave * QW;
+  const int wave_pos_max = wj0 < nq ? base_pos + min(wj0 + QW, nq) - 1 : -1;
   const int ch = h0 + li % HT;
-  const bool col_ok = cj < nq;
-  const int pos = col_ok ? base_pos + cj : -1;
-
-  half8 qb[KSTEPS];
-  {
+  int pos[NS];
+  half8 qb[NS][KSTEPS];
+#pragma unroll
+  for (int cs = 0; cs < NS; ++cs) {
+    const int cj = wj0 + cs * QB + li / HT;
+    const bool col_ok = cj < nq;
+    pos[cs] = col_ok ? base_pos + cj : -1;
     const _Float16* qp =
         p.q + (static_cast<int64_t>(q_first + (col_ok ? cj : 0)) * p.num_q_heads + ch) * D + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      const half8 v = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(qp + kk * 32));
-      qb[kk] = col_ok ? v : half8{};
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + kk * 32);
+      const unsigned mask = col_ok ? 0xFFFFFFFFu : 0u;     // component-wise: no aggregate select
+      qb[cs][kk] = __builtin_bit_cast(half8, make_uint4(v.x & mask, v.y & mask, v.z & mask, v.w & mask));
     }
   }
-  const int t_end = min(len, base_pos + min(j0 + NW * QB, nq));   // tokens the group reads
+  const int t_end = min(len, base_pos + min(j0 + NW * QW, nq));   // tokens the group reads
 
-  float4_t o[DBLK];
+  float4_t o[NS][DBLK];
+  float m[NS], lsum[NS];
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db) o[db] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -FLT_MAX;
-  float lsum = 0.f;
+  for (int cs = 0; cs < NS; ++cs) {
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[cs][db] = float4_t{0.f, 0.f, 0.f, 0.f};
+    m[cs] = -FLT_MAX;
+    lsum[cs] = 0.f;
+  }
 
   if (t_end > 0) {
     const int ntiles = (t_end + KT - 1) / KT;
@@ -205,77 +226,100 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
         if (c % CPR == 0) rowok[u][r] = rg.ok[it] ? 1 : 0;
       }
     };
-    // One wave's 16 columns against the KT-token tile in buffer u: every 16-token
-    // score step first, then one max exchange and one softmax update for the tile.
+    // One wave's column sets against the KT-token tile in buffer u: every 16-token
+    // score step first (each K fragment feeding every set), then per set one max
+    // exchange and one softmax update for the tile, then P.V (each V fragment
+    // feeding every set).
     auto compute = [&](int u, int jt) __attribute__((always_inline)) {
       const int tok0 = jt * KT;
       if (tok0 > wave_pos_max) return;       // every column of this wave is past here
-      float4_t s[SUB];
+      float4_t s[NS][SUB];
 #pragma unroll
       for (int sub = 0; sub < SUB; ++sub) {
-        s[sub] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cs = 0; cs < NS; ++cs) s[cs][sub] = float4_t{0.f, 0.f, 0.f, 0.f};
         if (sub > 0 && tok0 + sub * 16 > wave_pos_max) continue;   // step wholly masked
         const unsigned char* krow = &klds[u][(sub * 16 + li) * KROWB + grp * 16];
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(krow + kk * 64);
-          s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, kv), qb[kk],
-                                                         s[sub], 0, 0, 0);
+          const half8 kv = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(krow + kk * 64));
+#pragma unroll
+          for (int cs = 0; cs < NS; ++cs)
+            s[cs][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qb[cs][kk], s[cs][sub], 0, 0, 0);
         }
       }
-      float sr[SUB][4];
+      unsigned ok4[SUB];                     // rows 4*grp .. 4*grp+3 of each step: validity flags
 #pragma unroll
-      for (int sub = 0; sub < SUB; ++sub) {
-        // rows 4*grp .. 4*grp+3 of this step: their validity flags as one word
-        const unsigned ok4 = *reinterpret_cast<const unsigned*>(&rowok[u][sub * 16 + 4 * grp]);
+      for (int sub = 0; sub < SUB; ++sub)
+        ok4[sub] = *reinterpret_cast<const unsigned*>(&rowok[u][sub * 16 + 4 * grp]);
+      half4 pa[NS][SUB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = tok0 + sub * 16 + 4 * grp + r;
-          const bool vis = ((ok4 >> (8 * r)) & 0xFFu) != 0 && t <= pos;
-          sr[sub][r] = vis ? s[sub][r] * p.scale_log2 : -INFINITY;
+      for (int cs = 0; cs < NS; ++cs) {
+        float sr[SUB][4];
+#pragma unroll
+        for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = tok0 + sub * 16 + 4 * grp + r;
+            const bool vis = ((ok4[sub] >> (8 * r)) & 0xFFu) != 0 && t <= pos[cs];
+            sr[sub][r] = vis ? s[cs][sub][r] * p.scale_log2 : -INFINITY;
+          }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int sub = 0; sub < SUB; ++sub)
+          mt = fmaxf(mt, fmaxf(fmaxf(sr[sub][0], sr[sub][1]), fmaxf(sr[sub][2], sr[sub][3])));
+        mt = fmaxf(mt, shfl_xor(mt, 16));
+        mt = fmaxf(mt, shfl_xor(mt, 32));
+        const bool moved = mt > m[cs] + kSlack;
+        const float m_new = moved ? mt : m[cs];
+        float pr[SUB][4];
+#pragma unroll
+        for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pr[sub][r] = fast_exp2(sr[sub][r] - m_new);
+        if (__builtin_amdgcn_ballot_w64(moved)) {
+          const float alpha = fast_exp2(m[cs] - m_new);
+          lsum[cs] *= alpha;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ar = shfl(alpha, 4 * grp + r);
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) o[cs][db][r] *= ar;
+          }
         }
-      }
-      float mt = -INFINITY;
 #pragma unroll
-      for (int sub = 0; sub < SUB; ++sub)
-        mt = fmaxf(mt, fmaxf(fmaxf(sr[sub][0], sr[sub][1]), fmaxf(sr[sub][2], sr[sub][3])));
-      mt = fmaxf(mt, shfl_xor(mt, 16));
-      mt = fmaxf(mt, shfl_xor(mt, 32));
-      const bool moved = mt > m + kSlack;
-      const float m_new = moved ? mt : m;
-      float pr[SUB][4];
-#pragma unroll
-      for (int sub = 0; sub < SUB; ++sub)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pr[sub][r] = fast_exp2(sr[sub][r] - m_new);
-      if (__builtin_amdgcn_ballot_w64(moved)) {
-        const float alpha = fast_exp2(m - m_new);
-        lsum *= alpha;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = shfl(alpha, 4 * grp + r);
-#pragma unroll
-          for (int db = 0; db < DBLK; ++db) o[db][r] *= ar;
+        for (int sub = 0; sub < SUB; ++sub) {
+          lsum[cs] += (pr[sub][0] + pr[sub][1]) + (pr[sub][2] + pr[sub][3]);
+          pa[cs][sub] = half4{static_cast<_Float16>(pr[sub][0]), static_cast<_Float16>(pr[sub][1]),
+                              static_cast<_Float16>(pr[sub][2]), static_cast<_Float16>(pr[sub][3])};
         }
+        m[cs] = m_new;
       }
+      // P.V over 32 tokens per MFMA (the double-rate 16x16x32 form): slots 0-3 of a
+      // lane's operand are tokens 4*grp..4*grp+3 of one 16-token step, slots 4-7
+      // the same rows of the next step, in A (probabilities) and B (transposed V)
+      // alike, so the sum over k pairs each probability with its own V row.
+      typedef __attribute__((address_space(3))) short4_t lds_short4;
 #pragma unroll
-      for (int sub = 0; sub < SUB; ++sub)
-        lsum += (pr[sub][0] + pr[sub][1]) + (pr[sub][2] + pr[sub][3]);
-      m = m_new;
+      for (int sp = 0; sp < SUB; sp += 2) {
+        const unsigned char* src0 =
+            &vlds[u][(sp * 16 + 4 * grp + (li >> 2)) * VROWB + 8 * (li & 3)];
+        const unsigned char* src1 = src0 + 16 * VROWB;
+        half8 pa8[NS];
 #pragma unroll
-      for (int sub = 0; sub < SUB; ++sub) {
-        if (sub > 0 && tok0 + sub * 16 > wave_pos_max) continue;
-        const half4 pa = half4{static_cast<_Float16>(pr[sub][0]), static_cast<_Float16>(pr[sub][1]),
-                               static_cast<_Float16>(pr[sub][2]), static_cast<_Float16>(pr[sub][3])};
-        const unsigned char* src =
-            &vlds[u][(sub * 16 + 4 * grp + (li >> 2)) * VROWB + 8 * (li & 3)];
+        for (int cs = 0; cs < NS; ++cs)
+          pa8[cs] = half8{pa[cs][sp][0], pa[cs][sp][1], pa[cs][sp][2], pa[cs][sp][3],
+                          pa[cs][sp + 1][0], pa[cs][sp + 1][1], pa[cs][sp + 1][2], pa[cs][sp + 1][3]};
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-          typedef __attribute__((address_space(3))) short4_t lds_short4;
-          const short4_t raw =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src + 32 * db));
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(half4, raw), o[db],
-                                                        0, 0, 0);
+          const half4 v0 = __builtin_bit_cast(
+              half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src0 + 32 * db)));
+          const half4 v1 = __builtin_bit_cast(
+              half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src1 + 32 * db)));
+          const half8 vf = half8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+          for (int cs = 0; cs < NS; ++cs)
+            o[cs][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], vf, o[cs][db], 0, 0, 0);
         }
       }
     };
@@ -297,21 +341,24 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
     if (jt < ntiles) step(ra, 0, jt);
   }
 
-  // Denominator of column li, then each lane's output rows: columns 4*grp + r.
-  float l = lsum + shfl_xor(lsum, 16);
-  l = l + shfl_xor(l, 32);
-  float lr[4];
+  // Per set: denominator of column li, then each lane's output rows, columns 4*grp + r.
 #pragma unroll
-  for (int r = 0; r < 4; ++r) lr[r] = shfl(l, 4 * grp + r);
+  for (int cs = 0; cs < NS; ++cs) {
+    float l = lsum[cs] + shfl_xor(lsum[cs], 16);
+    l = l + shfl_xor(l, 32);
+    float lr[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int c = 4 * grp + r;
-    const int qj = wj0 + c / HT;
-    if (qj >= nq) continue;
-    const float inv = lr[r] > 0.f ? 1.f / lr[r] : 0.f;   // a query with no token: zeros
-    float* dst = p.out + (static_cast<int64_t>(q_first + qj) * p.num_q_heads + h0 + c % HT) * D;
+    for (int r = 0; r < 4; ++r) lr[r] = shfl(l, 4 * grp + r);
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) dst[db * 16 + li] = o[db][r] * inv;
+    for (int r = 0; r < 4; ++r) {
+      const int c = 4 * grp + r;
+      const int qj = wj0 + cs * QB + c / HT;
+      if (qj >= nq) continue;
+      const float inv = lr[r] > 0.f ? 1.f / lr[r] : 0.f;   // a query with no token: zeros
+      float* dst = p.out + (static_cast<int64_t>(q_first + qj) * p.num_q_heads + h0 + c % HT) * D;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) dst[db * 16 + li] = o[cs][db][r] * inv;
+    }
   }
 }
 
@@ -360,7 +407,7 @@ using namespace pkv_decode;
 extern "C" int32_t pa_prefill_queries_per_item(int32_t num_q_heads, int32_t num_kv_heads) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
   const int ht = head_tile_for(num_q_heads / num_kv_heads);
-  return ht > 0 ? kPrefillWaves * 16 / ht : 0;
+  return ht > 0 ? kPrefillWaves * kPrefillSets * 16 / ht : 0;
 }
 
 extern "C" int pa_prefill_plan(const int32_t* q_lens, const int32_t* context_lens,

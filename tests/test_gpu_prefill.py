@@ -84,7 +84,7 @@ def test_prefill_plan_covers_blocks_largest_first():
     print("\n[case] prefill plan", flush=True)
     qlens, lens = [40, 0, 7, 33], [300, 5, 7, 33]
     qb = int(_lib.lib().pa_prefill_queries_per_item(32, 8))
-    assert qb == 32                    # 8 waves x 16 columns / 4 heads per KV head
+    assert qb == 64                    # 8 waves x 2 sets x 16 columns / 4 heads per KV head
     items = _lib.prefill_plan(qlens, lens, 32, 8)
     blocks = [(int(x) >> 16, int(x) & 0xFFFF) for x in items]
     want = sorted((s, b) for s, n in enumerate(qlens) for b in range(-(-n // qb)))
