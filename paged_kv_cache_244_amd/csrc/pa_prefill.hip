@@ -35,7 +35,9 @@
 // with the operand layouts of the decode kernel for head groups
 // (pa_decode_mfma.hip): K read from LDS in the A layout, V through
 // ds_read_b64_tr_b16 (two 4-token reads per operand), P from the S^T output
-// layout rounded to fp16.  Column c
+// layout rounded to fp16.  The softmax denominators come from the matrix cores
+// too: the same P times a block of ones, so numerator and denominator sum the
+// same rounded weights and no lane adds scores on the vector ALUs.  Column c
 // masks every token past its own position, and a wave skips 16-token steps
 // that lie wholly past its queries.  One pass, no split: the group walks
 // tokens [0, last position of its block + 1).
@@ -146,6 +148,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
   // This wave's queries; per set, this lane's column (query cj, head ch, last visible token pos).
   const int wj0 = j0 + wave * QW;
   const int wave_pos_max = wj0 < nq ? base_pos + min(wj0 + QW, nq) - 1 : -1;
+  const int wave_pos_min = base_pos + wj0;   // every column of the wave sees tokens up to here
   const int ch = h0 + li % HT;
   int pos[NS];
   half8 qb[NS][KSTEPS];
@@ -165,15 +168,18 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
   }
   const int t_end = min(len, base_pos + min(j0 + NW * QW, nq));   // tokens the group reads
 
-  float4_t o[NS][DBLK];
-  float m[NS], lsum[NS];
+  // o: numerators; den: denominators, the same P times a block of ones (every
+  // lane's row r of den[cs] holds the sum for column 4*grp + r of set cs).
+  float4_t o[NS][DBLK], den[NS];
+  float m[NS];
 #pragma unroll
   for (int cs = 0; cs < NS; ++cs) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) o[cs][db] = float4_t{0.f, 0.f, 0.f, 0.f};
+    den[cs] = float4_t{0.f, 0.f, 0.f, 0.f};
     m[cs] = -FLT_MAX;
-    lsum[cs] = 0.f;
   }
+  const half8 ones = half8{1, 1, 1, 1, 1, 1, 1, 1};
 
   if (t_end > 0) {
     const int ntiles = (t_end + KT - 1) / KT;
@@ -248,51 +254,58 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
             s[cs][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qb[cs][kk], s[cs][sub], 0, 0, 0);
         }
       }
-      unsigned ok4[SUB];                     // rows 4*grp .. 4*grp+3 of each step: validity flags
+      // Masking is needed only where some column of this wave sees part of the tile
+      // (the diagonal) or some row is not a valid token (the last tile): elsewhere
+      // every score enters as it is.
+      const bool masked = tok0 + KT - 1 > wave_pos_min || tok0 + KT > t_end;
+      if (masked) {
+        unsigned ok4[SUB];                   // rows 4*grp .. 4*grp+3 of each step: validity flags
 #pragma unroll
-      for (int sub = 0; sub < SUB; ++sub)
-        ok4[sub] = *reinterpret_cast<const unsigned*>(&rowok[u][sub * 16 + 4 * grp]);
+        for (int sub = 0; sub < SUB; ++sub)
+          ok4[sub] = *reinterpret_cast<const unsigned*>(&rowok[u][sub * 16 + 4 * grp]);
+#pragma unroll
+        for (int cs = 0; cs < NS; ++cs)
+#pragma unroll
+          for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = tok0 + sub * 16 + 4 * grp + r;
+              const bool vis = ((ok4[sub] >> (8 * r)) & 0xFFu) != 0 && t <= pos[cs];
+              s[cs][sub][r] = vis ? s[cs][sub][r] : -INFINITY;
+            }
+      }
       half4 pa[NS][SUB];
 #pragma unroll
       for (int cs = 0; cs < NS; ++cs) {
-        float sr[SUB][4];
-#pragma unroll
-        for (int sub = 0; sub < SUB; ++sub)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = tok0 + sub * 16 + 4 * grp + r;
-            const bool vis = ((ok4[sub] >> (8 * r)) & 0xFFu) != 0 && t <= pos[cs];
-            sr[sub][r] = vis ? s[cs][sub][r] * p.scale_log2 : -INFINITY;
-          }
+        // Maximum of the raw scores (the scale is positive), then in log2 units.
         float mt = -INFINITY;
 #pragma unroll
         for (int sub = 0; sub < SUB; ++sub)
-          mt = fmaxf(mt, fmaxf(fmaxf(sr[sub][0], sr[sub][1]), fmaxf(sr[sub][2], sr[sub][3])));
+          mt = fmaxf(mt, fmaxf(fmaxf(s[cs][sub][0], s[cs][sub][1]), fmaxf(s[cs][sub][2], s[cs][sub][3])));
         mt = fmaxf(mt, shfl_xor(mt, 16));
         mt = fmaxf(mt, shfl_xor(mt, 32));
+        mt *= p.scale_log2;
         const bool moved = mt > m[cs] + kSlack;
         const float m_new = moved ? mt : m[cs];
         float pr[SUB][4];
 #pragma unroll
         for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) pr[sub][r] = fast_exp2(sr[sub][r] - m_new);
+          for (int r = 0; r < 4; ++r) pr[sub][r] = fast_exp2(fmaf(s[cs][sub][r], p.scale_log2, -m_new));
         if (__builtin_amdgcn_ballot_w64(moved)) {
           const float alpha = fast_exp2(m[cs] - m_new);
-          lsum[cs] *= alpha;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float ar = shfl(alpha, 4 * grp + r);
+            den[cs][r] *= ar;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) o[cs][db][r] *= ar;
           }
         }
 #pragma unroll
-        for (int sub = 0; sub < SUB; ++sub) {
-          lsum[cs] += (pr[sub][0] + pr[sub][1]) + (pr[sub][2] + pr[sub][3]);
+        for (int sub = 0; sub < SUB; ++sub)
           pa[cs][sub] = half4{static_cast<_Float16>(pr[sub][0]), static_cast<_Float16>(pr[sub][1]),
                               static_cast<_Float16>(pr[sub][2]), static_cast<_Float16>(pr[sub][3])};
-        }
         m[cs] = m_new;
       }
       // P.V over 32 tokens per MFMA (the double-rate 16x16x32 form): slots 0-3 of a
@@ -310,6 +323,9 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
         for (int cs = 0; cs < NS; ++cs)
           pa8[cs] = half8{pa[cs][sp][0], pa[cs][sp][1], pa[cs][sp][2], pa[cs][sp][3],
                           pa[cs][sp + 1][0], pa[cs][sp + 1][1], pa[cs][sp + 1][2], pa[cs][sp + 1][3]};
+#pragma unroll
+        for (int cs = 0; cs < NS; ++cs)
+          den[cs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], ones, den[cs], 0, 0, 0);
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
           const half4 v0 = __builtin_bit_cast(
@@ -341,20 +357,15 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
     if (jt < ntiles) step(ra, 0, jt);
   }
 
-  // Per set: denominator of column li, then each lane's output rows, columns 4*grp + r.
+  // Per set: each lane's output rows, columns 4*grp + r, over their denominators.
 #pragma unroll
   for (int cs = 0; cs < NS; ++cs) {
-    float l = lsum[cs] + shfl_xor(lsum[cs], 16);
-    l = l + shfl_xor(l, 32);
-    float lr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lr[r] = shfl(l, 4 * grp + r);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = 4 * grp + r;
       const int qj = wj0 + cs * QB + c / HT;
       if (qj >= nq) continue;
-      const float inv = lr[r] > 0.f ? 1.f / lr[r] : 0.f;   // a query with no token: zeros
+      const float inv = den[cs][r] > 0.f ? 1.f / den[cs][r] : 0.f;   // a query with no token: zeros
       float* dst = p.out + (static_cast<int64_t>(q_first + qj) * p.num_q_heads + h0 + c % HT) * D;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) dst[db * 16 + li] = o[cs][db][r] * inv;
