@@ -1,0 +1,43 @@
+"""kv_swap_blocks argument checks that need no GPU.
+
+Every call here is refused (or is a no-op) before the library touches the HIP
+runtime: bad sizes, geometry that is not built, nothing to copy, NULL pools and
+too many pairs.  The copies themselves are checked on the GPU
+(tests/test_gpu_swap.py).
+"""
+
+import ctypes
+
+from paged_kv_cache_244_amd import _lib
+
+
+def _arr(*ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def _call(dst_blocks=4, src_blocks=4, layers=1, pairs=1, hkv=2, d=64, bs=16, pools=None, pair_ptr=8):
+    pools = pools if pools is not None else [_arr(16)] * 4
+    return _lib.lib().kv_swap_blocks(pools[0], pools[1], dst_blocks, pools[2], pools[3], src_blocks,
+                                     layers, pair_ptr, pairs, hkv, d, bs, None)
+
+
+def test_sizes_and_geometry_are_checked_first():
+    assert _call(dst_blocks=0) == _lib.PKV_ERR_INVALID_ARG
+    assert _call(src_blocks=-1) == _lib.PKV_ERR_INVALID_ARG
+    assert _call(layers=-1) == _lib.PKV_ERR_INVALID_ARG
+    assert _call(pairs=-1) == _lib.PKV_ERR_INVALID_ARG
+    assert _call(hkv=0) == _lib.PKV_ERR_INVALID_ARG
+    assert _call(d=96) == _lib.PKV_ERR_UNSUPPORTED
+    assert _call(bs=12) == _lib.PKV_ERR_UNSUPPORTED
+
+
+def test_nothing_to_copy_is_a_no_op():
+    assert _call(pairs=0, pools=[None] * 4, pair_ptr=None) == _lib.PKV_OK
+    assert _call(layers=0, pools=[None] * 4, pair_ptr=None) == _lib.PKV_OK
+
+
+def test_null_pointers_and_too_many_pairs():
+    assert _call(pools=[None, _arr(16), _arr(16), _arr(16)]) == _lib.PKV_ERR_INVALID_ARG
+    assert _call(pair_ptr=None) == _lib.PKV_ERR_INVALID_ARG
+    assert _call(pairs=65536) == _lib.PKV_ERR_INVALID_ARG
+    assert b"65535" in _lib.lib().pkv_last_error()
