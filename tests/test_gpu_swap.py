@@ -13,7 +13,9 @@ checks:
   swapped back in: decode output bit-identical to before, and within the
   tolerance of the oracle; sharing survives (the group's blocks copied once);
 * a deferred swap-out with a second stream that does not wait: the parked
-  device blocks are not handed to the other request before the copy is done.
+  device blocks are not handed to the other request before the copy is done;
+* the benchmark's set at full size (32 OPT-13B requests, 1,734 blocks) out and
+  back twice: every request's logical K/V bitwise unchanged.
 """
 
 import ctypes
@@ -232,3 +234,47 @@ def test_deferred_swap_out_with_a_second_stream():
     got = _decode_all(c, [x], q, 1.0 / np.sqrt(d), 1)[0][0]
     want = attention.attend_one(q[0].cpu().numpy(), toks[0], toks[1], 1.0 / np.sqrt(d))
     paths.assert_attention_close(got, want)
+
+
+def test_swap_workload_full_size_round_trip():
+    """The benchmark's swap set (every other request of the OPT-13B decode batch,
+    40 x 128 heads, B = 16) out to the host tier and back, twice: every moved
+    request's logical K and V, gathered through its table, are bitwise what they
+    were, and the requests that stayed are untouched."""
+    import torch
+
+    from paged_kv_cache_244_amd import workloads
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    print("\n[case] swap full-size OPT-13B set", flush=True)
+    w = workloads.opt13b()
+    lens = [int(L) for L in w.lengths]
+    bs = w.block_size
+    moved_idx = list(range(0, len(lens), 2))
+    moved_blocks = sum(-(-lens[i] // bs) for i in moved_idx)
+    dev = torch.device("cuda")
+    c = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, bs, initial_order=w.initial_order,
+                     num_q_heads=w.num_q_heads, host_blocks=moved_blocks)
+    seqs = [c.new_sequence() for _ in lens]
+    c.write(c.reserve_many(seqs, lens), torch.from_numpy(w.k_tokens).to(dev),
+            torch.from_numpy(w.v_tokens).to(dev))
+
+    def logical(seq):
+        tables, _ = c.alloc.export([seq], c.alloc.num_blocks, 0)
+        n = c.length(seq)
+        t = torch.arange(n, device=dev)
+        blocks = torch.from_numpy(tables[0]).to(dev).long()[t // bs]
+        return c.k[0][blocks, :, t % bs, :], c.v[0][blocks, :, t % bs, :]
+
+    before = {s: logical(s) for s in seqs}
+    moved = [seqs[i] for i in moved_idx]
+    for _ in range(2):
+        assert c.swap_out(moved) == moved_blocks
+        assert c.swap_in(moved) == moved_blocks
+    torch.cuda.synchronize()
+    for s in seqs:
+        k, v = logical(s)
+        assert torch.equal(k.view(torch.int16), before[s][0].view(torch.int16)), f"request {s}: K"
+        assert torch.equal(v.view(torch.int16), before[s][1].view(torch.int16)), f"request {s}: V"
+    st = c.alloc.stats()
+    assert st["swapped_out_blocks"] == st["swapped_in_blocks"] == 2 * moved_blocks
