@@ -176,9 +176,10 @@ class Scenario:
     def step(self, t, partition, ev_pair, plans):
         cache = self.cache
         layer = t % len(cache.k)            # the pool replica this step writes and reads
-        s, batch = cache.decode_step(self.seqs, self.max_blocks, partition_size=partition)
+        # reserve, tables, plan and the new tokens' write: one host call, one launch
+        _, batch = cache.decode_step(self.seqs, self.max_blocks, partition_size=partition,
+                                     k_new=self.step_k[t], v_new=self.step_v[t], layer=layer)
         plans.append(batch.plan)
-        cache.write(s, self.step_k[t], self.step_v[t], layer=layer)
         if ev_pair is not None:
             ev_pair[0].record(cache.stream)
         cache.attend(self.step_q[t], batch, self.w.scale, layer=layer, out=self.out)

@@ -154,6 +154,26 @@ int kv_swap_blocks(void* const* dst_k, void* const* dst_v, int32_t dst_num_block
 int pkv_upload(void* dst, const void* src, uint64_t bytes, void* stream);
 
 /*
+ * pkv_upload_write — pkv_upload and kv_cache_write of one decode step in one
+ * launch (one kernel boundary fewer per step).  [B] "The page table, relocated
+ * into attention": the step's host-made tables go to the GPU and each new
+ * token lands in its slot.  Part of the launch copies `bytes` from pinned host
+ * memory `src` to device memory `dst` (as pkv_upload); the rest writes the
+ * num_tokens new tokens (as kv_cache_write) reading `slot_mapping` where it
+ * is, which may be device memory or pinned host memory, typically the slots
+ * inside `src` itself (the device copy is made by the same launch, so it must
+ * not be read by it).  The two parts run concurrently: the copy must not
+ * target memory the write reads or writes.  Either part may be empty; both
+ * empty is a no-op.  A step with copy-on-write pairs needs the copies between
+ * the two, so it uses pkv_upload, kv_copy_blocks and kv_cache_write instead.
+ * Errors: as pkv_upload and kv_cache_write.
+ */
+int pkv_upload_write(void* dst, const void* src, uint64_t bytes, void* k_cache, void* v_cache,
+                     int32_t num_blocks, const void* k_new, const void* v_new,
+                     const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, void* stream);
+
+/*
  * Workspace bytes pa_decode needs for a split-context launch (0 when a single
  * partition covers max_context_len, or partition_size == 0).
  */

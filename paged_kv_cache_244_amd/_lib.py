@@ -88,6 +88,9 @@ _SIGNATURES = {
     "kv_copy_blocks": (c_int32, [POINTER(c_void_p), POINTER(c_void_p), c_int32, c_void_p, c_int32,
                                  c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "pkv_upload": (c_int32, [c_void_p, c_void_p, ctypes.c_uint64, c_void_p]),
+    "pkv_upload_write": (c_int32, [c_void_p, c_void_p, ctypes.c_uint64, c_void_p, c_void_p, c_int32,
+                                   c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                   c_void_p]),
     "kv_swap_blocks": (c_int32, [POINTER(c_void_p), POINTER(c_void_p), c_int32, POINTER(c_void_p),
                                  POINTER(c_void_p), c_int32, c_int32, c_void_p, c_int32, c_int32,
                                  c_int32, c_int32, c_void_p]),

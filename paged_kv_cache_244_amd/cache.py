@@ -55,14 +55,21 @@ class _Staging:
             self.host[i] = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
         return i
 
-    def _send(self, i, total, stream):
+    def _send(self, i, total, stream, write=None):
+        """Copy ``total`` bytes of ring slot i to the device buffer.  ``write`` (a
+        callable taking the device buffer's address and the pinned slot) replaces the
+        plain copy with one launch that also writes the step's new tokens."""
         if self.dev.numel() < total:
             self.dev = torch.empty(total, dtype=torch.uint8, device=self.device)
         if total:
             # A library kernel reads the pinned buffer over the bus: no copy-engine
             # hand-off between the step's kernels.
-            _lib._check(_lib.lib().pkv_upload(self.dev.data_ptr(), self.host[i].data_ptr(),
-                                              (total + 15) // 16 * 16, stream.cuda_stream))
+            nbytes = (total + 15) // 16 * 16
+            if write is None:
+                _lib._check(_lib.lib().pkv_upload(self.dev.data_ptr(), self.host[i].data_ptr(),
+                                                  nbytes, stream.cuda_stream))
+            else:
+                write(self.dev.data_ptr(), self.host[i].data_ptr(), nbytes)
             ev = torch.cuda.Event()
             ev.record(stream)
             self.events[i] = ev
@@ -85,10 +92,12 @@ class _Staging:
             views.append(t.view(a.shape))
         return views
 
-    def fill_and_upload(self, fill, stream):
+    def fill_and_upload(self, fill, stream, write=None):
         """``fill(host_ptr, capacity)`` writes the host buffer in place and returns the
         bytes used, or None with ``needed`` bytes to retry with.  Returns
-        (result of fill, device buffer, pinned host buffer) after one asynchronous copy."""
+        (result of fill, device buffer, pinned host buffer) after one asynchronous copy.
+        ``write(result)``, if given, returns the fused copy-and-write for ``_send`` (or
+        None for a plain copy)."""
         i = self._slot(0)
         while True:
             host = self.host[i]
@@ -97,7 +106,8 @@ class _Staging:
                 break
             self.host[i] = torch.empty(max(fill.needed, 2 * host.numel()), dtype=torch.uint8,
                                        pin_memory=True)
-        return res, self._send(i, int(res.total_bytes), stream), self.host[i]
+        fused = write(res) if write is not None else None
+        return res, self._send(i, int(res.total_bytes), stream, fused), self.host[i]
 
 
 _TORCH_DTYPE = {"i4": torch.int32, "i8": torch.int64, "f4": torch.float32, "f2": torch.float16}
@@ -300,10 +310,14 @@ class PagedKVCache:
         self._copy_pairs_dev(pairs_dev)
         return slots_dev
 
-    def decode_step(self, seqs, max_blocks=None, partition_size="auto"):
+    def decode_step(self, seqs, max_blocks=None, partition_size="auto", k_new=None, v_new=None,
+                    layer=0):
         """One decode step's host work in one library call and one upload: reserve one
         slot per sequence (issuing copy-on-write copies), export tables and lengths and
-        plan the launch (``kv_decode_step_host``).  Returns (device slots, DecodeBatch)."""
+        plan the launch (``kv_decode_step_host``).  With ``k_new``/``v_new`` ([S, kv_heads,
+        head_dim] fp16 device tensors) the new tokens are written into ``layer`` too; a
+        step without copy-on-write copies does the upload and the write in one launch
+        (``pkv_upload_write``).  Returns (device slots, DecodeBatch)."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
         if self._pending:
             self.retire()
@@ -319,8 +333,27 @@ class PagedKVCache:
                 fill.needed = alloc.needed
             return lay
 
-        lay, dev, host = self._staging.fill_and_upload(fill, self.stream)
         n = int(seqs.shape[0])
+        if k_new is not None:
+            want = (n, self.num_kv_heads, self.head_dim)
+            for x in (k_new, v_new):
+                if (x is None or tuple(x.shape) != want or x.dtype != torch.float16 or not x.is_cuda
+                        or not x.is_contiguous()):
+                    raise ValueError(f"k_new/v_new must be contiguous device fp16 {want}")
+
+        def fused(lay):
+            if k_new is None or lay.num_pairs:
+                return None                  # copy-on-write copies go between upload and write
+
+            def launch(dev_ptr, host_ptr, nbytes):
+                _lib._check(_lib.lib().pkv_upload_write(
+                    dev_ptr, host_ptr, nbytes, self.k[layer].data_ptr(), self.v[layer].data_ptr(),
+                    self.num_blocks, k_new.data_ptr(), v_new.data_ptr(),
+                    host_ptr + lay.slots_offset, n, self.num_kv_heads, self.head_dim,
+                    self.block_size, self._stream_ptr))
+            return launch
+
+        lay, dev, host = self._staging.fill_and_upload(fill, self.stream, fused)
         lens_host = host[lay.lens_offset:lay.lens_offset + 4 * n].numpy().view(np.int32).copy()
         if lay.num_pairs:
             _lib.kv_copy_blocks(self.k, self.v, DeviceArray(dev, lay.pairs_offset, torch.int32,
@@ -328,6 +361,8 @@ class PagedKVCache:
                                 stream=self.stream)
         plan = {name: int(getattr(lay.plan, name)) for name, _ in _lib.DecodePlan._fields_}
         slots = DeviceArray(dev, lay.slots_offset, torch.int64, (n,))
+        if k_new is not None and lay.num_pairs:
+            self.write(slots, k_new, v_new, layer=layer)
         batch = DecodeBatch(DeviceArray(dev, lay.tables_offset, torch.int32, (n, lay.max_blocks)),
                             DeviceArray(dev, lay.lens_offset, torch.int32, (n,)),
                             int(lay.max_context_len), lens_host,

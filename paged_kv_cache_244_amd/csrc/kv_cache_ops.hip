@@ -15,7 +15,8 @@
 // work items) read by a kernel straight from pinned host memory and stored in
 // device memory, on the caller's stream.  Same page, section "The page table,
 // relocated into attention": the tables are made on the host and must be in
-// GPU memory before the kernel walks them.
+// GPU memory before the kernel walks them.  pkv_upload_write does that copy and
+// the step's kv_cache_write in one launch.
 // kv_swap_blocks: "The KV cache is a systems problem" (rsw.lol), section
 // "Eviction and reuse can move costs elsewhere" — evicted blocks moved to a
 // pool in pinned host memory and back, block by block, by the same copy kernel
@@ -43,14 +44,15 @@ bool supported_geometry(int32_t head_dim, int32_t block_size) {
 }
 
 // One thread moves one 16-byte chunk (8 halves) of one token's K and V.
-// chunk index = token * chunks_per_token + head * chunks_per_row + d8.
-__global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(
+// chunk index = token * chunks_per_token + head * chunks_per_row + d8.  Workgroup
+// `wg` of `nwg` takes chunks wg * kThreads + lane, then every nwg * kThreads.
+__device__ __forceinline__ void write_chunks(
     uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, const uint4* __restrict__ k_new,
     const uint4* __restrict__ v_new, const int64_t* __restrict__ slot_mapping, int64_t total_chunks,
-    int32_t chunks_per_token, int32_t chunks_per_row, int32_t block_size, int64_t num_slots) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total_chunks;
-       idx += stride) {
+    int32_t chunks_per_token, int32_t chunks_per_row, int32_t block_size, int64_t num_slots,
+    int64_t wg, int64_t nwg) {
+  const int64_t stride = nwg * kThreads;
+  for (int64_t idx = wg * kThreads + threadIdx.x; idx < total_chunks; idx += stride) {
     const int64_t token = idx / chunks_per_token;
     const int32_t c = static_cast<int32_t>(idx - token * chunks_per_token);
     const int64_t slot = slot_mapping[token];
@@ -67,15 +69,44 @@ __global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(
   }
 }
 
+__global__ __launch_bounds__(kThreads) void kv_cache_write_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, const uint4* __restrict__ k_new,
+    const uint4* __restrict__ v_new, const int64_t* __restrict__ slot_mapping, int64_t total_chunks,
+    int32_t chunks_per_token, int32_t chunks_per_row, int32_t block_size, int64_t num_slots) {
+  write_chunks(k_cache, v_cache, k_new, v_new, slot_mapping, total_chunks, chunks_per_token,
+               chunks_per_row, block_size, num_slots, blockIdx.x, gridDim.x);
+}
+
 // Host-to-device copy as a kernel: 16 bytes per lane, grid-stride.  The loads
 // cross PCIe (the source is pinned host memory the GPU can address); running
 // on the compute queue keeps the step's kernels free of copy-engine handoffs.
+__device__ __forceinline__ void copy16(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                       int64_t n16, int64_t wg, int64_t nwg) {
+  const int64_t stride = nwg * kThreads;
+  for (int64_t i = wg * kThreads + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 __global__ __launch_bounds__(kThreads) void upload_kernel(uint4* __restrict__ dst,
                                                           const uint4* __restrict__ src,
                                                           int64_t n16) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16; i += stride)
-    dst[i] = src[i];
+  copy16(dst, src, n16, blockIdx.x, gridDim.x);
+}
+
+// The upload and the write of a decode step in one launch: workgroups
+// [0, up_wgs) copy the step buffer, the rest write the new tokens, reading their
+// slots from the pinned buffer itself (its device copy is being made by this
+// same launch).  One launch instead of two saves a kernel boundary per step.
+__global__ __launch_bounds__(kThreads) void upload_write_kernel(
+    uint4* __restrict__ dst, const uint4* __restrict__ src, int64_t n16, int32_t up_wgs,
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, const uint4* __restrict__ k_new,
+    const uint4* __restrict__ v_new, const int64_t* __restrict__ slot_mapping, int64_t total_chunks,
+    int32_t chunks_per_token, int32_t chunks_per_row, int32_t block_size, int64_t num_slots) {
+  if (static_cast<int32_t>(blockIdx.x) < up_wgs) {
+    copy16(dst, src, n16, blockIdx.x, up_wgs);
+  } else {
+    write_chunks(k_cache, v_cache, k_new, v_new, slot_mapping, total_chunks, chunks_per_token,
+                 chunks_per_row, block_size, num_slots, blockIdx.x - up_wgs, gridDim.x - up_wgs);
+  }
 }
 
 constexpr int kMaxLayersPerLaunch = 32;
@@ -288,4 +319,59 @@ extern "C" int pkv_upload(void* dst, const void* src, uint64_t bytes, void* stre
                      static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
                      reinterpret_cast<const uint4*>(dev_src), n16);
   return hip_status("pkv_upload launch");
+}
+
+extern "C" int pkv_upload_write(void* dst, const void* src, uint64_t bytes, void* k_cache,
+                                void* v_cache, int32_t num_blocks, const void* k_new,
+                                const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_upload_write: bad sizes (tokens %d, blocks %d, heads %d)",
+                num_tokens, num_blocks, num_kv_heads);
+  if (!supported_geometry(head_dim, block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_upload_write: head_dim %d / block_size %d not built",
+                head_dim, block_size);
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(src) % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_upload_write: pointers and size must be multiples of 16");
+  if (bytes == 0 && num_tokens == 0) return PKV_OK;
+  const char* dev_src = nullptr;
+  if (bytes > 0) {
+    if (!dst || !src) return fail(PKV_ERR_INVALID_ARG, "pkv_upload_write: NULL buffer");
+    bool src_host = false, dst_host = true;
+    dev_src = static_cast<const char*>(kernel_address(src, &src_host));
+    if (!dev_src || !src_host)
+      return fail(PKV_ERR_INVALID_ARG, "pkv_upload_write: source is not pinned host memory");
+    if (!kernel_address(dst, &dst_host) || dst_host)
+      return fail(PKV_ERR_INVALID_ARG, "pkv_upload_write: destination is not device memory");
+    if (reinterpret_cast<uintptr_t>(dev_src) % 16 != 0)
+      return fail(PKV_ERR_INVALID_ARG, "pkv_upload_write: device address of the source is misaligned");
+  }
+  const int64_t* dev_slots = nullptr;
+  if (num_tokens > 0) {
+    if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+      return fail(PKV_ERR_INVALID_ARG, "pkv_upload_write: NULL pointer");
+    bool slots_host = false;
+    dev_slots = static_cast<const int64_t*>(kernel_address(slot_mapping, &slots_host));
+    if (!dev_slots)
+      return fail(PKV_ERR_INVALID_ARG,
+                  "pkv_upload_write: slot_mapping is neither device memory nor pinned host memory");
+  }
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  int64_t up = (n16 + kThreads - 1) / kThreads;
+  if (up > 1024) up = 1024;
+  const int32_t chunks_per_row = head_dim / 8;
+  const int32_t chunks_per_token = num_kv_heads * chunks_per_row;
+  const int64_t total = static_cast<int64_t>(num_tokens) * chunks_per_token;
+  int64_t wr = (total + kThreads - 1) / kThreads;
+  if (wr > 65536 * 16) wr = 65536 * 16;
+  hipLaunchKernelGGL(upload_write_kernel, dim3(static_cast<unsigned>(up + wr)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
+                     reinterpret_cast<const uint4*>(dev_src), n16, static_cast<int32_t>(up),
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), dev_slots,
+                     total, chunks_per_token, chunks_per_row, block_size,
+                     static_cast<int64_t>(num_blocks) * block_size);
+  return hip_status("pkv_upload_write launch");
 }
