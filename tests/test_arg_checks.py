@@ -1,4 +1,4 @@
-"""kv_swap_blocks argument checks that need no GPU.
+"""kv_swap_blocks and pkv_upload_write argument checks that need no GPU.
 
 Every call here is refused (or is a no-op) before the library touches the HIP
 runtime: bad sizes, geometry that is not built, nothing to copy, NULL pools and
@@ -41,3 +41,23 @@ def test_null_pointers_and_too_many_pairs():
     assert _call(pair_ptr=None) == _lib.PKV_ERR_INVALID_ARG
     assert _call(pairs=65536) == _lib.PKV_ERR_INVALID_ARG
     assert b"65535" in _lib.lib().pkv_last_error()
+
+
+def test_upload_write_arguments_checked_before_any_launch():
+    """pkv_upload_write refuses bad sizes, geometry and alignment, and does nothing
+    when both parts are empty, without touching the HIP runtime."""
+    lib = _lib.lib()
+
+    def call(bytes_=0, ntok=0, nb=4, hkv=2, d=64, bs=16, dst=None, src=None):
+        return lib.pkv_upload_write(dst, src, bytes_, None, None, nb, None, None, None, ntok, hkv,
+                                    d, bs, None)
+
+    assert call() == _lib.PKV_OK
+    assert call(ntok=-1) == _lib.PKV_ERR_INVALID_ARG
+    assert call(nb=0) == _lib.PKV_ERR_INVALID_ARG
+    assert call(d=96) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(bs=24) == _lib.PKV_ERR_UNSUPPORTED
+    assert call(bytes_=24, dst=16, src=16) == _lib.PKV_ERR_INVALID_ARG          # size % 16
+    assert call(bytes_=32, dst=8, src=16) == _lib.PKV_ERR_INVALID_ARG           # alignment
+    assert call(bytes_=32) == _lib.PKV_ERR_INVALID_ARG                          # NULL buffers
+    assert call(ntok=4) == _lib.PKV_ERR_INVALID_ARG                             # NULL pools
