@@ -23,8 +23,7 @@
 // Each wave holds two sets of 16 "columns", (query, head) pairs: column c of
 // set cs = (query wj0 + cs * 16/HT + c / HT, head h0 + c % HT).  Every K or V
 // fragment a wave reads from LDS feeds one MFMA per set, which halves the LDS
-// bytes per flop (LDS bandwidth, not the matrix cores, bounded one set).  Per
-// 16 tokens and set:
+// bytes per flop.  Per 16 tokens and set:
 //
 //   S^T[t][c] = sum_d K[t][d] Q[c][d]     v_mfma_f32_16x16x32_f16, D/32 steps
 //
@@ -38,9 +37,10 @@
 // layout rounded to fp16.  The softmax denominators come from the matrix cores
 // too: the same P times a block of ones, so numerator and denominator sum the
 // same rounded weights and no lane adds scores on the vector ALUs.  Column c
-// masks every token past its own position, and a wave skips 16-token steps
-// that lie wholly past its queries.  One pass, no split: the group walks
-// tokens [0, last position of its block + 1).
+// masks every token past its own position; tiles that every column of a wave
+// sees whole skip the masking, and a wave skips 16-token steps that lie wholly
+// past its queries.  One pass, no split: the group walks tokens [0, last
+// position of its block + 1).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
