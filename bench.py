@@ -15,8 +15,9 @@ stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample of requests.
     python bench.py [--steps K] [--warmup W] [--workload opt13b|gqa|long_context]
 
 Other workloads: ``prefill`` (prompt-phase attention, FLOP/s against the fp16
-matrix peak) and ``swap`` (requests moved to the pinned host tier and back,
-GB/s against the host link).
+matrix peak), ``swap`` (requests moved to the pinned host tier and back, GB/s
+against the host link) and ``beams`` (beam-search-like fork / cancel churn with
+copy-on-write, tokens/s with the decode roofline on unique bytes).
 """
 
 from __future__ import annotations
@@ -44,7 +45,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="opt13b",
                     choices=["opt13b", "gqa", "long_context", "parallel_sampling", "tiny", "prefill",
-                             "swap"])
+                             "swap", "beams"])
     ap.add_argument("--partition", default="auto",
                     help="tokens per split-context partition, 0 = one pass, or 'auto'")
     ap.add_argument("--kernel-policy", default="default", choices=["default", "valu"],
@@ -559,6 +560,136 @@ def swap_cpu_baseline(w, blocks=512):
             "seconds": round(dt, 3)}
 
 
+def _beam_replay(w, steps):
+    """The churn schedule on a host-only allocator (same initial order, same calls as
+    the cache makes): per step the logical and unique (distinct blocks' filled slots)
+    tokens attention reads, and the copy-on-write pairs of the step's append."""
+    _lib = _lib_mod()
+    a = _lib.BlockAllocator(w.num_blocks, w.block_size, w.initial_order)
+    groups = []
+    for L in w.prompt_lengths:
+        s = a.create()
+        a.append(s, int(L))
+        groups.append([s] + [a.fork(s) for _ in range(w.beams - 1)])
+    logical, unique, pairs = [], [], []
+    bs = w.block_size
+    for t in range(steps):
+        groups = _beam_prune(w, t, groups, a.free, a.fork)
+        seqs = [s for g in groups for s in g]
+        _, p = a.append_batch(seqs)
+        pairs.append(int(p.shape[0]))
+        lens = a.lengths(seqs)
+        tables, _ = a.export(seqs, int(max(lens) + bs - 1) // bs, -1)
+        fill = {}
+        for row, L in zip(tables, lens):
+            for j in range(-(-int(L) // bs)):
+                fill[int(row[j])] = min(bs, int(L) - j * bs)
+        logical.append(int(lens.sum()))
+        unique.append(sum(fill.values()))
+    return logical, unique, pairs
+
+
+def _beam_prune(w, t, groups, free, fork):
+    plan = w.prune_plan(t)
+    if plan is None:
+        return groups
+    out = []
+    for g, (drop, src) in zip(groups, plan):
+        for i in drop:
+            free(g[i])
+        keep = [s for i, s in enumerate(g) if i not in drop]
+        out.append(keep + [fork(g[j]) for j in src])
+    return out
+
+
+def churn_bench(args):
+    """Beam-search-like churn: 8 prompts x 8 beams (OPT-13B attention shape); every
+    step appends one token to each of the 64 beams and attends; every 4th step each
+    prompt cancels 4 beams and forks 4 survivors, so copy-on-write copies (every
+    layer) and immediate reuse of freed blocks recur with work queued.  The pool has
+    several layers (>= 2 GiB, one written and read per step, as a model's layers
+    would be); copies go to every layer.  Metric: generated tokens per second;
+    roofline: decode attention over the unique K/V bytes it reads."""
+    import torch
+
+    from paged_kv_cache_244_amd import workloads
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    dev = torch.device("cuda:0")
+    w = workloads.beams()
+    total_steps = args.warmup + args.steps
+    tok_bytes = 2 * w.num_kv_heads * w.head_dim * 2
+    layers = max(1, -(-(2 << 30) // (w.num_blocks * w.block_size * tok_bytes)))
+    logical, unique, pairs = _beam_replay(w, total_steps)
+    cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                         num_layers=layers, initial_order=w.initial_order, device=dev, poison=False,
+                         num_q_heads=w.num_q_heads)
+    pk, pv = _to_dev([w.prompt_k, w.prompt_v], dev)
+    groups = []
+    for L in w.prompt_lengths:
+        s = cache.new_sequence()
+        groups.append([s])
+    slots = cache.reserve_many([g[0] for g in groups], [int(L) for L in w.prompt_lengths])
+    for layer in range(layers):
+        cache.write(slots, pk, pv, layer=layer)
+    for g in groups:
+        g.extend(cache.fork(g[0]) for _ in range(w.beams - 1))
+    inputs = [_to_dev(list(w.step_inputs(t)), dev) for t in range(total_steps)]
+    out = torch.empty((w.num_prompts * w.beams, w.num_q_heads, w.head_dim), dtype=torch.float32,
+                      device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(t, e=None):
+        nonlocal groups
+        groups = _beam_prune(w, t, groups, cache.free, cache.fork)
+        seqs = [s for g in groups for s in g]
+        k, v, q = inputs[t]
+        layer = t % layers
+        _, batch = cache.decode_step(seqs, k_new=k, v_new=v, layer=layer)
+        if e is not None:
+            e[0].record(cache.stream)
+        cache.attend(q, batch, w.scale, layer=layer, out=out)
+        if e is not None:
+            e[1].record(cache.stream)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in ev]
+    timed = slice(args.warmup, total_steps)
+    uniq = float(np.mean(unique[timed])) * tok_bytes
+    logi = float(np.mean(logical[timed])) * tok_bytes
+    dec_s = float(np.mean(ms)) / 1e3
+    achieved = uniq / dec_s / 1e9
+    s_count = w.num_prompts * w.beams
+    result = {
+        "metric": "beam-search churn: generated tokens/s (decode roofline on unique K/V bytes)",
+        "value": round(s_count * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "beams: 8 prompts of U{256..1024} tokens x 8 beams, prune 4 and fork 4 "
+                               "every 4 steps", "requests": s_count, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "layers": layers, "cow_pairs_per_step": round(float(np.mean(pairs[timed])), 2),
+                   "unique_kv_bytes_per_step": int(uniq), "logical_kv_bytes_per_step": int(logi)},
+        "decode_us": round(dec_s * 1e6, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_decode"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def prefill_cpu_baseline(w, prompt=1024):
     """The oracle's attend_prefill_paged on one request's first ``prompt`` tokens."""
     from threadpoolctl import threadpool_limits
@@ -592,13 +723,13 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode path has no multi-GPU sharding in this build)", file=sys.stderr)
         sys.exit(2)
-    if args.workload in ("prefill", "swap"):
+    if args.workload in ("prefill", "swap", "beams"):
         import torch
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(1)
         torch.cuda.set_device(0)
-        (prefill_bench if args.workload == "prefill" else swap_bench)(args)
+        {"prefill": prefill_bench, "swap": swap_bench, "beams": churn_bench}[args.workload](args)
         return
 
     import torch

@@ -281,6 +281,80 @@ def prefill(seed: int = 6, batch: int = 16) -> PrefillWorkload:
                            _normal(s_q, (total, hq, d), np.float16))
 
 
+@dataclass
+class BeamWorkload:
+    """Beam-search-like churn: each prompt forks into ``beams`` requests sharing its
+    blocks; every ``prune_every`` steps each prompt cancels ``prune`` beams and forks
+    as many survivors, so copy-on-write copies and the reuse of freed blocks recur
+    while kernels are queued.  The schedule and every input are drawn from seeds."""
+
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    scale: float
+    prompt_lengths: np.ndarray   # int32 [P]
+    beams: int
+    prune_every: int
+    prune: int
+    num_blocks: int
+    initial_order: np.ndarray
+    prompt_k: np.ndarray         # float16 [sum(P), Hkv, D]
+    prompt_v: np.ndarray
+    step_seed: np.random.SeedSequence
+    schedule_seed: np.random.SeedSequence
+
+    @property
+    def num_prompts(self) -> int:
+        return int(self.prompt_lengths.shape[0])
+
+    def step_inputs(self, step: int):
+        """New-token K, V ``[P*beams, Hkv, D]`` and q ``[P*beams, Hq, D]`` fp16 for one step."""
+        s = self.num_prompts * self.beams
+        child = np.random.SeedSequence(self.step_seed.entropy,
+                                       spawn_key=tuple(self.step_seed.spawn_key) + (step,))
+        sk, sv, sq = child.spawn(3)
+        return (_normal(sk, (s, self.num_kv_heads, self.head_dim), np.float16),
+                _normal(sv, (s, self.num_kv_heads, self.head_dim), np.float16),
+                _normal(sq, (s, self.num_q_heads, self.head_dim), np.float16))
+
+    def prune_plan(self, step: int):
+        """None, or per prompt (beam positions to cancel, beam positions to fork), the
+        positions indexing that prompt's current beam list."""
+        if step == 0 or step % self.prune_every:
+            return None
+        child = np.random.SeedSequence(self.schedule_seed.entropy,
+                                       spawn_key=tuple(self.schedule_seed.spawn_key) + (step,))
+        g = np.random.Generator(np.random.PCG64(child))
+        plan = []
+        for _ in range(self.num_prompts):
+            drop = g.choice(self.beams, size=self.prune, replace=False)
+            keep = np.setdiff1d(np.arange(self.beams), drop)
+            plan.append((sorted(int(x) for x in drop), [int(x) for x in g.choice(keep, size=self.prune)]))
+        return plan
+
+
+def beams(seed: int = 7, num_prompts: int = 8, beams: int = 8, prune_every: int = 4,
+          prune: int = 4, max_steps: int = 256, block_size: int = 16) -> BeamWorkload:
+    """8 prompts of U{256..1024} tokens x 8 beams, OPT-13B attention shape (40 x 128)."""
+    root = np.random.SeedSequence(seed)
+    s_len, s_perm, s_k, s_v, s_steps, s_sched = root.spawn(6)
+    plen = np.random.Generator(np.random.PCG64(s_len)).integers(256, 1024 + 1, size=num_prompts)
+    plen = plen.astype(np.int32)
+    hq = hkv = 40
+    d = 128
+    # Pool: every beam holding a private copy of everything it could write, plus the prompts.
+    private = num_prompts * beams * ((max_steps + block_size - 1) // block_size + 1)
+    num_blocks = int(math.ceil(1.2 * (private + sum(-(-int(p) // block_size) for p in plen))))
+    order = np.random.Generator(np.random.PCG64(s_perm)).permutation(num_blocks).astype(np.int32)
+    total = int(plen.sum())
+    return BeamWorkload("beams", hq, hkv, d, block_size, 1.0 / math.sqrt(d), plen, beams,
+                        prune_every, prune, num_blocks, order,
+                        _normal(s_k, (total, hkv, d), np.float16),
+                        _normal(s_v, (total, hkv, d), np.float16), s_steps, s_sched)
+
+
 WORKLOADS = {
     "tiny": tiny,
     "opt13b": opt13b,
