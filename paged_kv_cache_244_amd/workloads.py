@@ -286,7 +286,10 @@ class BeamWorkload:
     """Beam-search-like churn: each prompt forks into ``beams`` requests sharing its
     blocks; every ``prune_every`` steps each prompt cancels ``prune`` beams and forks
     as many survivors, so copy-on-write copies and the reuse of freed blocks recur
-    while kernels are queued.  The schedule and every input are drawn from seeds."""
+    while kernels are queued ("Only 20.4% of your KV cache held actual tokens",
+    section "The part everyone forgets: pages enable sharing, not just packing":
+    beams kept or killed every step, dead ones giving their references back).  The
+    schedule and every input are drawn from seeds."""
 
     name: str
     num_q_heads: int
