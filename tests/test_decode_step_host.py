@@ -153,3 +153,24 @@ def test_empty_step():
     lay = a.decode_step_host(np.zeros(0, dtype=np.int32), 0, -1, 8, 8, 64, _lib.PKV_F16, -1,
                              buf.ctypes.data, buf.nbytes)
     assert lay.plan.num_items == 0 and lay.total_bytes == 0 and lay.max_blocks == 1
+
+
+def test_swapped_sequence_is_refused_and_nothing_changes():
+    """A step listing a sequence swapped out to the host tier fails with
+    PKV_ERR_SWAPPED before anything changes; after swapping it back in the same
+    step succeeds."""
+    a = BlockAllocator(64, 16, np.arange(64))
+    a.add_host_tier(16)
+    s0, s1 = a.create(), a.create()
+    a.append(s0, 40)
+    a.append(s1, 17)
+    a.swap_out([s1])
+    before = a.stats()
+    buf = np.zeros(1 << 16, dtype=np.uint8)
+    seqs = np.array([s0, s1], dtype=np.int32)
+    with pytest.raises(_lib.Swapped):
+        a.decode_step_host(seqs, 0, -1, 8, 2, 64, _lib.PKV_F16, -1, buf.ctypes.data, buf.nbytes)
+    assert a.stats() == before and a.length(s0) == 40
+    a.swap_in([s1])
+    lay = a.decode_step_host(seqs, 0, -1, 8, 2, 64, _lib.PKV_F16, -1, buf.ctypes.data, buf.nbytes)
+    assert lay is not None and a.lengths(seqs).tolist() == [41, 18]
