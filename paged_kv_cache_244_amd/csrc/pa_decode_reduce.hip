@@ -16,10 +16,36 @@ namespace {
 // thread; only requests with more than one partition do work.  The (m_p, l_p)
 // pairs are the same for every thread (broadcast loads) and all loads of a
 // group of 16 partitions are issued before any is used, so a request's
-// partials arrive in a few memory round trips instead of one per partition.
+// partials arrive in a few memory round trips instead of one per partition:
+// with at most 32 partitions, one round trip for (m_p, l_p) and o_p together.
+// Up to N partials in one round trip: every (m_p, l_p) and o_p loaded together,
+// then combined.  (N fixed at compile time: 16 and 32 each fit their cases best.)
+template <int N, int D>
+__device__ __forceinline__ float combine_one_pass(const float2* ml, const float* o, int nparts) {
+  float2 mlv[N];
+  float ov[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const bool in = u < nparts;
+    mlv[u] = in ? ml[u] : make_float2(-FLT_MAX, 0.f);
+    ov[u] = in ? o[static_cast<int64_t>(u) * D] : 0.f;
+  }
+  float mmax = -FLT_MAX;
+#pragma unroll
+  for (int u = 0; u < N; ++u) mmax = fmaxf(mmax, mlv[u].x);
+  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const float w = fast_exp2(mlv[u].x - mmax);
+    den = fmaf(w, mlv[u].y, den);
+    num = fmaf(w, ov[u], num);
+  }
+  return num / den;
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void pa_decode_reduce_kernel(DecodeParams p) {
-  constexpr int U = 16;
+  constexpr int U = 16;                      // partials per round trip, two-pass path
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const int d = threadIdx.x;
@@ -29,6 +55,15 @@ __global__ __launch_bounds__(D) void pa_decode_reduce_kernel(DecodeParams p) {
   const int64_t base = (static_cast<int64_t>(seq) * p.num_q_heads + h) * p.max_parts;
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + base;
   const float* o = p.ws_o + base * D + d;
+  float* const dst = p.out + (static_cast<int64_t>(seq) * p.num_q_heads + h) * D + d;
+  if (nparts <= 16) {
+    *dst = combine_one_pass<16, D>(ml, o, nparts);
+    return;
+  }
+  if (nparts <= 32) {
+    *dst = combine_one_pass<32, D>(ml, o, nparts);
+    return;
+  }
   float mmax = -FLT_MAX;
   for (int c = 0; c < nparts; c += U) {
     float mv[U];
@@ -54,7 +89,7 @@ __global__ __launch_bounds__(D) void pa_decode_reduce_kernel(DecodeParams p) {
       num = fmaf(w, ov[u], num);
     }
   }
-  p.out[(static_cast<int64_t>(seq) * p.num_q_heads + h) * D + d] = num / den;
+  *dst = num / den;
 }
 
 }  // namespace
