@@ -68,13 +68,14 @@ def kv_bytes(lengths, w):
     return int(np.sum(lengths, dtype=np.int64)) * 2 * w.num_kv_heads * w.head_dim * 2
 
 
-def counter_traffic(workload_name):
-    """HBM bytes per pa_decode launch from the committed rocprofv3 counter summary,
+def counter_traffic(workload_name, kernel="pa_decode"):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary,
     or None when there is none for this workload or the kernel source changed since."""
     import hashlib
     import re
 
-    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload_name}_hbm_counters.md")
+    stem = kernel if workload_name is None else f"{kernel}_{workload_name}"
+    path = os.path.join(ROOT, "profiles", f"{stem}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\s*(\{.*?\})\s*```", open(path).read(), flags=re.S)
@@ -420,6 +421,7 @@ def prefill_bench(args):
     baseline = None
     if args.cpu_seconds > 0:
         baseline = prefill_cpu_baseline(w)
+    counters = counter_traffic(None, kernel="pa_prefill")
     result = {
         "metric": "paged prefill attention TFLOP/s (% of fp16 matrix peak)",
         "value": round(flops * args.steps / wall / 1e12, 2),
@@ -437,7 +439,8 @@ def prefill_bench(args):
                                round(float(np.percentile(ms, 90)) * 1e3, 2)],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "pa_prefill"},
+                     "traffic": counters["traffic_bytes_per_launch"] if counters else None,
+                     "kernel": "pa_prefill"},
         "cpu_baseline": baseline,
     }
     print(json.dumps(result), flush=True)
