@@ -154,3 +154,30 @@ def test_prefill_workload_full_size_sampled_rows():
         vals = w.v_tokens[starts[i]:row + 1, g:g + 1]
         want = attention.attend_one(w.q[row, h:h + 1], keys, vals, w.scale)
         paths.assert_attention_close(out[row, h:h + 1], want)
+
+
+def test_prefill_random_shapes():
+    """Random shapes against the oracle: every head grouping the kernel builds, both
+    head sizes, every block size, 1-5 requests with random context lengths and
+    random new-query counts (zero included: nothing to compute for that request;
+    fewer than the context: a continued chunk)."""
+    rng = np.random.default_rng(2027)
+    groupings = [(8, 8), (16, 8), (32, 8), (16, 2), (32, 2), (64, 4)]
+    for it in range(8):
+        hq, hkv = groupings[int(rng.integers(len(groupings)))]
+        d = int(rng.choice([64, 128]))
+        bs = int(rng.choice([8, 16, 32, 64, 128]))
+        n = int(rng.integers(1, 6))
+        lens = [int(x) for x in rng.integers(0, 300, size=n)]
+        qlens = [int(rng.integers(0, L + 1)) if rng.random() < 0.5 else L for L in lens]
+        print(f"\n[case] prefill random #{it}: hq={hq} hkv={hkv} d={d} bs={bs} lens={lens} "
+              f"qlens={qlens}", flush=True)
+        if sum(qlens) == 0:
+            continue
+        c, tables, lens_h, starts, q = _setup(hq, hkv, d, bs, [max(L, 1) for L in lens], qlens,
+                                              seed=it)
+        scale = 1.0 / np.sqrt(d)
+        got = _run(c, tables, lens_h, starts, q, scale)
+        want = attention.attend_prefill_paged(q, c.k[0].cpu().numpy(), c.v[0].cpu().numpy(),
+                                              tables.astype(np.int64), lens_h, starts, bs, scale)
+        paths.assert_attention_close(got, want)
