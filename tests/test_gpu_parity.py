@@ -257,3 +257,27 @@ def _long_context_ref(rows):
             out[i] = attention.attend_one(w.q[i], k, v, w.scale)
         _LC[key] = out
     return _LC[key]
+
+
+def test_random_shapes():
+    """Random combinations against the oracle: head grouping (VALU and MFMA kernels),
+    head size, block size, partition (one pass, explicit, the planner's choice),
+    query dtype, and lengths from empty to a few thousand tokens."""
+    rng = np.random.default_rng(4242)
+    groupings = [(1, 1), (4, 4), (8, 2), (6, 2), (16, 2), (32, 8), (12, 1), (64, 4)]
+    for it in range(10):
+        hq, hkv = groupings[int(rng.integers(len(groupings)))]
+        d = int(rng.choice([64, 128]))
+        bs = int(rng.choice([8, 16, 32, 64, 128]))
+        qd = np.float32 if rng.random() < 0.3 else np.float16
+        n = int(rng.integers(1, 9))
+        lens = [int(x) for x in rng.integers(0, 3000, size=n)]
+        lens[int(rng.integers(n))] = int(rng.choice([0, 1, bs, bs + 1]))
+        part = rng.choice(["auto", 0, bs, 256, 1024])
+        part = part if part == "auto" else int(part)
+        print(f"\n[case] decode random #{it}: hq={hq} hkv={hkv} d={d} bs={bs} q={np.dtype(qd).name} "
+              f"part={part} lens={lens}", flush=True)
+        w = workloads.custom(f"rand{it}", 500 + it, lens, hq, hkv, d, bs, q_dtype=qd)
+        got = paths.run_gpu(w, part, out_only=True)["out"]
+        want = paths.run_oracle(w)["out"]
+        paths.assert_attention_close(got, want)
