@@ -149,8 +149,13 @@ def _cpu_model():
 
 def gpu_info():
     """Device name, partition modes and clock limits from amd-smi (child processes, read
-    only), or None where the tool is missing or says nothing usable."""
+    only), or None where the tool is missing or says nothing usable.  Skipped under
+    rocprofv3 (it exports ROCPROF_OUTPUT_PATH): the profiler's library would start in each
+    child, and the amd-smi launcher replaces itself through /usr/bin/env."""
     import subprocess
+
+    if "ROCPROF_OUTPUT_PATH" in os.environ:
+        return None
 
     def query(args):
         try:
