@@ -144,6 +144,44 @@ def test_schedule_does_not_change_bits():
             assert np.array_equal(got.view(np.uint32), planned["out"].view(np.uint32)), wpc
 
 
+@pytest.mark.parametrize("hq,hkv,q_dtype", [(8, 8, np.float16), (8, 2, np.float16),
+                                             (4, 2, np.float32)])
+def test_workspace_reused_across_partition_sizes(hq, hkv, q_dtype):
+    """One split-context workspace, sized for the largest of several partition
+    sizes, serves launches of those sizes in a row without being cleared; each
+    launch is within tolerance of the oracle and bitwise equal to the same
+    launch made earlier with the same workspace."""
+    import torch
+
+    from paged_kv_cache_244_amd import _lib
+    kernel = "mfma" if hq // hkv >= 4 and q_dtype == np.float16 else "valu"
+    _announce(f"workspace reuse hq={hq} hkv={hkv} q={np.dtype(q_dtype).name} ({kernel})")
+    lengths = [900, 3, 40, 2000, 129, 0, 600, 1]
+    w = workloads.custom("ws_reuse", 12, lengths, hq, hkv, 128, 16, q_dtype=q_dtype)
+    ref = paths.run_oracle(w)
+    base = paths.run_gpu(w, 0)
+    c, batch, q = base["cache"], base["batch"], base["q_dev"]
+    qd = _lib.PKV_F16 if q_dtype == np.float16 else _lib.PKV_F32
+    max_len = batch.max_len
+    sizes = (32, 64, 256)
+    nbytes = max(_lib.pa_decode_workspace_size(w.num_seqs, hq, 128, max_len, p_) for p_ in sizes)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    plans = {p_: _lib.plan(w.lengths, hq, hkv, 128, 16, qd, partition_size=p_)[0].view(np.uint32)
+             for p_ in sizes}
+    first = {}
+    for part in (32, 256, 64, 32, 256):
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+        items = torch.from_numpy(np.ascontiguousarray(plans[part]).view(np.int32)).cuda()
+        _lib.pa_decode(out, q, c.k[0], c.v[0], batch.tables, batch.lens, w.scale, max_len,
+                       partition_size=part, workspace=ws, stream=c.stream, work_items=items)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        paths.assert_attention_close(got, ref["out"])
+        if part in first:
+            assert np.array_equal(got.view(np.uint32), first[part].view(np.uint32)), part
+        first.setdefault(part, got)
+
+
 def test_copy_blocks_multi_layer_bit_exact():
     import torch
 
