@@ -58,6 +58,9 @@ def parse_args():
     ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
                     help="K/V layout: the paged pool (the product path) or one contiguous row "
                          "per (request, KV head) without a block table, for comparison")
+    ap.add_argument("--no-prefix-groups", action="store_true",
+                    help="parallel_sampling and beams: read shared prompt blocks once per "
+                         "request instead of once per group (for comparison)")
     ap.add_argument("--replicas", type=int, default=0,
                     help="pool replicas rotated over the steps, as a model's layers would be "
                          "(0 = enough for 2 GiB of K/V pools, so no step finds its pool in the "
@@ -233,7 +236,10 @@ class Scenario:
         # reserve, tables, plan and the new tokens' write: one host call, one launch
         _, batch = cache.decode_step(self.seqs, self.max_blocks, partition_size=partition,
                                      k_new=self.step_k[t], v_new=self.step_v[t], layer=layer)
-        plans.append(batch.plan)
+        grouped = batch.group_items_dev is not None
+        plans.append(dict(batch.plan,
+                          num_groups=batch.groups_dev.shape[0] if grouped else 0,
+                          num_group_items=batch.group_items_dev.shape[0] if grouped else 0))
         if ev_pair is not None:
             ev_pair[0].record(cache.stream)
         cache.attend(self.step_q[t], batch, self.w.scale, layer=layer, out=self.out)
@@ -284,7 +290,7 @@ def decode_scenario(w, total_steps, dev, replicas=0):
                     max_blocks, out, extra={"pool_replicas": nrep})
 
 
-def sampling_scenario(sw, total_steps, dev, replicas=0):
+def sampling_scenario(sw, total_steps, dev, replicas=0, prefix_groups=True):
     """Prompts forked into samples sharing their blocks; the first step copies the
     partly filled last prompt block of every sample but one per prompt."""
     import torch
@@ -296,7 +302,7 @@ def sampling_scenario(sw, total_steps, dev, replicas=0):
     nrep = replicas_for(sw.num_blocks, sw, replicas)
     cache = PagedKVCache(sw.num_blocks, sw.num_kv_heads, sw.head_dim, sw.block_size,
                          num_layers=nrep, initial_order=sw.initial_order, device=dev, poison=False,
-                         num_q_heads=sw.num_q_heads)
+                         num_q_heads=sw.num_q_heads, prefix_groups=prefix_groups)
     prompts = [cache.new_sequence() for _ in range(sw.num_prompts)]
     slots = cache.reserve_many(prompts, sw.prompt_lengths)
     pk, pv = _to_dev([sw.prompt_k, sw.prompt_v], dev)
@@ -680,7 +686,7 @@ def churn_bench(args):
     logical, unique, pairs = _beam_replay(w, total_steps)
     cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
                          num_layers=layers, initial_order=w.initial_order, device=dev, poison=False,
-                         num_q_heads=w.num_q_heads)
+                         num_q_heads=w.num_q_heads, prefix_groups=not args.no_prefix_groups)
     pk, pv = _to_dev([w.prompt_k, w.prompt_v], dev)
     groups = []
     for L in w.prompt_lengths:
@@ -737,6 +743,7 @@ def churn_bench(args):
                                "every 4 steps", "requests": s_count, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "layers": layers, "cow_pairs_per_step": round(float(np.mean(pairs[timed])), 2),
+                   "prefix_groups": not args.no_prefix_groups,
                    "unique_kv_bytes_per_step": int(uniq), "logical_kv_bytes_per_step": int(logi)},
         "decode_us": round(dec_s * 1e6, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -808,7 +815,8 @@ def main():
 
     total_steps = args.warmup + args.steps
     if args.workload == "parallel_sampling":
-        sc = sampling_scenario(workloads.parallel_sampling(), total_steps, dev, args.replicas)
+        sc = sampling_scenario(workloads.parallel_sampling(), total_steps, dev, args.replicas,
+                               prefix_groups=not args.no_prefix_groups)
     else:
         w = {"long_context": lambda: workloads.long_context(16),
              "tiny": workloads.tiny}.get(args.workload, workloads.WORKLOADS.get(args.workload))()
@@ -887,7 +895,9 @@ def main():
             "workload": f"{w.name} decode layer",
             "num_seqs": sc.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": "f16",
-            "q_dtype": np.dtype(w.q_dtype).name, "partition_size": partition,
+            "q_dtype": np.dtype(w.q_dtype).name, "partition_size": plans[-1]["partition_size"],
+            "prefix_groups": plans[-1]["num_groups"],
+            "group_pieces": plans[-1]["num_group_items"],
             "kernel_policy": args.kernel_policy, "layout": args.layout,
             "schedule": "planner work list, largest piece first",
             "work_items": plans[-1]["num_items"], "waves_per_cu": plans[-1]["waves_per_cu"],
@@ -905,7 +915,9 @@ def main():
                      "traffic_over_algorithmic": (round(traffic["traffic_bytes_per_launch"]
                                                        / traffic["algorithmic_bytes_per_launch"], 4)
                                                  if traffic else None),
-                     "kernel": "pa_decode (partition + reduce launches)"},
+                     "kernel": ("pa_decode_grouped (group pieces, remaining pieces, reduce)"
+                                if plans[-1]["num_groups"] else
+                                "pa_decode (partition + reduce launches)")},
         "cpu_baseline": baseline,
         "gpu": GPU_INFO,
     }

@@ -309,6 +309,80 @@ int pa_decode(float* out, const void* q, int32_t q_dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Prefix groups.  Parallel samples of one prompt map their prompt blocks to
+ * the same physical blocks, and beams share every block up to where they
+ * diverged ([B] "The part everyone forgets: pages enable sharing, not just
+ * packing").  Decode reads each request's whole context, so such a block is
+ * otherwise read once per request holding it.  A group lists requests whose
+ * first tokens live in the same physical blocks; pa_decode_grouped reads
+ * those blocks once for all members.
+ *
+ * Descriptor of group g: int32 row g of [num_groups][PKV_GROUP_STRIDE]:
+ * the member count n (1 <= n <= 16 / (num_q_heads / num_kv_heads)), then the
+ * n members' request indices; the remaining entries are ignored.
+ */
+#define PKV_GROUP_STRIDE 17
+
+/*
+ * pa_decode_plan_groups — host only: pa_decode_plan, then prefix groups.
+ * Requests are ordered by their block ids; neighbours whose leading FULL
+ * blocks (the first floor(len / block_size) entries of a row) are the same
+ * physical blocks form groups, a member joining only when the group's saved
+ * partition reads do not shrink.  Grouping is used when it saves at least a
+ * quarter of the batch's token reads, with fp16 q, head_dim 64 or 128 and at
+ * most 8 query heads per KV head; then a one-pass plan (partition_size 0)
+ * becomes a plan with 64-token partitions (rounded up to block_size).
+ *   block_tables   : HOST int32 [num_seqs][max_blocks_per_seq].
+ *   items          : HOST uint32 [items_capacity]: the plan's pieces minus
+ *                    the group pieces (plan->num_items of them).
+ *   groups         : HOST int32 [groups_capacity][PKV_GROUP_STRIDE]; at most
+ *                    num_seqs / 2 groups are formed.
+ *   group_items    : HOST uint32 [items_capacity]: PKV_ITEM(group, partition)
+ *                    for every partition that all members' tables share.
+ * Other arguments and errors as pa_decode_plan.  With no worthwhile group,
+ * *num_groups = *num_group_items = 0 and the result is pa_decode_plan's.
+ */
+int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t q_dtype, int32_t partition_size, int32_t num_compute_units,
+                          uint32_t* items, int32_t items_capacity, pkv_decode_plan* plan,
+                          int32_t* groups, int32_t groups_capacity, int32_t* num_groups,
+                          uint32_t* group_items, int32_t* num_group_items);
+
+/*
+ * pa_decode_grouped — pa_decode where some pieces are run by prefix groups.
+ * A group piece (group, p) computes partition p of every member at once: one
+ * wave per (piece, KV head) reads the partition's K/V tiles once, through
+ * the block table of the group's first member, for the query heads of all
+ * members (MFMA, as pa_decode's head-group kernel; P rounded to fp16).  Its
+ * results go where pa_decode's own piece (member, p) would put them, so the
+ * launch's log-sum-exp combine merges both kinds.  Launches: the group
+ * pieces, the remaining pieces (work_items), then the combine.
+ *   groups, num_groups       : device int32 [num_groups][PKV_GROUP_STRIDE].
+ *   group_items, num_group_items : device uint32 PKV_ITEM(group, partition).
+ * The caller guarantees, as pa_decode_plan_groups does, that for every group
+ * piece the partition's tokens lie in the same physical blocks in every
+ * member's table and within every member's length, and that the group pieces
+ * and work_items together name each piece of each request exactly once.
+ * Other arguments as pa_decode.  Errors as pa_decode, plus
+ * PKV_ERR_UNSUPPORTED for group pieces with q not fp16 or more than 8 query
+ * heads per KV head, and PKV_ERR_INVALID_ARG for group pieces with
+ * partition_size 0 or missing group arrays.  With num_group_items 0 it is
+ * pa_decode.
+ */
+int pa_decode_grouped(float* out, const void* q, int32_t q_dtype,
+                      const void* k_cache, const void* v_cache, int32_t num_blocks,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, float scale, int32_t max_context_len,
+                      int32_t partition_size, const uint32_t* work_items, int32_t num_work_items,
+                      int32_t waves_per_cu, const int32_t* groups, int32_t num_groups,
+                      const uint32_t* group_items, int32_t num_group_items,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_contiguous — the same decode attention over the layout without a
  * block table, for measuring what the table costs: [A] "The old answer,
  * imported honestly" (one contiguous region per request, sized for its
@@ -524,8 +598,15 @@ typedef struct {
   int32_t max_blocks;       /* table width used                                         */
   int32_t max_context_len;  /* longest length after the append                          */
   int32_t reserved;
-  pkv_decode_plan plan;
+  pkv_decode_plan plan;     /* plan.num_items: the pieces at items_offset               */
+  uint64_t groups_offset;   /* int32 [num_groups][PKV_GROUP_STRIDE] (PKV_STEP_GROUPS)   */
+  uint64_t group_items_offset; /* uint32 [num_group_items]                              */
+  int32_t num_groups;
+  int32_t num_group_items;
 } kv_step_layout;
+
+/* kv_decode_step_host flags. */
+enum { PKV_STEP_GROUPS = 1 };
 
 /*
  * kv_decode_step_host — the host side of one decode step in one call, laid out
@@ -543,6 +624,10 @@ typedef struct {
  *   pad_value          : table entries past a sequence's blocks.
  *   num_q_heads ... num_compute_units : as pa_decode_plan (block size and
  *                        partition rules included).
+ *   flags              : PKV_STEP_GROUPS plans prefix groups as
+ *                        pa_decode_plan_groups does (for pa_decode_grouped),
+ *                        from the blocks that were full before the append
+ *                        (an append never rewrites a full block).
  *   buffer, buffer_bytes: caller's host memory (pinned memory lets the copy
  *                        run asynchronously); filled as *layout describes.
  * Everything is checked, and the space needed computed, before anything
@@ -552,8 +637,8 @@ typedef struct {
 int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
                         int32_t max_blocks_per_seq, int32_t pad_value, int32_t num_q_heads,
                         int32_t num_kv_heads, int32_t head_dim, int32_t q_dtype,
-                        int32_t partition_size, int32_t num_compute_units, void* buffer,
-                        uint64_t buffer_bytes, kv_step_layout* layout);
+                        int32_t partition_size, int32_t num_compute_units, int32_t flags,
+                        void* buffer, uint64_t buffer_bytes, kv_step_layout* layout);
 
 #ifdef __cplusplus
 }

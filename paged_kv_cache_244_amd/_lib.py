@@ -69,7 +69,9 @@ class StepLayout(ctypes.Structure):
                 ("tables_offset", ctypes.c_uint64), ("lens_offset", ctypes.c_uint64),
                 ("items_offset", ctypes.c_uint64), ("total_bytes", ctypes.c_uint64),
                 ("num_pairs", c_int32), ("max_blocks", c_int32), ("max_context_len", c_int32),
-                ("reserved", c_int32), ("plan", DecodePlan)]
+                ("reserved", c_int32), ("plan", DecodePlan),
+                ("groups_offset", ctypes.c_uint64), ("group_items_offset", ctypes.c_uint64),
+                ("num_groups", c_int32), ("num_group_items", c_int32)]
 
 
 class KVStats(ctypes.Structure):
@@ -134,8 +136,17 @@ _SIGNATURES = {
                                          c_void_p]),
     "kv_allocator_stats": (c_int32, [c_void_p, POINTER(KVStats)]),
     "kv_decode_step_host": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
-                                      c_int32, c_int32, c_int32, c_int32, c_void_p, ctypes.c_uint64,
-                                      POINTER(StepLayout)]),
+                                      c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                      ctypes.c_uint64, POINTER(StepLayout)]),
+    "pa_decode_plan_groups": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,
+                                        c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                        c_int32, POINTER(DecodePlan), c_void_p, c_int32,
+                                        POINTER(c_int32), c_void_p, POINTER(c_int32)]),
+    "pa_decode_grouped": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                    c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
+                                    c_int32, c_float, c_int32, c_int32, c_void_p, c_int32, c_int32,
+                                    c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_size_t,
+                                    c_void_p]),
 }
 
 _lib = None
@@ -297,6 +308,41 @@ def plan(context_lens, num_q_heads, num_kv_heads, head_dim, block_size, q_dtype=
     return items[: info["num_items"]].copy(), info
 
 
+GROUP_STRIDE = 17                     # PKV_GROUP_STRIDE: count, then up to 16 members
+PKV_STEP_GROUPS = 1
+
+
+def plan_groups(block_tables, context_lens, num_q_heads, num_kv_heads, head_dim, block_size,
+                q_dtype=PKV_F16, partition_size=-1, num_compute_units=0):
+    """``pa_decode_plan_groups``: the decode plan with prefix groups, from host tables.
+
+    Returns (items, plan, groups, group_items): the remaining work items, the plan dict
+    (its num_items counts them), groups int32 [num_groups, 17] (count, members) and
+    group_items uint32 (group << 16 | partition).  No worthwhile group: groups is empty
+    and the rest equals ``plan``'s result.
+    """
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    n = int(lens.shape[0])
+    if tables.ndim != 2 or tables.shape[0] != n:
+        raise ValueError("block_tables must be [num_seqs, max_blocks]")
+    cap = int(lib().pa_decode_plan_capacity(n, int(lens.max()) if n else 0, int(block_size)))
+    items = np.empty(max(cap, 1), dtype=np.uint32)
+    gitems = np.empty(max(cap, 1), dtype=np.uint32)
+    gcap = max(1, n // 2)
+    groups = np.empty((gcap, GROUP_STRIDE), dtype=np.int32)
+    pl, ng, ngi = DecodePlan(), c_int32(0), c_int32(0)
+    _check(lib().pa_decode_plan_groups(
+        tables.ctypes.data if tables.size else None, int(tables.shape[1]),
+        lens.ctypes.data if n else None, n, int(num_q_heads), int(num_kv_heads), int(head_dim),
+        int(block_size), int(q_dtype), int(partition_size), int(num_compute_units),
+        items.ctypes.data, int(items.shape[0]), byref(pl), groups.ctypes.data, gcap, byref(ng),
+        gitems.ctypes.data, byref(ngi)))
+    info = {name: int(getattr(pl, name)) for name, _ in DecodePlan._fields_}
+    return (items[: info["num_items"]].copy(), info, groups[: ng.value].copy(),
+            gitems[: ngi.value].copy())
+
+
 def _items(work_items):
     torch = _torch()
     if work_items.dim() != 1:
@@ -313,6 +359,41 @@ def set_kernel_policy(policy: int) -> int:
     if rc < 0:
         _check(rc)
     return rc
+
+
+def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, partition_size, groups, group_items, workspace=None,
+                      stream=None, work_items=None, waves_per_cu=0):
+    """``pa_decode`` with prefix groups: ``groups`` a device int32 [num_groups, 17] tensor
+    and ``group_items`` a device int32/uint32 tensor of (group << 16 | partition) pieces,
+    as ``plan_groups`` returns them; ``work_items`` the remaining pieces."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_geometry(k_cache, v_cache)
+    s, hq, dq = (int(x) for x in q.shape)
+    if dq != d or tuple(out.shape) != (s, hq, d):
+        raise ValueError("q and out must be [S, Hq, head_dim]")
+    if q.dtype != torch.float16:
+        raise TypeError("grouped decode needs fp16 q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or tuple(context_lens.shape) != (s,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    if groups.dim() != 2 or groups.shape[1] != GROUP_STRIDE:
+        raise ValueError(f"groups must be int32 [num_groups, {GROUP_STRIDE}]")
+    items_ptr, n_items = c_void_p(None), 0
+    if work_items is not None:
+        items_ptr, n_items = _items(work_items)
+    g_ptr, n_g = _items(group_items)
+    ws_ptr, ws_bytes = c_void_p(None), 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(lib().pa_decode_grouped(
+        _dev(out, torch.float32, "out"), _dev(q, q.dtype, "q"), PKV_F16,
+        _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"), nb,
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, bs, float(scale),
+        int(max_context_len), int(partition_size), items_ptr, n_items, int(waves_per_cu),
+        _dev(groups, torch.int32, "groups"), int(groups.shape[0]), g_ptr, n_g, ws_ptr, ws_bytes,
+        _stream(stream)))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):
@@ -570,7 +651,8 @@ class BlockAllocator:
         return tables, lens
 
     def decode_step_host(self, seqs, max_blocks, pad_value, num_q_heads, num_kv_heads, head_dim,
-                         q_dtype, partition_size, buffer_ptr, buffer_bytes, num_compute_units=0):
+                         q_dtype, partition_size, buffer_ptr, buffer_bytes, num_compute_units=0,
+                         flags=0):
         """One decode step's host work into a caller buffer (``kv_decode_step_host``).
 
         ``seqs`` must be a C-contiguous int32 array.  Returns the StepLayout, or None when
@@ -580,7 +662,7 @@ class BlockAllocator:
         rc = lib().kv_decode_step_host(self._h, seqs.ctypes.data, int(seqs.shape[0]),
                                        int(max_blocks), int(pad_value), int(num_q_heads),
                                        int(num_kv_heads), int(head_dim), int(q_dtype),
-                                       int(partition_size), int(num_compute_units),
+                                       int(partition_size), int(num_compute_units), int(flags),
                                        buffer_ptr, int(buffer_bytes), byref(lay))
         if rc == PKV_ERR_INVALID_ARG and lay.total_bytes > buffer_bytes:
             self.needed = int(lay.total_bytes)

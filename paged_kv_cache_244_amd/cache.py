@@ -145,12 +145,17 @@ class PagedKVCache:
 
     ``num_q_heads`` and ``q_dtype`` describe the queries that will attend (they
     decide the kernel and so the schedule that ``decode_step`` and ``batch``
-    prepare); defaults: one query head per KV head, fp16.
+    prepare); defaults: one query head per KV head, fp16.  ``prefix_groups``
+    lets ``decode_step`` group requests that share leading physical blocks
+    (forked samples and beams) so that ``attend`` reads those blocks once per
+    group (``pa_decode_grouped``); the planner uses groups only where they pay.
     """
 
     def __init__(self, num_blocks, num_kv_heads, head_dim, block_size, num_layers=1,
                  initial_order=None, device="cuda", poison=True, stream=None,
-                 num_q_heads=None, q_dtype=None, host_blocks=0, host_order=None):
+                 num_q_heads=None, q_dtype=None, host_blocks=0, host_order=None,
+                 prefix_groups=True):
+        self.prefix_groups = bool(prefix_groups)
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
@@ -326,9 +331,12 @@ class PagedKVCache:
         qd = _lib.PKV_F16 if self.q_dtype == torch.float16 else _lib.PKV_F32
         alloc = self.alloc
 
+        flags = _lib.PKV_STEP_GROUPS if self.prefix_groups else 0
+
         def fill(ptr, cap):
             lay = alloc.decode_step_host(seqs, max_blocks or 0, self.num_blocks, self.num_q_heads,
-                                         self.num_kv_heads, self.head_dim, qd, part, ptr, cap)
+                                         self.num_kv_heads, self.head_dim, qd, part, ptr, cap,
+                                         flags=flags)
             if lay is None:
                 fill.needed = alloc.needed
             return lay
@@ -368,6 +376,11 @@ class PagedKVCache:
                             int(lay.max_context_len), lens_host,
                             DeviceArray(dev, lay.items_offset, torch.int32, (plan["num_items"],)),
                             plan, key)
+        if lay.num_group_items:
+            batch.groups_dev = DeviceArray(dev, lay.groups_offset, torch.int32,
+                                           (lay.num_groups, _lib.GROUP_STRIDE))
+            batch.group_items_dev = DeviceArray(dev, lay.group_items_offset, torch.int32,
+                                                (lay.num_group_items,))
         return slots, batch
 
     def write(self, slots, k_new: torch.Tensor, v_new: torch.Tensor, layer: int = 0):
@@ -469,6 +482,17 @@ class PagedKVCache:
             raise ValueError("out must be a contiguous device fp32 [S, Hq, head_dim] tensor")
         part = info["partition_size"]
         ws = self.workspace(s, hq, batch.max_len, part)
+        if key == batch.plan_key and batch.group_items_dev is not None:
+            g, gi = batch.groups_dev, batch.group_items_dev
+            _lib._check(_lib.lib().pa_decode_grouped(
+                out.data_ptr(), q.data_ptr(), _lib.PKV_F16, self.k[layer].data_ptr(),
+                self.v[layer].data_ptr(), self.num_blocks, batch.tables_dev.ptr,
+                batch.tables_dev.shape[1], batch.lens_dev.ptr, s, hq, self.num_kv_heads, d,
+                self.block_size, float(scale), batch.max_len, part, items.ptr, items.shape[0],
+                info["waves_per_cu"], g.ptr, g.shape[0], gi.ptr, gi.shape[0],
+                ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                self._stream_ptr))
+            return out
         _lib._check(_lib.lib().pa_decode(
             out.data_ptr(), q.data_ptr(), _lib.PKV_F16 if q.dtype == torch.float16 else _lib.PKV_F32,
             self.k[layer].data_ptr(), self.v[layer].data_ptr(), self.num_blocks,
@@ -490,10 +514,11 @@ class DecodeBatch:
     made for."""
 
     __slots__ = ("tables_dev", "lens_dev", "max_len", "lens_host", "items_dev", "plan",
-                 "plan_key", "num_seqs")
+                 "plan_key", "num_seqs", "groups_dev", "group_items_dev")
 
     def __init__(self, tables, lens, max_len, lens_host, items, plan, plan_key):
         self.tables_dev, self.lens_dev, self.items_dev = tables, lens, items
+        self.groups_dev = self.group_items_dev = None     # prefix groups, when planned
         self.max_len = max_len
         self.lens_host = lens_host
         self.plan = plan

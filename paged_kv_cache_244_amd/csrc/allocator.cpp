@@ -21,6 +21,7 @@
 #include <new>
 #include <vector>
 
+#include "decode_plan.h"
 #include "errors.h"
 #include "pagedkv.h"
 
@@ -478,9 +479,11 @@ int kv_export_block_tables(const kv_allocator* a, const int32_t* seqs, int32_t n
 int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
                         int32_t max_blocks_per_seq, int32_t pad_value, int32_t num_q_heads,
                         int32_t num_kv_heads, int32_t head_dim, int32_t q_dtype,
-                        int32_t partition_size, int32_t num_compute_units, void* buffer,
-                        uint64_t buffer_bytes, kv_step_layout* layout) {
+                        int32_t partition_size, int32_t num_compute_units, int32_t flags,
+                        void* buffer, uint64_t buffer_bytes, kv_step_layout* layout) {
   if (!a || !layout) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  if (flags & ~static_cast<int32_t>(PKV_STEP_GROUPS))
+    return fail(PKV_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   *layout = kv_step_layout{};
   if (num_seqs < 0 || num_seqs > 65535)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs %d outside [0, 65535]", num_seqs);
@@ -509,13 +512,25 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
   if (blocks_wanted > width)
     return fail(PKV_ERR_INVALID_ARG, "a sequence needs %lld blocks > max_blocks_per_seq %d",
                 static_cast<long long>(blocks_wanted), width);
-  // The plan, into scratch first: its size decides the layout.
-  static thread_local std::vector<uint32_t> items;
-  items.resize(static_cast<size_t>(std::max(1, pa_decode_plan_capacity(num_seqs, static_cast<int32_t>(longest), B))));
+  // The plan, into scratch first: its size decides the layout.  Prefix groups
+  // come from the blocks that are full before the append: the append leaves
+  // them as they are (only a partly filled last block can be copied on write),
+  // so they are what the tables hold after it.
+  static thread_local std::vector<uint32_t> items, group_items;
+  static thread_local std::vector<int32_t> groups, nfull;
+  static thread_local std::vector<const int32_t*> rows;
   pkv_decode_plan plan{};
-  if (int rc = pa_decode_plan(lens.data(), num_seqs, num_q_heads, num_kv_heads, head_dim, B, q_dtype,
-                              partition_size, num_compute_units, items.data(),
-                              static_cast<int32_t>(items.size()), &plan))
+  rows.resize(static_cast<size_t>(num_seqs));
+  nfull.resize(static_cast<size_t>(num_seqs));
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const kv_allocator::Seq& s = a->seqs[seqs[i]];
+    rows[i] = s.blocks.data();
+    nfull[i] = (flags & PKV_STEP_GROUPS) ? static_cast<int32_t>(s.length / B) : 0;
+  }
+  if (int rc = pkv_plan::plan_with_groups(rows.data(), nfull.data(), lens.data(), num_seqs,
+                                          num_q_heads, num_kv_heads, head_dim, B, q_dtype,
+                                          partition_size, num_compute_units, items, &plan, groups,
+                                          group_items))
     return rc;
   auto up16 = [](uint64_t x) { return (x + 15) & ~static_cast<uint64_t>(15); };
   kv_step_layout L{};
@@ -524,7 +539,11 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
   L.tables_offset = up16(L.pairs_offset + 8ull * num_seqs);
   L.lens_offset = up16(L.tables_offset + 4ull * num_seqs * static_cast<uint64_t>(width));
   L.items_offset = up16(L.lens_offset + 4ull * num_seqs);
-  L.total_bytes = up16(L.items_offset + 4ull * static_cast<uint64_t>(plan.num_items));
+  L.groups_offset = up16(L.items_offset + 4ull * static_cast<uint64_t>(plan.num_items));
+  L.group_items_offset = up16(L.groups_offset + 4ull * groups.size());
+  L.total_bytes = up16(L.group_items_offset + 4ull * group_items.size());
+  L.num_groups = static_cast<int32_t>(groups.size() / PKV_GROUP_STRIDE);
+  L.num_group_items = static_cast<int32_t>(group_items.size());
   L.max_blocks = width;
   L.max_context_len = static_cast<int32_t>(longest);
   L.plan = plan;
@@ -552,6 +571,9 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
   }
   if (plan.num_items > 0)
     std::memcpy(base + L.items_offset, items.data(), sizeof(uint32_t) * plan.num_items);
+  if (!groups.empty()) std::memcpy(base + L.groups_offset, groups.data(), 4 * groups.size());
+  if (!group_items.empty())
+    std::memcpy(base + L.group_items_offset, group_items.data(), 4 * group_items.size());
   *layout = L;
   return PKV_OK;
 }

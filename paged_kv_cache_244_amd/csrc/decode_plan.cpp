@@ -214,3 +214,223 @@ extern "C" int pa_decode_plan(const int32_t* context_lens, int32_t num_seqs, int
   return PKV_OK;
 }
 
+
+// ---------------------------------------------------------------- prefix groups
+//
+// Parallel samples of one prompt map their prompt blocks to the same physical
+// blocks, and beams share every block up to where they diverged ("Only 20.4%
+// of your KV cache held actual tokens" (blog.teqners.com), section "The part
+// everyone forgets: pages enable sharing, not just packing").  Decode reads a
+// request's whole context every step, so a shared block is read once per
+// request that holds it.  Grouping such requests lets one wave read the block
+// once for all of them.
+
+namespace pkv_plan {
+namespace {
+
+int32_t leading_equal(const int32_t* a, int32_t na, const int32_t* b, int32_t nb) {
+  const int32_t n = std::min(na, nb);
+  int32_t j = 0;
+  while (j < n && a[j] == b[j]) ++j;
+  return j;
+}
+
+// Requests sorted by their full block ids (equal lists keep index order), so
+// that those sharing the longest prefixes are neighbours; then runs of
+// neighbours become groups of at most max_members, a member joining only if
+// the group's saving ((members - 1) x shared partitions) does not shrink.
+// shared_parts[i]: partitions of request i that its group covers.
+void form_groups(const int32_t* const* blocks, const int32_t* nfull, int32_t n, int32_t bpp,
+                 int32_t max_members, std::vector<int32_t>& groups,
+                 std::vector<int32_t>& shared_parts, int64_t& saved_parts) {
+  groups.clear();
+  shared_parts.assign(static_cast<size_t>(n), 0);
+  saved_parts = 0;
+  if (max_members < 2 || bpp <= 0) return;
+  // Requests by first block (integer keys), then, inside each run of equal
+  // first blocks, by the rest of their blocks; a request alone in its run
+  // shares nothing and is dropped.
+  static thread_local std::vector<uint64_t> keys;
+  static thread_local std::vector<int32_t> order;
+  keys.clear();
+  order.clear();
+  for (int32_t i = 0; i < n; ++i)
+    if (nfull[i] >= bpp)
+      keys.push_back(static_cast<uint64_t>(static_cast<uint32_t>(blocks[i][0])) << 32 |
+                     static_cast<uint32_t>(i));
+  std::sort(keys.begin(), keys.end());
+  for (size_t a = 0; a < keys.size();) {
+    size_t b = a + 1;
+    while (b < keys.size() && keys[b] >> 32 == keys[a] >> 32) ++b;
+    if (b - a >= 2) {
+      // Every member of the run holds its first `lcp` blocks in common: order
+      // them by what follows.
+      const size_t start = order.size();
+      const int32_t head = static_cast<int32_t>(keys[a] & 0xFFFFFFFFu);
+      int32_t lcp = nfull[head];
+      for (size_t i = a; i < b; ++i) {
+        const int32_t m = static_cast<int32_t>(keys[i] & 0xFFFFFFFFu);
+        order.push_back(m);
+        lcp = std::min(lcp, leading_equal(blocks[head], lcp, blocks[m], nfull[m]));
+      }
+      std::stable_sort(order.begin() + start, order.end(), [&](int32_t x, int32_t y) {
+        return std::lexicographical_compare(blocks[x] + lcp, blocks[x] + nfull[x],
+                                            blocks[y] + lcp, blocks[y] + nfull[y]);
+      });
+    }
+    a = b;
+  }
+  size_t k = 0;
+  while (k < order.size()) {
+    const int32_t first = order[k];
+    int32_t common = nfull[first];
+    size_t end = k + 1;
+    while (end < order.size() && static_cast<int32_t>(end - k) < max_members) {
+      const int32_t next = order[end];
+      const int32_t c =
+          std::min(common, leading_equal(blocks[first], nfull[first], blocks[next], nfull[next]));
+      const int64_t members = static_cast<int64_t>(end - k);
+      if (c / bpp == 0 || members * (c / bpp) < (members - 1) * (common / bpp)) break;
+      common = c;
+      ++end;
+    }
+    const int32_t members = static_cast<int32_t>(end - k);
+    const int32_t parts = common / bpp;
+    if (members >= 2 && parts >= 1) {
+      groups.push_back(members);
+      for (size_t i = k; i < end; ++i) {
+        groups.push_back(order[i]);
+        shared_parts[order[i]] = parts;
+      }
+      groups.resize(groups.size() + (PKV_GROUP_STRIDE - 1 - members), -1);
+      saved_parts += static_cast<int64_t>(members - 1) * parts;
+      k = end;
+    } else {
+      ++k;
+    }
+  }
+}
+
+}  // namespace
+
+int plan_with_groups(const int32_t* const* blocks, const int32_t* nfull, const int32_t* lens,
+                     int32_t n, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t q_dtype, int32_t partition_size,
+                     int32_t num_compute_units, std::vector<uint32_t>& items,
+                     pkv_decode_plan* plan, std::vector<int32_t>& groups,
+                     std::vector<uint32_t>& group_items) {
+  groups.clear();
+  group_items.clear();
+  int32_t longest = 0;
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    longest = std::max(longest, lens[i]);
+    total += std::max(0, lens[i]);
+  }
+  auto plan_items = [&](int32_t part) {
+    items.resize(static_cast<size_t>(std::max(1, pa_decode_plan_capacity(n, longest, block_size))));
+    const int rc = pa_decode_plan(lens, n, num_q_heads, num_kv_heads, head_dim, block_size,
+                                  q_dtype, part, num_compute_units, items.data(),
+                                  static_cast<int32_t>(items.size()), plan);
+    items.resize(rc == PKV_OK ? static_cast<size_t>(plan->num_items) : 0);
+    return rc;
+  };
+  // Shapes the group kernel serves; anything else (bad arguments included, which
+  // pa_decode_plan reports) plans without groups.
+  const int group = num_kv_heads > 0 && num_q_heads % num_kv_heads == 0 ? num_q_heads / num_kv_heads : 0;
+  if (q_dtype != PKV_F16 || group < 1 || group > 8 || n < 2 || block_size <= 0 ||
+      (head_dim != 64 && head_dim != 128) || n > 65535 ||
+      (partition_size > 0 && partition_size % block_size != 0))
+    return plan_items(partition_size);
+  // The partition size the plain plan would take, and the one groups use.
+  int32_t base = partition_size;
+  if (base < 0) {
+    static thread_local std::vector<int32_t> clamped;
+    clamped.resize(static_cast<size_t>(n));
+    for (int32_t i = 0; i < n; ++i) clamped[i] = std::max(0, lens[i]);
+    const KernelChoice kc = choose_kernel(q_dtype, group);
+    base = auto_partition(clamped.data(), n, num_q_heads / kc.gt,
+                          num_compute_units > 0 ? num_compute_units : 256, block_size);
+  }
+  const int32_t part =
+      base > 0 ? base : (kGroupPartitionTokens + block_size - 1) / block_size * block_size;
+  static thread_local std::vector<int32_t> shared_parts;
+  int64_t saved_parts = 0;
+  form_groups(blocks, nfull, n, part / block_size, 16 / group, groups, shared_parts, saved_parts);
+  if (groups.empty() ||
+      static_cast<double>(saved_parts) * part < kGroupMinSavedFraction * static_cast<double>(total)) {
+    groups.clear();
+    return plan_items(partition_size);
+  }
+  if (int rc = plan_items(part)) {
+    groups.clear();
+    return rc;
+  }
+  const int32_t ngroups = static_cast<int32_t>(groups.size() / PKV_GROUP_STRIDE);
+  for (int32_t g = 0; g < ngroups; ++g) {
+    const int32_t first = groups[static_cast<size_t>(g) * PKV_GROUP_STRIDE + 1];
+    for (int32_t j = 0; j < shared_parts[first]; ++j) group_items.push_back(PKV_ITEM(g, j));
+  }
+  size_t kept = 0;
+  for (size_t i = 0; i < items.size(); ++i) {
+    const uint32_t it = items[i];
+    if (static_cast<int32_t>(it & 0xFFFFu) >= shared_parts[it >> 16]) items[kept++] = it;
+  }
+  items.resize(kept);
+  plan->num_items = static_cast<int32_t>(kept);
+  return PKV_OK;
+}
+
+}  // namespace pkv_plan
+
+extern "C" int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t q_dtype, int32_t partition_size,
+                                     int32_t num_compute_units, uint32_t* items,
+                                     int32_t items_capacity, pkv_decode_plan* plan,
+                                     int32_t* groups, int32_t groups_capacity,
+                                     int32_t* num_groups, uint32_t* group_items,
+                                     int32_t* num_group_items) {
+  if (!plan || !num_groups || !num_group_items)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan_groups: NULL output");
+  *num_groups = 0;
+  *num_group_items = 0;
+  if (num_seqs < 0 || num_seqs > 65535 || max_blocks_per_seq < 0 || block_size <= 0 ||
+      groups_capacity < 0 || items_capacity < 0)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan_groups: bad sizes");
+  if (num_seqs > 0 && (!context_lens || (!block_tables && max_blocks_per_seq > 0)))
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan_groups: NULL input");
+  static thread_local std::vector<const int32_t*> rows;
+  static thread_local std::vector<int32_t> nfull, lens;
+  static thread_local std::vector<uint32_t> rest, gitems;
+  static thread_local std::vector<int32_t> gdesc;
+  rows.resize(static_cast<size_t>(num_seqs));
+  nfull.resize(static_cast<size_t>(num_seqs));
+  lens.resize(static_cast<size_t>(num_seqs));
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    lens[i] = std::max(0, context_lens[i]);
+    rows[i] = block_tables + static_cast<int64_t>(i) * max_blocks_per_seq;
+    nfull[i] = std::min(lens[i] / block_size, max_blocks_per_seq);
+  }
+  if (int rc = plan_with_groups(rows.data(), nfull.data(), lens.data(), num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, q_dtype, partition_size,
+                                num_compute_units, rest, plan, gdesc, gitems))
+    return rc;
+  const int32_t ng = static_cast<int32_t>(gdesc.size() / PKV_GROUP_STRIDE);
+  if (static_cast<int64_t>(rest.size()) > items_capacity ||
+      static_cast<int64_t>(gitems.size()) > items_capacity)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan_groups: %zu + %zu items do not fit in %d",
+                rest.size(), gitems.size(), items_capacity);
+  if (ng > groups_capacity)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan_groups: %d groups do not fit in %d", ng,
+                groups_capacity);
+  if ((!rest.empty() && !items) || (!gitems.empty() && !group_items) || (ng > 0 && !groups))
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan_groups: NULL output array");
+  if (!rest.empty()) std::memcpy(items, rest.data(), sizeof(uint32_t) * rest.size());
+  if (!gitems.empty()) std::memcpy(group_items, gitems.data(), sizeof(uint32_t) * gitems.size());
+  if (ng > 0) std::memcpy(groups, gdesc.data(), sizeof(int32_t) * gdesc.size());
+  *num_groups = ng;
+  *num_group_items = static_cast<int32_t>(gitems.size());
+  return PKV_OK;
+}

@@ -5,6 +5,9 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <vector>
+
+#include "pagedkv.h"
 
 namespace pkv_plan {
 
@@ -38,5 +41,25 @@ inline size_t workspace_bytes_for(int32_t S, int32_t Hq, int32_t D, int64_t part
 // the VALU kernel for one-pass launches over skewed lengths.
 constexpr int kMfmaWavesPerCu = 6;
 constexpr int kValuSkewedWavesPerCu = 4;
+
+// Prefix groups (pa_decode_grouped): requests whose leading blocks are the
+// same physical blocks.  blocks[i] points at request i's block ids, of which
+// the first nfull[i] are full (never rewritten while shared).  Plans the
+// launch as pa_decode_plan; then, if grouping saves at least
+// kGroupMinSavedFraction of the batch's token reads, switches a one-pass plan
+// to partitions of kGroupPartitionTokens (rounded up to the block size) and
+// returns the groups ([n][PKV_GROUP_STRIDE] ints: count, members), their work
+// items (group, partition) and the plan's remaining items.  Without a
+// worthwhile group, groups and group_items come back empty and the plan is
+// pa_decode_plan's.  items holds the remaining items on return; its size is
+// plan->num_items.
+constexpr int32_t kGroupPartitionTokens = 64;
+constexpr double kGroupMinSavedFraction = 0.25;
+int plan_with_groups(const int32_t* const* blocks, const int32_t* nfull, const int32_t* lens,
+                     int32_t n, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t q_dtype, int32_t partition_size,
+                     int32_t num_compute_units, std::vector<uint32_t>& items,
+                     pkv_decode_plan* plan, std::vector<int32_t>& groups,
+                     std::vector<uint32_t>& group_items);
 
 }  // namespace pkv_plan

@@ -104,8 +104,11 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                 float scale, int32_t max_context_len, int32_t partition_size,
                 const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
-                void* workspace, size_t workspace_bytes, void* stream, int64_t row_chunks) {
+                void* workspace, size_t workspace_bytes, void* stream, int64_t row_chunks,
+                const int32_t* groups = nullptr, int32_t num_groups = 0,
+                const uint32_t* group_items = nullptr, int32_t num_group_items = 0) {
   const bool contig = row_chunks > 0;
+  const bool grouped = num_group_items > 0;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0 || num_work_items < 0 ||
       waves_per_cu < 0)
@@ -128,10 +131,25 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   if (!fn)
     return fail(PKV_ERR_UNSUPPORTED, "pa_decode: head_dim %d / block_size %d not built", head_dim,
                 block_size);
+  KernelFn group_fn = nullptr;
+  if (grouped) {
+    if (q_dtype != PKV_F16 || num_q_heads / num_kv_heads > 8)
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "pa_decode_grouped: groups need fp16 q and at most 8 query heads per KV head");
+    if (partition_size <= 0)
+      return fail(PKV_ERR_INVALID_ARG, "pa_decode_grouped: groups need partition_size > 0");
+    if (!groups || num_groups <= 0 || !group_items)
+      return fail(PKV_ERR_INVALID_ARG, "pa_decode_grouped: group arrays missing");
+    group_fn = pick_mfma_group_kernel(head_dim, block_size);
+    if (!group_fn)
+      return fail(PKV_ERR_UNSUPPORTED, "pa_decode_grouped: head_dim %d / block_size %d not built",
+                  head_dim, block_size);
+  }
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || (!contig && !block_tables) || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: NULL pointer");
-  if (work_items && num_work_items == 0) return PKV_OK;
+  const bool regular = !work_items || num_work_items > 0;
+  if (!regular && !grouped) return PKV_OK;
 
   int64_t clamp64 = static_cast<int64_t>(max_blocks_per_seq) * block_size;
   if (clamp64 > max_context_len) clamp64 = max_context_len;
@@ -185,8 +203,32 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                                          align256(n * head_dim * sizeof(float)));
   }
 
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (grouped) {
+    // Prefix groups first: their partials (or, for a member whose whole
+    // context is one shared partition, its output) are in place before the
+    // reduce below, which is enqueued after them on the same stream.
+    DecodeParams gp = prm;
+    gp.items = group_items;
+    gp.num_items = num_group_items;
+    gp.groups = groups;
+    gp.num_groups = num_groups;
+    unsigned glds = 0;
+    e = reserve_lds_bytes(reinterpret_cast<const void*>(group_fn), pkv_plan::kMfmaWavesPerCu, &glds);
+    if (e != hipSuccess)
+      return fail(PKV_ERR_HIP, "pa_decode_grouped: kernel attributes: %s", hipGetErrorString(e));
+    const int ny = num_group_items < kMaxGridY ? num_group_items : kMaxGridY;
+    const dim3 ggrid(static_cast<unsigned>(num_kv_heads), static_cast<unsigned>(ny),
+                     static_cast<unsigned>((num_group_items + ny - 1) / ny));
+    hipLaunchKernelGGL(group_fn, ggrid, dim3(kWave), glds, st, gp);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(PKV_ERR_HIP, "pa_decode_grouped launch: %s", hipGetErrorString(e));
+  }
+
   unsigned dyn_lds = 0;
-  hipError_t e = reserve_lds_bytes(reinterpret_cast<const void*>(fn), waves_per_cu, &dyn_lds);
+  e = reserve_lds_bytes(reinterpret_cast<const void*>(fn), waves_per_cu, &dyn_lds);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode: kernel attributes: %s", hipGetErrorString(e));
 
   // One wave per workgroup: the dispatcher then places work at wave granularity.
@@ -203,10 +245,11 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     grid.y = static_cast<unsigned>(ny);
     grid.z = static_cast<unsigned>((num_work_items + ny - 1) / ny);
   }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(fn, grid, dim3(kWave), dyn_lds, st, prm);
-  e = hipGetLastError();
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode launch: %s", hipGetErrorString(e));
+  if (regular) {
+    hipLaunchKernelGGL(fn, grid, dim3(kWave), dyn_lds, st, prm);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode launch: %s", hipGetErrorString(e));
+  }
   if (parts > 1) {
     e = launch_reduce(prm, head_dim, st);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode reduce launch: %s", hipGetErrorString(e));
@@ -228,6 +271,26 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, scale, max_context_len, partition_size, work_items,
                      num_work_items, waves_per_cu, workspace, workspace_bytes, stream, 0);
+}
+
+extern "C" int pa_decode_grouped(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                 const void* v_cache, int32_t num_blocks,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, float scale, int32_t max_context_len,
+                                 int32_t partition_size, const uint32_t* work_items,
+                                 int32_t num_work_items, int32_t waves_per_cu,
+                                 const int32_t* groups, int32_t num_groups,
+                                 const uint32_t* group_items, int32_t num_group_items,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_groups < 0 || num_group_items < 0)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_grouped: negative group sizes");
+  return decode_impl(out, q, q_dtype, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, scale, max_context_len, partition_size, work_items,
+                     num_work_items, waves_per_cu, workspace, workspace_bytes, stream, 0, groups,
+                     num_groups, group_items, num_group_items);
 }
 
 extern "C" int pa_decode_contiguous(float* out, const void* q, int32_t q_dtype,

@@ -7,6 +7,8 @@
 #include <cfloat>
 #include <cstdint>
 
+#include "pagedkv.h"
+
 namespace pkv_decode {
 
 constexpr int kWave = 64;
@@ -41,7 +43,14 @@ struct DecodeParams {
   int32_t max_parts;
   int32_t num_items;
   int64_t row_chunks;         // contiguous layout only: 16-byte chunks per (request, KV head) row
+  const int32_t* groups;      // group launches: [num_groups][kGroupStride] (count, requests...)
+  int32_t num_groups;
 };
+
+// A prefix group (pagedkv.h, pa_decode_grouped): requests whose first tokens
+// are stored in the same physical blocks.  Row i of the descriptor array: the
+// member count, then the members' request indices.
+constexpr int kGroupStride = PKV_GROUP_STRIDE;
 
 // Where the tiles of one (request, KV head) live.  Paged: block id b (from the
 // table) of KV head g starts at chunk (b * Hkv + g) * CHUNKS.  Contiguous
@@ -111,7 +120,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // The (request, partition) piece handled by this workgroup.  With a work list,
 // grid (y, z) enumerates its entries in order (y fastest); without one, grid y
 // is the request and z the partition.  Returns false for entries to skip.
-__device__ __forceinline__ bool scheduled_piece(const DecodeParams& p, int& seq, int& part) {
+__device__ __forceinline__ bool scheduled_piece(const DecodeParams& p, int& seq, int& part,
+                                                int limit) {
   if (p.items) {
     const unsigned k = blockIdx.y + blockIdx.z * gridDim.y;
     if (k >= static_cast<unsigned>(p.num_items)) return false;
@@ -122,7 +132,11 @@ __device__ __forceinline__ bool scheduled_piece(const DecodeParams& p, int& seq,
     seq = static_cast<int>(blockIdx.y);
     part = static_cast<int>(blockIdx.z);
   }
-  return seq < p.num_seqs && part < p.max_parts;
+  return seq < limit && part < p.max_parts;
+}
+
+__device__ __forceinline__ bool scheduled_piece(const DecodeParams& p, int& seq, int& part) {
+  return scheduled_piece(p, seq, part, p.num_seqs);
 }
 
 __device__ __forceinline__ int clamped_len(const DecodeParams& p, int seq) {
@@ -135,6 +149,11 @@ __device__ __forceinline__ int clamped_len(const DecodeParams& p, int seq) {
 // groups of GT in {4, 8, 16} query heads and fp16 queries.
 using KernelFn = void (*)(DecodeParams);
 KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt, bool contiguous);
+
+// The same kernel over prefix groups (pa_decode_grouped): a work item is
+// (group, partition), grid x the KV head, and the 16 rows of the tile are
+// (member i / G, query head i % G) pairs, G = num_q_heads / num_kv_heads.
+KernelFn pick_mfma_group_kernel(int head_dim, int block_size);
 
 // VALU kernel (pa_decode_valu.hip): one wave per (request, head tile,
 // partition), GT in {1, 2, 4} query heads per wave, fp32 or fp16 queries.

@@ -40,7 +40,11 @@ namespace {
 
 constexpr float kSlack = 8.f;
 
-template <int D, int B, int GT, bool kContig>
+// kGroups: the launch runs prefix groups (GT is 16): the tile's rows are the
+// query heads of several requests that read the same physical blocks over the
+// piece's tokens, so each K/V tile is read once for all of them.  The block
+// table and length of the group's first member describe the piece.
+template <int D, int B, int GT, bool kContig, bool kGroups>
 __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
 #ifndef PKV_MFMA_DEPTH
 #define PKV_MFMA_DEPTH 2
@@ -62,32 +66,58 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
   const int lane = threadIdx.x;
   const int grp = lane >> 4;                 // lane group: tokens 4*grp..4*grp+3 of a tile
   const int li = lane & 15;                  // head index (scores) / column (outputs)
-  int seq, part;
-  if (!scheduled_piece(p, seq, part)) return;
-  const int h0 = blockIdx.x * GT;
-  const int kvh = h0 / p.group;
+  int seq, part;                             // seq: the request, or the group (kGroups)
+  if (!scheduled_piece(p, seq, part, kGroups ? p.num_groups : p.num_seqs)) return;
+  // Tile row r: query head h0 + r of request seq; with groups, query head
+  // h0 + r % G of member r / G.  Rows at or past `rows` are unused.
+  int h0, kvh, rows, rep;
+  const int32_t* members = nullptr;
+  if constexpr (kGroups) {
+    kvh = blockIdx.x;
+    h0 = kvh * p.group;
+    members = p.groups + static_cast<int64_t>(seq) * kGroupStride + 1;
+    const int cap = GT / p.group;            // members that fit in the tile
+    const int n = members[-1];
+    rows = (n < 1 ? 1 : (n > cap ? cap : n)) * p.group;
+  } else {
+    h0 = blockIdx.x * GT;
+    kvh = h0 / p.group;
+    rows = GT;
+  }
+  // Request and query head of tile row r (r < rows); member ids out of range read as 0.
+  auto row_seq = [&](int r) {
+    if constexpr (kGroups) {
+      const int m = members[r / p.group];
+      return static_cast<unsigned>(m) < static_cast<unsigned>(p.num_seqs) ? m : 0;
+    } else {
+      return seq;
+    }
+  };
+  auto row_head = [&](int r) { return kGroups ? h0 + r % p.group : h0 + r; };
+  rep = row_seq(0);
 
   // Independent loads first: table ids, queries, length.
   const int32_t* table =
-      kContig ? nullptr : p.block_tables + static_cast<int64_t>(seq) * p.max_blocks_per_seq;
+      kContig ? nullptr : p.block_tables + static_cast<int64_t>(rep) * p.max_blocks_per_seq;
   const int blk_begin = part * (p.part_tokens / B);
   const int staged_first = block_id<kContig>(table, blk_begin + lane, p.max_blocks_per_seq);
   half8 qb[KSTEPS];                          // Q^T as the B operand: head li, dims kk*32 + 8*grp
   {
+    const int r = li < rows ? li : 0;
     const _Float16* qp = static_cast<const _Float16*>(p.q) +
-                         (static_cast<int64_t>(seq) * p.num_q_heads + h0 + (li < GT ? li : 0)) * D +
+                         (static_cast<int64_t>(row_seq(r)) * p.num_q_heads + row_head(r)) * D +
                          8 * grp;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       const half8 v = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(qp + kk * 32));
-      qb[kk] = li < GT ? v : half8{};
+      qb[kk] = li < rows ? v : half8{};
     }
   }
-  const int len = clamped_len(p, seq);
+  const int len = clamped_len(p, rep);
   const int t_begin = part * p.part_tokens;
-  float* const out_rows = p.out + (static_cast<int64_t>(seq) * p.num_q_heads + h0) * D;
   if (t_begin >= len) {
-    if (part == 0) {                          // empty context: defined as zeros
+    if (!kGroups && part == 0) {              // empty context: defined as zeros
+      float* const out_rows = p.out + (static_cast<int64_t>(seq) * p.num_q_heads + h0) * D;
       for (int x = lane; x < GT * D / 4; x += kWave)
         reinterpret_cast<float4*>(out_rows)[x] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -243,14 +273,18 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * grp + r;
-    if (h >= GT) continue;
-    if (nparts == 1) {
+    if (h >= rows) continue;
+    // A member's own partition count decides whether this piece is its whole
+    // context (write the output) or one of several partials.
+    const int rs = row_seq(h);
+    const int np = kGroups ? (clamped_len(p, rs) + p.part_tokens - 1) / p.part_tokens : nparts;
+    const int64_t orow = static_cast<int64_t>(rs) * p.num_q_heads + row_head(h);
+    if (np == 1) {
       const float inv = 1.f / lr[r];
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) out_rows[h * D + db * 16 + li] = o[db][r] * inv;
+      for (int db = 0; db < DBLK; ++db) p.out[orow * D + db * 16 + li] = o[db][r] * inv;
     } else {
-      const int64_t slot =
-          (static_cast<int64_t>(seq) * p.num_q_heads + h0 + h) * p.max_parts + part;
+      const int64_t slot = orow * p.max_parts + part;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) p.ws_o[slot * D + db * 16 + li] = o[db][r];
       if (li == 0) {
@@ -264,9 +298,9 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
 template <int D, int B, bool kContig>
 KernelFn pick_gt(int gt) {
   switch (gt) {
-    case 4: return pa_decode_mfma_kernel<D, B, 4, kContig>;
-    case 8: return pa_decode_mfma_kernel<D, B, 8, kContig>;
-    case 16: return pa_decode_mfma_kernel<D, B, 16, kContig>;
+    case 4: return pa_decode_mfma_kernel<D, B, 4, kContig, false>;
+    case 8: return pa_decode_mfma_kernel<D, B, 8, kContig, false>;
+    case 16: return pa_decode_mfma_kernel<D, B, 16, kContig, false>;
     default: return nullptr;
   }
 }
@@ -283,7 +317,25 @@ KernelFn pick_b(int b, int gt) {
   }
 }
 
+template <int D>
+KernelFn pick_group_b(int b) {
+  switch (b) {
+    case 8: return pa_decode_mfma_kernel<D, 8, 16, false, true>;
+    case 16: return pa_decode_mfma_kernel<D, 16, 16, false, true>;
+    case 32: return pa_decode_mfma_kernel<D, 32, 16, false, true>;
+    case 64: return pa_decode_mfma_kernel<D, 64, 16, false, true>;
+    case 128: return pa_decode_mfma_kernel<D, 128, 16, false, true>;
+    default: return nullptr;
+  }
+}
+
 }  // namespace
+
+KernelFn pick_mfma_group_kernel(int head_dim, int block_size) {
+  if (head_dim == 64) return pick_group_b<64>(block_size);
+  if (head_dim == 128) return pick_group_b<128>(block_size);
+  return nullptr;
+}
 
 KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt, bool contiguous) {
   if (contiguous) {

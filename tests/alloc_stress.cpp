@@ -29,6 +29,59 @@
     }                                                                         \
   } while (0)
 
+// Prefix groups of one step (kv_decode_step_host with PKV_STEP_GROUPS): every
+// group piece lies in the same physical blocks of all its members' tables and
+// within their lengths, and group pieces plus the remaining work items name
+// each (request, partition) piece exactly once.
+static long g_grouped_steps = 0;
+
+static void check_groups(const char* base, const kv_step_layout& lay, int32_t n, int32_t bs) {
+  g_grouped_steps += lay.num_groups > 0;
+  const int32_t* tables = reinterpret_cast<const int32_t*>(base + lay.tables_offset);
+  const int32_t* lens = reinterpret_cast<const int32_t*>(base + lay.lens_offset);
+  const uint32_t* items = reinterpret_cast<const uint32_t*>(base + lay.items_offset);
+  const int32_t* groups = reinterpret_cast<const int32_t*>(base + lay.groups_offset);
+  const uint32_t* gitems = reinterpret_cast<const uint32_t*>(base + lay.group_items_offset);
+  const int32_t pt = lay.plan.partition_size;
+  const int32_t w = lay.max_blocks;
+  std::map<std::pair<int32_t, int32_t>, int> seen;
+  for (int32_t i = 0; i < lay.plan.num_items; ++i)
+    seen[std::make_pair(static_cast<int32_t>(items[i] >> 16), static_cast<int32_t>(items[i] & 0xFFFF))] += 1;
+  if (lay.num_group_items > 0) CHECK(pt > 0 && pt % bs == 0);
+  for (int32_t g = 0; g < lay.num_groups; ++g) {
+    const int32_t* row = groups + static_cast<int64_t>(g) * PKV_GROUP_STRIDE;
+    CHECK(row[0] >= 2 && row[0] <= 4);         // 8 query heads over 2 KV heads: 16 / 4 members
+    std::set<int32_t> mem(row + 1, row + 1 + row[0]);
+    CHECK(static_cast<int32_t>(mem.size()) == row[0]);
+    for (int32_t m : mem) CHECK(m >= 0 && m < n);
+  }
+  for (int32_t k = 0; k < lay.num_group_items; ++k) {
+    const int32_t g = static_cast<int32_t>(gitems[k] >> 16), p = static_cast<int32_t>(gitems[k] & 0xFFFF);
+    CHECK(g < lay.num_groups);
+    const int32_t* row = groups + static_cast<int64_t>(g) * PKV_GROUP_STRIDE;
+    const int32_t first = row[1];
+    for (int32_t j = 0; j < row[0]; ++j) {
+      const int32_t m = row[1 + j];
+      CHECK(static_cast<int64_t>(p + 1) * pt <= lens[m]);
+      for (int32_t b = p * pt / bs; b < (p + 1) * pt / bs; ++b)
+        CHECK(b < w && tables[static_cast<int64_t>(m) * w + b] == tables[static_cast<int64_t>(first) * w + b]);
+      seen[std::make_pair(m, p)] += 1;
+    }
+  }
+  for (int32_t s = 0; s < n; ++s) {
+    const int32_t np = pt > 0 && lens[s] > 0 ? (lens[s] + pt - 1) / pt : 1;
+    for (int32_t p = 0; p < np; ++p) {
+      const int count = seen[std::make_pair(s, p)];
+      CHECK(count == 1);
+    }
+  }
+  size_t total = 0;
+  for (const auto& kv : seen) total += kv.second;
+  size_t want = 0;
+  for (int32_t s = 0; s < n; ++s) want += pt > 0 && lens[s] > 0 ? (lens[s] + pt - 1) / pt : 1;
+  CHECK(total == want);
+}
+
 int main(int argc, char** argv) {
   const int iters = argc > 1 ? std::atoi(argv[1]) : 20000;
   std::mt19937 rng(7);
@@ -92,11 +145,12 @@ int main(int argc, char** argv) {
           kv_step_layout lay{};
           const int32_t n = static_cast<int32_t>(batch.size());
           const int32_t part = static_cast<int32_t>(rng() % 3) == 0 ? -1 : bs * (1 + rng() % 4);
-          rc = kv_decode_step_host(a, batch.data(), n, 0, -1, 8, 2, 64, PKV_F16, part, 0, nullptr,
-                                   0, &lay);
+          const int32_t flags = rng() % 2 ? PKV_STEP_GROUPS : 0;
+          rc = kv_decode_step_host(a, batch.data(), n, 0, -1, 8, 2, 64, PKV_F16, part, 0, flags,
+                                   nullptr, 0, &lay);
           CHECK(rc == PKV_ERR_INVALID_ARG && lay.total_bytes > 0);
           std::vector<char> buf(lay.total_bytes);
-          rc = kv_decode_step_host(a, batch.data(), n, 0, -1, 8, 2, 64, PKV_F16, part, 0,
+          rc = kv_decode_step_host(a, batch.data(), n, 0, -1, 8, 2, 64, PKV_F16, part, 0, flags,
                                    buf.data(), buf.size(), &lay);
           if (rc == PKV_OK) {
             ncow = lay.num_pairs;
@@ -104,7 +158,11 @@ int main(int argc, char** argv) {
             std::map<int32_t, int64_t> want;
             for (int32_t s : batch) want[s] = (want.count(s) ? want[s] : len[s]) + 1;
             for (int32_t i = 0; i < n; ++i) CHECK(lens_out[i] == want[batch[i]]);
-            CHECK(lay.plan.num_items >= 1 && lay.items_offset + 4ull * lay.plan.num_items <= buf.size());
+            CHECK(lay.plan.num_items + lay.num_group_items >= 1 &&
+                  lay.items_offset + 4ull * lay.plan.num_items <= buf.size());
+            CHECK(flags || lay.num_groups == 0);
+            CHECK(lay.group_items_offset + 4ull * lay.num_group_items <= buf.size());
+            check_groups(buf.data(), lay, n, bs);
           }
         }
         if (rc == PKV_OK) {
@@ -252,6 +310,6 @@ int main(int argc, char** argv) {
     CHECK(st.host_free_blocks == nh && st.swapped_seqs == 0);
     kv_allocator_destroy(a);
   }
-  std::printf("ok\n");
+  std::printf("ok grouped_steps=%ld\n", g_grouped_steps);
   return 0;
 }

@@ -36,4 +36,7 @@ def test_allocator_under_asan_ubsan(tmp_path):
     run = subprocess.run([exe, "40000"], capture_output=True, text=True, env=env, timeout=600)
     if "runtime does not come first" in run.stderr:
         pytest.skip("ASan runtime cannot initialise under this host's preload order")
-    assert run.returncode == 0 and run.stdout.strip() == "ok", (run.stdout[-2000:], run.stderr[-4000:])
+    assert run.returncode == 0 and run.stdout.startswith("ok"), (run.stdout[-2000:], run.stderr[-4000:])
+    grouped = int(run.stdout.split("grouped_steps=")[1])
+    assert grouped > 0, "no step formed prefix groups: the group planner went unexercised"
+    print(run.stdout.strip())
