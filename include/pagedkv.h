@@ -331,7 +331,7 @@ int pa_decode(float* out, const void* q, int32_t q_dtype,
  * partition reads do not shrink.  Grouping is used when it saves at least a
  * quarter of the batch's token reads, with fp16 q, head_dim 64 or 128 and at
  * most 8 query heads per KV head; then a one-pass plan (partition_size 0)
- * becomes a plan with 64-token partitions (rounded up to block_size).
+ * becomes a plan with 128-token partitions (rounded up to block_size).
  *   block_tables   : HOST int32 [num_seqs][max_blocks_per_seq].
  *   items          : HOST uint32 [items_capacity]: the plan's pieces minus
  *                    the group pieces (plan->num_items of them).
@@ -365,6 +365,8 @@ int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_blocks_per_se
  * piece the partition's tokens lie in the same physical blocks in every
  * member's table and within every member's length, and that the group pieces
  * and work_items together name each piece of each request exactly once.
+ * work_items NULL means every piece, as for pa_decode; when the groups cover
+ * every piece, pass any non-NULL address with num_work_items 0.
  * Other arguments as pa_decode.  Errors as pa_decode, plus
  * PKV_ERR_UNSUPPORTED for group pieces with q not fp16 or more than 8 query
  * heads per KV head, and PKV_ERR_INVALID_ARG for group pieces with

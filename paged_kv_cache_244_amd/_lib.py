@@ -378,10 +378,12 @@ def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scal
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
     if groups.dim() != 2 or groups.shape[1] != GROUP_STRIDE:
         raise ValueError(f"groups must be int32 [num_groups, {GROUP_STRIDE}]")
+    g_ptr, n_g = _items(group_items)
     items_ptr, n_items = c_void_p(None), 0
     if work_items is not None:
-        items_ptr, n_items = _items(work_items)
-    g_ptr, n_g = _items(group_items)
+        # An empty list (every piece grouped) still needs an address: NULL means
+        # "every piece" to the library.
+        items_ptr, n_items = _items(work_items) if work_items.numel() else (g_ptr, 0)
     ws_ptr, ws_bytes = c_void_p(None), 0
     if workspace is not None:
         ws_ptr = _dev(workspace, torch.uint8, "workspace")

@@ -53,7 +53,7 @@ constexpr int kValuSkewedWavesPerCu = 4;
 // worthwhile group, groups and group_items come back empty and the plan is
 // pa_decode_plan's.  items holds the remaining items on return; its size is
 // plan->num_items.
-constexpr int32_t kGroupPartitionTokens = 64;
+constexpr int32_t kGroupPartitionTokens = 128;
 constexpr double kGroupMinSavedFraction = 0.25;
 int plan_with_groups(const int32_t* const* blocks, const int32_t* nfull, const int32_t* lens,
                      int32_t n, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

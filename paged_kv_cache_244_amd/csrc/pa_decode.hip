@@ -240,7 +240,7 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   // order must carry similar work: the head tiles of one piece do.
   dim3 grid(static_cast<unsigned>(prm.num_head_tiles), static_cast<unsigned>(num_seqs),
             static_cast<unsigned>(parts));
-  if (work_items) {
+  if (work_items && num_work_items > 0) {   // an empty list (every piece grouped) launches nothing
     const int ny = num_work_items < kMaxGridY ? num_work_items : kMaxGridY;
     grid.y = static_cast<unsigned>(ny);
     grid.z = static_cast<unsigned>((num_work_items + ny - 1) / ny);

@@ -69,9 +69,9 @@ def test_parallel_sampling_groups_one_per_prompt():
         width = -(-(int(w.prompt_lengths.max()) + steps) // B)
         tables, lens = a.export(samples, width, -1)
         items, plan, groups, gitems = _lib.plan_groups(tables, lens, 40, 40, 128, B)
-        assert plan["partition_size"] == 64          # one-pass plan switched to 64-token pieces
+        assert plan["partition_size"] == 128         # one-pass plan switched to 128-token pieces
         _check_cover(tables, lens, items, plan, groups, gitems, 16)
-        full_parts = (w.prompt_lengths // B) * B // 64
+        full_parts = (w.prompt_lengths // B) * B // 128
         want = sorted(list(range(i * 8, i * 8 + 8)) for i in range(w.num_prompts) if full_parts[i] > 0)
         got = sorted(sorted(g[1:1 + g[0]].tolist()) for g in groups)
         assert got == want

@@ -8,6 +8,8 @@ the fp64 oracle (max-abs 2e-3, relative L2 1e-3) over each sample's own
 logical view (its prompt, then its own tokens), at several steps, for MHA
 (groups of 8 samples) and for 8 query heads over 2 KV heads (groups of 4
 samples); the same steps with grouping off must agree within the same bound.
+The output is read back through the cache's stream alone: every launch of
+the grouped decode must be ordered on that stream.
 """
 
 import numpy as np
@@ -59,8 +61,12 @@ def test_grouped_decode_matches_oracle(hq, hkv, d, bs):
                                      v_new=torch.from_numpy(step_v[t]).to(dev))
             grouped.append(batch.group_items_dev is not None)
             out = c.attend(torch.from_numpy(step_q[t]).to(dev), batch, scale)
-            torch.cuda.synchronize()
-            outs.append(out.cpu().numpy())
+            # Read the output through the cache's own stream only.
+            host = torch.empty(out.shape, dtype=out.dtype, pin_memory=True)
+            with torch.cuda.stream(c.stream):
+                host.copy_(out, non_blocking=True)
+            c.stream.synchronize()
+            outs.append(host.numpy().copy())
         return outs, grouped
 
     got, grouped = run(True)
@@ -76,3 +82,41 @@ def test_grouped_decode_matches_oracle(hq, hkv, d, bs):
             want[i] = attention.attend_one(step_q[t, i], keys, vals, scale)
         paths.assert_attention_close(got[t], want)
         paths.assert_attention_close(plain[t], want)
+
+
+def test_groups_covering_every_piece():
+    """Forks of a 256-token prompt before any append: every block is shared, so
+    the group pieces cover every partition and no work item remains (the launch
+    then runs the group kernel and the reduce only)."""
+    import torch
+
+    from paged_kv_cache_244_amd import _lib
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    print("\n[case] groups covering every piece", flush=True)
+    rng = np.random.default_rng(21)
+    hq, hkv, d, bs, L = 8, 8, 128, 16, 256
+    c = PagedKVCache(64, hkv, d, bs, initial_order=rng.permutation(64).astype(np.int32),
+                     num_q_heads=hq, q_dtype=torch.float16)
+    k = rng.standard_normal((L, hkv, d)).astype(np.float16)
+    v = rng.standard_normal((L, hkv, d)).astype(np.float16)
+    p = c.new_sequence()
+    c.write(c.reserve_many([p], [L]), torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    kids = [c.fork(p) for _ in range(4)]
+    tables, lens = c.alloc.export(kids, L // bs, -1)
+    items, plan, groups, gitems = _lib.plan_groups(tables, lens, hq, hkv, d, bs)
+    assert len(items) == 0 and len(groups) == 1 and len(gitems) == L // plan["partition_size"]
+    q = rng.standard_normal((4, hq, d)).astype(np.float16)
+    out = torch.full((4, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(_lib.pa_decode_workspace_size(4, hq, d, L, plan["partition_size"]),
+                     dtype=torch.uint8, device="cuda")
+    _lib.pa_decode_grouped(out, torch.from_numpy(q).cuda(), c.k[0], c.v[0],
+                           torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                           1.0 / np.sqrt(d), L, plan["partition_size"],
+                           torch.from_numpy(groups).cuda(),
+                           torch.from_numpy(gitems.view(np.int32)).cuda(), workspace=ws,
+                           work_items=torch.empty(0, dtype=torch.int32, device="cuda"),
+                           stream=c.stream)
+    torch.cuda.synchronize()
+    want = np.stack([attention.attend_one(q[i], k, v, 1.0 / np.sqrt(d)) for i in range(4)])
+    paths.assert_attention_close(out.cpu().numpy(), want)
