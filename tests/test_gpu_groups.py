@@ -6,8 +6,9 @@ forgets: pages enable sharing, not just packing"); the grouped launch reads
 each such block once for a whole group.  Every output row is checked against
 the fp64 oracle (max-abs 2e-3, relative L2 1e-3) over each sample's own
 logical view (its prompt, then its own tokens), at several steps, for MHA
-(groups of 8 samples) and for 8 query heads over 2 KV heads (groups of 4
-samples); the same steps with grouping off must agree within the same bound.
+(groups of 8 samples), 4 query heads per KV head (groups of 4) and 8 per KV
+head (groups of 2), block sizes 8 to 128; the same steps with grouping off
+must agree within the same bound.
 The output is read back through the cache's stream alone: every launch of
 the grouped decode must be ordered on that stream.
 """
@@ -21,7 +22,8 @@ from tests import paths
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("hq,hkv,d,bs", [(8, 8, 128, 16), (8, 2, 64, 32), (4, 4, 128, 8)])
+@pytest.mark.parametrize("hq,hkv,d,bs", [(8, 8, 128, 16), (8, 2, 64, 32), (4, 4, 128, 8),
+                                         (16, 2, 64, 128), (8, 1, 128, 64)])
 def test_grouped_decode_matches_oracle(hq, hkv, d, bs):
     import torch
 
