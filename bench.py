@@ -703,13 +703,15 @@ def churn_bench(args):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
+    part = "auto" if args.partition == "auto" else int(args.partition)
+
     def step(t, e=None):
         nonlocal groups
         groups = _beam_prune(w, t, groups, cache.free, cache.fork)
         seqs = [s for g in groups for s in g]
         k, v, q = inputs[t]
         layer = t % layers
-        _, batch = cache.decode_step(seqs, k_new=k, v_new=v, layer=layer)
+        _, batch = cache.decode_step(seqs, k_new=k, v_new=v, layer=layer, partition_size=part)
         if e is not None:
             e[0].record(cache.stream)
         cache.attend(q, batch, w.scale, layer=layer, out=out)

@@ -328,19 +328,27 @@ int pa_decode(float* out, const void* q, int32_t q_dtype,
  * Requests are ordered by their block ids; neighbours whose leading FULL
  * blocks (the first floor(len / block_size) entries of a row) are the same
  * physical blocks form groups, a member joining only when the group's saved
- * partition reads do not shrink.  Grouping is used when it saves at least a
+ * block reads do not shrink.  Grouping is used when it saves at least a
  * quarter of the batch's token reads, with fp16 q, head_dim 64 or 128 and at
  * most 8 query heads per KV head; then a one-pass plan (partition_size 0)
- * becomes a plan with 128-token partitions (rounded up to block_size).
+ * becomes a plan with 256-token partitions (rounded up to block_size).
+ * A group's shared length Ls is its common full blocks times block_size.
+ * Group pieces cover its whole partitions and, when Ls ends inside a
+ * partition, that partition's tokens before Ls; each member's own piece of
+ * that partition then starts at Ls (if the member has tokens there).
  *   block_tables   : HOST int32 [num_seqs][max_blocks_per_seq].
  *   items          : HOST uint32 [items_capacity]: the plan's pieces minus
  *                    the group pieces (plan->num_items of them).
  *   groups         : HOST int32 [groups_capacity][PKV_GROUP_STRIDE]; at most
  *                    num_seqs / 2 groups are formed.
  *   group_items    : HOST uint32 [items_capacity]: PKV_ITEM(group, partition)
- *                    for every partition that all members' tables share.
- * Other arguments and errors as pa_decode_plan.  With no worthwhile group,
- * *num_groups = *num_group_items = 0 and the result is pa_decode_plan's.
+ *                    for every partition the group's shared blocks reach.
+ *   shared_lens    : HOST int32 [num_seqs]: Ls for members of a group whose
+ *                    Ls ends inside a partition, else 0.
+ * plan->workspace_bytes is the workspace pa_decode_grouped needs (one spare
+ * partial slot per request).  Other arguments and errors as pa_decode_plan.
+ * With no worthwhile group, *num_groups = *num_group_items = 0, shared_lens
+ * is not written and the result is pa_decode_plan's.
  */
 int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_blocks_per_seq,
                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -348,7 +356,7 @@ int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_blocks_per_se
                           int32_t q_dtype, int32_t partition_size, int32_t num_compute_units,
                           uint32_t* items, int32_t items_capacity, pkv_decode_plan* plan,
                           int32_t* groups, int32_t groups_capacity, int32_t* num_groups,
-                          uint32_t* group_items, int32_t* num_group_items);
+                          uint32_t* group_items, int32_t* num_group_items, int32_t* shared_lens);
 
 /*
  * pa_decode_grouped — pa_decode where some pieces are run by prefix groups.
@@ -361,6 +369,17 @@ int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_blocks_per_se
  * pieces, the remaining pieces (work_items), then the combine.
  *   groups, num_groups       : device int32 [num_groups][PKV_GROUP_STRIDE].
  *   group_items, num_group_items : device uint32 PKV_ITEM(group, partition).
+ *   shared_lens              : device int32 [num_seqs] as pa_decode_plan_groups
+ *                              writes it, or NULL when no shared length ends
+ *                              inside a partition.  A group piece (g, p) stops
+ *                              at its first member's shared length when that
+ *                              falls inside partition p; a listed piece
+ *                              (request, p) of such a partition starts there
+ *                              and its partial goes to a spare slot.
+ *   workspace                : pa_decode_workspace_size(num_seqs, num_q_heads,
+ *                              head_dim, max_context_len + partition_size,
+ *                              partition_size) bytes: one spare partition
+ *                              slot per request.
  * The caller guarantees, as pa_decode_plan_groups does, that for every group
  * piece the partition's tokens lie in the same physical blocks in every
  * member's table and within every member's length, and that the group pieces
@@ -382,7 +401,8 @@ int pa_decode_grouped(float* out, const void* q, int32_t q_dtype,
                       int32_t partition_size, const uint32_t* work_items, int32_t num_work_items,
                       int32_t waves_per_cu, const int32_t* groups, int32_t num_groups,
                       const uint32_t* group_items, int32_t num_group_items,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      const int32_t* shared_lens, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /*
  * pa_decode_contiguous — the same decode attention over the layout without a
@@ -603,6 +623,8 @@ typedef struct {
   pkv_decode_plan plan;     /* plan.num_items: the pieces at items_offset               */
   uint64_t groups_offset;   /* int32 [num_groups][PKV_GROUP_STRIDE] (PKV_STEP_GROUPS)   */
   uint64_t group_items_offset; /* uint32 [num_group_items]                              */
+  uint64_t shared_lens_offset; /* int32 [num_seqs] when num_groups > 0 (see
+                                  pa_decode_plan_groups)                                */
   int32_t num_groups;
   int32_t num_group_items;
 } kv_step_layout;

@@ -71,6 +71,7 @@ class StepLayout(ctypes.Structure):
                 ("num_pairs", c_int32), ("max_blocks", c_int32), ("max_context_len", c_int32),
                 ("reserved", c_int32), ("plan", DecodePlan),
                 ("groups_offset", ctypes.c_uint64), ("group_items_offset", ctypes.c_uint64),
+                ("shared_lens_offset", ctypes.c_uint64),
                 ("num_groups", c_int32), ("num_group_items", c_int32)]
 
 
@@ -141,12 +142,12 @@ _SIGNATURES = {
     "pa_decode_plan_groups": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,
                                         c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                         c_int32, POINTER(DecodePlan), c_void_p, c_int32,
-                                        POINTER(c_int32), c_void_p, POINTER(c_int32)]),
+                                        POINTER(c_int32), c_void_p, POINTER(c_int32), c_void_p]),
     "pa_decode_grouped": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                                     c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                     c_int32, c_float, c_int32, c_int32, c_void_p, c_int32, c_int32,
-                                    c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_size_t,
-                                    c_void_p]),
+                                    c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
+                                    c_size_t, c_void_p]),
 }
 
 _lib = None
@@ -316,10 +317,12 @@ def plan_groups(block_tables, context_lens, num_q_heads, num_kv_heads, head_dim,
                 q_dtype=PKV_F16, partition_size=-1, num_compute_units=0):
     """``pa_decode_plan_groups``: the decode plan with prefix groups, from host tables.
 
-    Returns (items, plan, groups, group_items): the remaining work items, the plan dict
-    (its num_items counts them), groups int32 [num_groups, 17] (count, members) and
-    group_items uint32 (group << 16 | partition).  No worthwhile group: groups is empty
-    and the rest equals ``plan``'s result.
+    Returns (items, plan, groups, group_items, shared_lens): the remaining work items,
+    the plan dict (its num_items counts them; its workspace_bytes covers the grouped
+    launch), groups int32 [num_groups, 17] (count, members), group_items uint32
+    (group << 16 | partition) and shared_lens int32 [num_seqs] (a group's shared length
+    where it ends inside a partition, else 0).  No worthwhile group: groups is empty and
+    the rest equals ``plan``'s result.
     """
     tables = np.ascontiguousarray(block_tables, dtype=np.int32)
     lens = np.ascontiguousarray(context_lens, dtype=np.int32)
@@ -331,16 +334,17 @@ def plan_groups(block_tables, context_lens, num_q_heads, num_kv_heads, head_dim,
     gitems = np.empty(max(cap, 1), dtype=np.uint32)
     gcap = max(1, n // 2)
     groups = np.empty((gcap, GROUP_STRIDE), dtype=np.int32)
+    shared = np.zeros(max(n, 1), dtype=np.int32)
     pl, ng, ngi = DecodePlan(), c_int32(0), c_int32(0)
     _check(lib().pa_decode_plan_groups(
         tables.ctypes.data if tables.size else None, int(tables.shape[1]),
         lens.ctypes.data if n else None, n, int(num_q_heads), int(num_kv_heads), int(head_dim),
         int(block_size), int(q_dtype), int(partition_size), int(num_compute_units),
         items.ctypes.data, int(items.shape[0]), byref(pl), groups.ctypes.data, gcap, byref(ng),
-        gitems.ctypes.data, byref(ngi)))
+        gitems.ctypes.data, byref(ngi), shared.ctypes.data))
     info = {name: int(getattr(pl, name)) for name, _ in DecodePlan._fields_}
     return (items[: info["num_items"]].copy(), info, groups[: ng.value].copy(),
-            gitems[: ngi.value].copy())
+            gitems[: ngi.value].copy(), shared[:n].copy())
 
 
 def _items(work_items):
@@ -363,10 +367,13 @@ def set_kernel_policy(policy: int) -> int:
 
 def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                       max_context_len, partition_size, groups, group_items, workspace=None,
-                      stream=None, work_items=None, waves_per_cu=0):
-    """``pa_decode`` with prefix groups: ``groups`` a device int32 [num_groups, 17] tensor
-    and ``group_items`` a device int32/uint32 tensor of (group << 16 | partition) pieces,
-    as ``plan_groups`` returns them; ``work_items`` the remaining pieces."""
+                      stream=None, work_items=None, waves_per_cu=0, shared_lens=None):
+    """``pa_decode`` with prefix groups: ``groups`` a device int32 [num_groups, 17] tensor,
+    ``group_items`` a device int32/uint32 tensor of (group << 16 | partition) pieces and
+    ``shared_lens`` a device int32 [S] tensor (or None), as ``plan_groups`` returns them;
+    ``work_items`` the remaining pieces.  The workspace is
+    ``pa_decode_workspace_size(S, Hq, D, max_context_len + partition_size, partition_size)``
+    bytes (one spare slot per request)."""
     torch = _torch()
     nb, hkv, bs, d = _pool_geometry(k_cache, v_cache)
     s, hq, dq = (int(x) for x in q.shape)
@@ -394,8 +401,9 @@ def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scal
         _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
         _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, bs, float(scale),
         int(max_context_len), int(partition_size), items_ptr, n_items, int(waves_per_cu),
-        _dev(groups, torch.int32, "groups"), int(groups.shape[0]), g_ptr, n_g, ws_ptr, ws_bytes,
-        _stream(stream)))
+        _dev(groups, torch.int32, "groups"), int(groups.shape[0]), g_ptr, n_g,
+        _dev(shared_lens, torch.int32, "shared_lens") if shared_lens is not None else None,
+        ws_ptr, ws_bytes, _stream(stream)))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):

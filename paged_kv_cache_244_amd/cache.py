@@ -381,6 +381,7 @@ class PagedKVCache:
                                            (lay.num_groups, _lib.GROUP_STRIDE))
             batch.group_items_dev = DeviceArray(dev, lay.group_items_offset, torch.int32,
                                                 (lay.num_group_items,))
+            batch.shared_dev = DeviceArray(dev, lay.shared_lens_offset, torch.int32, (n,))
         return slots, batch
 
     def write(self, slots, k_new: torch.Tensor, v_new: torch.Tensor, layer: int = 0):
@@ -481,15 +482,17 @@ class PagedKVCache:
                 or not out.is_contiguous()):
             raise ValueError("out must be a contiguous device fp32 [S, Hq, head_dim] tensor")
         part = info["partition_size"]
-        ws = self.workspace(s, hq, batch.max_len, part)
-        if key == batch.plan_key and batch.group_items_dev is not None:
+        grouped = key == batch.plan_key and batch.group_items_dev is not None
+        # a grouped launch keeps one spare partial slot per request
+        ws = self.workspace(s, hq, batch.max_len + (part if grouped else 0), part)
+        if grouped:
             g, gi = batch.groups_dev, batch.group_items_dev
             _lib._check(_lib.lib().pa_decode_grouped(
                 out.data_ptr(), q.data_ptr(), _lib.PKV_F16, self.k[layer].data_ptr(),
                 self.v[layer].data_ptr(), self.num_blocks, batch.tables_dev.ptr,
                 batch.tables_dev.shape[1], batch.lens_dev.ptr, s, hq, self.num_kv_heads, d,
                 self.block_size, float(scale), batch.max_len, part, items.ptr, items.shape[0],
-                info["waves_per_cu"], g.ptr, g.shape[0], gi.ptr, gi.shape[0],
+                info["waves_per_cu"], g.ptr, g.shape[0], gi.ptr, gi.shape[0], batch.shared_dev.ptr,
                 ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
                 self._stream_ptr))
             return out
@@ -514,11 +517,11 @@ class DecodeBatch:
     made for."""
 
     __slots__ = ("tables_dev", "lens_dev", "max_len", "lens_host", "items_dev", "plan",
-                 "plan_key", "num_seqs", "groups_dev", "group_items_dev")
+                 "plan_key", "num_seqs", "groups_dev", "group_items_dev", "shared_dev")
 
     def __init__(self, tables, lens, max_len, lens_host, items, plan, plan_key):
         self.tables_dev, self.lens_dev, self.items_dev = tables, lens, items
-        self.groups_dev = self.group_items_dev = None     # prefix groups, when planned
+        self.groups_dev = self.group_items_dev = self.shared_dev = None   # prefix groups
         self.max_len = max_len
         self.lens_host = lens_host
         self.plan = plan

@@ -517,7 +517,7 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
   // them as they are (only a partly filled last block can be copied on write),
   // so they are what the tables hold after it.
   static thread_local std::vector<uint32_t> items, group_items;
-  static thread_local std::vector<int32_t> groups, nfull;
+  static thread_local std::vector<int32_t> groups, nfull, shared_lens;
   static thread_local std::vector<const int32_t*> rows;
   pkv_decode_plan plan{};
   rows.resize(static_cast<size_t>(num_seqs));
@@ -530,7 +530,7 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
   if (int rc = pkv_plan::plan_with_groups(rows.data(), nfull.data(), lens.data(), num_seqs,
                                           num_q_heads, num_kv_heads, head_dim, B, q_dtype,
                                           partition_size, num_compute_units, items, &plan, groups,
-                                          group_items))
+                                          group_items, shared_lens))
     return rc;
   auto up16 = [](uint64_t x) { return (x + 15) & ~static_cast<uint64_t>(15); };
   kv_step_layout L{};
@@ -541,7 +541,8 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
   L.items_offset = up16(L.lens_offset + 4ull * num_seqs);
   L.groups_offset = up16(L.items_offset + 4ull * static_cast<uint64_t>(plan.num_items));
   L.group_items_offset = up16(L.groups_offset + 4ull * groups.size());
-  L.total_bytes = up16(L.group_items_offset + 4ull * group_items.size());
+  L.shared_lens_offset = up16(L.group_items_offset + 4ull * group_items.size());
+  L.total_bytes = up16(L.shared_lens_offset + 4ull * shared_lens.size());
   L.num_groups = static_cast<int32_t>(groups.size() / PKV_GROUP_STRIDE);
   L.num_group_items = static_cast<int32_t>(group_items.size());
   L.max_blocks = width;
@@ -574,6 +575,8 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
   if (!groups.empty()) std::memcpy(base + L.groups_offset, groups.data(), 4 * groups.size());
   if (!group_items.empty())
     std::memcpy(base + L.group_items_offset, group_items.data(), 4 * group_items.size());
+  if (!shared_lens.empty())
+    std::memcpy(base + L.shared_lens_offset, shared_lens.data(), 4 * shared_lens.size());
   *layout = L;
   return PKV_OK;
 }

@@ -238,15 +238,15 @@ int32_t leading_equal(const int32_t* a, int32_t na, const int32_t* b, int32_t nb
 // Requests sorted by their full block ids (equal lists keep index order), so
 // that those sharing the longest prefixes are neighbours; then runs of
 // neighbours become groups of at most max_members, a member joining only if
-// the group's saving ((members - 1) x shared partitions) does not shrink.
-// shared_parts[i]: partitions of request i that its group covers.
-void form_groups(const int32_t* const* blocks, const int32_t* nfull, int32_t n, int32_t bpp,
+// the group's saving ((members - 1) x shared blocks) does not shrink.
+// shared_blocks[i]: leading blocks request i holds in common with its group.
+void form_groups(const int32_t* const* blocks, const int32_t* nfull, int32_t n,
                  int32_t max_members, std::vector<int32_t>& groups,
-                 std::vector<int32_t>& shared_parts, int64_t& saved_parts) {
+                 std::vector<int32_t>& shared_blocks, int64_t& saved_blocks) {
   groups.clear();
-  shared_parts.assign(static_cast<size_t>(n), 0);
-  saved_parts = 0;
-  if (max_members < 2 || bpp <= 0) return;
+  shared_blocks.assign(static_cast<size_t>(n), 0);
+  saved_blocks = 0;
+  if (max_members < 2) return;
   // Requests by first block (integer keys), then, inside each run of equal
   // first blocks, by the rest of their blocks; a request alone in its run
   // shares nothing and is dropped.
@@ -255,7 +255,7 @@ void form_groups(const int32_t* const* blocks, const int32_t* nfull, int32_t n, 
   keys.clear();
   order.clear();
   for (int32_t i = 0; i < n; ++i)
-    if (nfull[i] >= bpp)
+    if (nfull[i] >= 1)
       keys.push_back(static_cast<uint64_t>(static_cast<uint32_t>(blocks[i][0])) << 32 |
                      static_cast<uint32_t>(i));
   std::sort(keys.begin(), keys.end());
@@ -290,20 +290,19 @@ void form_groups(const int32_t* const* blocks, const int32_t* nfull, int32_t n, 
       const int32_t c =
           std::min(common, leading_equal(blocks[first], nfull[first], blocks[next], nfull[next]));
       const int64_t members = static_cast<int64_t>(end - k);
-      if (c / bpp == 0 || members * (c / bpp) < (members - 1) * (common / bpp)) break;
+      if (c == 0 || members * c < (members - 1) * static_cast<int64_t>(common)) break;
       common = c;
       ++end;
     }
     const int32_t members = static_cast<int32_t>(end - k);
-    const int32_t parts = common / bpp;
-    if (members >= 2 && parts >= 1) {
+    if (members >= 2 && common >= 1) {
       groups.push_back(members);
       for (size_t i = k; i < end; ++i) {
         groups.push_back(order[i]);
-        shared_parts[order[i]] = parts;
+        shared_blocks[order[i]] = common;
       }
       groups.resize(groups.size() + (PKV_GROUP_STRIDE - 1 - members), -1);
-      saved_parts += static_cast<int64_t>(members - 1) * parts;
+      saved_blocks += static_cast<int64_t>(members - 1) * common;
       k = end;
     } else {
       ++k;
@@ -318,9 +317,10 @@ int plan_with_groups(const int32_t* const* blocks, const int32_t* nfull, const i
                      int32_t block_size, int32_t q_dtype, int32_t partition_size,
                      int32_t num_compute_units, std::vector<uint32_t>& items,
                      pkv_decode_plan* plan, std::vector<int32_t>& groups,
-                     std::vector<uint32_t>& group_items) {
+                     std::vector<uint32_t>& group_items, std::vector<int32_t>& shared_lens) {
   groups.clear();
   group_items.clear();
+  shared_lens.clear();
   int32_t longest = 0;
   int64_t total = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -342,42 +342,61 @@ int plan_with_groups(const int32_t* const* blocks, const int32_t* nfull, const i
       (head_dim != 64 && head_dim != 128) || n > 65535 ||
       (partition_size > 0 && partition_size % block_size != 0))
     return plan_items(partition_size);
-  // The partition size the plain plan would take, and the one groups use.
-  int32_t base = partition_size;
-  if (base < 0) {
+  static thread_local std::vector<int32_t> shared_blocks;
+  int64_t saved_blocks = 0;
+  form_groups(blocks, nfull, n, 16 / group, groups, shared_blocks, saved_blocks);
+  if (groups.empty() || static_cast<double>(saved_blocks) * block_size <
+                            kGroupMinSavedFraction * static_cast<double>(total)) {
+    groups.clear();
+    return plan_items(partition_size);
+  }
+  // The partition size the plain plan would take, or, for a one-pass plan, the
+  // groups' own.
+  int32_t part = partition_size;
+  if (part < 0) {
     static thread_local std::vector<int32_t> clamped;
     clamped.resize(static_cast<size_t>(n));
     for (int32_t i = 0; i < n; ++i) clamped[i] = std::max(0, lens[i]);
     const KernelChoice kc = choose_kernel(q_dtype, group);
-    base = auto_partition(clamped.data(), n, num_q_heads / kc.gt,
+    part = auto_partition(clamped.data(), n, num_q_heads / kc.gt,
                           num_compute_units > 0 ? num_compute_units : 256, block_size);
   }
-  const int32_t part =
-      base > 0 ? base : (kGroupPartitionTokens + block_size - 1) / block_size * block_size;
-  static thread_local std::vector<int32_t> shared_parts;
-  int64_t saved_parts = 0;
-  form_groups(blocks, nfull, n, part / block_size, 16 / group, groups, shared_parts, saved_parts);
-  if (groups.empty() ||
-      static_cast<double>(saved_parts) * part < kGroupMinSavedFraction * static_cast<double>(total)) {
-    groups.clear();
-    return plan_items(partition_size);
-  }
+  if (part == 0) part = (kGroupPartitionTokens + block_size - 1) / block_size * block_size;
   if (int rc = plan_items(part)) {
     groups.clear();
     return rc;
   }
+  // Group pieces: every whole partition of the shared prefix, then, when the
+  // prefix ends inside a partition, that partition up to the prefix's end (its
+  // members' own pieces for it start there; shared_lens tells the kernels).
+  shared_lens.assign(static_cast<size_t>(n), 0);
   const int32_t ngroups = static_cast<int32_t>(groups.size() / PKV_GROUP_STRIDE);
   for (int32_t g = 0; g < ngroups; ++g) {
-    const int32_t first = groups[static_cast<size_t>(g) * PKV_GROUP_STRIDE + 1];
-    for (int32_t j = 0; j < shared_parts[first]; ++j) group_items.push_back(PKV_ITEM(g, j));
+    const int32_t* row = groups.data() + static_cast<size_t>(g) * PKV_GROUP_STRIDE;
+    const int32_t ls = shared_blocks[row[1]] * block_size;
+    const int32_t whole = ls / part;
+    const int32_t pieces = whole + (ls % part != 0 ? 1 : 0);
+    for (int32_t j = 0; j < pieces; ++j) group_items.push_back(PKV_ITEM(g, j));
+    if (ls % part != 0)
+      for (int32_t i = 1; i <= row[0]; ++i) shared_lens[row[i]] = ls;
   }
+  // Remaining pieces: a member's partitions past the shared prefix, and the
+  // partition the prefix ends in when the member has tokens past it.
   size_t kept = 0;
   for (size_t i = 0; i < items.size(); ++i) {
     const uint32_t it = items[i];
-    if (static_cast<int32_t>(it & 0xFFFFu) >= shared_parts[it >> 16]) items[kept++] = it;
+    const int32_t s = static_cast<int32_t>(it >> 16);
+    const int32_t p = static_cast<int32_t>(it & 0xFFFFu);
+    const int32_t ls = shared_blocks[s] * block_size;
+    const bool covered = static_cast<int64_t>(p + 1) * part <= ls ||
+                         (static_cast<int64_t>(p) * part < ls && lens[s] <= ls);
+    if (!covered) items[kept++] = it;
   }
   items.resize(kept);
   plan->num_items = static_cast<int32_t>(kept);
+  // Partials per request: one more slot for a member whose own piece of the
+  // boundary partition is separate from the group's.
+  plan->workspace_bytes = workspace_bytes_for(n, num_q_heads, head_dim, plan->max_parts + 1);
   return PKV_OK;
 }
 
@@ -391,7 +410,7 @@ extern "C" int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_bl
                                      int32_t items_capacity, pkv_decode_plan* plan,
                                      int32_t* groups, int32_t groups_capacity,
                                      int32_t* num_groups, uint32_t* group_items,
-                                     int32_t* num_group_items) {
+                                     int32_t* num_group_items, int32_t* shared_lens) {
   if (!plan || !num_groups || !num_group_items)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan_groups: NULL output");
   *num_groups = 0;
@@ -404,7 +423,7 @@ extern "C" int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_bl
   static thread_local std::vector<const int32_t*> rows;
   static thread_local std::vector<int32_t> nfull, lens;
   static thread_local std::vector<uint32_t> rest, gitems;
-  static thread_local std::vector<int32_t> gdesc;
+  static thread_local std::vector<int32_t> gdesc, shared;
   rows.resize(static_cast<size_t>(num_seqs));
   nfull.resize(static_cast<size_t>(num_seqs));
   lens.resize(static_cast<size_t>(num_seqs));
@@ -415,7 +434,7 @@ extern "C" int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_bl
   }
   if (int rc = plan_with_groups(rows.data(), nfull.data(), lens.data(), num_seqs, num_q_heads,
                                 num_kv_heads, head_dim, block_size, q_dtype, partition_size,
-                                num_compute_units, rest, plan, gdesc, gitems))
+                                num_compute_units, rest, plan, gdesc, gitems, shared))
     return rc;
   const int32_t ng = static_cast<int32_t>(gdesc.size() / PKV_GROUP_STRIDE);
   if (static_cast<int64_t>(rest.size()) > items_capacity ||
@@ -425,11 +444,15 @@ extern "C" int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_bl
   if (ng > groups_capacity)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan_groups: %d groups do not fit in %d", ng,
                 groups_capacity);
-  if ((!rest.empty() && !items) || (!gitems.empty() && !group_items) || (ng > 0 && !groups))
+  if ((!rest.empty() && !items) || (!gitems.empty() && !group_items) ||
+      (ng > 0 && (!groups || !shared_lens)))
     return fail(PKV_ERR_INVALID_ARG, "pa_decode_plan_groups: NULL output array");
   if (!rest.empty()) std::memcpy(items, rest.data(), sizeof(uint32_t) * rest.size());
   if (!gitems.empty()) std::memcpy(group_items, gitems.data(), sizeof(uint32_t) * gitems.size());
-  if (ng > 0) std::memcpy(groups, gdesc.data(), sizeof(int32_t) * gdesc.size());
+  if (ng > 0) {
+    std::memcpy(groups, gdesc.data(), sizeof(int32_t) * gdesc.size());
+    std::memcpy(shared_lens, shared.data(), sizeof(int32_t) * shared.size());
+  }
   *num_groups = ng;
   *num_group_items = static_cast<int32_t>(gitems.size());
   return PKV_OK;

@@ -49,17 +49,18 @@ constexpr int kValuSkewedWavesPerCu = 4;
 // kGroupMinSavedFraction of the batch's token reads, switches a one-pass plan
 // to partitions of kGroupPartitionTokens (rounded up to the block size) and
 // returns the groups ([n][PKV_GROUP_STRIDE] ints: count, members), their work
-// items (group, partition) and the plan's remaining items.  Without a
-// worthwhile group, groups and group_items come back empty and the plan is
-// pa_decode_plan's.  items holds the remaining items on return; its size is
-// plan->num_items.
-constexpr int32_t kGroupPartitionTokens = 128;
+// items (group, partition) and, per request, the shared length when it ends
+// inside a partition (else 0).  items holds the remaining items on return
+// (plan->num_items of them); plan->workspace_bytes covers one spare partial
+// slot per request.  Without a worthwhile group, groups, group_items and
+// shared_lens come back empty and the plan is pa_decode_plan's.
+constexpr int32_t kGroupPartitionTokens = 256;
 constexpr double kGroupMinSavedFraction = 0.25;
 int plan_with_groups(const int32_t* const* blocks, const int32_t* nfull, const int32_t* lens,
                      int32_t n, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, int32_t q_dtype, int32_t partition_size,
                      int32_t num_compute_units, std::vector<uint32_t>& items,
                      pkv_decode_plan* plan, std::vector<int32_t>& groups,
-                     std::vector<uint32_t>& group_items);
+                     std::vector<uint32_t>& group_items, std::vector<int32_t>& shared_lens);
 
 }  // namespace pkv_plan

@@ -106,7 +106,8 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                 const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
                 void* workspace, size_t workspace_bytes, void* stream, int64_t row_chunks,
                 const int32_t* groups = nullptr, int32_t num_groups = 0,
-                const uint32_t* group_items = nullptr, int32_t num_group_items = 0) {
+                const uint32_t* group_items = nullptr, int32_t num_group_items = 0,
+                const int32_t* shared_lens = nullptr) {
   const bool contig = row_chunks > 0;
   const bool grouped = num_group_items > 0;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
@@ -165,6 +166,7 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     part_tokens = partition_size;
     parts = parts_for(len_clamp, partition_size);
   }
+  if (grouped) parts += 1;   // one spare partial slot per request (pa_decode_grouped)
   if (parts > 65535)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode: more than 65535 partitions per request");
 
@@ -189,6 +191,7 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
   prm.part_tokens = part_tokens;
   prm.max_parts = static_cast<int32_t>(parts);
   prm.row_chunks = row_chunks;
+  prm.shared = grouped ? shared_lens : nullptr;
 
   if (parts > 1) {
     const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, parts);
@@ -283,14 +286,15 @@ extern "C" int pa_decode_grouped(float* out, const void* q, int32_t q_dtype, con
                                  int32_t num_work_items, int32_t waves_per_cu,
                                  const int32_t* groups, int32_t num_groups,
                                  const uint32_t* group_items, int32_t num_group_items,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 const int32_t* shared_lens, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   if (num_groups < 0 || num_group_items < 0)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode_grouped: negative group sizes");
   return decode_impl(out, q, q_dtype, k_cache, v_cache, num_blocks, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, scale, max_context_len, partition_size, work_items,
                      num_work_items, waves_per_cu, workspace, workspace_bytes, stream, 0, groups,
-                     num_groups, group_items, num_group_items);
+                     num_groups, group_items, num_group_items, shared_lens);
 }
 
 extern "C" int pa_decode_contiguous(float* out, const void* q, int32_t q_dtype,

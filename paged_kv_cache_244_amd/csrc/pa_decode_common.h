@@ -45,6 +45,7 @@ struct DecodeParams {
   int64_t row_chunks;         // contiguous layout only: 16-byte chunks per (request, KV head) row
   const int32_t* groups;      // group launches: [num_groups][kGroupStride] (count, requests...)
   int32_t num_groups;
+  const int32_t* shared;      // group launches: [S] shared length ending inside a partition, or 0; may be NULL
 };
 
 // A prefix group (pagedkv.h, pa_decode_grouped): requests whose first tokens
@@ -142,6 +143,20 @@ __device__ __forceinline__ bool scheduled_piece(const DecodeParams& p, int& seq,
 __device__ __forceinline__ int clamped_len(const DecodeParams& p, int seq) {
   const int len = p.context_lens[seq];
   return len < 0 ? 0 : (len > p.len_clamp ? p.len_clamp : len);
+}
+
+// Shared length of request seq when it ends inside a partition (group
+// launches), else 0.
+__device__ __forceinline__ int shared_len(const DecodeParams& p, int seq) {
+  return p.shared ? p.shared[seq] : 0;
+}
+
+// Partials request seq (of length len) combines: one per partition, plus a
+// spare (slot nparts) for its own tokens of the partition its shared length
+// ends in, when it has tokens past that length.  One partial means the piece
+// writes the output itself.
+__device__ __forceinline__ int partials_of(int nparts, int shared, int len) {
+  return nparts + (shared > 0 && len > shared ? 1 : 0);
 }
 
 // MFMA head-group kernel, defined in pa_decode_mfma.hip: 16-token tiles, scores

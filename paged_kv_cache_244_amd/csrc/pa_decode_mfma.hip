@@ -114,6 +114,7 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
     }
   }
   const int len = clamped_len(p, rep);
+  const int shared = shared_len(p, rep);
   const int t_begin = part * p.part_tokens;
   if (t_begin >= len) {
     if (!kGroups && part == 0) {              // empty context: defined as zeros
@@ -123,8 +124,16 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
     }
     return;
   }
-  const int t_end = min(len, t_begin + p.part_tokens);
+  // A shared prefix that ends inside this partition splits it: a group piece
+  // takes the tokens before that point, a request's own piece the rest (from
+  // a block boundary, so whole tiles are skipped and, with 8-token blocks, the
+  // first tile is masked up to it), its partial kept in the spare slot.
+  const bool split = shared > t_begin && shared < t_begin + p.part_tokens;
+  const int t_first = !kGroups && split ? shared : t_begin;
+  const int t_end = min(kGroups && split ? shared : len, t_begin + p.part_tokens);
+  if (t_first >= t_end) return;               // no tokens of its own here
   const int nparts = (len + p.part_tokens - 1) / p.part_tokens;
+  const int skip_tiles = (t_first - t_begin) / TT;
   const int nblk = (t_end - 1) / B - blk_begin + 1;
   const int ntiles = (t_end - t_begin + TT - 1) / TT;
   const TileAddressing<kContig, CHUNKS> at(p, seq, kvh);
@@ -148,6 +157,8 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
                        : 0);
     const int tile0 = c0 * TPB / BPT;                         // first tile of this chunk
     const int cn = min(kWave * TPB / BPT, ntiles - tile0);    // tiles in this chunk
+    const int j0 = skip_tiles > tile0 ? skip_tiles - tile0 : 0;   // first tile to compute
+    if (j0 >= cn) continue;
 
     // Physical block (raw table entry) and row inside it of token row r of tile jj.
     auto locate = [&](int jj, int r, int& raw, int& row) {
@@ -184,7 +195,8 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
       auto token_ok = [&](int r) {
         int raw, row;
         locate(jj, r, raw, row);
-        return tok0 + r < t_end && static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks);
+        return tok0 + r >= t_first && tok0 + r < t_end &&
+               static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks);
       };
       // V tile into LDS first (its latency hides behind the score MFMAs).
 #pragma unroll
@@ -241,8 +253,8 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
     };
 
 #pragma unroll
-    for (int u = 0; u < DEPTH; ++u) issue(kbuf[u], vbuf[u], u < cn ? u : cn - 1);
-    int j = 0;
+    for (int u = 0; u < DEPTH; ++u) issue(kbuf[u], vbuf[u], j0 + u < cn ? j0 + u : cn - 1);
+    int j = j0;
     for (; j + 2 * DEPTH - 1 < cn; j += DEPTH) {
 #pragma unroll
       for (int u = 0; u < DEPTH; ++u) {
@@ -277,14 +289,20 @@ __global__ __launch_bounds__(kWave) void pa_decode_mfma_kernel(DecodeParams p) {
     // A member's own partition count decides whether this piece is its whole
     // context (write the output) or one of several partials.
     const int rs = row_seq(h);
-    const int np = kGroups ? (clamped_len(p, rs) + p.part_tokens - 1) / p.part_tokens : nparts;
+    int np = nparts, own_slot = !kGroups && split ? nparts : part;
+    if constexpr (kGroups) {
+      const int rl = clamped_len(p, rs);
+      np = partials_of((rl + p.part_tokens - 1) / p.part_tokens, shared_len(p, rs), rl);
+    } else {
+      np = partials_of(nparts, shared, len);
+    }
     const int64_t orow = static_cast<int64_t>(rs) * p.num_q_heads + row_head(h);
     if (np == 1) {
       const float inv = 1.f / lr[r];
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) p.out[orow * D + db * 16 + li] = o[db][r] * inv;
     } else {
-      const int64_t slot = orow * p.max_parts + part;
+      const int64_t slot = orow * p.max_parts + own_slot;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) p.ws_o[slot * D + db * 16 + li] = o[db][r];
       if (li == 0) {

@@ -50,7 +50,11 @@ __global__ __launch_bounds__(D) void pa_decode_reduce_kernel(DecodeParams p) {
   const int seq = blockIdx.y;
   const int d = threadIdx.x;
   const int len = clamped_len(p, seq);
-  const int nparts = (len + p.part_tokens - 1) / p.part_tokens;
+  // Partitions, plus the spare slot of a request whose shared prefix ends
+  // inside a partition and that has tokens past it (slots 0..nparts-1 stay
+  // contiguous).
+  const int nparts =
+      partials_of((len + p.part_tokens - 1) / p.part_tokens, shared_len(p, seq), len);
   if (nparts <= 1) return;
   const int64_t base = (static_cast<int64_t>(seq) * p.num_q_heads + h) * p.max_parts;
   const float2* ml = reinterpret_cast<const float2*>(p.ws_ml) + base;

@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
   QueryRegs<GT, kQF32> qr;
   qr.load(p.q, (static_cast<int64_t>(seq) * p.num_q_heads + h0) * D + dchunk * 8, D);
   const int len = clamped_len(p, seq);
+  const int shared = shared_len(p, seq);
   const int t_begin = part * p.part_tokens;
   if (t_begin >= len) {
     if (part == 0 && row == 0) {             // empty context: defined as zeros
@@ -141,6 +142,14 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
   }
   const int t_end = min(len, t_begin + p.part_tokens);
   const int nparts = (len + p.part_tokens - 1) / p.part_tokens;
+  // When the request's shared prefix ends inside this partition, a group
+  // piece has its tokens before that point: start there (block-aligned, so a
+  // whole number of tiles in) and keep the partial in the spare slot.
+  const bool own_rest = shared > t_begin && shared < t_begin + p.part_tokens;
+  const int skip_tiles = own_rest ? (shared - t_begin) / TT : 0;
+  if (own_rest && shared >= t_end) return;   // no tokens of its own here
+  const int slot_part = own_rest ? nparts : part;
+  const int np_eff = partials_of(nparts, shared, len);
 
   float m[GT], l[GT], o[GT][8];
 #pragma unroll
@@ -174,6 +183,8 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
                        : 0);
     const int tile0 = c0 * TPB;                               // first tile of this chunk
     const int cn = min(kWave * TPB, ntiles - tile0);          // tiles in this chunk
+    const int j0 = skip_tiles > tile0 ? skip_tiles - tile0 : 0;   // first tile to compute
+    if (j0 >= cn) continue;
 
     auto issue = [&](uint4 (&kr)[NLD], uint4 (&vr)[NLD], int jj) {
       int ph = __builtin_amdgcn_readlane(staged, jj / TPB);
@@ -228,8 +239,8 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
     // an L2 hit) so every path into the loop has the same DEPTH tiles in flight
     // and the compiler waits for exactly the tile it consumes.
 #pragma unroll
-    for (int u = 0; u < DEPTH; ++u) issue(kbuf[u], vbuf[u], u < cn ? u : cn - 1);
-    int j = 0;
+    for (int u = 0; u < DEPTH; ++u) issue(kbuf[u], vbuf[u], j0 + u < cn ? j0 + u : cn - 1);
+    int j = j0;
     for (; j + 2 * DEPTH - 1 < cn; j += DEPTH) {   // steady state: unconditional issues
 #pragma unroll
       for (int u = 0; u < DEPTH; ++u) {
@@ -267,7 +278,7 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
   }
 
   if (row != 0) return;
-  if (nparts == 1) {
+  if (np_eff == 1) {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       const float inv = 1.f / l[g];
@@ -280,7 +291,7 @@ __global__ __launch_bounds__(kWave) void pa_decode_partition_kernel(DecodeParams
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       const int64_t slot =
-          (static_cast<int64_t>(seq) * p.num_q_heads + h0 + g) * p.max_parts + part;
+          (static_cast<int64_t>(seq) * p.num_q_heads + h0 + g) * p.max_parts + slot_part;
       float4* dst = reinterpret_cast<float4*>(p.ws_o + slot * D + dchunk * 8);
       dst[0] = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
       dst[1] = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);

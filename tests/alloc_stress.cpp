@@ -30,9 +30,9 @@
   } while (0)
 
 // Prefix groups of one step (kv_decode_step_host with PKV_STEP_GROUPS): every
-// group piece lies in the same physical blocks of all its members' tables and
-// within their lengths, and group pieces plus the remaining work items name
-// each (request, partition) piece exactly once.
+// token of every request is computed exactly once, by a group piece or by the
+// request's own piece; tokens a group covers lie in the same physical blocks
+// of all its members' tables and within their lengths.
 static long g_grouped_steps = 0;
 
 static void check_groups(const char* base, const kv_step_layout& lay, int32_t n, int32_t bs) {
@@ -42,44 +42,47 @@ static void check_groups(const char* base, const kv_step_layout& lay, int32_t n,
   const uint32_t* items = reinterpret_cast<const uint32_t*>(base + lay.items_offset);
   const int32_t* groups = reinterpret_cast<const int32_t*>(base + lay.groups_offset);
   const uint32_t* gitems = reinterpret_cast<const uint32_t*>(base + lay.group_items_offset);
+  const int32_t* shared =
+      lay.num_groups > 0 ? reinterpret_cast<const int32_t*>(base + lay.shared_lens_offset) : nullptr;
   const int32_t pt = lay.plan.partition_size;
   const int32_t w = lay.max_blocks;
-  std::map<std::pair<int32_t, int32_t>, int> seen;
-  for (int32_t i = 0; i < lay.plan.num_items; ++i)
-    seen[std::make_pair(static_cast<int32_t>(items[i] >> 16), static_cast<int32_t>(items[i] & 0xFFFF))] += 1;
+  std::vector<std::vector<int>> count(static_cast<size_t>(n));
+  for (int32_t s = 0; s < n; ++s) count[s].assign(static_cast<size_t>(lens[s]), 0);
+  for (int32_t i = 0; i < lay.plan.num_items; ++i) {
+    const int32_t s = static_cast<int32_t>(items[i] >> 16), p = static_cast<int32_t>(items[i] & 0xFFFF);
+    CHECK(s < n);
+    int64_t lo = pt > 0 ? static_cast<int64_t>(p) * pt : 0;
+    const int64_t hi = pt > 0 ? std::min<int64_t>(lo + pt, lens[s]) : lens[s];
+    if (shared && shared[s] > lo && shared[s] < lo + pt) lo = shared[s];
+    CHECK(lo < hi || lens[s] == 0);
+    for (int64_t t = lo; t < hi; ++t) count[s][t] += 1;
+  }
   if (lay.num_group_items > 0) CHECK(pt > 0 && pt % bs == 0);
   for (int32_t g = 0; g < lay.num_groups; ++g) {
     const int32_t* row = groups + static_cast<int64_t>(g) * PKV_GROUP_STRIDE;
     CHECK(row[0] >= 2 && row[0] <= 4);         // 8 query heads over 2 KV heads: 16 / 4 members
     std::set<int32_t> mem(row + 1, row + 1 + row[0]);
     CHECK(static_cast<int32_t>(mem.size()) == row[0]);
-    for (int32_t m : mem) CHECK(m >= 0 && m < n);
+    for (int32_t m : mem) CHECK(m >= 0 && m < n && shared[m] == shared[row[1]]);
   }
   for (int32_t k = 0; k < lay.num_group_items; ++k) {
     const int32_t g = static_cast<int32_t>(gitems[k] >> 16), p = static_cast<int32_t>(gitems[k] & 0xFFFF);
     CHECK(g < lay.num_groups);
     const int32_t* row = groups + static_cast<int64_t>(g) * PKV_GROUP_STRIDE;
     const int32_t first = row[1];
+    const int64_t lo = static_cast<int64_t>(p) * pt;
+    int64_t hi = lo + pt;
+    if (shared[first] > lo && shared[first] < hi) hi = shared[first];
     for (int32_t j = 0; j < row[0]; ++j) {
       const int32_t m = row[1 + j];
-      CHECK(static_cast<int64_t>(p + 1) * pt <= lens[m]);
-      for (int32_t b = p * pt / bs; b < (p + 1) * pt / bs; ++b)
+      CHECK(hi <= lens[m]);
+      for (int64_t b = lo / bs; b < (hi + bs - 1) / bs; ++b)
         CHECK(b < w && tables[static_cast<int64_t>(m) * w + b] == tables[static_cast<int64_t>(first) * w + b]);
-      seen[std::make_pair(m, p)] += 1;
+      for (int64_t t = lo; t < hi; ++t) count[m][t] += 1;
     }
   }
-  for (int32_t s = 0; s < n; ++s) {
-    const int32_t np = pt > 0 && lens[s] > 0 ? (lens[s] + pt - 1) / pt : 1;
-    for (int32_t p = 0; p < np; ++p) {
-      const int count = seen[std::make_pair(s, p)];
-      CHECK(count == 1);
-    }
-  }
-  size_t total = 0;
-  for (const auto& kv : seen) total += kv.second;
-  size_t want = 0;
-  for (int32_t s = 0; s < n; ++s) want += pt > 0 && lens[s] > 0 ? (lens[s] + pt - 1) / pt : 1;
-  CHECK(total == want);
+  for (int32_t s = 0; s < n; ++s)
+    for (int c : count[s]) CHECK(c == 1);
 }
 
 int main(int argc, char** argv) {

@@ -86,18 +86,23 @@ def test_grouped_decode_matches_oracle(hq, hkv, d, bs):
         paths.assert_attention_close(plain[t], want)
 
 
-def test_groups_covering_every_piece():
-    """Forks of a 256-token prompt before any append: every block is shared, so
-    the group pieces cover every partition and no work item remains (the launch
-    then runs the group kernel and the reduce only)."""
+@pytest.mark.parametrize("L", [256, 192, 200])
+def test_groups_of_unappended_forks(L):
+    """Forks of an L-token prompt before any append, with 256-token partitions.
+    L = 256: every block is shared and the group pieces cover every piece (no work
+    item remains; the launch runs the group kernel and the reduce only).  L = 192:
+    the shared length ends inside partition 0 and the forks have no tokens past it,
+    so the group piece is each fork's whole context and writes its output.  L = 200:
+    each fork's own tokens 192..199 are its piece of partition 0, kept in the spare
+    slot and combined with the group's partial by the reduce."""
     import torch
 
     from paged_kv_cache_244_amd import _lib
     from paged_kv_cache_244_amd.cache import PagedKVCache
 
-    print("\n[case] groups covering every piece", flush=True)
-    rng = np.random.default_rng(21)
-    hq, hkv, d, bs, L = 8, 8, 128, 16, 256
+    print(f"\n[case] groups of unappended forks L={L}", flush=True)
+    rng = np.random.default_rng(21 + L)
+    hq, hkv, d, bs, part = 8, 8, 128, 16, 256
     c = PagedKVCache(64, hkv, d, bs, initial_order=rng.permutation(64).astype(np.int32),
                      num_q_heads=hq, q_dtype=torch.float16)
     k = rng.standard_normal((L, hkv, d)).astype(np.float16)
@@ -105,19 +110,23 @@ def test_groups_covering_every_piece():
     p = c.new_sequence()
     c.write(c.reserve_many([p], [L]), torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
     kids = [c.fork(p) for _ in range(4)]
-    tables, lens = c.alloc.export(kids, L // bs, -1)
-    items, plan, groups, gitems = _lib.plan_groups(tables, lens, hq, hkv, d, bs)
-    assert len(items) == 0 and len(groups) == 1 and len(gitems) == L // plan["partition_size"]
+    tables, lens = c.alloc.export(kids, -(-L // bs), -1)
+    items, plan, groups, gitems, shared = _lib.plan_groups(tables, lens, hq, hkv, d, bs,
+                                                           partition_size=part)
+    assert len(groups) == 1 and len(gitems) == 1
+    assert len(items) == (4 if L % bs else 0)
+    assert shared.tolist() == [0 if L == part else L // bs * bs] * 4
     q = rng.standard_normal((4, hq, d)).astype(np.float16)
     out = torch.full((4, hq, d), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(_lib.pa_decode_workspace_size(4, hq, d, L, plan["partition_size"]),
+    ws = torch.empty(_lib.pa_decode_workspace_size(4, hq, d, L + part, part),
                      dtype=torch.uint8, device="cuda")
+    items_dev = torch.from_numpy(items.view(np.int32)).cuda() if len(items) else \
+        torch.empty(0, dtype=torch.int32, device="cuda")
     _lib.pa_decode_grouped(out, torch.from_numpy(q).cuda(), c.k[0], c.v[0],
                            torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
-                           1.0 / np.sqrt(d), L, plan["partition_size"],
-                           torch.from_numpy(groups).cuda(),
+                           1.0 / np.sqrt(d), L, part, torch.from_numpy(groups).cuda(),
                            torch.from_numpy(gitems.view(np.int32)).cuda(), workspace=ws,
-                           work_items=torch.empty(0, dtype=torch.int32, device="cuda"),
+                           work_items=items_dev, shared_lens=torch.from_numpy(shared).cuda(),
                            stream=c.stream)
     torch.cuda.synchronize()
     want = np.stack([attention.attend_one(q[i], k, v, 1.0 / np.sqrt(d)) for i in range(4)])
