@@ -652,8 +652,11 @@ def _beam_replay(w, steps):
     return logical, unique, pairs
 
 
-def _beam_prune(w, t, groups, free, fork):
-    plan = w.prune_plan(t)
+def _beam_prune(w, t, groups, free, fork, plan=False):
+    """Cancel and fork beams per the workload's schedule for step t (``plan``: that
+    schedule, drawn beforehand, or False to draw it here)."""
+    if plan is False:
+        plan = w.prune_plan(t)
     if plan is None:
         return groups
     out = []
@@ -704,10 +707,13 @@ def churn_bench(args):
           for _ in range(args.steps)]
 
     part = "auto" if args.partition == "auto" else int(args.partition)
+    # The cancel/fork schedule is the workload's input: drawn before timing, so the
+    # timed steps hold the allocator's forks and frees but not the random draws.
+    schedule = [w.prune_plan(t) for t in range(total_steps)]
 
     def step(t, e=None):
         nonlocal groups
-        groups = _beam_prune(w, t, groups, cache.free, cache.fork)
+        groups = _beam_prune(w, t, groups, cache.free, cache.fork, schedule[t])
         seqs = [s for g in groups for s in g]
         k, v, q = inputs[t]
         layer = t % layers
