@@ -420,13 +420,27 @@ class PagedKVCache:
         return items.view(np.int32), info
 
     def batch(self, seqs, max_blocks=None, pad_value=None, partition_size="auto") -> "DecodeBatch":
-        """Upload the block tables, lengths and launch schedule of ``seqs`` for decode.
+        """Upload the block tables, lengths and launch schedule of ``seqs`` for decode
+        (with prefix groups where they pay, as ``decode_step`` plans them).
 
         The returned device tensors stay valid until the next upload.
         """
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
         tables, lens, max_len = self._tables(seqs, max_blocks, pad_value)
         key = (self.num_q_heads, self.q_dtype, partition_size)
+        if self.prefix_groups and self.q_dtype == torch.float16:
+            part = -1 if partition_size == "auto" else int(partition_size)
+            items, info, groups, gitems, shared = _lib.plan_groups(
+                tables, lens, self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size,
+                _lib.PKV_F16, part)
+            if len(groups):
+                t, l_, it, g, gi, sh = self.upload(tables, lens, items.view(np.int32), groups,
+                                                   gitems.view(np.int32), shared)
+                batch = DecodeBatch(DeviceArray.of(t), DeviceArray.of(l_), max_len, lens,
+                                    DeviceArray.of(it), info, key)
+                batch.groups_dev, batch.group_items_dev = DeviceArray.of(g), DeviceArray.of(gi)
+                batch.shared_dev = DeviceArray.of(sh)
+                return batch
         items, info = self._plan(lens, *key)
         t, l_, it = self.upload(tables, lens, items)
         return DecodeBatch(DeviceArray.of(t), DeviceArray.of(l_), max_len, lens,

@@ -69,21 +69,29 @@ def test_grouped_decode_matches_oracle(hq, hkv, d, bs):
                 host.copy_(out, non_blocking=True)
             c.stream.synchronize()
             outs.append(host.numpy().copy())
+        # The table-upload path (batch(), no append) plans the same groups.
+        b2 = c.batch(samples)
+        grouped.append(b2.group_items_dev is not None)
+        out2 = c.attend(torch.from_numpy(step_q[steps - 1]).to(dev), b2, scale)
+        torch.cuda.synchronize()
+        outs.append(out2.cpu().numpy())
         return outs, grouped
 
     got, grouped = run(True)
     plain, plain_grouped = run(False)
     assert all(grouped), "the planner did not group the forked samples"
     assert not any(plain_grouped)
-    for t in range(steps):
+    # Outputs of steps 0..steps-1, then the batch() output for the last step's q.
+    for t, (g_out, p_out) in enumerate(zip(got, plain)):
+        tt = min(t, steps - 1)
         want = np.zeros((n, hq, d), dtype=np.float64)
         for i in range(n):
             p = i // samples_per
-            keys = np.concatenate([pk[p], step_k[:t + 1, i]])
-            vals = np.concatenate([pv[p], step_v[:t + 1, i]])
-            want[i] = attention.attend_one(step_q[t, i], keys, vals, scale)
-        paths.assert_attention_close(got[t], want)
-        paths.assert_attention_close(plain[t], want)
+            keys = np.concatenate([pk[p], step_k[:tt + 1, i]])
+            vals = np.concatenate([pv[p], step_v[:tt + 1, i]])
+            want[i] = attention.attend_one(step_q[tt, i], keys, vals, scale)
+        paths.assert_attention_close(g_out, want)
+        paths.assert_attention_close(p_out, want)
 
 
 @pytest.mark.parametrize("L", [256, 192, 200])
