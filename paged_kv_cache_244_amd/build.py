@@ -71,7 +71,24 @@ def build(jobs: int = 4) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs)
     os.replace(tmp, LIB_PATH)
+    build_c_abi_test(cc)
     return LIB_PATH
+
+
+C_ABI_TEST_SRC = os.path.join(ROOT, "tests", "c_abi_decode.cpp")
+C_ABI_TEST_BIN = os.path.join(ROOT, "tests", "c_abi_decode")
+
+
+def build_c_abi_test(cc: str) -> str:
+    """The host program that drives the library through its C ABI alone (tests/):
+    host C++ linked against libpagedkv.so and the HIP runtime, found next to it."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(cc)))
+    tmp = C_ABI_TEST_BIN + ".tmp"
+    _run([cc, "-x", "c++", C_ABI_TEST_SRC, "-o", tmp, "-O2", "-std=c++17", f"-I{INCLUDE}",
+          f"-I{rocm}/include", "-D__HIP_PLATFORM_AMD__", f"-L{PKG_DIR}", "-lpagedkv",
+          f"-L{rocm}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../paged_kv_cache_244_amd"])
+    os.replace(tmp, C_ABI_TEST_BIN)
+    return C_ABI_TEST_BIN
 
 
 if __name__ == "__main__":
