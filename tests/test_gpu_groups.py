@@ -139,3 +139,71 @@ def test_groups_of_unappended_forks(L):
     torch.cuda.synchronize()
     want = np.stack([attention.attend_one(q[i], k, v, 1.0 / np.sqrt(d)) for i in range(4)])
     paths.assert_attention_close(out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_grouped_decode_random_churn(seed):
+    """Random fork trees with cancellations over several steps, random shapes: every
+    request's output against the oracle over its own token history (its prompt, the
+    tokens its ancestors appended before it forked, then its own), for every row.
+    Groups form and dissolve as requests fork and diverge."""
+    import torch
+
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    rng = np.random.default_rng(1000 + seed)
+    hq, hkv = [(8, 8), (8, 2), (16, 2), (4, 1)][seed % 4]
+    d = [64, 128][seed % 2]
+    bs = [8, 16, 32, 16][seed % 4]
+    print(f"\n[case] grouped random churn seed={seed} hq={hq} hkv={hkv} d={d} B={bs}", flush=True)
+    scale = 1.0 / np.sqrt(d)
+    nb = 1200
+    c = PagedKVCache(nb, hkv, d, bs, initial_order=rng.permutation(nb).astype(np.int32),
+                     num_q_heads=hq, q_dtype=torch.float16)
+    dev = torch.device("cuda")
+    hist = {}                                   # request -> (keys, values) token lists
+    live = []
+    for _ in range(3):
+        L = int(rng.integers(20, 400))
+        k = rng.standard_normal((L, hkv, d)).astype(np.float16)
+        v = rng.standard_normal((L, hkv, d)).astype(np.float16)
+        p = c.new_sequence()
+        c.write(c.reserve_many([p], [L]), torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev))
+        for _ in range(int(rng.integers(2, 6))):
+            s = c.fork(p)
+            hist[s] = (list(k), list(v))
+            live.append(s)
+        c.free(p)
+    grouped_steps = 0
+    for step in range(6):
+        if step and step % 2 == 0:              # cancel some, fork survivors
+            rng.shuffle(live)
+            drop = live[: len(live) // 3]
+            live = live[len(live) // 3:]
+            for s in drop:
+                c.free(s)
+                del hist[s]
+            for s in list(rng.choice(live, size=len(drop))):
+                t = c.fork(int(s))
+                hist[t] = (list(hist[int(s)][0]), list(hist[int(s)][1]))
+                live.append(t)
+        n = len(live)
+        k_new = rng.standard_normal((n, hkv, d)).astype(np.float16)
+        v_new = rng.standard_normal((n, hkv, d)).astype(np.float16)
+        q = rng.standard_normal((n, hq, d)).astype(np.float16)
+        _, batch = c.decode_step(live, k_new=torch.from_numpy(k_new).to(dev),
+                                 v_new=torch.from_numpy(v_new).to(dev))
+        grouped_steps += batch.group_items_dev is not None
+        out = c.attend(torch.from_numpy(q).to(dev), batch, scale)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        want = np.zeros((n, hq, d), dtype=np.float64)
+        for i, s in enumerate(live):
+            hist[s][0].append(k_new[i])
+            hist[s][1].append(v_new[i])
+            want[i] = attention.attend_one(q[i], np.stack(hist[s][0]), np.stack(hist[s][1]), scale)
+        paths.assert_attention_close(got, want)
+    assert grouped_steps > 0, "no step formed prefix groups"
+    for s in live:
+        c.free(s)
+    assert c.alloc.stats()["free_blocks"] == nb
