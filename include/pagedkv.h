@@ -380,10 +380,13 @@ int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_blocks_per_se
  *                              head_dim, max_context_len + partition_size,
  *                              partition_size) bytes: one spare partition
  *                              slot per request.
- * The caller guarantees, as pa_decode_plan_groups does, that for every group
- * piece the partition's tokens lie in the same physical blocks in every
- * member's table and within every member's length, and that the group pieces
- * and work_items together name each piece of each request exactly once.
+ * The caller guarantees, as pa_decode_plan_groups does, that members are
+ * request indices in [0, num_seqs), that for every group piece the
+ * partition's tokens lie in the same physical blocks in every member's table
+ * and within every member's length, and that the group pieces and work_items
+ * together name each piece of each request exactly once.  Like the block
+ * tables, these device-resident lists are not validated on the launch path
+ * (a member index out of range is read as request 0).
  * work_items NULL means every piece, as for pa_decode; when the groups cover
  * every piece, pass any non-NULL address with num_work_items 0.
  * Other arguments as pa_decode.  Errors as pa_decode, plus
