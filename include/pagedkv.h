@@ -201,6 +201,10 @@ typedef struct {
   int32_t num_items;        /* work items written to items[]                         */
   int32_t waves_per_cu;     /* residency limit to pass to pa_decode (0 = none)       */
   uint64_t workspace_bytes; /* = pa_decode_workspace_size for this schedule          */
+  int32_t fuse_groups;      /* pa_decode_plan_groups: 1 = run the group pieces and the
+                               remaining pieces in one launch (pa_decode_grouped's
+                               fuse), 0 = separate launches; 0 from pa_decode_plan    */
+  int32_t reserved;
 } pkv_decode_plan;
 
 /* Packing of one work item: (request << 16) | partition. */
@@ -346,7 +350,10 @@ int pa_decode(float* out, const void* q, int32_t q_dtype,
  *   shared_lens    : HOST int32 [num_seqs]: Ls for members of a group whose
  *                    Ls ends inside a partition, else 0.
  * plan->workspace_bytes is the workspace pa_decode_grouped needs (one spare
- * partial slot per request).  Other arguments and errors as pa_decode_plan.
+ * partial slot per request).  plan->fuse_groups is 1 when the remaining
+ * pieces hold at least half as many token reads as the group pieces: both
+ * kinds then gain from sharing one launch; when the group pieces dominate,
+ * the remaining ones would only slow them down.  Other arguments and errors as pa_decode_plan.
  * With no worthwhile group, *num_groups = *num_group_items = 0, shared_lens
  * is not written and the result is pa_decode_plan's.
  */
@@ -369,6 +376,9 @@ int pa_decode_plan_groups(const int32_t* block_tables, int32_t max_blocks_per_se
  * pieces, the remaining pieces (work_items), then the combine.
  *   groups, num_groups       : device int32 [num_groups][PKV_GROUP_STRIDE].
  *   group_items, num_group_items : device uint32 PKV_ITEM(group, partition).
+ *   fuse                     : 1 = group pieces and work_items in one launch
+ *                              (when built for the shape, with a work list),
+ *                              0 = a launch for each; plan->fuse_groups.
  *   shared_lens              : device int32 [num_seqs] as pa_decode_plan_groups
  *                              writes it, or NULL when no shared length ends
  *                              inside a partition.  A group piece (g, p) stops
@@ -404,8 +414,8 @@ int pa_decode_grouped(float* out, const void* q, int32_t q_dtype,
                       int32_t partition_size, const uint32_t* work_items, int32_t num_work_items,
                       int32_t waves_per_cu, const int32_t* groups, int32_t num_groups,
                       const uint32_t* group_items, int32_t num_group_items,
-                      const int32_t* shared_lens, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      const int32_t* shared_lens, int32_t fuse, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /*
  * pa_decode_contiguous — the same decode attention over the layout without a

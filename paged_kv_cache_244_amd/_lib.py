@@ -61,7 +61,8 @@ class Swapped(PagedKVError):
 
 class DecodePlan(ctypes.Structure):
     _fields_ = [("partition_size", c_int32), ("max_parts", c_int32), ("num_items", c_int32),
-                ("waves_per_cu", c_int32), ("workspace_bytes", ctypes.c_uint64)]
+                ("waves_per_cu", c_int32), ("workspace_bytes", ctypes.c_uint64),
+                ("fuse_groups", c_int32), ("reserved", c_int32)]
 
 
 class StepLayout(ctypes.Structure):
@@ -146,8 +147,8 @@ _SIGNATURES = {
     "pa_decode_grouped": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                                     c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32,
                                     c_int32, c_float, c_int32, c_int32, c_void_p, c_int32, c_int32,
-                                    c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
-                                    c_size_t, c_void_p]),
+                                    c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32,
+                                    c_void_p, c_size_t, c_void_p]),
 }
 
 _lib = None
@@ -367,7 +368,7 @@ def set_kernel_policy(policy: int) -> int:
 
 def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                       max_context_len, partition_size, groups, group_items, workspace=None,
-                      stream=None, work_items=None, waves_per_cu=0, shared_lens=None):
+                      stream=None, work_items=None, waves_per_cu=0, shared_lens=None, fuse=1):
     """``pa_decode`` with prefix groups: ``groups`` a device int32 [num_groups, 17] tensor,
     ``group_items`` a device int32/uint32 tensor of (group << 16 | partition) pieces and
     ``shared_lens`` a device int32 [S] tensor (or None), as ``plan_groups`` returns them;
@@ -403,7 +404,7 @@ def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scal
         int(max_context_len), int(partition_size), items_ptr, n_items, int(waves_per_cu),
         _dev(groups, torch.int32, "groups"), int(groups.shape[0]), g_ptr, n_g,
         _dev(shared_lens, torch.int32, "shared_lens") if shared_lens is not None else None,
-        ws_ptr, ws_bytes, _stream(stream)))
+        int(fuse), ws_ptr, ws_bytes, _stream(stream)))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-HIP_SOURCES = ["pa_decode.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip", "pa_decode_reduce.hip",
+HIP_SOURCES = ["pa_decode.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip", "pa_decode_fused.hip",
+               "pa_decode_reduce.hip",
                "pa_prefill.hip", "kv_cache_ops.hip"]
 HOST_SOURCES = ["allocator.cpp", "decode_plan.cpp", "errors.cpp"]
 

@@ -507,7 +507,8 @@ class PagedKVCache:
                 batch.tables_dev.shape[1], batch.lens_dev.ptr, s, hq, self.num_kv_heads, d,
                 self.block_size, float(scale), batch.max_len, part, items.ptr, items.shape[0],
                 info["waves_per_cu"], g.ptr, g.shape[0], gi.ptr, gi.shape[0], batch.shared_dev.ptr,
-                ws.data_ptr() if ws is not None else None, ws.numel() if ws is not None else 0,
+                info["fuse_groups"], ws.data_ptr() if ws is not None else None,
+                ws.numel() if ws is not None else 0,
                 self._stream_ptr))
             return out
         _lib._check(_lib.lib().pa_decode(

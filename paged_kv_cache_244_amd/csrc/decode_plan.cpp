@@ -394,6 +394,24 @@ int plan_with_groups(const int32_t* const* blocks, const int32_t* nfull, const i
   }
   items.resize(kept);
   plan->num_items = static_cast<int32_t>(kept);
+  // One launch for both kinds of piece when the remaining ones carry at least
+  // half the group pieces' token reads (measured on MI355X: parallel sampling,
+  // ratio 1.15, 13% faster in one launch; beams, ratio 0.35, 4% slower).
+  int64_t group_tokens = 0, rest_tokens = 0;
+  for (uint32_t it : group_items) {
+    const int32_t* row = groups.data() + static_cast<size_t>(it >> 16) * PKV_GROUP_STRIDE;
+    const int64_t lo = static_cast<int64_t>(it & 0xFFFFu) * part;
+    const int64_t ls = shared_blocks[row[1]] * block_size;
+    group_tokens += std::min<int64_t>(lo + part, ls) - lo;
+  }
+  for (uint32_t it : items) {
+    const int32_t s_ = static_cast<int32_t>(it >> 16);
+    int64_t lo = static_cast<int64_t>(it & 0xFFFFu) * part;
+    const int64_t ls = shared_blocks[s_] * block_size;
+    if (ls > lo && ls < lo + part) lo = ls;
+    rest_tokens += std::min<int64_t>(lo + part, std::max(0, lens[s_])) - lo;
+  }
+  plan->fuse_groups = 2 * rest_tokens >= group_tokens ? 1 : 0;
   // Partials per request: one more slot for a member whose own piece of the
   // boundary partition is separate from the group's.
   plan->workspace_bytes = workspace_bytes_for(n, num_q_heads, head_dim, plan->max_parts + 1);

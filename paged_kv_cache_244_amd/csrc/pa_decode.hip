@@ -107,7 +107,7 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                 void* workspace, size_t workspace_bytes, void* stream, int64_t row_chunks,
                 const int32_t* groups = nullptr, int32_t num_groups = 0,
                 const uint32_t* group_items = nullptr, int32_t num_group_items = 0,
-                const int32_t* shared_lens = nullptr) {
+                const int32_t* shared_lens = nullptr, int32_t fuse = 0) {
   const bool contig = row_chunks > 0;
   const bool grouped = num_group_items > 0;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
@@ -208,6 +208,31 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
+  // Group pieces and a listed rest in one launch when the shape has a fused
+  // kernel (pa_decode_fused.hip); then the reduce.
+  FusedFn fused = grouped && fuse && work_items
+                      ? pick_fused_kernel(head_dim, block_size, kc.gt, kc.mfma)
+                      : nullptr;
+  if (fused) {
+    DecodeParams gp = prm;
+    gp.items = group_items;
+    gp.num_items = num_group_items;
+    gp.groups = groups;
+    gp.num_groups = num_groups;
+    const int64_t group_wgs = static_cast<int64_t>(num_group_items) * num_kv_heads;
+    const int64_t wgs = group_wgs + static_cast<int64_t>(num_work_items) * prm.num_head_tiles;
+    if (wgs > INT32_MAX)
+      return fail(PKV_ERR_INVALID_ARG, "pa_decode_grouped: %lld workgroups in one launch",
+                  static_cast<long long>(wgs));
+    hipLaunchKernelGGL(fused, dim3(static_cast<unsigned>(wgs)), dim3(kWave), 0, st, gp, prm,
+                       static_cast<int>(group_wgs));
+    e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(PKV_ERR_HIP, "pa_decode_grouped launch: %s", hipGetErrorString(e));
+    e = launch_reduce(prm, head_dim, st);   // grouped launches always keep more than one slot
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode reduce launch: %s", hipGetErrorString(e));
+    return PKV_OK;
+  }
   if (grouped) {
     // Prefix groups first: their partials (or, for a member whose whole
     // context is one shared partition, its output) are in place before the
@@ -286,7 +311,7 @@ extern "C" int pa_decode_grouped(float* out, const void* q, int32_t q_dtype, con
                                  int32_t num_work_items, int32_t waves_per_cu,
                                  const int32_t* groups, int32_t num_groups,
                                  const uint32_t* group_items, int32_t num_group_items,
-                                 const int32_t* shared_lens, void* workspace,
+                                 const int32_t* shared_lens, int32_t fuse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   if (num_groups < 0 || num_group_items < 0)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode_grouped: negative group sizes");
@@ -294,7 +319,7 @@ extern "C" int pa_decode_grouped(float* out, const void* q, int32_t q_dtype, con
                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, scale, max_context_len, partition_size, work_items,
                      num_work_items, waves_per_cu, workspace, workspace_bytes, stream, 0, groups,
-                     num_groups, group_items, num_group_items, shared_lens);
+                     num_groups, group_items, num_group_items, shared_lens, fuse);
 }
 
 extern "C" int pa_decode_contiguous(float* out, const void* q, int32_t q_dtype,

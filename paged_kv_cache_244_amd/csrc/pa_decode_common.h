@@ -121,23 +121,31 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // The (request, partition) piece handled by this workgroup.  With a work list,
 // grid (y, z) enumerates its entries in order (y fastest); without one, grid y
 // is the request and z the partition.  Returns false for entries to skip.
-__device__ __forceinline__ bool scheduled_piece(const DecodeParams& p, int& seq, int& part,
-                                                int limit) {
+// by, bz, gdy: the workgroup's (virtual) grid y and z and the grid's y extent.
+__device__ __forceinline__ bool scheduled_piece_at(const DecodeParams& p, unsigned by, unsigned bz,
+                                                   unsigned gdy, int& seq, int& part, int limit) {
   if (p.items) {
-    const unsigned k = blockIdx.y + blockIdx.z * gridDim.y;
+    const unsigned k = by + bz * gdy;
     if (k >= static_cast<unsigned>(p.num_items)) return false;
     const uint32_t it = p.items[k];
     seq = static_cast<int>(it >> 16);
     part = static_cast<int>(it & 0xFFFFu);
   } else {
-    seq = static_cast<int>(blockIdx.y);
-    part = static_cast<int>(blockIdx.z);
+    seq = static_cast<int>(by);
+    part = static_cast<int>(bz);
   }
   return seq < limit && part < p.max_parts;
 }
 
-__device__ __forceinline__ bool scheduled_piece(const DecodeParams& p, int& seq, int& part) {
-  return scheduled_piece(p, seq, part, p.num_seqs);
+// A workgroup's position in a launch of one kernel family: grid x (head tile,
+// or KV head for groups) and the work-list coordinates.
+struct PieceSlot {
+  int x;
+  unsigned y, z, gdy;
+};
+
+__device__ __forceinline__ PieceSlot launch_slot() {
+  return PieceSlot{static_cast<int>(blockIdx.x), blockIdx.y, blockIdx.z, gridDim.y};
 }
 
 __device__ __forceinline__ int clamped_len(const DecodeParams& p, int seq) {
@@ -169,6 +177,13 @@ KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt, bool contiguous)
 // (group, partition), grid x the KV head, and the 16 rows of the tile are
 // (member i / G, query head i % G) pairs, G = num_q_heads / num_kv_heads.
 KernelFn pick_mfma_group_kernel(int head_dim, int block_size);
+
+// Group pieces and remaining pieces in one launch (pa_decode_fused.hip):
+// grid x = group_wgs + remaining workgroups; arguments (group launch
+// parameters, remaining-piece parameters, group_wgs).  gt and mfma name the
+// remaining pieces' kernel as the shape alone would use it.
+using FusedFn = void (*)(DecodeParams, DecodeParams, int);
+FusedFn pick_fused_kernel(int head_dim, int block_size, int gt, bool mfma);
 
 // VALU kernel (pa_decode_valu.hip): one wave per (request, head tile,
 // partition), GT in {1, 2, 4} query heads per wave, fp32 or fp16 queries.

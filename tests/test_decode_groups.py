@@ -211,3 +211,28 @@ def test_step_host_groups_match_plan_groups():
         assert np.array_equal(shared2, shared)
         assert ctypes.sizeof(lay) == ctypes.sizeof(_lib.StepLayout)
         a.close()
+
+
+def test_fuse_decision_follows_token_reads():
+    """One launch for group and remaining pieces when the remaining pieces read at
+    least half as many tokens as the group pieces.  Parallel sampling 30 steps in
+    (samples' own tokens comparable to the shared prompts): fused.  Beam-like forks of
+    long prompts with few own tokens: separate launches."""
+    w, a, samples = _sampling_state(30)
+    tables, lens = a.export(samples, 64, -1)
+    _, plan, groups, _, _ = _lib.plan_groups(tables, lens, 40, 40, 128, B)
+    assert len(groups) and plan["fuse_groups"] == 1
+    a.close()
+    b = _lib.BlockAllocator(800, B, None)
+    kids = []
+    for _ in range(8):
+        p = b.create()
+        b.append(p, 600)
+        kids += [b.fork(p) for _ in range(8)]
+        b.free(p)
+    for _ in range(20):
+        b.append_batch(kids)
+    tables, lens = b.export(kids, 40, -1)
+    _, plan, groups, _, _ = _lib.plan_groups(tables, lens, 40, 40, 128, B)
+    assert len(groups) and plan["fuse_groups"] == 0
+    b.close()

@@ -94,21 +94,23 @@ def test_grouped_decode_matches_oracle(hq, hkv, d, bs):
         paths.assert_attention_close(p_out, want)
 
 
+@pytest.mark.parametrize("fuse", [0, 1])
 @pytest.mark.parametrize("L", [256, 192, 200])
-def test_groups_of_unappended_forks(L):
+def test_groups_of_unappended_forks(L, fuse):
     """Forks of an L-token prompt before any append, with 256-token partitions.
     L = 256: every block is shared and the group pieces cover every piece (no work
     item remains; the launch runs the group kernel and the reduce only).  L = 192:
     the shared length ends inside partition 0 and the forks have no tokens past it,
     so the group piece is each fork's whole context and writes its output.  L = 200:
     each fork's own tokens 192..199 are its piece of partition 0, kept in the spare
-    slot and combined with the group's partial by the reduce."""
+    slot and combined with the group's partial by the reduce.  fuse=1 runs the group
+    and remaining pieces in one launch, fuse=0 in two."""
     import torch
 
     from paged_kv_cache_244_amd import _lib
     from paged_kv_cache_244_amd.cache import PagedKVCache
 
-    print(f"\n[case] groups of unappended forks L={L}", flush=True)
+    print(f"\n[case] groups of unappended forks L={L} fuse={fuse}", flush=True)
     rng = np.random.default_rng(21 + L)
     hq, hkv, d, bs, part = 8, 8, 128, 16, 256
     c = PagedKVCache(64, hkv, d, bs, initial_order=rng.permutation(64).astype(np.int32),
@@ -135,7 +137,7 @@ def test_groups_of_unappended_forks(L):
                            1.0 / np.sqrt(d), L, part, torch.from_numpy(groups).cuda(),
                            torch.from_numpy(gitems.view(np.int32)).cuda(), workspace=ws,
                            work_items=items_dev, shared_lens=torch.from_numpy(shared).cuda(),
-                           stream=c.stream)
+                           stream=c.stream, fuse=fuse)
     torch.cuda.synchronize()
     want = np.stack([attention.attend_one(q[i], k, v, 1.0 / np.sqrt(d)) for i in range(4)])
     paths.assert_attention_close(out.cpu().numpy(), want)
