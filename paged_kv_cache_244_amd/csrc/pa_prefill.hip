@@ -108,7 +108,10 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
   constexpr int KSTEPS = D / 32;
   constexpr int DBLK = D / 16;
   constexpr int CPR = D / 8;                 // 16-byte chunks per token row
-  constexpr int KROWB = D * 2 + 16;          // LDS bytes per K row (padded against conflicts)
+  // LDS bytes per K row.  Padding measured at D = 128 (SQ_LDS_BANK_CONFLICT):
+  // 32 B leaves no bank conflicts, 16 B left 0.7 conflict cycles per LDS
+  // instruction.  D = 64 keeps 16 B (not measured).
+  constexpr int KROWB = D * 2 + (D == 128 ? 32 : 16);
   constexpr int VROWB = D * 2 + 32;          // LDS bytes per V row (transposed reads)
   constexpr int LPT = (KT * CPR + NT - 1) / NT;   // chunks of K (and V) a thread moves per tile
   constexpr int CHUNKS = B * D / 8;          // 16-byte chunks per (block, KV head)
