@@ -96,7 +96,8 @@ def test_grouped_decode_matches_oracle(hq, hkv, d, bs):
 
 @pytest.mark.parametrize("fuse", [0, 1])
 @pytest.mark.parametrize("L", [256, 192, 200])
-def test_groups_of_unappended_forks(L, fuse):
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (8, 2, 64), (16, 2, 128)])
+def test_groups_of_unappended_forks(hq, hkv, d, L, fuse):
     """Forks of an L-token prompt before any append, with 256-token partitions.
     L = 256: every block is shared and the group pieces cover every piece (no work
     item remains; the launch runs the group kernel and the reduce only).  L = 192:
@@ -104,15 +105,17 @@ def test_groups_of_unappended_forks(L, fuse):
     so the group piece is each fork's whole context and writes its output.  L = 200:
     each fork's own tokens 192..199 are its piece of partition 0, kept in the spare
     slot and combined with the group's partial by the reduce.  fuse=1 runs the group
-    and remaining pieces in one launch, fuse=0 in two."""
+    and remaining pieces in one launch, fuse=0 in two; the remaining pieces run on
+    the VALU body for one query head per KV head and on the MFMA body for 4 and 8."""
     import torch
 
     from paged_kv_cache_244_amd import _lib
     from paged_kv_cache_244_amd.cache import PagedKVCache
 
-    print(f"\n[case] groups of unappended forks L={L} fuse={fuse}", flush=True)
-    rng = np.random.default_rng(21 + L)
-    hq, hkv, d, bs, part = 8, 8, 128, 16, 256
+    print(f"\n[case] groups of unappended forks hq={hq} hkv={hkv} d={d} L={L} fuse={fuse}",
+          flush=True)
+    rng = np.random.default_rng(21 + L + hq + d)
+    bs, part = 16, 256
     c = PagedKVCache(64, hkv, d, bs, initial_order=rng.permutation(64).astype(np.int32),
                      num_q_heads=hq, q_dtype=torch.float16)
     k = rng.standard_normal((L, hkv, d)).astype(np.float16)
@@ -123,7 +126,8 @@ def test_groups_of_unappended_forks(L, fuse):
     tables, lens = c.alloc.export(kids, -(-L // bs), -1)
     items, plan, groups, gitems, shared = _lib.plan_groups(tables, lens, hq, hkv, d, bs,
                                                            partition_size=part)
-    assert len(groups) == 1 and len(gitems) == 1
+    cap = 16 // (hq // hkv)                     # members per group: 16 tile rows
+    assert len(groups) == -(-4 // cap) and len(gitems) == len(groups)
     assert len(items) == (4 if L % bs else 0)
     assert shared.tolist() == [0 if L == part else L // bs * bs] * 4
     q = rng.standard_normal((4, hq, d)).astype(np.float16)
