@@ -42,7 +42,8 @@ METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + µs/step, OPT-13
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50; parallel_sampling: its 128 steps)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="opt13b",
                     choices=["opt13b", "gqa", "long_context", "parallel_sampling", "tiny", "prefill",
@@ -53,6 +54,10 @@ def parse_args():
                     help="head-group kernel: MFMA (default for fp16 groups of >= 4) or VALU")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="only measure the HBM read ceiling (pkv_read_probe) and exit")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the read-ceiling measurement that the decode line reports")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
@@ -201,6 +206,59 @@ def copy_probe():
                       "kernel": "elementwise copy (torch copy_)"}), flush=True)
 
 
+PROBE_TILE_BYTES = 4096
+
+
+def read_ceiling(dev, nbytes=4 << 30, reps=5):
+    """HBM read bandwidth of the library's plain read kernel (pkv_read_probe) over a
+    4 GiB buffer (16x the last-level cache), in order and as 4 KiB tiles gathered in
+    a seeded random order (the access pattern of a paged pool); the best of a few
+    grid sizes, median of ``reps`` launches each, timed with HIP events on the
+    launch stream."""
+    import torch
+
+    from paged_kv_cache_244_amd import _lib
+
+    num_tiles = nbytes // PROBE_TILE_BYTES
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.zero_()
+    perm = torch.randperm(num_tiles, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    order = perm.to(dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    result = {}
+    for mode, order_ptr in (("sequential", None), ("tile_gather", order.data_ptr())):
+        best = None
+        for wgs in (1024, 2048, 4096):
+            ms = []
+            for _ in range(reps + 1):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                _lib._check(_lib.lib().pkv_read_probe(buf.data_ptr(), num_tiles, order_ptr,
+                                                      sink.data_ptr(), wgs, stream.cuda_stream))
+                e1.record(stream)
+                e1.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            gbs = nbytes / (float(np.median(ms[1:])) / 1e3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, wgs, float(np.median(ms[1:])))
+        result[mode] = {"gbs": round(best[0], 1), "workgroups": best[1],
+                        "us": round(best[2] * 1e3, 1)}
+    del buf, order
+    torch.cuda.empty_cache()
+    result["bytes"] = nbytes
+    result["kernel"] = "pkv_read_probe (read_probe_kernel)"
+    return result
+
+
+def stream_probe():
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(json.dumps({"read_ceiling": read_ceiling(dev), "gpu": GPU_INFO}), flush=True)
+
+
 REPLICA_TARGET_BYTES = 2 << 30
 
 
@@ -230,12 +288,13 @@ class Scenario:
     def workspace(self, part, max_len):
         return self.cache.workspace(self.num_seqs, self.w.num_q_heads, max_len, part)
 
-    def step(self, t, partition, ev_pair, plans):
+    def step(self, t, partition, ev_pair, plans, marks=None):
         cache = self.cache
         layer = t % len(cache.k)            # the pool replica this step writes and reads
         # reserve, tables, plan and the new tokens' write: one host call, one launch
         _, batch = cache.decode_step(self.seqs, self.max_blocks, partition_size=partition,
-                                     k_new=self.step_k[t], v_new=self.step_v[t], layer=layer)
+                                     k_new=self.step_k[t], v_new=self.step_v[t], layer=layer,
+                                     marks=marks)
         grouped = batch.group_items_dev is not None
         plans.append(dict(batch.plan,
                           num_groups=batch.groups_dev.shape[0] if grouped else 0,
@@ -393,7 +452,7 @@ class ContiguousScenario:
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.out.device)
         return self.ws if need else None
 
-    def step(self, t, partition, ev_pair, plans):
+    def step(self, t, partition, ev_pair, plans, marks=None):
         _lib = _lib_mod()
         w, r = self.w, t % len(self.k)
         pos = self.lens.copy()
@@ -787,10 +846,54 @@ def prefill_cpu_baseline(w, prompt=1024):
             "seconds": round(dt, 2)}
 
 
+def write_copy_times(marks, ev, sc, w):
+    """Times of the step's other launches from the marks decode_step recorded:
+    the upload of the step buffer fused with the new tokens' write (steps
+    without copies), or on copy-on-write steps the upload, the block copy (every
+    pool replica) and the separate write.  Bytes are algorithmic: a write moves
+    T tokens of K and V in and out; a copy reads and writes whole blocks."""
+    tok = 2 * w.num_kv_heads * w.head_dim * 2                     # K+V bytes of one token
+    block = tok * w.block_size
+    layers = len(sc.cache.k)
+    t = sc.num_seqs
+    fused, upload, copy, write, pairs = [], [], [], [], []
+    for m, (d0, _) in zip(marks, ev):
+        if m["pairs"]:
+            upload.append(m["upload"].elapsed_time(m["copy0"]))
+            copy.append(m["copy0"].elapsed_time(m["copy1"]))
+            write.append(m["copy1"].elapsed_time(d0))
+            pairs.append(m["pairs"])
+        else:
+            fused.append(m["upload"].elapsed_time(d0))
+
+    def rate(nbytes, ms):
+        gbs = nbytes / (ms / 1e3) / 1e9
+        return round(gbs, 1), round(gbs / HBM_PEAK_GBS, 4)
+
+    res = {"write_bytes_per_step": 2 * t * tok}
+    if fused:
+        res["upload_write_us"] = round(float(np.mean(fused)) * 1e3, 2)
+        res["upload_write_steps"] = len(fused)
+    if copy:
+        cbytes = 2 * float(np.mean(pairs)) * layers * block
+        cms = float(np.mean(copy))
+        wms = float(np.mean(write))
+        res.update({
+            "copy_steps": len(copy), "copy_pairs_per_step": round(float(np.mean(pairs)), 1),
+            "copy_layers": layers, "copy_bytes_per_step": int(cbytes),
+            "copy_us": round(cms * 1e3, 2), "copy_gbs_frac": rate(cbytes, cms),
+            "write_us": round(wms * 1e3, 2), "write_gbs_frac": rate(2 * t * tok, wms),
+            "upload_us_copy_steps": round(float(np.mean(upload)) * 1e3, 2)})
+    return res
+
+
 def main():
     args = parse_args()
     if args.copy_probe:
         copy_probe()
+        return
+    if args.stream_probe:
+        stream_probe()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -799,6 +902,8 @@ def main():
     global GPU_INFO
     GPU_INFO = gpu_info()                   # before this process touches the GPU
     if args.workload in ("prefill", "swap", "beams"):
+        if args.steps is None:
+            args.steps = 50
         import torch
         if not torch.cuda.is_available():
             print("bench.py needs a GPU", file=sys.stderr)
@@ -821,21 +926,40 @@ def main():
     _lib.set_kernel_policy(_lib.PKV_POLICY_VALU if args.kernel_policy == "valu"
                            else _lib.PKV_POLICY_DEFAULT)
 
-    total_steps = args.warmup + args.steps
-    if args.workload == "parallel_sampling":
-        sc = sampling_scenario(workloads.parallel_sampling(), total_steps, dev, args.replicas,
+    ps = args.workload == "parallel_sampling"
+    if ps:
+        # The workload's statement: 128 steps from the fork on, step 0 being the one
+        # that copies the partly filled last prompt block.  The timed run starts
+        # at step 0 on a fresh cache; the warmup runs on a separate one.
+        sw = workloads.parallel_sampling()
+        if args.steps is None:
+            args.steps = sw.steps
+        if args.warmup:
+            warm = sampling_scenario(sw, args.warmup, dev, args.replicas,
+                                     prefix_groups=not args.no_prefix_groups)
+            for t in range(args.warmup):
+                warm.step(t, "auto", None, [])
+            torch.cuda.synchronize()
+            del warm
+            torch.cuda.empty_cache()
+        first_step = 0
+        sc = sampling_scenario(sw, args.steps, dev, args.replicas,
                                prefix_groups=not args.no_prefix_groups)
     else:
+        if args.steps is None:
+            args.steps = 50
+        first_step = args.warmup
         w = {"long_context": lambda: workloads.long_context(16),
              "tiny": workloads.tiny}.get(args.workload, workloads.WORKLOADS.get(args.workload))()
-        sc = decode_scenario(w, total_steps, dev, args.replicas)
+        sc = decode_scenario(w, args.warmup + args.steps, dev, args.replicas)
         if args.layout == "contiguous":
             base = sc
-            sc = ContiguousScenario(base, total_steps, dev, args.replicas)
+            sc = ContiguousScenario(base, args.warmup + args.steps, dev, args.replicas)
             del base
             torch.cuda.empty_cache()
-    if args.layout == "contiguous" and args.workload == "parallel_sampling":
+    if args.layout == "contiguous" and ps:
         raise SystemExit("the contiguous layout is measured on the decode workloads only")
+    total_steps = first_step + args.steps
     w = sc.w
     # The planner's automatic choice for the lengths the run ends at (they grow by
     # total_steps tokens), then kept fixed so every timed step runs one schedule shape.
@@ -846,22 +970,23 @@ def main():
     sc.workspace(partition, int(sc.lengths.max()) + total_steps)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    def timing_event():
+        return torch.cuda.Event(enable_timing=True)
+
+    ev = [(timing_event(), timing_event()) for _ in range(args.steps)]
+    marks = [{"upload": timing_event(), "copy0": timing_event(), "copy1": timing_event()}
+             for _ in range(args.steps)] if args.layout == "paged" else [None] * args.steps
     step_bytes, unique_step_bytes = [], []
     plans = []
 
-    def step(t, timed_slot=None):
-        sc.step(t, partition, ev[timed_slot] if timed_slot is not None else None, plans)
-
     lengths = sc.lengths.copy()
-    for t in range(args.warmup):
-        step(t)
+    for t in range(first_step):
+        sc.step(t, partition, None, plans)
         lengths += 1
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, timed_slot=i)
+        sc.step(first_step + i, partition, ev[i], plans, marks[i])
         lengths += 1
         step_bytes.append(kv_bytes(lengths, w))
         if sc.unique_bytes is not None:
@@ -879,9 +1004,11 @@ def main():
         # Shared prompt blocks are read from HBM once; the roofline counts unique bytes.
         sc.extra["unique_kv_bytes_per_step"] = int(np.mean(unique_step_bytes))
         achieved = float(np.mean(unique_step_bytes)) / decode_avg_s / 1e9
+    writes_copies = (write_copy_times(marks, ev, sc, w) if args.layout == "paged" else None)
 
     # The committed counter summaries describe the paged kernels only.
     traffic = counter_traffic(args.workload) if args.layout == "paged" else None
+    ceiling = None if args.no_read_probe else read_ceiling(dev)
     baseline = None
     if args.cpu_seconds > 0 and hasattr(w, "offsets") and args.layout == "paged":
         baseline = cpu_baseline(w, args.cpu_seconds)
@@ -897,10 +1024,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": f"{w.name} decode layer",
+            "arithmetic": "fp16 K/V (and q, except the tiny case) read, fp32 softmax and "
+                          "accumulation",
+            "timed_steps": [first_step, first_step + args.steps - 1],
             "num_seqs": sc.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": "f16",
             "q_dtype": np.dtype(w.q_dtype).name, "partition_size": plans[-1]["partition_size"],
@@ -925,7 +1055,11 @@ def main():
                                                  if traffic else None),
                      "kernel": ("pa_decode_grouped (group pieces, remaining pieces, reduce)"
                                 if plans[-1]["num_groups"] else
-                                "pa_decode (partition + reduce launches)")},
+                                "pa_decode (partition + reduce launches)"),
+                     "measured_peak": ceiling,
+                     "frac_of_measured": (round(achieved / ceiling["tile_gather"]["gbs"], 4)
+                                          if ceiling else None)},
+        "write_copy": writes_copies,
         "cpu_baseline": baseline,
         "gpu": GPU_INFO,
     }

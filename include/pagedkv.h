@@ -442,9 +442,9 @@ int pa_decode_contiguous(float* out, const void* q, int32_t q_dtype,
 
 /*
  * pa_prefill — causal attention of each request's new tokens (the prompt, or
- * the next chunk of one) over its block table.  [C] "Prompt processing and
- * incremental decoding impose different shapes of work": many queries per
- * request at once, bound by arithmetic rather than bytes; [B] "The page table,
+ * the next chunk of one) over its block table.  [C] "Memory savings change
+ * the scheduling question" contrasts this prompt phase with decoding: many
+ * queries per request at once, bound by arithmetic rather than bytes; [B] "The page table,
  * relocated into attention": keys and values come through the table, after
  * kv_cache_write stored the new tokens.
  *
@@ -676,6 +676,24 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
                         int32_t num_kv_heads, int32_t head_dim, int32_t q_dtype,
                         int32_t partition_size, int32_t num_compute_units, int32_t flags,
                         void* buffer, uint64_t buffer_bytes, kv_step_layout* layout);
+
+/*
+ * pkv_read_probe — the HBM read ceiling that decode is measured against.
+ * [B] "Why the KV cache is the thing that limits your batch": decode reads
+ * every cached key and value once per step and does little arithmetic per
+ * byte, so the read bandwidth the device reaches bounds its time from below.
+ *
+ * Reads num_tiles 4 KiB tiles of src (device memory, 16-byte aligned,
+ * num_tiles * 4096 bytes) once each, in order when tile_order is NULL, else in
+ * the order of tile_order (device int32 [num_tiles]; entries outside
+ * [0, num_tiles) are skipped), with `workgroups` 256-thread workgroups on
+ * `stream`.  sink: device uint32 [1], written only for a data pattern that
+ * zeros never produce (it keeps the loads from being dropped).  Asynchronous;
+ * time it with events on the stream.  Errors: PKV_ERR_INVALID_ARG for
+ * negative sizes, NULL or misaligned pointers; PKV_ERR_HIP for a failed launch.
+ */
+int pkv_read_probe(const void* src, int64_t num_tiles, const int32_t* tile_order, uint32_t* sink,
+                   int32_t workgroups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -100,8 +100,9 @@ def attend_prefill_paged(q, k_pool, v_pool, block_tables, context_lens, q_starts
                          scale):
     """Causal attention of each request's new tokens over its block table (float64).
 
-    The prompt phase ("The KV cache is a systems problem", section "Prompt
-    processing and incremental decoding impose different shapes of work"):
+    The prompt phase ("The KV cache is a systems problem", section "Memory
+    savings change the scheduling question", where it is set against
+    incremental decoding):
     request i holds L_i tokens, the last Q_i = q_starts[i+1] - q_starts[i] of
     which are its new queries; query j sits at position L_i - Q_i + j and sees
     tokens 0..that position, gathered through the table as in ``attend_paged``.

@@ -98,6 +98,7 @@ _SIGNATURES = {
     "kv_swap_blocks": (c_int32, [POINTER(c_void_p), POINTER(c_void_p), c_int32, POINTER(c_void_p),
                                  POINTER(c_void_p), c_int32, c_int32, c_void_p, c_int32, c_int32,
                                  c_int32, c_int32, c_void_p]),
+    "pkv_read_probe": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_void_p]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode_set_kernel_policy": (c_int32, [c_int32]),
     "pa_decode_plan": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,

@@ -28,14 +28,29 @@ import torch
 from . import _lib
 
 
+class _Stamp:
+    """Which upload a set of device views came from: ring slot and its generation.
+    ``current()`` is False once a later upload has reused that slot's device buffer."""
+
+    __slots__ = ("staging", "slot", "gen")
+
+    def __init__(self, staging, slot, gen):
+        self.staging, self.slot, self.gen = staging, slot, gen
+
+    def current(self) -> bool:
+        return self.staging.gen[self.slot] == self.gen
+
+
 class _Staging:
     """Uploads several small host arrays with ONE host-to-device copy.
 
     The arrays are packed (16-byte aligned) into a pinned host buffer taken from a
-    ring, copied asynchronously into a device buffer, and returned as typed views
-    of that buffer.  A pinned ring slot is reused only after the copy that last
-    read it has completed; the device buffer is reused in stream order, so views
-    stay valid until the next ``upload`` on the same stream.
+    ring, copied asynchronously into the device buffer of the same ring slot, and
+    returned as typed views of that buffer.  A pinned slot is reused only after the
+    copy that last read it has completed; a device slot is reused in stream order,
+    ``depth`` uploads later.  So the views of one upload (say a decode step's
+    tables) stay valid while up to ``depth - 1`` other uploads (a prefill, a swap)
+    run in between; each upload's stamp (``last_stamp``) tells whether they still are.
     """
 
     def __init__(self, device, depth: int = 4, nbytes: int = 1 << 20):
@@ -43,10 +58,12 @@ class _Staging:
         self.host = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
         self.events = [None] * depth
         self.next = 0
-        self.dev = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.dev = [torch.empty(nbytes, dtype=torch.uint8, device=device) for _ in range(depth)]
+        self.gen = [0] * depth
+        self.last_stamp = None
 
     def _slot(self, nbytes):
-        """Next pinned ring slot, once the copy that last read it is done."""
+        """Next ring slot, once the copy that last read its pinned buffer is done."""
         i = self.next
         self.next = (i + 1) % len(self.host)
         if self.events[i] is not None:
@@ -55,25 +72,31 @@ class _Staging:
             self.host[i] = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
         return i
 
-    def _send(self, i, total, stream, write=None):
-        """Copy ``total`` bytes of ring slot i to the device buffer.  ``write`` (a
-        callable taking the device buffer's address and the pinned slot) replaces the
-        plain copy with one launch that also writes the step's new tokens."""
-        if self.dev.numel() < total:
-            self.dev = torch.empty(total, dtype=torch.uint8, device=self.device)
+    def _send(self, i, total, stream, write=None, mark=None):
+        """Copy ``total`` bytes of ring slot i's pinned buffer to its device buffer.
+        ``write`` (a callable taking the device buffer's address and the pinned slot)
+        replaces the plain copy with one launch that also writes the step's new tokens.
+        ``mark``, an event, is recorded on the stream just before the launch."""
+        if self.dev[i].numel() < total:
+            self.dev[i] = torch.empty(total, dtype=torch.uint8, device=self.device)
+        self.gen[i] += 1
+        self.last_stamp = _Stamp(self, i, self.gen[i])
+        dev = self.dev[i]
         if total:
             # A library kernel reads the pinned buffer over the bus: no copy-engine
             # hand-off between the step's kernels.
             nbytes = (total + 15) // 16 * 16
+            if mark is not None:
+                mark.record(stream)
             if write is None:
-                _lib._check(_lib.lib().pkv_upload(self.dev.data_ptr(), self.host[i].data_ptr(),
+                _lib._check(_lib.lib().pkv_upload(dev.data_ptr(), self.host[i].data_ptr(),
                                                   nbytes, stream.cuda_stream))
             else:
-                write(self.dev.data_ptr(), self.host[i].data_ptr(), nbytes)
+                write(dev.data_ptr(), self.host[i].data_ptr(), nbytes)
             ev = torch.cuda.Event()
             ev.record(stream)
             self.events[i] = ev
-        return self.dev
+        return dev
 
     def upload(self, arrays, stream):
         arrays = [np.ascontiguousarray(a) for a in arrays]
@@ -92,7 +115,7 @@ class _Staging:
             views.append(t.view(a.shape))
         return views
 
-    def fill_and_upload(self, fill, stream, write=None):
+    def fill_and_upload(self, fill, stream, write=None, mark=None):
         """``fill(host_ptr, capacity)`` writes the host buffer in place and returns the
         bytes used, or None with ``needed`` bytes to retry with.  Returns
         (result of fill, device buffer, pinned host buffer) after one asynchronous copy.
@@ -107,7 +130,7 @@ class _Staging:
             self.host[i] = torch.empty(max(fill.needed, 2 * host.numel()), dtype=torch.uint8,
                                        pin_memory=True)
         fused = write(res) if write is not None else None
-        return res, self._send(i, int(res.total_bytes), stream, fused), self.host[i]
+        return res, self._send(i, int(res.total_bytes), stream, fused, mark), self.host[i]
 
 
 _TORCH_DTYPE = {"i4": torch.int32, "i8": torch.int64, "f4": torch.float32, "f2": torch.float16}
@@ -117,17 +140,19 @@ class DeviceArray:
     """A typed region of a device buffer: its address for the library, and a torch
     view built only when asked for (``tensor()``)."""
 
-    __slots__ = ("base", "offset", "dtype", "shape", "ptr", "_t")
+    __slots__ = ("base", "offset", "dtype", "shape", "ptr", "_t", "stamp")
 
-    def __init__(self, base, offset, dtype, shape):
+    def __init__(self, base, offset, dtype, shape, stamp=None):
         self.base, self.offset, self.dtype, self.shape = base, int(offset), dtype, tuple(shape)
         self.ptr = base.data_ptr() + self.offset
         self._t = None
+        self.stamp = stamp          # the staging upload holding it, if any
 
     @classmethod
     def of(cls, t):
         a = cls.__new__(cls)
         a.base, a.offset, a.dtype, a.shape, a.ptr, a._t = t, 0, t.dtype, tuple(t.shape), t.data_ptr(), t
+        a.stamp = None
         return a
 
     def tensor(self):
@@ -316,13 +341,24 @@ class PagedKVCache:
         return slots_dev
 
     def decode_step(self, seqs, max_blocks=None, partition_size="auto", k_new=None, v_new=None,
-                    layer=0):
+                    layer=0, marks=None):
         """One decode step's host work in one library call and one upload: reserve one
         slot per sequence (issuing copy-on-write copies), export tables and lengths and
         plan the launch (``kv_decode_step_host``).  With ``k_new``/``v_new`` ([S, kv_heads,
         head_dim] fp16 device tensors) the new tokens are written into ``layer`` too; a
         step without copy-on-write copies does the upload and the write in one launch
-        (``pkv_upload_write``).  Returns (device slots, DecodeBatch)."""
+        (``pkv_upload_write``).  Returns (device slots, DecodeBatch).
+
+        The slots and the batch's device arrays sit in one slot of the cache's
+        staging ring, which later uploads (steps, batches, prefills, swaps,
+        reserves) reuse only after the ring's other slots: up to 3 of them may run
+        between this call and ``attend``; after more, ``attend`` and ``write``
+        raise instead of reading another call's bytes.
+
+        ``marks`` (for timing) is a dict of events created with timing enabled:
+        "upload" is recorded just before the upload launch and, on a step with
+        copy-on-write copies, "copy0" / "copy1" just before and after them;
+        ``marks["pairs"]`` is set to the number of copied blocks."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
         if self._pending:
             self.retire()
@@ -361,14 +397,21 @@ class PagedKVCache:
                     self.block_size, self._stream_ptr))
             return launch
 
-        lay, dev, host = self._staging.fill_and_upload(fill, self.stream, fused)
+        lay, dev, host = self._staging.fill_and_upload(
+            fill, self.stream, fused, None if marks is None else marks["upload"])
         lens_host = host[lay.lens_offset:lay.lens_offset + 4 * n].numpy().view(np.int32).copy()
+        if marks is not None:
+            marks["pairs"] = int(lay.num_pairs)
         if lay.num_pairs:
+            if marks is not None:
+                marks["copy0"].record(self.stream)
             _lib.kv_copy_blocks(self.k, self.v, DeviceArray(dev, lay.pairs_offset, torch.int32,
                                                             (lay.num_pairs, 2)).tensor(),
                                 stream=self.stream)
+            if marks is not None:
+                marks["copy1"].record(self.stream)
         plan = {name: int(getattr(lay.plan, name)) for name, _ in _lib.DecodePlan._fields_}
-        slots = DeviceArray(dev, lay.slots_offset, torch.int64, (n,))
+        slots = DeviceArray(dev, lay.slots_offset, torch.int64, (n,), self._staging.last_stamp)
         if k_new is not None and lay.num_pairs:
             self.write(slots, k_new, v_new, layer=layer)
         batch = DecodeBatch(DeviceArray(dev, lay.tables_offset, torch.int32, (n, lay.max_blocks)),
@@ -376,6 +419,7 @@ class PagedKVCache:
                             int(lay.max_context_len), lens_host,
                             DeviceArray(dev, lay.items_offset, torch.int32, (plan["num_items"],)),
                             plan, key)
+        batch.stamp = self._staging.last_stamp
         if lay.num_group_items:
             batch.groups_dev = DeviceArray(dev, lay.groups_offset, torch.int32,
                                            (lay.num_groups, _lib.GROUP_STRIDE))
@@ -390,6 +434,8 @@ class PagedKVCache:
             _lib.kv_cache_write(self.k[layer], self.v[layer], k_new, v_new, slots,
                                 stream=self.stream)
             return
+        if slots.stamp is not None and not slots.stamp.current():
+            raise RuntimeError("slots are stale: later uploads have reused their staging buffer")
         t = slots.shape[0]
         want = (t, self.num_kv_heads, self.head_dim)
         for x in (k_new, v_new):
@@ -423,7 +469,9 @@ class PagedKVCache:
         """Upload the block tables, lengths and launch schedule of ``seqs`` for decode
         (with prefix groups where they pay, as ``decode_step`` plans them).
 
-        The returned device tensors stay valid until the next upload.
+        The returned device arrays live in one slot of the cache's staging ring: they
+        stay valid while fewer than 4 later uploads have been made (``attend``
+        refuses a batch whose slot was reused).
         """
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
         tables, lens, max_len = self._tables(seqs, max_blocks, pad_value)
@@ -440,11 +488,14 @@ class PagedKVCache:
                                     DeviceArray.of(it), info, key)
                 batch.groups_dev, batch.group_items_dev = DeviceArray.of(g), DeviceArray.of(gi)
                 batch.shared_dev = DeviceArray.of(sh)
+                batch.stamp = self._staging.last_stamp
                 return batch
         items, info = self._plan(lens, *key)
         t, l_, it = self.upload(tables, lens, items)
-        return DecodeBatch(DeviceArray.of(t), DeviceArray.of(l_), max_len, lens,
-                           DeviceArray.of(it), info, key)
+        batch = DecodeBatch(DeviceArray.of(t), DeviceArray.of(l_), max_len, lens,
+                            DeviceArray.of(it), info, key)
+        batch.stamp = self._staging.last_stamp
+        return batch
 
     def workspace(self, num_seqs, num_q_heads, max_context_len, partition_size):
         need = _lib.pa_decode_workspace_size(num_seqs, num_q_heads, self.head_dim, max_context_len,
@@ -479,6 +530,11 @@ class PagedKVCache:
         other than the one the batch was planned for.
         """
         s, hq, d = q.shape
+        if batch.stamp is not None and not batch.stamp.current():
+            raise RuntimeError(
+                "DecodeBatch is stale: its tables and work list were in a staging buffer that "
+                f"{len(self._staging.dev)} later uploads (decode steps, batches, prefills, swaps, "
+                "reserves) have reused; make the batch again")
         key = (hq, q.dtype, batch.plan_key[2] if partition_size is None else partition_size)
         if key == batch.plan_key:
             items, info = batch.items_dev, batch.plan
@@ -532,10 +588,11 @@ class DecodeBatch:
     made for."""
 
     __slots__ = ("tables_dev", "lens_dev", "max_len", "lens_host", "items_dev", "plan",
-                 "plan_key", "num_seqs", "groups_dev", "group_items_dev", "shared_dev")
+                 "plan_key", "num_seqs", "groups_dev", "group_items_dev", "shared_dev", "stamp")
 
     def __init__(self, tables, lens, max_len, lens_host, items, plan, plan_key):
         self.tables_dev, self.lens_dev, self.items_dev = tables, lens, items
+        self.stamp = None          # the upload that holds the device arrays (cache-made batches)
         self.groups_dev = self.group_items_dev = self.shared_dev = None   # prefix groups
         self.max_len = max_len
         self.lens_host = lens_host

@@ -12,7 +12,7 @@
 // Rows of the 16-wide head dimension beyond GT are zero queries (unused).  The
 // output layout of S^T (lane (g, i) holds tokens 4g..4g+3 of head i) is exactly
 // the A-operand layout P needs, so P goes from the softmax straight into the
-// second MFMA after rounding to fp16 (P is in [0, 1]).  V must be consumed with
+// second MFMA after rounding to fp16 (P is in [0, 2^kSlack], see below).  V must be consumed with
 // tokens along K, i.e. transposed relative to the pool: each V tile is written
 // to LDS (rows padded by 32 bytes so the reads below hit distinct banks) and
 // read back with ds_read_b64_tr_b16, which hands every lane the four tokens of
@@ -20,11 +20,15 @@
 // 16 bytes of token row i at column chunk 4*kk + g.
 //
 // Softmax: S^T is scaled into log2 units and masked (tokens past the context
-// get -inf; their V rows are zeroed in LDS).  The running max of head i is kept
-// identical in its four lane groups (max exchanged with two shuffles per
-// tile); each lane accumulates its share of the denominator and the four
-// shares are summed once at the end.  O rows are rescaled by their head's
-// factor each tile.
+// get -inf; their V rows are zeroed in LDS).  The reference max of head i is
+// kept identical in its four lane groups (max exchanged with two shuffles per
+// tile).  Rescaling is lazy: the reference max moves only when a tile's max
+// exceeds it by more than kSlack = 8 (log2 units), so P = 2^(s - m) stays at
+// most 2^8, where fp16 still holds it to 2^-11 relative; O and the denominator
+// are rescaled only in tiles where some head's reference moved (a wave-uniform
+// ballot).  Each lane accumulates its share of the denominator from the same
+// fp16-rounded P that feeds the P.V product, and the four shares are summed
+// once at the end.
 //
 // Work decomposition, masking, partitions and the workspace format are those of
 // the VALU kernel in pa_decode_valu.hip, so both feed the same reduce kernel.

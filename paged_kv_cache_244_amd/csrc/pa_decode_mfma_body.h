@@ -214,10 +214,13 @@ __device__ __forceinline__ void mfma_piece(const DecodeParams& p, PieceSlot slot
           for (int db = 0; db < DBLK; ++db) o[db][r] *= ar;
         }
       }
-      lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       m = m_new;
       const half4 pa = half4{static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1]),
                              static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])};
+      // The denominator sums the same fp16-rounded weights the P.V product uses,
+      // so numerator and denominator carry one rounding.
+      lsum += (static_cast<float>(pa[0]) + static_cast<float>(pa[1])) +
+              (static_cast<float>(pa[2]) + static_cast<float>(pa[3]));
       __syncthreads();                        // V tile visible in LDS
       const unsigned char* src = vl + (4 * grp + (li >> 2)) * ROWB + 8 * (li & 3);
 #pragma unroll

@@ -1,10 +1,10 @@
 // Paged prefill: causal attention of a request's new (prompt) tokens over its
 // block table, on the gfx950 matrix cores.
 //
-// "The KV cache is a systems problem" (rsw.lol), section "Prompt processing
-// and incremental decoding impose different shapes of work": the prompt phase
-// attends many query tokens at once and is bound by arithmetic, decode by
-// bytes.  The keys and values are read through the request's block table ("Only
+// "The KV cache is a systems problem" (rsw.lol), section "Memory savings change
+// the scheduling question", which contrasts the prompt phase with incremental
+// decoding: the prompt phase attends many query tokens at once and is bound by
+// arithmetic, decode by bytes.  The keys and values are read through the request's block table ("Only
 // 20.4% of your KV cache held actual tokens" (blog.teqners.com), section "The
 // page table, relocated into attention"), after kv_cache_write stored the
 // prompt's own tokens.

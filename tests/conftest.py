@@ -24,6 +24,18 @@ def pytest_collection_modifyitems(config, items):
     pass
 
 
+def pytest_sessionfinish(session, exitstatus):
+    # PKV_MARGINS=<file>: write every attention comparison's margins (test, label,
+    # rows, max_abs, rel_l2) as JSON, for the parity-margins summary.
+    path = os.environ.get("PKV_MARGINS")
+    paths = sys.modules.get("tests.paths")
+    if path and paths is not None:
+        import json
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump({"exitstatus": int(exitstatus), "margins": paths.MARGINS}, f, indent=0)
+
+
 @pytest.fixture(scope="session")
 def rng():
     import numpy as np

@@ -12,12 +12,18 @@ Pools start filled with NaN so that unused slots are poisoned on both sides,
 and table padding is an out-of-range block id on both sides.
 """
 
+import os
+
 import numpy as np
 
 from oracle import alloc_model, attention, cache
 
 TOL_MAX_ABS = 2e-3
 TOL_REL_L2 = 1e-3
+
+# Every attention comparison of the session: (test, label, rows compared, max_abs,
+# rel_l2).  conftest.py writes them out when PKV_MARGINS names a file.
+MARGINS = []
 
 
 def split_tokens(w):
@@ -104,7 +110,9 @@ def run_gpu(w, partition_size, cache_obj=None, out_only=False, schedule="plan"):
     return res
 
 
-def assert_attention_close(got, want, rows=None):
+def assert_attention_close(got, want, rows=None, label=""):
+    """max-abs and relative-L2 error of ``got`` against the fp64 oracle, over every
+    row (or the listed ones); records the margins, then asserts the bounds."""
     if rows is not None:
         got, want = got[rows], want[rows]
     got = np.asarray(got, dtype=np.float64)
@@ -112,6 +120,9 @@ def assert_attention_close(got, want, rows=None):
     max_abs = float(np.abs(err).max()) if err.size else 0.0
     denom = float(np.linalg.norm(want))
     rel = float(np.linalg.norm(err)) / denom if denom > 0 else float(np.linalg.norm(err))
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    MARGINS.append({"test": test, "label": label, "rows": int(got.shape[0]) if got.ndim else 1,
+                    "max_abs": max_abs, "rel_l2": rel})
     assert np.isfinite(got).all(), "non-finite output"
     assert max_abs <= TOL_MAX_ABS and rel <= TOL_REL_L2, f"max_abs {max_abs:.3e} rel_l2 {rel:.3e}"
     return max_abs, rel

@@ -231,48 +231,67 @@ def test_cache_write_skips_negative_and_out_of_range_slots():
 
 # ---------------------------------------------------------------------- full-size workloads
 
-def _sample_rows(w, n=8):
-    order = np.argsort(w.lengths)
-    picks = {int(order[0]), int(order[-1])}
-    rng = np.random.default_rng(0)
-    picks.update(int(x) for x in rng.choice(w.num_seqs, size=min(n, w.num_seqs), replace=False))
-    return sorted(picks)
+def _kernel_name(w, policy=0):
+    group = w.num_q_heads // w.num_kv_heads
+    return "mfma" if group >= 4 and w.q.dtype == np.float16 and policy == 0 else "valu"
 
 
 @pytest.mark.parametrize("name", ["opt13b", "gqa"])
 def test_full_size_workload(name):
     """Full-size inputs in the launch configuration the benchmark times (the planner's
     automatic partition size, work list and residency limit), plus a fixed 512-token
-    split (or none); pools and tables compared whole, attention on sampled requests."""
+    split (or none), and for head groups the VALU kernel too; pools and tables
+    compared whole, attention on every request and head."""
+    from paged_kv_cache_244_amd import _lib
     _announce(f"full size {name}")
     w = workloads.WORKLOADS[name]()
-    rows = _sample_rows(w)
-    ref = paths.run_oracle(w, sample=rows)
+    ref = paths.run_oracle(w)
     got = paths.run_gpu(w, "auto")
     auto = got["plan"]["partition_size"]
     assert np.array_equal(got["tables"], ref["tables"])
     paths.assert_pools_bit_exact(got, ref)
-    paths.assert_attention_close(got["out"], ref["out"], rows=rows)
+    paths.assert_attention_close(got["out"], ref["out"],
+                                 label=f"{name} {_kernel_name(w)} P={auto} (bench launch)")
     c, batch, q = got["cache"], got["batch"], got["q_dev"]
     other = 512 if auto != 512 else 0
     out = c.attend(q, batch, w.scale, partition_size=other).cpu().numpy()
-    paths.assert_attention_close(out, ref["out"], rows=rows)
+    paths.assert_attention_close(out, ref["out"], label=f"{name} {_kernel_name(w)} P={other}")
+    if _kernel_name(w) == "mfma":
+        try:
+            _lib.set_kernel_policy(_lib.PKV_POLICY_VALU)
+            for part in ("auto", 512):     # "auto": the batch's own plan
+                out = c.attend(q, batch, w.scale, partition_size=part).cpu().numpy()
+                shown = auto if part == "auto" else part
+                paths.assert_attention_close(out, ref["out"], label=f"{name} valu P={shown}")
+        finally:
+            _lib.set_kernel_policy(_lib.PKV_POLICY_DEFAULT)
 
 
 @pytest.mark.parametrize("block_size", [8, 16, 32, 64, 128])
 def test_long_context_block_sweep(block_size):
     """16 requests of 8K-32K tokens, 32/8 heads; every block size against one oracle
-    output (the logical data does not depend on the block size)."""
+    output over all 16 requests (the logical data does not depend on the block size),
+    in the planner's launch and with the 512-token partitions of the workload's
+    statement; at B=16 the VALU kernel too."""
+    from paged_kv_cache_244_amd import _lib
     _announce(f"long context B={block_size}")
     w = _long_context_base()
     if block_size != 16:
         w = workloads.with_block_size(w, block_size)
-    rows = [0, 5, 11]
+    ref = _long_context_ref()
     got = paths.run_gpu(w, "auto", out_only=True)
-    paths.assert_attention_close(got["out"], _long_context_ref(rows), rows=rows)
+    auto = got["plan"]["partition_size"]
+    paths.assert_attention_close(got["out"], ref, label=f"long_context B={block_size} mfma P={auto}")
     c, batch, q = got["cache"], got["batch"], got["q_dev"]
     out = c.attend(q, batch, w.scale, partition_size=512).cpu().numpy()
-    paths.assert_attention_close(out, _long_context_ref(rows), rows=rows)
+    paths.assert_attention_close(out, ref, label=f"long_context B={block_size} mfma P=512")
+    if block_size == 16:
+        try:
+            _lib.set_kernel_policy(_lib.PKV_POLICY_VALU)
+            out = c.attend(q, batch, w.scale, partition_size="auto").cpu().numpy()
+            paths.assert_attention_close(out, ref, label=f"long_context B=16 valu P={auto}")
+        finally:
+            _lib.set_kernel_policy(_lib.PKV_POLICY_DEFAULT)
 
 
 _LC = {}
@@ -284,17 +303,17 @@ def _long_context_base():
     return _LC["w"]
 
 
-def _long_context_ref(rows):
-    key = tuple(rows)
-    if key not in _LC:
+def _long_context_ref():
+    """fp64 oracle output of every request of the long-context workload (computed once)."""
+    if "ref" not in _LC:
         from oracle import attention
         w = _long_context_base()
         out = np.zeros((w.num_seqs, w.num_q_heads, w.head_dim))
-        for i in rows:
+        for i in range(w.num_seqs):
             k, v = w.tokens(i)
             out[i] = attention.attend_one(w.q[i], k, v, w.scale)
-        _LC[key] = out
-    return _LC[key]
+        _LC["ref"] = out
+    return _LC["ref"]
 
 
 def test_random_shapes():

@@ -12,7 +12,7 @@ allocator + kv_copy_blocks + kv_cache_write + pa_decode) is checked against:
   bytes over the whole pool at chosen steps;
 * each sample's logical view, gathered through its table, equals its prompt
   followed by its own tokens (the other readers' view survives copy-on-write);
-* the fp64 oracle attention for sampled rows, within the stated tolerance.
+* the fp64 oracle attention for every sample, within the stated tolerance.
 """
 
 import numpy as np
@@ -68,7 +68,6 @@ def test_parallel_sampling_128_steps():
 
     own_k = [[] for _ in samples]          # each sample's own tokens, for the logical check
     own_v = [[] for _ in samples]
-    rng = np.random.default_rng(0)
     for step in range(w.steps):
         k_new, v_new, q = w.step_inputs(step)
         # HIP path: one decode step (copy-on-write copies are issued inside).
@@ -99,10 +98,9 @@ def test_parallel_sampling_128_steps():
         gv = c.v[0].cpu().numpy()
         if step in CHECK_POOLS:
             paths.assert_pools_bit_exact({"k": gk, "v": gv}, {"k": kp, "v": vp})
-        rows = sorted(set(rng.choice(len(samples), size=6, replace=False).tolist()) | {0, 7})
         got = out.cpu().numpy()
         want = np.zeros_like(got, dtype=np.float64)
-        for i in rows:
+        for i in range(len(samples)):
             p = i // n
             lo, hi = offs[p], offs[p + 1]
             keys = np.concatenate([w.prompt_k[lo:hi], np.array(own_k[i])])
@@ -114,7 +112,8 @@ def test_parallel_sampling_128_steps():
             assert np.array_equal(oc.gather_logical(gv, tables[i], L, B).view(np.uint16),
                                   vals.view(np.uint16))
             want[i] = attention.attend_one(q[i], keys, vals, w.scale)
-        paths.assert_attention_close(got, want, rows=rows)
+        paths.assert_attention_close(got, want, label=f"parallel_sampling step {step} "
+                                     f"(groups={batch.group_items_dev is not None})")
     for s in samples:
         c.free(s)
     assert c.alloc.stats()["free_blocks"] == w.num_blocks, "all blocks reclaimed"
