@@ -313,6 +313,33 @@ int pa_decode(float* out, const void* q, int32_t q_dtype,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_noalloc — pa_decode without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Arguments, layout, results and
+ * errors are pa_decode's, minus workspace/workspace_bytes: the split-context
+ * partials go to a fixed array of PKV_NOALLOC_WORKSPACE_BYTES (64 MiB) that the
+ * library keeps in each GPU's memory from its first use until the process
+ * ends.  The call allocates nothing (no hipMalloc, no hipFree, no allocating
+ * library routine); its first call on a device looks the array's address up
+ * once.  A launch whose workspace (pa_decode_workspace_size for its sizes)
+ * exceeds the array fails with PKV_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares that GPU's array: calls that can overlap on one
+ * GPU (several streams, several threads) race on it and must be serialised by
+ * the caller, e.g. by issuing them on one stream.  Nothing in the array needs
+ * clearing: each partial it holds is written before it is read in the same call.
+ * Outputs are bitwise those of pa_decode with the same arguments.
+ */
+#define PKV_NOALLOC_WORKSPACE_BYTES (64u << 20)
+int pa_decode_noalloc(float* out, const void* q, int32_t q_dtype,
+                      const void* k_cache, const void* v_cache, int32_t num_blocks,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, float scale, int32_t max_context_len,
+                      int32_t partition_size, const uint32_t* work_items,
+                      int32_t num_work_items, int32_t waves_per_cu, void* stream);
+
+/*
  * Prefix groups.  Parallel samples of one prompt map their prompt blocks to
  * the same physical blocks, and beams share every block up to where they
  * diverged ([B] "The part everyone forgets: pages enable sharing, not just

@@ -108,6 +108,10 @@ _SIGNATURES = {
                             c_int32, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                             c_float, c_int32, c_int32, c_void_p, c_int32, c_int32,
                             c_void_p, c_size_t, c_void_p]),
+    "pa_decode_noalloc": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
+                                    c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,
+                                    c_int32, c_int32, c_float, c_int32, c_int32, c_void_p, c_int32,
+                                    c_int32, c_void_p]),
     "pa_decode_contiguous": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32,
                                        c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
                                        c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p,
@@ -449,6 +453,41 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, bs, float(scale),
         int(max_context_len), int(partition_size), items_ptr, n_items, int(waves_per_cu),
         ws_ptr, ws_bytes, _stream(stream)))
+
+
+PKV_NOALLOC_WORKSPACE_BYTES = 64 << 20     # pagedkv.h
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, partition_size=512, stream=None, work_items=None,
+                      waves_per_cu=0):
+    """``pa_decode`` with the split-context partials in the library's fixed per-GPU
+    array (``PKV_NOALLOC_WORKSPACE_BYTES``) instead of a caller workspace: the call
+    allocates no device memory.  Calls that may overlap on one GPU race on that
+    array; issue them on one stream."""
+    torch = _torch()
+    nb, hkv, bs, d = _pool_geometry(k_cache, v_cache)
+    s, hq, dq = (int(x) for x in q.shape)
+    if dq != d or tuple(out.shape) != (s, hq, d):
+        raise ValueError("q and out must be [S, Hq, head_dim]")
+    if q.dtype == torch.float32:
+        qd = PKV_F32
+    elif q.dtype == torch.float16:
+        qd = PKV_F16
+    else:
+        raise TypeError("q must be float32 or float16")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or tuple(context_lens.shape) != (s,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    items_ptr, n_items = c_void_p(None), 0
+    if work_items is not None:
+        items_ptr, n_items = _items(work_items)
+    _check(lib().pa_decode_noalloc(
+        _dev(out, torch.float32, "out"), _dev(q, q.dtype, "q"), qd,
+        _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"), nb,
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(context_lens, torch.int32, "context_lens"), s, hq, hkv, d, bs, float(scale),
+        int(max_context_len), int(partition_size), items_ptr, n_items, int(waves_per_cu),
+        _stream(stream)))
 
 
 def pa_decode_contiguous(out, q, k_rows, v_rows, context_lens, scale, max_context_len,

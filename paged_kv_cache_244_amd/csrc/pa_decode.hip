@@ -17,6 +17,7 @@
 #include <cfloat>
 #include <cstdint>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "decode_plan.h"
@@ -299,6 +300,79 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, scale, max_context_len, partition_size, work_items,
                      num_work_items, waves_per_cu, workspace, workspace_bytes, stream, 0);
+}
+
+// ---- pa_decode_noalloc: the split-context workspace in a library-owned array ----
+
+namespace {
+
+// Split-context partials for pa_decode_noalloc.  Each GPU the library runs on
+// holds its own copy of this array until the process ends.  In host code the
+// name `scratch` is only a host-side stand-in, never a device address: kernels
+// get the per-device address that hipGetSymbolAddress returns.
+__device__ __align__(256) unsigned char scratch[PKV_NOALLOC_WORKSPACE_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, void*>> g_scratch_addr;   // (device, address of its scratch)
+
+// Device address of the current device's scratch array, looked up once per device
+// with that device current.
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode_noalloc: hipGetDevice: %s",
+                                   hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  for (const auto& c : g_scratch_addr)
+    if (c.first == dev) {
+      *out = c.second;
+      return PKV_OK;
+    }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr)
+    return fail(PKV_ERR_HIP, "pa_decode_noalloc: hipGetSymbolAddress(scratch): %s",
+                hipGetErrorString(e));
+  g_scratch_addr.emplace_back(dev, ptr);
+  *out = ptr;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_decode_noalloc(float* out, const void* q, int32_t q_dtype, const void* k_cache,
+                                 const void* v_cache, int32_t num_blocks,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, float scale, int32_t max_context_len,
+                                 int32_t partition_size, const uint32_t* work_items,
+                                 int32_t num_work_items, int32_t waves_per_cu, void* stream) {
+  // The workspace this launch needs, by the same arithmetic as pa_decode's.
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0)
+    return fail(PKV_ERR_INVALID_ARG, "pa_decode_noalloc: bad sizes");
+  int64_t clamp64 = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  if (clamp64 > max_context_len) clamp64 = max_context_len;
+  const int64_t parts = partition_size == 0
+                            ? 1
+                            : parts_for(static_cast<int32_t>(clamp64), partition_size);
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, parts);
+  if (need > PKV_NOALLOC_WORKSPACE_BYTES)
+    return fail(PKV_ERR_WORKSPACE,
+                "pa_decode_noalloc: this launch needs %zu bytes of split-context workspace, more "
+                "than the library's fixed %zu; use pa_decode with a caller workspace, or a larger "
+                "partition_size", need, static_cast<size_t>(PKV_NOALLOC_WORKSPACE_BYTES));
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_address(&ws);
+    if (rc != PKV_OK) return rc;
+  }
+  return decode_impl(out, q, q_dtype, k_cache, v_cache, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                     head_dim, block_size, scale, max_context_len, partition_size, work_items,
+                     num_work_items, waves_per_cu, ws, need > 0 ? PKV_NOALLOC_WORKSPACE_BYTES : 0,
+                     stream, 0);
 }
 
 extern "C" int pa_decode_grouped(float* out, const void* q, int32_t q_dtype, const void* k_cache,
