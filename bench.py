@@ -58,6 +58,11 @@ def parse_args():
                     help="only measure the HBM read ceiling (pkv_read_probe) and exit")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the read-ceiling measurement that the decode line reports")
+    ap.add_argument("--time-every", type=int, default=5,
+                    help="decode workloads: events time the decode launches of every n-th "
+                         "timed step (each event pair is a pair of barrier packets that "
+                         "costs the GPU several microseconds, so timing every step would "
+                         "slow the steps being measured)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
@@ -206,6 +211,19 @@ def copy_probe():
                       "kernel": "elementwise copy (torch copy_)"}), flush=True)
 
 
+def timing_pairs(n, stream):
+    """n (start, stop) pairs of timing events, each recorded once so that it exists:
+    the library's kernels then record into them (``_lib.time_next_call``)."""
+    import torch
+
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    for a, b in pairs:
+        a.record(stream)
+        b.record(stream)
+    return pairs
+
+
 PROBE_TILE_BYTES = 4096
 
 
@@ -213,8 +231,8 @@ def read_ceiling(dev, nbytes=4 << 30, reps=5):
     """HBM read bandwidth of the library's plain read kernel (pkv_read_probe) over a
     4 GiB buffer (16x the last-level cache), in order and as 4 KiB tiles gathered in
     a seeded random order (the access pattern of a paged pool); the best of a few
-    grid sizes, median of ``reps`` launches each, timed with HIP events on the
-    launch stream."""
+    grid sizes, median of ``reps`` launches each, timed by the kernel's own start
+    and end events (``_lib.time_next_call``) on the launch stream."""
     import torch
 
     from paged_kv_cache_244_amd import _lib
@@ -231,13 +249,10 @@ def read_ceiling(dev, nbytes=4 << 30, reps=5):
         best = None
         for wgs in (1024, 2048, 4096):
             ms = []
-            for _ in range(reps + 1):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+            for e0, e1 in timing_pairs(reps + 1, stream):
+                _lib.time_next_call(e0, e1)
                 _lib._check(_lib.lib().pkv_read_probe(buf.data_ptr(), num_tiles, order_ptr,
                                                       sink.data_ptr(), wgs, stream.cuda_stream))
-                e1.record(stream)
                 e1.synchronize()
                 ms.append(e0.elapsed_time(e1))
             gbs = nbytes / (float(np.median(ms[1:])) / 1e3) / 1e9
@@ -509,18 +524,14 @@ def prefill_bench(args):
     out = torch.empty(qd.shape, dtype=torch.float32, device=dev)
     lens = [int(L) for L in w.lengths]
     stream = cache.stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev = timing_pairs(args.steps, stream)
 
     def step(slot=None):
         seqs = [cache.new_sequence() for _ in lens]
         slots = cache.reserve_many(seqs, lens)
         cache.write(slots, kd, vd)
-        if slot is not None:
-            ev[slot][0].record(stream)
-        cache.prefill(qd, seqs, lens, w.scale, out=out)
-        if slot is not None:
-            ev[slot][1].record(stream)
+        cache.prefill(qd, seqs, lens, w.scale, out=out,
+                      timing=ev[slot] if slot is not None else None)
         for sq in seqs:
             cache.free(sq)
 
@@ -762,8 +773,7 @@ def churn_bench(args):
     inputs = [_to_dev(list(w.step_inputs(t)), dev) for t in range(total_steps)]
     out = torch.empty((w.num_prompts * w.beams, w.num_q_heads, w.head_dim), dtype=torch.float32,
                       device=dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev = timing_pairs(args.steps, cache.stream)
 
     part = "auto" if args.partition == "auto" else int(args.partition)
     # The cancel/fork schedule is the workload's input: drawn before timing, so the
@@ -777,11 +787,7 @@ def churn_bench(args):
         k, v, q = inputs[t]
         layer = t % layers
         _, batch = cache.decode_step(seqs, k_new=k, v_new=v, layer=layer, partition_size=part)
-        if e is not None:
-            e[0].record(cache.stream)
-        cache.attend(q, batch, w.scale, layer=layer, out=out)
-        if e is not None:
-            e[1].record(cache.stream)
+        cache.attend(q, batch, w.scale, layer=layer, out=out, timing=e)
 
     for t in range(args.warmup):
         step(t)
@@ -846,25 +852,29 @@ def prefill_cpu_baseline(w, prompt=1024):
             "seconds": round(dt, 2)}
 
 
-def write_copy_times(marks, ev, sc, w):
-    """Times of the step's other launches from the marks decode_step recorded:
-    the upload of the step buffer fused with the new tokens' write (steps
-    without copies), or on copy-on-write steps the upload, the block copy (every
-    pool replica) and the separate write.  Bytes are algorithmic: a write moves
+def write_copy_times(marks, sc, w):
+    """Kernel times of the step's other launches, from the events decode_step
+    passed to the library: the upload of the step buffer fused with the new
+    tokens' write (steps without copies), or on copy-on-write steps the upload,
+    the block copy (every pool replica) and the separate write.  Bytes are algorithmic: a write moves
     T tokens of K and V in and out; a copy reads and writes whole blocks."""
     tok = 2 * w.num_kv_heads * w.head_dim * 2                     # K+V bytes of one token
     block = tok * w.block_size
     layers = len(sc.cache.k)
     t = sc.num_seqs
     fused, upload, copy, write, pairs = [], [], [], [], []
-    for m, (d0, _) in zip(marks, ev):
+
+    def span(pair):
+        return pair[0].elapsed_time(pair[1])
+
+    for m in marks:
         if m["pairs"]:
-            upload.append(m["upload"].elapsed_time(m["copy0"]))
-            copy.append(m["copy0"].elapsed_time(m["copy1"]))
-            write.append(m["copy1"].elapsed_time(d0))
+            upload.append(span(m["upload"]))
+            copy.append(span(m["copy"]))
+            write.append(span(m["write"]))
             pairs.append(m["pairs"])
         else:
-            fused.append(m["upload"].elapsed_time(d0))
+            fused.append(span(m["upload"]))
 
     def rate(nbytes, ms):
         gbs = nbytes / (ms / 1e3) / 1e9
@@ -970,12 +980,20 @@ def main():
     sc.workspace(partition, int(sc.lengths.max()) + total_steps)
     torch.cuda.synchronize()
 
-    def timing_event():
-        return torch.cuda.Event(enable_timing=True)
-
-    ev = [(timing_event(), timing_event()) for _ in range(args.steps)]
-    marks = [{"upload": timing_event(), "copy0": timing_event(), "copy1": timing_event()}
-             for _ in range(args.steps)] if args.layout == "paged" else [None] * args.steps
+    stream = torch.cuda.current_stream(dev)
+    every = max(1, args.time_every)
+    # Decode: marker events on every `every`-th timed step.  Other launches of the
+    # step (upload and write, copy-on-write copies): the kernels' own start and end
+    # (kernel-level events) on every 2*every-th step, shifted, and on the first step
+    # of a parallel-sampling run, whose copies follow a synchronisation.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          if i % every == 0 else None for i in range(args.steps)]
+    mark_steps = {i for i in range(args.steps) if i % (2 * every) == every // 2 + every}
+    if ps:
+        mark_steps.add(0)
+    marks = [dict(zip(("upload", "copy", "write"), timing_pairs(3, stream)))
+             if args.layout == "paged" and i in mark_steps else None for i in range(args.steps)]
+    torch.cuda.synchronize()
     step_bytes, unique_step_bytes = [], []
     plans = []
 
@@ -994,17 +1012,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    decode_ms = [a.elapsed_time(b) for a, b in ev]
+    timed = [i for i in range(args.steps) if ev[i] is not None]
+    decode_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
     decode_avg_s = float(np.mean(decode_ms)) / 1e3
-    bytes_avg = float(np.mean(step_bytes))
     total_bytes = float(np.sum(step_bytes))
     value = total_bytes / wall / 1e9
-    achieved = bytes_avg / decode_avg_s / 1e9
+    # The roofline: bytes of the steps whose decode was timed over their mean time.
+    achieved = float(np.mean([step_bytes[i] for i in timed])) / decode_avg_s / 1e9
+    bytes_avg = float(np.mean(step_bytes))
     if unique_step_bytes:
         # Shared prompt blocks are read from HBM once; the roofline counts unique bytes.
         sc.extra["unique_kv_bytes_per_step"] = int(np.mean(unique_step_bytes))
-        achieved = float(np.mean(unique_step_bytes)) / decode_avg_s / 1e9
-    writes_copies = (write_copy_times(marks, ev, sc, w) if args.layout == "paged" else None)
+        achieved = float(np.mean([unique_step_bytes[i] for i in timed])) / decode_avg_s / 1e9
+    writes_copies = (write_copy_times([m for m in marks if m is not None], sc, w)
+                     if args.layout == "paged" else None)
 
     # The committed counter summaries describe the paged kernels only.
     traffic = counter_traffic(args.workload) if args.layout == "paged" else None
@@ -1044,6 +1065,7 @@ def main():
             **sc.extra,
         },
         "decode_us": round(decode_avg_s * 1e6, 2),
+        "decode_timed_steps": len(timed),
         "decode_us_median": round(float(np.median(decode_ms)) * 1e3, 2),
         "decode_us_p10_p90": [round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
                               round(float(np.percentile(decode_ms, 90)) * 1e3, 2)],

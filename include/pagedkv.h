@@ -705,6 +705,21 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
                         void* buffer, uint64_t buffer_bytes, kv_step_layout* layout);
 
 /*
+ * pkv_time_next_call — kernel-level timing of the next device call made on
+ * this thread (pa_decode*, pa_prefill, kv_cache_write, kv_copy_blocks,
+ * kv_swap_blocks, pkv_upload*, pkv_read_probe).  That call launches its
+ * kernels through hipExtLaunchKernel: its first kernel records start_event
+ * when it starts, and every kernel records stop_event when it ends, so after
+ * the call completes hipEventElapsedTime(start, stop) is the time from the
+ * first kernel's start to the last kernel's end, without the marker packets
+ * that a hipEventRecord on either side puts into the stream.  Both are
+ * hipEvent_t (as void*) created by the caller with timing enabled, or NULL.
+ * The setting is consumed by the next such call, whether it succeeds or not.
+ * Returns PKV_OK.
+ */
+int pkv_time_next_call(void* start_event, void* stop_event);
+
+/*
  * pkv_read_probe — the HBM read ceiling that decode is measured against.
  * [B] "Why the KV cache is the thing that limits your batch": decode reads
  * every cached key and value once per step and does little arithmetic per

@@ -98,6 +98,7 @@ _SIGNATURES = {
     "kv_swap_blocks": (c_int32, [POINTER(c_void_p), POINTER(c_void_p), c_int32, POINTER(c_void_p),
                                  POINTER(c_void_p), c_int32, c_int32, c_void_p, c_int32, c_int32,
                                  c_int32, c_int32, c_void_p]),
+    "pkv_time_next_call": (c_int32, [c_void_p, c_void_p]),
     "pkv_read_probe": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_void_p]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode_set_kernel_policy": (c_int32, [c_int32]),
@@ -410,6 +411,15 @@ def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scal
         _dev(groups, torch.int32, "groups"), int(groups.shape[0]), g_ptr, n_g,
         _dev(shared_lens, torch.int32, "shared_lens") if shared_lens is not None else None,
         int(fuse), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def time_next_call(start=None, stop=None):
+    """Kernel-level timing of the next library device call on this thread: pass two
+    torch.cuda.Event(enable_timing=True) that have been recorded once (so that they
+    exist); afterwards start.elapsed_time(stop) spans its first kernel's start to its
+    last kernel's end.  None clears."""
+    lib().pkv_time_next_call(None if start is None else c_void_p(start.cuda_event),
+                             None if stop is None else c_void_p(stop.cuda_event))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):

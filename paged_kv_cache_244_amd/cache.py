@@ -41,6 +41,47 @@ class _Stamp:
         return self.staging.gen[self.slot] == self.gen
 
 
+class _RingMarks:
+    """Bookkeeping of a staging ring of ``depth`` slots (no device work).
+
+    Upload u uses slot u % depth.  A completion mark (an event) follows every
+    ``mark_every``-th upload only, since each is a barrier packet that costs the
+    GPU a few microseconds between kernels.  Slot i, last read by upload u, may
+    be written again once the first mark at or after u has completed; that mark
+    exists because it comes at most mark_every - 1 uploads after u, before the
+    slot's next use."""
+
+    def __init__(self, depth, mark_every):
+        if not 0 < mark_every < depth:
+            raise ValueError("need 0 < mark_every < depth")
+        self.depth, self.mark_every = depth, mark_every
+        self.count = 0                      # uploads issued so far
+        self.marks = []                     # (upload index, handle), oldest first
+        self.last_use = [-1] * depth        # upload that last read each slot, or -1
+
+    def next_slot(self):
+        """(slot of the next upload, handle of the mark to wait for first, or None)."""
+        i = self.count % self.depth
+        used = self.last_use[i]
+        if used < 0:
+            return i, None
+        while self.marks and self.marks[0][0] < used:
+            self.marks.pop(0)
+        return i, self.marks[0][1]
+
+    def issued(self, slot, read, make_mark):
+        """Account for the upload just issued in ``slot`` (``read``: it launched a
+        copy that reads the slot); ``make_mark()`` records and returns a mark when
+        one is due.  Returns the upload's index."""
+        u = self.count
+        self.count += 1
+        if read:
+            self.last_use[slot] = u
+        if u % self.mark_every == self.mark_every - 1:
+            self.marks.append((u, make_mark()))
+        return u
+
+
 class _Staging:
     """Uploads several small host arrays with ONE host-to-device copy.
 
@@ -51,23 +92,22 @@ class _Staging:
     ``depth`` uploads later.  So the views of one upload (say a decode step's
     tables) stay valid while up to ``depth - 1`` other uploads (a prefill, a swap)
     run in between; each upload's stamp (``last_stamp``) tells whether they still are.
+    Completion marks follow every ``mark_every``-th upload only (``_RingMarks``).
     """
 
-    def __init__(self, device, depth: int = 4, nbytes: int = 1 << 20):
+    def __init__(self, device, depth: int = 8, nbytes: int = 1 << 20, mark_every: int = 4):
         self.device = device
+        self.ring = _RingMarks(depth, mark_every)
         self.host = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(depth)]
-        self.events = [None] * depth
-        self.next = 0
         self.dev = [torch.empty(nbytes, dtype=torch.uint8, device=device) for _ in range(depth)]
         self.gen = [0] * depth
         self.last_stamp = None
 
     def _slot(self, nbytes):
         """Next ring slot, once the copy that last read its pinned buffer is done."""
-        i = self.next
-        self.next = (i + 1) % len(self.host)
-        if self.events[i] is not None:
-            self.events[i].synchronize()
+        i, wait = self.ring.next_slot()
+        if wait is not None:
+            wait.synchronize()
         if self.host[i].numel() < nbytes:
             self.host[i] = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
         return i
@@ -76,7 +116,7 @@ class _Staging:
         """Copy ``total`` bytes of ring slot i's pinned buffer to its device buffer.
         ``write`` (a callable taking the device buffer's address and the pinned slot)
         replaces the plain copy with one launch that also writes the step's new tokens.
-        ``mark``, an event, is recorded on the stream just before the launch."""
+        ``mark``, a (start, stop) pair of events, takes the launch's kernel times."""
         if self.dev[i].numel() < total:
             self.dev[i] = torch.empty(total, dtype=torch.uint8, device=self.device)
         self.gen[i] += 1
@@ -87,15 +127,19 @@ class _Staging:
             # hand-off between the step's kernels.
             nbytes = (total + 15) // 16 * 16
             if mark is not None:
-                mark.record(stream)
+                _lib.time_next_call(*mark)
             if write is None:
                 _lib._check(_lib.lib().pkv_upload(dev.data_ptr(), self.host[i].data_ptr(),
                                                   nbytes, stream.cuda_stream))
             else:
                 write(dev.data_ptr(), self.host[i].data_ptr(), nbytes)
+
+        def mark():
             ev = torch.cuda.Event()
             ev.record(stream)
-            self.events[i] = ev
+            return ev
+
+        self.ring.issued(i, total > 0, mark)
         return dev
 
     def upload(self, arrays, stream):
@@ -351,14 +395,16 @@ class PagedKVCache:
 
         The slots and the batch's device arrays sit in one slot of the cache's
         staging ring, which later uploads (steps, batches, prefills, swaps,
-        reserves) reuse only after the ring's other slots: up to 3 of them may run
+        reserves) reuse only after the ring's other slots: up to 7 of them may run
         between this call and ``attend``; after more, ``attend`` and ``write``
         raise instead of reading another call's bytes.
 
-        ``marks`` (for timing) is a dict of events created with timing enabled:
-        "upload" is recorded just before the upload launch and, on a step with
-        copy-on-write copies, "copy0" / "copy1" just before and after them;
-        ``marks["pairs"]`` is set to the number of copied blocks."""
+        ``marks`` (for timing) is a dict of (start, stop) pairs of timing events
+        that exist (recorded once): "upload" takes the kernel times of the upload
+        (fused with the write on steps without copies), and on steps with
+        copy-on-write copies "copy" and "write" those of the copy and the write
+        (``_lib.time_next_call``); ``marks["pairs"]`` is set to the number of
+        copied blocks."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
         if self._pending:
             self.retire()
@@ -404,15 +450,15 @@ class PagedKVCache:
             marks["pairs"] = int(lay.num_pairs)
         if lay.num_pairs:
             if marks is not None:
-                marks["copy0"].record(self.stream)
+                _lib.time_next_call(*marks["copy"])
             _lib.kv_copy_blocks(self.k, self.v, DeviceArray(dev, lay.pairs_offset, torch.int32,
                                                             (lay.num_pairs, 2)).tensor(),
                                 stream=self.stream)
-            if marks is not None:
-                marks["copy1"].record(self.stream)
         plan = {name: int(getattr(lay.plan, name)) for name, _ in _lib.DecodePlan._fields_}
         slots = DeviceArray(dev, lay.slots_offset, torch.int64, (n,), self._staging.last_stamp)
         if k_new is not None and lay.num_pairs:
+            if marks is not None:
+                _lib.time_next_call(*marks["write"])
             self.write(slots, k_new, v_new, layer=layer)
         batch = DecodeBatch(DeviceArray(dev, lay.tables_offset, torch.int32, (n, lay.max_blocks)),
                             DeviceArray(dev, lay.lens_offset, torch.int32, (n,)),
@@ -470,7 +516,7 @@ class PagedKVCache:
         (with prefix groups where they pay, as ``decode_step`` plans them).
 
         The returned device arrays live in one slot of the cache's staging ring: they
-        stay valid while fewer than 4 later uploads have been made (``attend``
+        stay valid while fewer than 8 later uploads have been made (``attend``
         refuses a batch whose slot was reused).
         """
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
@@ -506,11 +552,12 @@ class PagedKVCache:
             self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._workspace
 
-    def prefill(self, q, seqs, q_lens, scale, layer=0, out=None):
+    def prefill(self, q, seqs, q_lens, scale, layer=0, out=None, timing=None):
         """Causal attention of new tokens (``pa_prefill``): ``q`` [T, Hq, D] fp16 holds
         the last ``q_lens[i]`` tokens of each ``seqs[i]`` in order, whose K/V are
         already written.  Tables, lengths, query offsets and the work list go up in
-        one upload.  Returns out [T, Hq, D] fp32."""
+        one upload.  Returns out [T, Hq, D] fp32.  ``timing``, a (start, stop) pair of
+        existing timing events, takes the prefill kernel's start and end."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
         tables, lens, _ = self._tables(seqs, None, None)
         starts = _prefill_starts(q_lens)
@@ -518,16 +565,21 @@ class PagedKVCache:
         t_d, l_d, s_d, i_d = self.upload(tables, lens, starts, items.view(np.int32))
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        if timing is not None:
+            _lib.time_next_call(*timing)
         _lib.pa_prefill(out, q, s_d, self.k[layer], self.v[layer], t_d, l_d, scale, i_d,
                         stream=self.stream)
         return out
 
-    def attend(self, q, batch: "DecodeBatch", scale, partition_size=None, layer=0, out=None):
+    def attend(self, q, batch: "DecodeBatch", scale, partition_size=None, layer=0, out=None,
+               timing=None):
         """Decode attention for ``batch`` with the schedule planned for it.
 
         ``partition_size`` None keeps the batch's plan; "auto" or a number plans
         again (the library's policy, or that split), as does a query shape or dtype
-        other than the one the batch was planned for.
+        other than the one the batch was planned for.  ``timing``, a (start, stop)
+        pair of existing timing events, takes the decode kernels' start and end
+        (``_lib.time_next_call``).
         """
         s, hq, d = q.shape
         if batch.stamp is not None and not batch.stamp.current():
@@ -555,6 +607,8 @@ class PagedKVCache:
         grouped = key == batch.plan_key and batch.group_items_dev is not None
         # a grouped launch keeps one spare partial slot per request
         ws = self.workspace(s, hq, batch.max_len + (part if grouped else 0), part)
+        if timing is not None:
+            _lib.time_next_call(*timing)
         if grouped:
             g, gi = batch.groups_dev, batch.group_items_dev
             _lib._check(_lib.lib().pa_decode_grouped(

@@ -6,6 +6,7 @@
 
 namespace {
 thread_local char g_last_error[512] = "";
+thread_local pkv::CallTiming g_call_timing;
 }
 
 namespace pkv {
@@ -18,6 +19,13 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+CallTiming& call_timing() { return g_call_timing; }
+
 }  // namespace pkv
 
 extern "C" const char* pkv_last_error(void) { return g_last_error; }
+
+extern "C" int pkv_time_next_call(void* start_event, void* stop_event) {
+  pkv::call_timing() = pkv::CallTiming{start_event, stop_event};
+  return PKV_OK;
+}

@@ -28,6 +28,7 @@
 #include <cstdint>
 
 #include "errors.h"
+#include "launch.h"
 #include "pagedkv.h"
 
 namespace {
@@ -215,7 +216,7 @@ int launch_block_copy(const void* const* src_k, const void* const* src_v, void* 
       pools.dst_k[l] = static_cast<uint4*>(dk);
       pools.dst_v[l] = static_cast<uint4*>(dv);
     }
-    hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3(gx, num_pairs, 2 * n), dim3(kThreads), 0,
+    pkv::launch_kernel(kv_copy_blocks_kernel, dim3(gx, num_pairs, 2 * n), dim3(kThreads), 0,
                        stream, pools, block_pairs, src_blocks, dst_blocks, chunks_per_block);
     if (int rc = hip_status(what)) return rc;
   }
@@ -228,6 +229,7 @@ extern "C" int kv_cache_write(void* k_cache, void* v_cache, int32_t num_blocks, 
                               const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0)
     return fail(PKV_ERR_INVALID_ARG, "kv_cache_write: bad sizes (tokens %d, blocks %d, heads %d)",
                 num_tokens, num_blocks, num_kv_heads);
@@ -242,7 +244,7 @@ extern "C" int kv_cache_write(void* k_cache, void* v_cache, int32_t num_blocks, 
   const int64_t total = static_cast<int64_t>(num_tokens) * chunks_per_token;
   const int64_t want_blocks = (total + kThreads - 1) / kThreads;
   const unsigned grid = static_cast<unsigned>(want_blocks < 65536 * 16 ? want_blocks : 65536 * 16);
-  hipLaunchKernelGGL(kv_cache_write_kernel, dim3(grid), dim3(kThreads), 0,
+  pkv::launch_kernel(kv_cache_write_kernel, dim3(grid), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
                      static_cast<uint4*>(v_cache), static_cast<const uint4*>(k_new),
                      static_cast<const uint4*>(v_new), slot_mapping, total, chunks_per_token,
@@ -254,6 +256,7 @@ extern "C" int kv_copy_blocks(void* const* k_caches, void* const* v_caches, int3
                               const int32_t* block_pairs, int32_t num_pairs, int32_t num_blocks,
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   if (num_layers < 0 || num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0)
     return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: bad sizes");
   if (!supported_geometry(head_dim, block_size))
@@ -276,6 +279,7 @@ extern "C" int kv_swap_blocks(void* const* dst_k, void* const* dst_v, int32_t ds
                               int32_t num_layers, const int32_t* block_pairs, int32_t num_pairs,
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   if (num_layers < 0 || num_pairs < 0 || dst_num_blocks <= 0 || src_num_blocks <= 0 ||
       num_kv_heads <= 0)
     return fail(PKV_ERR_INVALID_ARG, "kv_swap_blocks: bad sizes");
@@ -296,6 +300,7 @@ extern "C" int kv_swap_blocks(void* const* dst_k, void* const* dst_v, int32_t ds
 }
 
 extern "C" int pkv_upload(void* dst, const void* src, uint64_t bytes, void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   if (bytes == 0) return PKV_OK;
   if (!dst || !src) return fail(PKV_ERR_INVALID_ARG, "pkv_upload: NULL pointer");
   if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0 ||
@@ -315,7 +320,7 @@ extern "C" int pkv_upload(void* dst, const void* src, uint64_t bytes, void* stre
   const int64_t n16 = static_cast<int64_t>(bytes / 16);
   int64_t blocks = (n16 + kThreads - 1) / kThreads;
   if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(upload_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+  pkv::launch_kernel(upload_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
                      reinterpret_cast<const uint4*>(dev_src), n16);
   return hip_status("pkv_upload launch");
@@ -326,6 +331,7 @@ extern "C" int pkv_upload_write(void* dst, const void* src, uint64_t bytes, void
                                 const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                 void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0)
     return fail(PKV_ERR_INVALID_ARG, "pkv_upload_write: bad sizes (tokens %d, blocks %d, heads %d)",
                 num_tokens, num_blocks, num_kv_heads);
@@ -366,7 +372,7 @@ extern "C" int pkv_upload_write(void* dst, const void* src, uint64_t bytes, void
   const int64_t total = static_cast<int64_t>(num_tokens) * chunks_per_token;
   int64_t wr = (total + kThreads - 1) / kThreads;
   if (wr > 65536 * 16) wr = 65536 * 16;
-  hipLaunchKernelGGL(upload_write_kernel, dim3(static_cast<unsigned>(up + wr)), dim3(kThreads), 0,
+  pkv::launch_kernel(upload_write_kernel, dim3(static_cast<unsigned>(up + wr)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
                      reinterpret_cast<const uint4*>(dev_src), n16, static_cast<int32_t>(up),
                      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),

@@ -225,7 +225,7 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     if (wgs > INT32_MAX)
       return fail(PKV_ERR_INVALID_ARG, "pa_decode_grouped: %lld workgroups in one launch",
                   static_cast<long long>(wgs));
-    hipLaunchKernelGGL(fused, dim3(static_cast<unsigned>(wgs)), dim3(kWave), 0, st, gp, prm,
+    pkv::launch_kernel(fused, dim3(static_cast<unsigned>(wgs)), dim3(kWave), 0, st, gp, prm,
                        static_cast<int>(group_wgs));
     e = hipGetLastError();
     if (e != hipSuccess)
@@ -250,7 +250,7 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     const int ny = num_group_items < kMaxGridY ? num_group_items : kMaxGridY;
     const dim3 ggrid(static_cast<unsigned>(num_kv_heads), static_cast<unsigned>(ny),
                      static_cast<unsigned>((num_group_items + ny - 1) / ny));
-    hipLaunchKernelGGL(group_fn, ggrid, dim3(kWave), glds, st, gp);
+    pkv::launch_kernel(group_fn, ggrid, dim3(kWave), glds, st, gp);
     e = hipGetLastError();
     if (e != hipSuccess)
       return fail(PKV_ERR_HIP, "pa_decode_grouped launch: %s", hipGetErrorString(e));
@@ -275,7 +275,7 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
     grid.z = static_cast<unsigned>((num_work_items + ny - 1) / ny);
   }
   if (regular) {
-    hipLaunchKernelGGL(fn, grid, dim3(kWave), dyn_lds, st, prm);
+    pkv::launch_kernel(fn, grid, dim3(kWave), dyn_lds, st, prm);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_decode launch: %s", hipGetErrorString(e));
   }
@@ -296,6 +296,7 @@ extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void*
                          int32_t max_context_len, int32_t partition_size,
                          const uint32_t* work_items, int32_t num_work_items, int32_t waves_per_cu,
                          void* workspace, size_t workspace_bytes, void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   return decode_impl(out, q, q_dtype, k_cache, v_cache, num_blocks, block_tables,
                      max_blocks_per_seq, context_lens, num_seqs, num_q_heads, num_kv_heads,
                      head_dim, block_size, scale, max_context_len, partition_size, work_items,
@@ -348,6 +349,7 @@ extern "C" int pa_decode_noalloc(float* out, const void* q, int32_t q_dtype, con
                                  int32_t block_size, float scale, int32_t max_context_len,
                                  int32_t partition_size, const uint32_t* work_items,
                                  int32_t num_work_items, int32_t waves_per_cu, void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   // The workspace this launch needs, by the same arithmetic as pa_decode's.
   if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0)
@@ -387,6 +389,7 @@ extern "C" int pa_decode_grouped(float* out, const void* q, int32_t q_dtype, con
                                  const uint32_t* group_items, int32_t num_group_items,
                                  const int32_t* shared_lens, int32_t fuse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   if (num_groups < 0 || num_group_items < 0)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode_grouped: negative group sizes");
   return decode_impl(out, q, q_dtype, k_cache, v_cache, num_blocks, block_tables,
@@ -404,6 +407,7 @@ extern "C" int pa_decode_contiguous(float* out, const void* q, int32_t q_dtype,
                                     const uint32_t* work_items, int32_t num_work_items,
                                     int32_t waves_per_cu, void* workspace, size_t workspace_bytes,
                                     void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   constexpr int32_t kTile = 16;
   if (row_tokens <= 0 || row_tokens % kTile != 0)
     return fail(PKV_ERR_INVALID_ARG, "pa_decode_contiguous: row_tokens %d not a positive multiple of 16",

@@ -6,6 +6,7 @@
 #include <cfloat>
 #include <cstdint>
 
+#include "launch.h"
 #include "pa_decode_common.h"
 
 namespace pkv_decode {
@@ -101,9 +102,9 @@ __global__ __launch_bounds__(D) void pa_decode_reduce_kernel(DecodeParams p) {
 hipError_t launch_reduce(const DecodeParams& prm, int head_dim, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(prm.num_q_heads), static_cast<unsigned>(prm.num_seqs));
   if (head_dim == 64)
-    hipLaunchKernelGGL(pa_decode_reduce_kernel<64>, grid, dim3(64), 0, stream, prm);
+    pkv::launch_kernel(pa_decode_reduce_kernel<64>, grid, dim3(64), 0, stream, prm);
   else
-    hipLaunchKernelGGL(pa_decode_reduce_kernel<128>, grid, dim3(128), 0, stream, prm);
+    pkv::launch_kernel(pa_decode_reduce_kernel<128>, grid, dim3(128), 0, stream, prm);
   return hipGetLastError();
 }
 

@@ -469,6 +469,7 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_starts, in
                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
                           const uint32_t* work_items, int32_t num_work_items, void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   if (num_seqs < 0 || num_seqs > 65535 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq <= 0 || num_work_items < 0)
     return fail(PKV_ERR_INVALID_ARG, "pa_prefill: bad sizes");
@@ -514,7 +515,7 @@ extern "C" int pa_prefill(float* out, const void* q, const int32_t* q_starts, in
   const int ny = num_work_items < kMaxGridY ? num_work_items : kMaxGridY;
   const dim3 grid(static_cast<unsigned>(num_q_heads / ht), static_cast<unsigned>(ny),
                   static_cast<unsigned>((num_work_items + ny - 1) / ny));
-  hipLaunchKernelGGL(fn, grid, dim3(kWave * kPrefillWaves), dyn, static_cast<hipStream_t>(stream),
+  pkv::launch_kernel(fn, grid, dim3(kWave * kPrefillWaves), dyn, static_cast<hipStream_t>(stream),
                      prm);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "pa_prefill launch: %s", hipGetErrorString(e));

@@ -17,6 +17,7 @@
 #include <cstdint>
 
 #include "errors.h"
+#include "launch.h"
 #include "pagedkv.h"
 
 namespace {
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const uint4* 
 
 extern "C" int pkv_read_probe(const void* src, int64_t num_tiles, const int32_t* tile_order,
                               uint32_t* sink, int32_t workgroups, void* stream) {
+  pkv::TimedCall timed;   // consumes the events of pkv_time_next_call
   if (num_tiles < 0 || workgroups <= 0)
     return fail(PKV_ERR_INVALID_ARG, "pkv_read_probe: num_tiles %lld, workgroups %d",
                 static_cast<long long>(num_tiles), workgroups);
@@ -65,7 +67,7 @@ extern "C" int pkv_read_probe(const void* src, int64_t num_tiles, const int32_t*
   if (!src || !sink) return fail(PKV_ERR_INVALID_ARG, "pkv_read_probe: NULL pointer");
   if (reinterpret_cast<uintptr_t>(src) % 16 != 0)
     return fail(PKV_ERR_INVALID_ARG, "pkv_read_probe: src must be 16-byte aligned");
-  hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(workgroups)),
+  pkv::launch_kernel(read_probe_kernel, dim3(static_cast<unsigned>(workgroups)),
                      dim3(kProbeThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint4*>(src), tile_order, num_tiles, sink);
   const hipError_t e = hipGetLastError();

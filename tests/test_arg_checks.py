@@ -1,4 +1,4 @@
-"""kv_swap_blocks and pkv_upload_write argument checks that need no GPU.
+"""kv_swap_blocks, pkv_upload_write and pkv_read_probe argument checks that need no GPU.
 
 Every call here is refused (or is a no-op) before the library touches the HIP
 runtime: bad sizes, geometry that is not built, nothing to copy, NULL pools and
@@ -61,3 +61,15 @@ def test_upload_write_arguments_checked_before_any_launch():
     assert call(bytes_=32, dst=8, src=16) == _lib.PKV_ERR_INVALID_ARG           # alignment
     assert call(bytes_=32) == _lib.PKV_ERR_INVALID_ARG                          # NULL buffers
     assert call(ntok=4) == _lib.PKV_ERR_INVALID_ARG                             # NULL pools
+
+
+def test_read_probe_arguments_checked_on_the_host():
+    lib = _lib.lib()
+    assert lib.pkv_read_probe(None, -1, None, None, 64, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_read_probe(None, 4, None, None, 0, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_read_probe(None, 4, None, None, 64, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_read_probe(8, 4, None, None, 64, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_read_probe(24, 4, None, 16, 64, None) == _lib.PKV_ERR_INVALID_ARG  # misaligned
+    assert b"aligned" in lib.pkv_last_error()
+    assert lib.pkv_read_probe(None, 0, None, None, 64, None) == _lib.PKV_OK           # nothing
+

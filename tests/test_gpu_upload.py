@@ -226,7 +226,7 @@ def test_decode_batch_survives_other_uploads_and_refuses_stale():
                      for i in range(len(lens))])
     paths.assert_attention_close(out, want, label="decode after prefill and swap uploads")
 
-    for _ in range(4):                     # wrap the staging ring
+    for _ in range(len(c._staging.dev)):   # wrap the staging ring
         c.upload(np.zeros(4, dtype=np.int32))
     with pytest.raises(RuntimeError, match="stale"):
         c.attend(q_dev, batch, scale)
