@@ -8,9 +8,11 @@ attention runs over every request's context through its block table.  Inputs
 
 Prints one JSON line.  ``value`` is algorithmic KV bytes read by decode
 attention per step (logical tokens only: sum(L) * 2 * Hkv * D * 2 B) divided
-by the wall time per step; ``roofline`` is the same byte count per pa_decode
-launch divided by that launch's time measured with HIP events on the launch
-stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample of requests.
+by the wall time per step; ``roofline`` is the same byte count per decode
+divided by the decode launches' duration: kernel-level HIP events (the first
+kernel's start to the last kernel's end, recorded by the launches themselves on
+the launch stream) on every 5th timed step.  ``cpu_baseline`` times the CPU
+oracle on a bounded sample of requests.
 
     python bench.py [--steps K] [--warmup W] [--workload opt13b|gqa|long_context]
 
@@ -50,6 +52,10 @@ def parse_args():
                              "swap", "beams"])
     ap.add_argument("--partition", default="auto",
                     help="tokens per split-context partition, 0 = one pass, or 'auto'")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="decode workloads: store the same requests and values in blocks of this "
+                         "many tokens (8, 16, 32, 64 or 128; 0 = the workload's own, 16); the "
+                         "long-context workload is stated as a sweep over all five")
     ap.add_argument("--kernel-policy", default="default", choices=["default", "valu"],
                     help="head-group kernel: MFMA (default for fp16 groups of >= 4) or VALU")
     ap.add_argument("--copy-probe", action="store_true",
@@ -59,10 +65,10 @@ def parse_args():
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the read-ceiling measurement that the decode line reports")
     ap.add_argument("--time-every", type=int, default=5,
-                    help="decode workloads: events time the decode launches of every n-th "
-                         "timed step (each event pair is a pair of barrier packets that "
-                         "costs the GPU several microseconds, so timing every step would "
-                         "slow the steps being measured)")
+                    help="decode workloads: the decode launches of every n-th timed step take "
+                         "kernel-level timing events (first kernel's start to last kernel's "
+                         "end); timed launches cost the GPU several microseconds more, so "
+                         "timing every step would slow the steps being measured")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="rough budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--layout", default="paged", choices=["paged", "contiguous"],
@@ -211,17 +217,45 @@ def copy_probe():
                       "kernel": "elementwise copy (torch copy_)"}), flush=True)
 
 
-def timing_pairs(n, stream):
-    """n (start, stop) pairs of timing events, each recorded once so that it exists:
-    the library's kernels then record into them (``_lib.time_next_call``)."""
-    import torch
+def kernel_timers(n):
+    """n library-made event pairs for kernel-level timing (``_lib.time_next_call``)."""
+    from paged_kv_cache_244_amd import _lib
+    return [_lib.KernelTimer() for _ in range(n)]
 
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(n)]
-    for a, b in pairs:
-        a.record(stream)
-        b.record(stream)
-    return pairs
+
+class TimingRing:
+    """Timing events in a small ring.  The HIP runtime slowed the steps of a run
+    measurably (1.27 -> 1.9-2.6 ms per prefill step on MI355X) once 60-100 events
+    were alive in the process, whether recorded or not, so a run keeps ``size``
+    event sets and reads each one's result just before reusing it (by then its
+    step finished long ago).  ``take(key)`` returns the set to use for ``key``;
+    ``results()`` returns {key: read(set)} for every key taken."""
+
+    def __init__(self, size, make, read):
+        self.slots = [[None, make()] for _ in range(size)]
+        self.n, self.read, self.out = 0, read, {}
+
+    def take(self, key):
+        slot = self.slots[self.n % len(self.slots)]
+        self.n += 1
+        if slot[0] is not None:
+            self.out[slot[0]] = self.read(slot[1])
+        slot[0] = key
+        return slot[1]
+
+    def results(self):
+        for slot in self.slots:
+            if slot[0] is not None:
+                self.out[slot[0]] = self.read(slot[1])
+                slot[0] = None
+        return self.out
+
+
+def timer_ring(size=8):
+    """Library-made events taking a call's kernel start and end."""
+    from paged_kv_cache_244_amd import _lib
+
+    return TimingRing(size, _lib.KernelTimer, lambda t: t.ms())
 
 
 PROBE_TILE_BYTES = 4096
@@ -249,12 +283,11 @@ def read_ceiling(dev, nbytes=4 << 30, reps=5):
         best = None
         for wgs in (1024, 2048, 4096):
             ms = []
-            for e0, e1 in timing_pairs(reps + 1, stream):
-                _lib.time_next_call(e0, e1)
+            for t in kernel_timers(reps + 1):
+                _lib.time_next_call(t)
                 _lib._check(_lib.lib().pkv_read_probe(buf.data_ptr(), num_tiles, order_ptr,
                                                       sink.data_ptr(), wgs, stream.cuda_stream))
-                e1.synchronize()
-                ms.append(e0.elapsed_time(e1))
+                ms.append(t.ms())
             gbs = nbytes / (float(np.median(ms[1:])) / 1e3) / 1e9
             if best is None or gbs > best[0]:
                 best = (gbs, wgs, float(np.median(ms[1:])))
@@ -303,7 +336,7 @@ class Scenario:
     def workspace(self, part, max_len):
         return self.cache.workspace(self.num_seqs, self.w.num_q_heads, max_len, part)
 
-    def step(self, t, partition, ev_pair, plans, marks=None):
+    def step(self, t, partition, timer, plans, marks=None):
         cache = self.cache
         layer = t % len(cache.k)            # the pool replica this step writes and reads
         # reserve, tables, plan and the new tokens' write: one host call, one launch
@@ -314,11 +347,8 @@ class Scenario:
         plans.append(dict(batch.plan,
                           num_groups=batch.groups_dev.shape[0] if grouped else 0,
                           num_group_items=batch.group_items_dev.shape[0] if grouped else 0))
-        if ev_pair is not None:
-            ev_pair[0].record(cache.stream)
-        cache.attend(self.step_q[t], batch, self.w.scale, layer=layer, out=self.out)
-        if ev_pair is not None:
-            ev_pair[1].record(cache.stream)
+        cache.attend(self.step_q[t], batch, self.w.scale, layer=layer, out=self.out,
+                     timing=timer)
 
 
 def _to_dev(arrays, dev):
@@ -467,7 +497,7 @@ class ContiguousScenario:
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.out.device)
         return self.ws if need else None
 
-    def step(self, t, partition, ev_pair, plans, marks=None):
+    def step(self, t, partition, timer, plans, marks=None):
         _lib = _lib_mod()
         w, r = self.w, t % len(self.k)
         pos = self.lens.copy()
@@ -482,14 +512,12 @@ class ContiguousScenario:
         self.v[r][self.arange, :, pos_d, :] = self.step_v[t]
         max_len = int(self.lens.max())
         ws = self.workspace(plan["partition_size"], max_len)
-        if ev_pair is not None:
-            ev_pair[0].record(self.stream)
+        if timer is not None:
+            _lib.time_next_call(timer)
         _lib.pa_decode_contiguous(self.out, self.step_q[t], self.k[r], self.v[r], lens_d, w.scale,
                                   max_len, partition_size=plan["partition_size"], workspace=ws,
                                   stream=self.stream, work_items=items_d,
                                   waves_per_cu=plan["waves_per_cu"])
-        if ev_pair is not None:
-            ev_pair[1].record(self.stream)
 
 
 def _lib_mod():
@@ -524,14 +552,14 @@ def prefill_bench(args):
     out = torch.empty(qd.shape, dtype=torch.float32, device=dev)
     lens = [int(L) for L in w.lengths]
     stream = cache.stream
-    ev = timing_pairs(args.steps, stream)
+    ring = timer_ring()
 
     def step(slot=None):
         seqs = [cache.new_sequence() for _ in lens]
         slots = cache.reserve_many(seqs, lens)
         cache.write(slots, kd, vd)
         cache.prefill(qd, seqs, lens, w.scale, out=out,
-                      timing=ev[slot] if slot is not None else None)
+                      timing=ring.take(slot) if slot is not None else None)
         for sq in seqs:
             cache.free(sq)
 
@@ -543,7 +571,7 @@ def prefill_bench(args):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [a.elapsed_time(b) for a, b in ev]
+    ms = list(ring.results().values())
     flops = float(w.flops())
     achieved = flops / (float(np.mean(ms)) / 1e3) / 1e12
     baseline = None
@@ -605,10 +633,14 @@ def swap_bench(args):
     seqs = [cache.new_sequence() for _ in lens]
     cache.write(cache.reserve_many(seqs, lens), kd, vd)
     moved = [seqs[i] for i in moved_idx]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    def read(e):
+        e[3].synchronize()
+        return e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3])
+
+    ring = TimingRing(4, lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)], read)
 
     def step(slot=None):
-        e = ev[slot] if slot is not None else None
+        e = ring.take(slot) if slot is not None else None
         n_out = cache.swap_out(moved, events=None if e is None else (e[0], e[1]))
         n_in = cache.swap_in(moved, events=None if e is None else (e[2], e[3]))
         assert n_out == n_in == moved_blocks
@@ -621,8 +653,9 @@ def swap_bench(args):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    out_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    in_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    times = list(ring.results().values())
+    out_ms = [t[0] for t in times]
+    in_ms = [t[1] for t in times]
     nbytes = moved_blocks * block_bytes
     gbs = lambda ms: nbytes / (ms / 1e3) / 1e9  # noqa: E731
     achieved = gbs(float(np.mean(out_ms + in_ms)))
@@ -773,7 +806,7 @@ def churn_bench(args):
     inputs = [_to_dev(list(w.step_inputs(t)), dev) for t in range(total_steps)]
     out = torch.empty((w.num_prompts * w.beams, w.num_q_heads, w.head_dim), dtype=torch.float32,
                       device=dev)
-    ev = timing_pairs(args.steps, cache.stream)
+    ring = timer_ring()
 
     part = "auto" if args.partition == "auto" else int(args.partition)
     # The cancel/fork schedule is the workload's input: drawn before timing, so the
@@ -794,10 +827,10 @@ def churn_bench(args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, ev[i])
+        step(args.warmup + i, ring.take(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = [a.elapsed_time(b) for a, b in ev]
+    ms = list(ring.results().values())
     timed = slice(args.warmup, total_steps)
     uniq = float(np.mean(unique[timed])) * tok_bytes
     logi = float(np.mean(logical[timed])) * tok_bytes
@@ -863,18 +896,14 @@ def write_copy_times(marks, sc, w):
     layers = len(sc.cache.k)
     t = sc.num_seqs
     fused, upload, copy, write, pairs = [], [], [], [], []
-
-    def span(pair):
-        return pair[0].elapsed_time(pair[1])
-
-    for m in marks:
-        if m["pairs"]:
-            upload.append(span(m["upload"]))
-            copy.append(span(m["copy"]))
-            write.append(span(m["write"]))
-            pairs.append(m["pairs"])
+    for m in marks:                      # (pairs, upload ms[, copy ms, write ms]) per step
+        if m[0]:
+            pairs.append(m[0])
+            upload.append(m[1])
+            copy.append(m[2])
+            write.append(m[3])
         else:
-            fused.append(span(m["upload"]))
+            fused.append(m[1])
 
     def rate(nbytes, ms):
         gbs = nbytes / (ms / 1e3) / 1e9
@@ -961,6 +990,8 @@ def main():
         first_step = args.warmup
         w = {"long_context": lambda: workloads.long_context(16),
              "tiny": workloads.tiny}.get(args.workload, workloads.WORKLOADS.get(args.workload))()
+        if args.block_size and args.block_size != w.block_size:
+            w = workloads.with_block_size(w, args.block_size)
         sc = decode_scenario(w, args.warmup + args.steps, dev, args.replicas)
         if args.layout == "contiguous":
             base = sc
@@ -969,6 +1000,8 @@ def main():
             torch.cuda.empty_cache()
     if args.layout == "contiguous" and ps:
         raise SystemExit("the contiguous layout is measured on the decode workloads only")
+    if ps and args.block_size and args.block_size != 16:
+        raise SystemExit("--block-size applies to the decode workloads, not parallel_sampling")
     total_steps = first_step + args.steps
     w = sc.w
     # The planner's automatic choice for the lengths the run ends at (they grow by
@@ -986,13 +1019,18 @@ def main():
     # step (upload and write, copy-on-write copies): the kernels' own start and end
     # (kernel-level events) on every 2*every-th step, shifted, and on the first step
     # of a parallel-sampling run, whose copies follow a synchronisation.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          if i % every == 0 else None for i in range(args.steps)]
+    decode_ring = timer_ring(4)
     mark_steps = {i for i in range(args.steps) if i % (2 * every) == every // 2 + every}
     if ps:
         mark_steps.add(0)
-    marks = [dict(zip(("upload", "copy", "write"), timing_pairs(3, stream)))
-             if args.layout == "paged" and i in mark_steps else None for i in range(args.steps)]
+
+    def read_marks(m):
+        if m["pairs"]:
+            return (m["pairs"], m["upload"].ms(), m["copy"].ms(), m["write"].ms())
+        return (0, m["upload"].ms())
+
+    mark_ring = TimingRing(4, lambda: dict(zip(("upload", "copy", "write"), kernel_timers(3))),
+                           read_marks)
     torch.cuda.synchronize()
     step_bytes, unique_step_bytes = [], []
     plans = []
@@ -1004,7 +1042,9 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        sc.step(first_step + i, partition, ev[i], plans, marks[i])
+        ev = decode_ring.take(i) if i % every == 0 else None
+        marks = mark_ring.take(i) if args.layout == "paged" and i in mark_steps else None
+        sc.step(first_step + i, partition, ev, plans, marks)
         lengths += 1
         step_bytes.append(kv_bytes(lengths, w))
         if sc.unique_bytes is not None:
@@ -1012,8 +1052,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    timed = [i for i in range(args.steps) if ev[i] is not None]
-    decode_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in timed]
+    decode_by_step = decode_ring.results()
+    timed = sorted(decode_by_step)
+    decode_ms = [decode_by_step[i] for i in timed]
     decode_avg_s = float(np.mean(decode_ms)) / 1e3
     total_bytes = float(np.sum(step_bytes))
     value = total_bytes / wall / 1e9
@@ -1024,7 +1065,7 @@ def main():
         # Shared prompt blocks are read from HBM once; the roofline counts unique bytes.
         sc.extra["unique_kv_bytes_per_step"] = int(np.mean(unique_step_bytes))
         achieved = float(np.mean([unique_step_bytes[i] for i in timed])) / decode_avg_s / 1e9
-    writes_copies = (write_copy_times([m for m in marks if m is not None], sc, w)
+    writes_copies = (write_copy_times(list(mark_ring.results().values()), sc, w)
                      if args.layout == "paged" else None)
 
     # The committed counter summaries describe the paged kernels only.
@@ -1048,15 +1089,16 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name} decode layer",
+            "workload": f"{w.name} decode layer" + (f", block size {w.block_size}"
+                                                    if w.block_size != 16 else ""),
             "arithmetic": "fp16 K/V (and q, except the tiny case) read, fp32 softmax and "
                           "accumulation",
             "timed_steps": [first_step, first_step + args.steps - 1],
             "num_seqs": sc.num_seqs, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": w.block_size, "kv_dtype": "f16",
             "q_dtype": np.dtype(w.q_dtype).name, "partition_size": plans[-1]["partition_size"],
-            "prefix_groups": plans[-1]["num_groups"],
-            "group_pieces": plans[-1]["num_group_items"],
+            "prefix_groups": plans[-1].get("num_groups", 0),
+            "group_pieces": plans[-1].get("num_group_items", 0),
             "kernel_policy": args.kernel_policy, "layout": args.layout,
             "schedule": "planner work list, largest piece first",
             "work_items": plans[-1]["num_items"], "waves_per_cu": plans[-1]["waves_per_cu"],
@@ -1066,6 +1108,7 @@ def main():
         },
         "decode_us": round(decode_avg_s * 1e6, 2),
         "decode_timed_steps": len(timed),
+        "decode_timing": f"kernel-level HIP events on every {every}th timed step",
         "decode_us_median": round(float(np.median(decode_ms)) * 1e3, 2),
         "decode_us_p10_p90": [round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
                               round(float(np.percentile(decode_ms, 90)) * 1e3, 2)],
@@ -1076,7 +1119,7 @@ def main():
                                                        / traffic["algorithmic_bytes_per_launch"], 4)
                                                  if traffic else None),
                      "kernel": ("pa_decode_grouped (group pieces, remaining pieces, reduce)"
-                                if plans[-1]["num_groups"] else
+                                if plans[-1].get("num_groups", 0) else
                                 "pa_decode (partition + reduce launches)"),
                      "measured_peak": ceiling,
                      "frac_of_measured": (round(achieved / ceiling["tile_gather"]["gbs"], 4)

@@ -720,6 +720,19 @@ int kv_decode_step_host(kv_allocator* a, const int32_t* seqs, int32_t num_seqs,
 int pkv_time_next_call(void* start_event, void* stop_event);
 
 /*
+ * Timing events for pkv_time_next_call, without recording anything on a
+ * stream.  pkv_event_create makes a hipEvent_t with timing enabled (*event,
+ * as void*); pkv_event_destroy releases one (NULL is a no-op);
+ * pkv_event_elapsed_ms waits for `stop` and stores the milliseconds from
+ * `start` to `stop` in *ms.  PKV_ERR_INVALID_ARG for NULL pointers,
+ * PKV_ERR_HIP when the runtime refuses (for instance an event that no call
+ * has recorded yet).
+ */
+int pkv_event_create(void** event);
+int pkv_event_destroy(void* event);
+int pkv_event_elapsed_ms(void* start, void* stop, float* ms);
+
+/*
  * pkv_read_probe — the HBM read ceiling that decode is measured against.
  * [B] "Why the KV cache is the thing that limits your batch": decode reads
  * every cached key and value once per step and does little arithmetic per

@@ -99,6 +99,9 @@ _SIGNATURES = {
                                  POINTER(c_void_p), c_int32, c_int32, c_void_p, c_int32, c_int32,
                                  c_int32, c_int32, c_void_p]),
     "pkv_time_next_call": (c_int32, [c_void_p, c_void_p]),
+    "pkv_event_create": (c_int32, [POINTER(c_void_p)]),
+    "pkv_event_destroy": (c_int32, [c_void_p]),
+    "pkv_event_elapsed_ms": (c_int32, [c_void_p, c_void_p, POINTER(c_float)]),
     "pkv_read_probe": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_void_p]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode_set_kernel_policy": (c_int32, [c_int32]),
@@ -413,13 +416,36 @@ def pa_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, scal
         int(fuse), ws_ptr, ws_bytes, _stream(stream)))
 
 
-def time_next_call(start=None, stop=None):
-    """Kernel-level timing of the next library device call on this thread: pass two
-    torch.cuda.Event(enable_timing=True) that have been recorded once (so that they
-    exist); afterwards start.elapsed_time(stop) spans its first kernel's start to its
-    last kernel's end.  None clears."""
-    lib().pkv_time_next_call(None if start is None else c_void_p(start.cuda_event),
-                             None if stop is None else c_void_p(stop.cuda_event))
+class KernelTimer:
+    """A (start, stop) pair of HIP timing events made by the library, recorded by the
+    kernels of a call when passed to ``time_next_call``; ``ms()`` waits for the call
+    and returns the time from its first kernel's start to its last kernel's end."""
+
+    __slots__ = ("start", "stop")
+
+    def __init__(self):
+        self.start, self.stop = c_void_p(), c_void_p()
+        _check(lib().pkv_event_create(byref(self.start)))
+        _check(lib().pkv_event_create(byref(self.stop)))
+
+    def ms(self) -> float:
+        out = c_float()
+        _check(lib().pkv_event_elapsed_ms(self.start, self.stop, byref(out)))
+        return float(out.value)
+
+    def __del__(self):
+        if _lib is not None:
+            _lib.pkv_event_destroy(self.start)
+            _lib.pkv_event_destroy(self.stop)
+
+
+def time_next_call(timer=None):
+    """Kernel-level timing of the next library device call on this thread: its
+    kernels record into ``timer`` (a KernelTimer); None clears."""
+    if timer is None:
+        lib().pkv_time_next_call(None, None)
+    else:
+        lib().pkv_time_next_call(timer.start, timer.stop)
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):

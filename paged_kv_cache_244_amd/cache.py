@@ -116,7 +116,7 @@ class _Staging:
         """Copy ``total`` bytes of ring slot i's pinned buffer to its device buffer.
         ``write`` (a callable taking the device buffer's address and the pinned slot)
         replaces the plain copy with one launch that also writes the step's new tokens.
-        ``mark``, a (start, stop) pair of events, takes the launch's kernel times."""
+        ``mark``, a ``_lib.KernelTimer``, takes the launch's kernel times."""
         if self.dev[i].numel() < total:
             self.dev[i] = torch.empty(total, dtype=torch.uint8, device=self.device)
         self.gen[i] += 1
@@ -127,7 +127,7 @@ class _Staging:
             # hand-off between the step's kernels.
             nbytes = (total + 15) // 16 * 16
             if mark is not None:
-                _lib.time_next_call(*mark)
+                _lib.time_next_call(mark)
             if write is None:
                 _lib._check(_lib.lib().pkv_upload(dev.data_ptr(), self.host[i].data_ptr(),
                                                   nbytes, stream.cuda_stream))
@@ -399,12 +399,11 @@ class PagedKVCache:
         between this call and ``attend``; after more, ``attend`` and ``write``
         raise instead of reading another call's bytes.
 
-        ``marks`` (for timing) is a dict of (start, stop) pairs of timing events
-        that exist (recorded once): "upload" takes the kernel times of the upload
-        (fused with the write on steps without copies), and on steps with
-        copy-on-write copies "copy" and "write" those of the copy and the write
-        (``_lib.time_next_call``); ``marks["pairs"]`` is set to the number of
-        copied blocks."""
+        ``marks`` (for timing) is a dict of ``_lib.KernelTimer``: "upload" takes
+        the kernel times of the upload (fused with the write on steps without
+        copies), and on steps with copy-on-write copies "copy" and "write" those
+        of the copy and the write (``_lib.time_next_call``); ``marks["pairs"]`` is
+        set to the number of copied blocks."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
         if self._pending:
             self.retire()
@@ -450,7 +449,7 @@ class PagedKVCache:
             marks["pairs"] = int(lay.num_pairs)
         if lay.num_pairs:
             if marks is not None:
-                _lib.time_next_call(*marks["copy"])
+                _lib.time_next_call(marks["copy"])
             _lib.kv_copy_blocks(self.k, self.v, DeviceArray(dev, lay.pairs_offset, torch.int32,
                                                             (lay.num_pairs, 2)).tensor(),
                                 stream=self.stream)
@@ -458,7 +457,7 @@ class PagedKVCache:
         slots = DeviceArray(dev, lay.slots_offset, torch.int64, (n,), self._staging.last_stamp)
         if k_new is not None and lay.num_pairs:
             if marks is not None:
-                _lib.time_next_call(*marks["write"])
+                _lib.time_next_call(marks["write"])
             self.write(slots, k_new, v_new, layer=layer)
         batch = DecodeBatch(DeviceArray(dev, lay.tables_offset, torch.int32, (n, lay.max_blocks)),
                             DeviceArray(dev, lay.lens_offset, torch.int32, (n,)),
@@ -556,8 +555,8 @@ class PagedKVCache:
         """Causal attention of new tokens (``pa_prefill``): ``q`` [T, Hq, D] fp16 holds
         the last ``q_lens[i]`` tokens of each ``seqs[i]`` in order, whose K/V are
         already written.  Tables, lengths, query offsets and the work list go up in
-        one upload.  Returns out [T, Hq, D] fp32.  ``timing``, a (start, stop) pair of
-        existing timing events, takes the prefill kernel's start and end."""
+        one upload.  Returns out [T, Hq, D] fp32.  ``timing``, a ``_lib.KernelTimer``,
+        takes the prefill kernel's start and end."""
         seqs = np.ascontiguousarray(seqs, dtype=np.int32)
         tables, lens, _ = self._tables(seqs, None, None)
         starts = _prefill_starts(q_lens)
@@ -566,7 +565,7 @@ class PagedKVCache:
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
         if timing is not None:
-            _lib.time_next_call(*timing)
+            _lib.time_next_call(timing)
         _lib.pa_prefill(out, q, s_d, self.k[layer], self.v[layer], t_d, l_d, scale, i_d,
                         stream=self.stream)
         return out
@@ -577,8 +576,8 @@ class PagedKVCache:
 
         ``partition_size`` None keeps the batch's plan; "auto" or a number plans
         again (the library's policy, or that split), as does a query shape or dtype
-        other than the one the batch was planned for.  ``timing``, a (start, stop)
-        pair of existing timing events, takes the decode kernels' start and end
+        other than the one the batch was planned for.  ``timing``, a
+        ``_lib.KernelTimer``, takes the decode kernels' start and end
         (``_lib.time_next_call``).
         """
         s, hq, d = q.shape
@@ -608,7 +607,7 @@ class PagedKVCache:
         # a grouped launch keeps one spare partial slot per request
         ws = self.workspace(s, hq, batch.max_len + (part if grouped else 0), part)
         if timing is not None:
-            _lib.time_next_call(*timing)
+            _lib.time_next_call(timing)
         if grouped:
             g, gi = batch.groups_dev, batch.group_items_dev
             _lib._check(_lib.lib().pa_decode_grouped(

@@ -74,3 +74,30 @@ extern "C" int pkv_read_probe(const void* src, int64_t num_tiles, const int32_t*
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_read_probe launch: %s", hipGetErrorString(e));
   return PKV_OK;
 }
+
+// Events for pkv_time_next_call: created here (not recorded), so that a caller
+// need not record an event on a stream merely to bring it into existence.
+extern "C" int pkv_event_create(void** event) {
+  if (!event) return fail(PKV_ERR_INVALID_ARG, "pkv_event_create: NULL");
+  hipEvent_t e = nullptr;
+  const hipError_t rc = hipEventCreate(&e);
+  if (rc != hipSuccess) return fail(PKV_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(rc));
+  *event = e;
+  return PKV_OK;
+}
+
+extern "C" int pkv_event_destroy(void* event) {
+  if (!event) return PKV_OK;
+  const hipError_t rc = hipEventDestroy(static_cast<hipEvent_t>(event));
+  if (rc != hipSuccess) return fail(PKV_ERR_HIP, "hipEventDestroy: %s", hipGetErrorString(rc));
+  return PKV_OK;
+}
+
+extern "C" int pkv_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return fail(PKV_ERR_INVALID_ARG, "pkv_event_elapsed_ms: NULL");
+  hipError_t rc = hipEventSynchronize(static_cast<hipEvent_t>(stop));
+  if (rc == hipSuccess)
+    rc = hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+  if (rc != hipSuccess) return fail(PKV_ERR_HIP, "pkv_event_elapsed_ms: %s", hipGetErrorString(rc));
+  return PKV_OK;
+}

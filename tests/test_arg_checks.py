@@ -73,3 +73,12 @@ def test_read_probe_arguments_checked_on_the_host():
     assert b"aligned" in lib.pkv_last_error()
     assert lib.pkv_read_probe(None, 0, None, None, 64, None) == _lib.PKV_OK           # nothing
 
+
+
+def test_event_helpers_refuse_null():
+    lib = _lib.lib()
+    assert lib.pkv_event_create(None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_event_destroy(None) == _lib.PKV_OK
+    import ctypes
+    ms = ctypes.c_float()
+    assert lib.pkv_event_elapsed_ms(None, None, ctypes.byref(ms)) == _lib.PKV_ERR_INVALID_ARG

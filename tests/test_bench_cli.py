@@ -30,3 +30,26 @@ def test_device_query_skipped_under_profiler(monkeypatch):
     monkeypatch.setattr(subprocess, "run", refuse)
     monkeypatch.setenv("ROCPROF_OUTPUT_PATH", "/tmp")
     assert bench.gpu_info() is None
+
+
+def test_timing_ring_reads_every_key_once_before_reuse():
+    """bench.TimingRing keeps a fixed number of event sets alive and reads each
+    set's result before handing it out again, so every key's value survives."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    made = []
+
+    def make():
+        made.append([None])
+        return made[-1]
+
+    ring = bench.TimingRing(3, make, lambda box: box[0])
+    for key in range(10):
+        box = ring.take(key)
+        box[0] = key * 10                 # the "measurement" of this key
+    assert len(made) == 3
+    assert ring.results() == {k: k * 10 for k in range(10)}
+    assert ring.results() == {k: k * 10 for k in range(10)}    # idempotent

@@ -15,16 +15,6 @@ from paged_kv_cache_244_amd import _lib
 pytestmark = pytest.mark.gpu
 
 
-def _pairs(n, stream):
-    import torch
-    out = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
-    for a, b in out:
-        a.record(stream)
-        b.record(stream)
-    return out
-
-
 def test_time_next_call_spans_the_kernel_and_is_consumed():
     import torch
 
@@ -34,19 +24,18 @@ def test_time_next_call_spans_the_kernel_and_is_consumed():
     buf = torch.zeros(tiles * 4096, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     order = torch.from_numpy(np.random.default_rng(5).permutation(tiles).astype(np.int32)).cuda()
-    (a, b), = _pairs(1, stream)
+    timer = _lib.KernelTimer()
     torch.cuda.synchronize()
     for order_ptr in (None, order.data_ptr()):
-        _lib.time_next_call(a, b)
+        _lib.time_next_call(timer)
         assert _lib.lib().pkv_read_probe(buf.data_ptr(), tiles, order_ptr, sink.data_ptr(), 2048,
                                          stream.cuda_stream) == _lib.PKV_OK
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b)
+        ms = timer.ms()
         # 256 MiB cannot be read in under ~20 us, nor should it take 100 ms
         assert 0.02 < ms < 100.0, ms
         # the setting was consumed: an untimed call leaves both events as they were
         _lib.lib().pkv_read_probe(buf.data_ptr(), tiles, order_ptr, sink.data_ptr(), 2048,
                                   stream.cuda_stream)
         torch.cuda.synchronize()
-        assert a.elapsed_time(b) == ms
+        assert timer.ms() == ms
     assert int(sink.item()) == 0
