@@ -1068,8 +1068,10 @@ def main():
     writes_copies = (write_copy_times(list(mark_ring.results().values()), sc, w)
                      if args.layout == "paged" else None)
 
-    # The committed counter summaries describe the paged kernels only.
-    traffic = counter_traffic(args.workload) if args.layout == "paged" else None
+    # The committed counter summaries describe the paged kernels at the workloads'
+    # own block size (16) only.
+    traffic = (counter_traffic(args.workload)
+               if args.layout == "paged" and w.block_size == 16 else None)
     ceiling = None if args.no_read_probe else read_ceiling(dev)
     baseline = None
     if args.cpu_seconds > 0 and hasattr(w, "offsets") and args.layout == "paged":
