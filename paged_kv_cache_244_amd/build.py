@@ -29,6 +29,10 @@ DEVICE_FLAGS = [
     "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source additions.  The prefill kernel's maxima run over scores that are
+# never NaN (finite fp16 inputs, -inf for masked tokens): without NaN handling
+# the compiler drops the quieting copy it otherwise puts before each max.
+SOURCE_FLAGS = {"pa_prefill.hip": ["-fno-honor-nans"]}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
                 f"-I{CSRC}"]
 
@@ -53,7 +57,8 @@ def build(jobs: int = 4) -> str:
     cmds, objs = [], []
     for src in HIP_SOURCES:
         obj = os.path.join(obj_dir, src + ".o")
-        cmds.append([cc, "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + DEVICE_FLAGS + COMMON_FLAGS)
+        cmds.append([cc, "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + DEVICE_FLAGS + COMMON_FLAGS
+                    + SOURCE_FLAGS.get(src, []))
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(obj_dir, src + ".o")

@@ -4,10 +4,10 @@
 // "The KV cache is a systems problem" (rsw.lol), section "Memory savings change
 // the scheduling question", which contrasts the prompt phase with incremental
 // decoding: the prompt phase attends many query tokens at once and is bound by
-// arithmetic, decode by bytes.  The keys and values are read through the request's block table ("Only
-// 20.4% of your KV cache held actual tokens" (blog.teqners.com), section "The
-// page table, relocated into attention"), after kv_cache_write stored the
-// prompt's own tokens.
+// arithmetic, decode by bytes.  The keys and values are read through the
+// request's block table ("Only 20.4% of your KV cache held actual tokens"
+// (blog.teqners.com), section "The page table, relocated into attention"),
+// after kv_cache_write stored the prompt's own tokens.
 //
 // Request i holds L_i cached tokens; its Q_i new queries are the last Q_i
 // positions, so query j sits at position L_i - Q_i + j and attends to tokens
@@ -15,15 +15,9 @@
 // prefix).
 //
 // One workgroup of 8 waves per work item (request, block of 8 * 2 * 16/HT
-// queries, tile of HT query heads of one KV head).  The waves load each
-// 64-token K/V tile once, together, into LDS (double-buffered, one barrier per
-// tile), so the L2 traffic per flop is an eighth of one wave working alone.
-// Measured on MI355X: 8 waves beat 4 and 16, and 64-token tiles beat 32 (half
-// the barriers; every wave of the workgroup reaches each barrier).
-// Each wave holds two sets of 16 "columns", (query, head) pairs: column c of
-// set cs = (query wj0 + cs * 16/HT + c / HT, head h0 + c % HT).  Every K or V
-// fragment a wave reads from LDS feeds one MFMA per set, which halves the LDS
-// bytes per flop.  Per 16 tokens and set:
+// queries, tile of HT query heads of one KV head).  Each wave holds two sets of
+// 16 "columns", (query, head) pairs: column c of set cs = (query wj0 + cs *
+// 16/HT + c / HT, head h0 + c % HT).  Per 16 tokens and set
 //
 //   S^T[t][c] = sum_d K[t][d] Q[c][d]     v_mfma_f32_16x16x32_f16, D/32 steps
 //
@@ -31,21 +25,40 @@
 //
 //   O[c][d]  += sum_t P[c][t] V[t][d]     v_mfma_f32_16x16x32_f16, D/16 blocks
 //
-// with the operand layouts of the decode kernel for head groups
-// (pa_decode_mfma.hip): K read from LDS in the A layout, V through
-// ds_read_b64_tr_b16 (two 4-token reads per operand), P from the S^T output
-// layout rounded to fp16.  The softmax denominators come from the matrix cores
-// too: the same P times a block of ones, so numerator and denominator sum the
-// same rounded weights and no lane adds scores on the vector ALUs.  Column c
-// masks every token past its own position; tiles that every column of a wave
-// sees whole skip the masking, and a wave skips 16-token steps that lie wholly
-// past its queries.  One pass, no split: the group walks tokens [0, last
+// with K read from LDS in the A layout, V through ds_read_b64_tr_b16 (two
+// 4-token reads per operand) and P taken from the S^T output layout rounded to
+// fp16.  The softmax denominators come from the matrix cores too (the same P
+// times a block of ones), so numerator and denominator sum the same rounded
+// weights.
+//
+// Keys and values move by 64-token tiles straight from memory into LDS
+// (buffer loads with an LDS destination: no registers, no vector-ALU work):
+// each wave loads 8 rows of a tile, which lie in one cache block, through a
+// buffer resource that spans only those rows of that block, so rows past the
+// last token the workgroup reads are out of range and arrive as zeros.  Rows
+// are unpadded; the 16-byte chunks of row r are stored XOR-permuted by a
+// function of r so that the 16 rows one K fragment read touches, and the 8
+// rows of a V transposed read, fall on distinct LDS banks.
+//
+// Waves 0-3 and 4-7 (one of each per SIMD) alternate between two phases per
+// tile, one phase apart: the matrix phase (P.V of the previous tile, then the
+// scores of this tile) and the softmax phase (mask, maximum, exponentials,
+// fp16 rounding, rare rescale) on the vector ALUs.  While one wave of a SIMD
+// keeps the matrix core busy the other runs its softmax, and every phase ends
+// at a workgroup barrier.  Two K and two V tile buffers: the loads of K(m+1)
+// and V(m) are issued at the start of phase 2m and waited for before the
+// barrier that ends phase 2m+1, so each has two phases in flight.
+//
+// Column c masks every token past its own position; tiles that every column of
+// a wave sees whole skip the masking, and a wave skips tiles that lie wholly
+// past its queries.  One pass, no split: the workgroup walks tokens [0, last
 // position of its block + 1).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cfloat>
 #include <cstdint>
+#include <type_traits>
 #include <vector>
 
 #include "errors.h"
@@ -79,54 +92,100 @@ struct PrefillParams {
 };
 
 constexpr float kSlack = 8.f;
+constexpr int kPrefillWaves = 8;   // waves per workgroup, sharing K/V tiles
+constexpr int kPrefillSets = 2;    // 16-column sets per wave, sharing LDS reads
+constexpr int kPrefillTile = 64;   // tokens per K/V tile
 
-// Unlike decode, every query block of a request reads the same prefix: K/V
-// loads here are ordinary (cached in L2), not streaming.
-__device__ __forceinline__ uint4 load_shared(const uint4* ptr) { return *ptr; }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-#ifndef PKV_PREFILL_WAVES
-#define PKV_PREFILL_WAVES 8
-#endif
-#ifndef PKV_PREFILL_TILE
-#define PKV_PREFILL_TILE 64
-#endif
-#ifndef PKV_PREFILL_SETS
-#define PKV_PREFILL_SETS 2
-#endif
-constexpr int kPrefillWaves = PKV_PREFILL_WAVES;   // waves per workgroup, sharing K/V tiles
-constexpr int kPrefillSets = PKV_PREFILL_SETS;     // 16-column sets per wave, sharing LDS reads
+// Word 3 of a buffer resource for plain byte-addressed (raw) access on gfx9-family GPUs.
+constexpr int kRawBufferWord3 = 0x00020000;
+// s_waitcnt operand: every outstanding vector-memory load done (vmcnt 0), the
+// other counters left unconstrained.  Loads into LDS count as vector-memory loads.
+constexpr int kWaitVmem = 0x0F70;
+
+// Logical 16-byte chunk c of tile row r sits at chunk c ^ lds_swizzle<D>(r) of
+// the row.  Rows are 2D bytes; a 256-byte line of LDS spans all 64 banks and
+// holds 128/D rows.  For line q (of the 16 rows of a K fragment) the swizzle
+// 2 (q mod D/16) + (q div D/16 mod 2) takes 16/(128/D) distinct values, which
+// puts the 16 rows' chunk of one K read on 16 distinct 16-byte bank groups, and
+// keeps the two chunks of a 32-byte V read together while moving it to a
+// different 32-byte bank group for each of 8 consecutive rows.
+template <int D>
+__device__ __forceinline__ int lds_swizzle(int r) {
+  constexpr int RPL = 128 / D;
+  constexpr int H = D / 16;
+  const int q = r / RPL;
+  return 2 * (q % H) + ((q / H) & 1);
+}
+
+// Maximum over the four lanes of a column (lanes l, l ^ 16, l ^ 32, l ^ 48).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second, v_permlane16_swap the odd rows of the first with
+// the even rows of the second; with both operands holding v, every lane finds
+// its partner's value in one of the two results.  The second operand is an
+// identity DPP move of v rather than v itself: given two identical operands the
+// compiler takes the two results to be equal and drops one.
+__device__ __forceinline__ float swap_max(float v, bool halves) {
+  const int b = __builtin_bit_cast(int, v);
+  const int c = __builtin_amdgcn_mov_dpp(b, 0xE4, 0xF, 0xF, false);   // quad_perm [0,1,2,3]
+  const auto x = halves ? __builtin_amdgcn_permlane32_swap(b, c, false, false)
+                        : __builtin_amdgcn_permlane16_swap(b, c, false, false);
+  return fmaxf(v, fmaxf(__builtin_bit_cast(float, static_cast<int>(x[0])),
+                        __builtin_bit_cast(float, static_cast<int>(x[1]))));
+}
+
+__device__ __forceinline__ float column_max(float v) {
+  return swap_max(swap_max(v, true), false);
+}
+
+// Wave-wide load of n (1 or 2) x 1 KiB from src straight into LDS at dst: load
+// i writes bytes [i * 1024, (i + 1) * 1024) of dst, lane l's 16 bytes at offset
+// l * 16 of them, read from src + voff_i.  Offsets at or past `bytes` are out of
+// range: no memory is read and zeros land in LDS.  src, bytes and dst must be
+// the same in every lane of the wave; the first-lane reads keep the compiler
+// from building the buffer resource in vector registers.  (A plain device
+// function: the buffer-resource type has no host form.)
+__device__ __forceinline__ void load_rows(const unsigned char* src, int bytes, unsigned char* dst,
+                                          unsigned voff0, unsigned voff1, int n) {
+  // readfirstlane yields a signed int: each half goes through unsigned before it
+  // is widened, so the low half never sign-extends into the high one.
+  const uint64_t a = reinterpret_cast<uint64_t>(src);
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+  const uint64_t a_s = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(a_s), 0, __builtin_amdgcn_readfirstlane(bytes), kRawBufferWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16, voff0, 0, 0, 0);
+  if (n > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 1024), 16, voff1, 0, 0, 0);
+}
 
 template <int D, int B, int HT>
 __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(PrefillParams p) {
   constexpr int NW = kPrefillWaves;
   constexpr int NS = kPrefillSets;
-  constexpr int NT = kWave * NW;             // threads
-  constexpr int KT = PKV_PREFILL_TILE;       // tokens per tile (KT/16 MFMA steps)
-  constexpr int SUB = KT / 16;
+  constexpr int KT = kPrefillTile;
+  constexpr int SUB = KT / 16;               // 16-token score steps per tile
   constexpr int QB = 16 / HT;                // queries per set
   constexpr int QW = NS * QB;                // queries per wave
   constexpr int KSTEPS = D / 32;
   constexpr int DBLK = D / 16;
   constexpr int CPR = D / 8;                 // 16-byte chunks per token row
-  // LDS bytes per K row.  Padding measured at D = 128 (SQ_LDS_BANK_CONFLICT):
-  // 32 B leaves no bank conflicts, 16 B left 0.7 conflict cycles per LDS
-  // instruction.  D = 64 keeps 16 B (not measured).
-  constexpr int KROWB = D * 2 + (D == 128 ? 32 : 16);
-  constexpr int VROWB = D * 2 + 32;          // LDS bytes per V row (transposed reads)
-  constexpr int LPT = (KT * CPR + NT - 1) / NT;   // chunks of K (and V) a thread moves per tile
-  constexpr int CHUNKS = B * D / 8;          // 16-byte chunks per (block, KV head)
-  constexpr int TPC = kWave * B / KT;        // tiles covered by 64 staged block ids
-  static_assert(LPT * NT == KT * CPR || (LPT == 1 && NT % (KT * CPR) == 0), "tile shape");
-  static_assert(TPC >= 1 && TPC * KT == kWave * B, "chunk shape");
+  constexpr int ROWB = 2 * D;                // bytes per token row, in memory and in LDS
+  constexpr int TILEB = KT * ROWB;
+  constexpr int RPW = KT / NW;               // tile rows each wave loads
+  constexpr int RPI = kWave * 16 / ROWB;     // rows one wave-wide 16-byte-per-lane load covers
+  constexpr int NI = RPW / RPI;              // such loads per wave, tile and tensor
+  static_assert(RPW % RPI == 0 && B % RPW == 0, "a wave's rows of a tile lie in one block");
+  static_assert(NI == 1 || NI == 2, "load_rows moves one or two 1 KiB pieces");
   static_assert(HT == 1 || HT == 2 || HT == 4 || HT == 8 || HT == 16, "head tile");
   static_assert(SUB % 2 == 0, "P.V takes 32 tokens per MFMA: tiles of a multiple of 32 tokens");
-  __shared__ __align__(16) unsigned char klds[2][KT * KROWB];
-  __shared__ __align__(16) unsigned char vlds[2][KT * VROWB];
-  __shared__ __align__(4) unsigned char rowok[2][KT];
+  __shared__ __align__(256) unsigned char kt0[TILEB], kt1[TILEB], vt0[TILEB], vt1[TILEB];
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
   const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int grp = lane >> 4;
   const int li = lane & 15;                  // column of S^T (scores) / of O (outputs)
   const unsigned k = blockIdx.y + blockIdx.z * gridDim.y;
@@ -171,209 +230,223 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
   }
   const int t_end = min(len, base_pos + min(j0 + NW * QW, nq));   // tokens the group reads
 
-  // o: numerators; den: denominators, the same P times a block of ones (every
-  // lane's row r of den[cs] holds the sum for column 4*grp + r of set cs).
-  float4_t o[NS][DBLK], den[NS];
-  float m[NS];
+  // Waves 0-3 run their matrix phases on even phases, waves 4-7 on odd ones.
+  // Each group gets its own copy of the schedule, so that no value one order
+  // needs is kept alive through the other's code.
+  auto run = [&](auto odd_phases) __attribute__((always_inline)) {
+    constexpr bool XO = decltype(odd_phases)::value;
+    // o: numerators; den: denominators, the same P times a block of ones (every
+    // lane's row r of den[cs] holds the sum for column 4*grp + r of set cs).
+    float4_t o[NS][DBLK], den[NS];
+    float m[NS];
 #pragma unroll
-  for (int cs = 0; cs < NS; ++cs) {
+    for (int cs = 0; cs < NS; ++cs) {
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) o[cs][db] = float4_t{0.f, 0.f, 0.f, 0.f};
-    den[cs] = float4_t{0.f, 0.f, 0.f, 0.f};
-    m[cs] = -FLT_MAX;
-  }
-  const half8 ones = half8{1, 1, 1, 1, 1, 1, 1, 1};
+      for (int db = 0; db < DBLK; ++db) o[cs][db] = float4_t{0.f, 0.f, 0.f, 0.f};
+      den[cs] = float4_t{0.f, 0.f, 0.f, 0.f};
+      m[cs] = -FLT_MAX;
+    }
 
-  if (t_end > 0) {
-    const int ntiles = (t_end + KT - 1) / KT;
-    const int64_t block_stride = static_cast<int64_t>(p.num_kv_heads) * CHUNKS;
-    const uint4* kbase = p.k_cache + kvh * static_cast<int64_t>(CHUNKS);
-    const uint4* vbase = p.v_cache + kvh * static_cast<int64_t>(CHUNKS);
-    struct TileRegs {
-      uint4 k[LPT], v[LPT];
-      bool ok[LPT];
-    };
-    TileRegs ra, rb;                         // two tiles in flight, in separate registers
-    int staged = 0;                          // block ids of chunk `staged_chunk`, one per lane
-    int staged_chunk = -1;
+    if (t_end > 0) {
+      const int n = (t_end + KT - 1) / KT;     // tiles
+      // Last tile this wave attends to (-1: none); wave-uniform.
+      const int last = wave_pos_max >= 0 ? min(n - 1, wave_pos_max / KT) : -1;
+      const half8 ones = half8{1, 1, 1, 1, 1, 1, 1, 1};
 
-    // Global -> registers for tile jt: thread tid moves chunks tid, tid + NT, ...
-    auto issue = [&](TileRegs& rg, int jt) __attribute__((always_inline)) {
-      const int chunk = jt / TPC;
-      if (chunk != staged_chunk) {           // wave-uniform: every wave stages the same ids
-        const int b = chunk * kWave + lane;
-        staged = b < p.max_blocks_per_seq ? table[b] : 0;
-        staged_chunk = chunk;
+      // Tile loads.  Lane `lane` of load i moves logical chunk (lane % CPR) ^ swizzle
+      // of row i * RPI + lane / CPR of this wave's rows into the LDS slot it writes.
+      const int64_t head_bytes = static_cast<int64_t>(B) * ROWB;               // one (block, KV head)
+      const int64_t block_bytes = static_cast<int64_t>(p.num_kv_heads) * head_bytes;
+      const unsigned char* kmem = reinterpret_cast<const unsigned char*>(p.k_cache) + kvh * head_bytes;
+      const unsigned char* vmem = reinterpret_cast<const unsigned char*>(p.v_cache) + kvh * head_bytes;
+      unsigned voff[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int rl = i * RPI + lane / CPR;
+        voff[i] = rl * ROWB + ((lane % CPR) ^ lds_swizzle<D>(wave * RPW + rl)) * 16;
       }
+      // Table entry of the block holding this wave's rows of tile jt (they lie in
+      // one block), or 0 for rows past t_end (tok < t_end <= cap: inside the
+      // table).  Read one phase pair before the tile's load needs it, so that its
+      // latency never stalls a phase.
+      auto block_of = [&](int jt) __attribute__((always_inline)) {
+        const int tok = jt * KT + wave * RPW;
+        return tok < t_end ? table[tok / B] : 0;
+      };
+      auto load_tile = [&](const unsigned char* mem, unsigned char* dst, int jt, int entry)
+          __attribute__((always_inline)) {
+        const int tok = jt * KT + wave * RPW;  // this wave's first row
+        const int rows = max(0, min(RPW, t_end - tok));
+        // The same id in every lane: kept in a scalar register, so the buffer
+        // resource is one too.
+        const int raw = __builtin_amdgcn_readfirstlane(entry);
+        const bool ok = rows > 0 && static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks);
+        load_rows(mem + (ok ? raw : 0) * block_bytes + (tok % B) * ROWB, ok ? rows * ROWB : 0,
+                  dst + wave * RPW * ROWB, voff[0], voff[NI - 1], NI);
+      };
+
+      // Fragment addresses (bytes within a tile buffer).  K: row li of a 16-token
+      // step, chunk grp + 4 kk.  V: row 4 grp + li / 4 of a 16-token step, bytes
+      // 32 db + 8 (li % 4) of it.
+      const int kswz = lds_swizzle<D>(li);
+      const int vrow = 4 * grp + (li >> 2);
+      const int vswz = lds_swizzle<D>(vrow);
+      int koff[KSTEPS], vof[DBLK];
 #pragma unroll
-      for (int it = 0; it < LPT; ++it) {
-        const int c = (it * NT + tid) % (KT * CPR);   // threads beyond the tile repeat a chunk
-        const int r = c / CPR;
-        const int t = jt * KT + r;
-        const int raw = __builtin_bit_cast(int, shfl(__builtin_bit_cast(float, staged),
-                                                     (t - chunk * kWave * B) / B));
-        const bool ok = t < t_end && static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks);
-        const int64_t off = (ok ? raw : 0) * block_stride + (t % B) * CPR + c % CPR;
-        rg.k[it] = load_shared(kbase + off);
-        rg.v[it] = load_shared(vbase + off);
-        rg.ok[it] = ok;
-      }
-    };
-    // Registers -> LDS buffer; invalid rows become zeros and are flagged.
-    auto store = [&](const TileRegs& rg, int u) __attribute__((always_inline)) {
+      for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = li * ROWB + ((grp + 4 * kk) ^ kswz) * 16;
 #pragma unroll
-      for (int it = 0; it < LPT; ++it) {
-        const int c = it * NT + tid;
-        if (c >= KT * CPR) break;            // (only when the group has more threads than chunks)
-        const int r = c / CPR;
-        const unsigned mask = rg.ok[it] ? 0xFFFFFFFFu : 0u;   // component-wise: no aggregate select
-        const uint4 kv = rg.k[it], vv = rg.v[it];
-        *reinterpret_cast<uint4*>(&klds[u][r * KROWB + (c % CPR) * 16]) =
-            make_uint4(kv.x & mask, kv.y & mask, kv.z & mask, kv.w & mask);
-        *reinterpret_cast<uint4*>(&vlds[u][r * VROWB + (c % CPR) * 16]) =
-            make_uint4(vv.x & mask, vv.y & mask, vv.z & mask, vv.w & mask);
-        if (c % CPR == 0) rowok[u][r] = rg.ok[it] ? 1 : 0;
-      }
-    };
-    // One wave's column sets against the KT-token tile in buffer u: every 16-token
-    // score step first (each K fragment feeding every set), then per set one max
-    // exchange and one softmax update for the tile, then P.V (each V fragment
-    // feeding every set).
-    auto compute = [&](int u, int jt) __attribute__((always_inline)) {
-      const int tok0 = jt * KT;
-      if (tok0 > wave_pos_max) return;       // every column of this wave is past here
-      float4_t s[NS][SUB];
+      for (int db = 0; db < DBLK; ++db)
+        vof[db] = vrow * ROWB + ((2 * db + ((li >> 1) & 1)) ^ vswz) * 16 + 8 * (li & 1);
+
+      float4_t s[NS][SUB];                     // scores of the tile last scored
+      half4 pa[NS][SUB];                       // its probabilities after the softmax phase
+
+      auto scores = [&](const unsigned char* kb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int sub = 0; sub < SUB; ++sub) {
+        for (int sub = 0; sub < SUB; ++sub) {
 #pragma unroll
-        for (int cs = 0; cs < NS; ++cs) s[cs][sub] = float4_t{0.f, 0.f, 0.f, 0.f};
-        if (sub > 0 && tok0 + sub * 16 > wave_pos_max) continue;   // step wholly masked
-        const unsigned char* krow = &klds[u][(sub * 16 + li) * KROWB + grp * 16];
+          for (int cs = 0; cs < NS; ++cs) s[cs][sub] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const half8 kv = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(krow + kk * 64));
+          for (int kk = 0; kk < KSTEPS; ++kk) {
+            const half8 kv =
+                __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(kb + sub * 16 * ROWB + koff[kk]));
 #pragma unroll
-          for (int cs = 0; cs < NS; ++cs)
-            s[cs][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qb[cs][kk], s[cs][sub], 0, 0, 0);
-        }
-      }
-      // Masking is needed only where some column of this wave sees part of the tile
-      // (the diagonal) or some row is not a valid token (the last tile): elsewhere
-      // every score enters as it is.
-      const bool masked = tok0 + KT - 1 > wave_pos_min || tok0 + KT > t_end;
-      if (masked) {
-        unsigned ok4[SUB];                   // rows 4*grp .. 4*grp+3 of each step: validity flags
-#pragma unroll
-        for (int sub = 0; sub < SUB; ++sub)
-          ok4[sub] = *reinterpret_cast<const unsigned*>(&rowok[u][sub * 16 + 4 * grp]);
-#pragma unroll
-        for (int cs = 0; cs < NS; ++cs)
-#pragma unroll
-          for (int sub = 0; sub < SUB; ++sub)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = tok0 + sub * 16 + 4 * grp + r;
-              const bool vis = ((ok4[sub] >> (8 * r)) & 0xFFu) != 0 && t <= pos[cs];
-              s[cs][sub][r] = vis ? s[cs][sub][r] : -INFINITY;
-            }
-      }
-      half4 pa[NS][SUB];
-#pragma unroll
-      for (int cs = 0; cs < NS; ++cs) {
-        // Maximum of the raw scores (the scale is positive), then in log2 units.
-        float mt = -INFINITY;
-#pragma unroll
-        for (int sub = 0; sub < SUB; ++sub)
-          mt = fmaxf(mt, fmaxf(fmaxf(s[cs][sub][0], s[cs][sub][1]), fmaxf(s[cs][sub][2], s[cs][sub][3])));
-        mt = fmaxf(mt, shfl_xor(mt, 16));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
-        mt *= p.scale_log2;
-        const bool moved = mt > m[cs] + kSlack;
-        const float m_new = moved ? mt : m[cs];
-        float pr[SUB][4];
-#pragma unroll
-        for (int sub = 0; sub < SUB; ++sub)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pr[sub][r] = fast_exp2(fmaf(s[cs][sub][r], p.scale_log2, -m_new));
-        if (__builtin_amdgcn_ballot_w64(moved)) {
-          const float alpha = fast_exp2(m[cs] - m_new);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float ar = shfl(alpha, 4 * grp + r);
-            den[cs][r] *= ar;
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db) o[cs][db][r] *= ar;
+            for (int cs = 0; cs < NS; ++cs)
+              s[cs][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qb[cs][kk], s[cs][sub], 0, 0, 0);
           }
         }
-#pragma unroll
-        for (int sub = 0; sub < SUB; ++sub)
-          pa[cs][sub] = half4{static_cast<_Float16>(pr[sub][0]), static_cast<_Float16>(pr[sub][1]),
-                              static_cast<_Float16>(pr[sub][2]), static_cast<_Float16>(pr[sub][3])};
-        m[cs] = m_new;
-      }
+      };
       // P.V over 32 tokens per MFMA (the double-rate 16x16x32 form): slots 0-3 of a
       // lane's operand are tokens 4*grp..4*grp+3 of one 16-token step, slots 4-7
       // the same rows of the next step, in A (probabilities) and B (transposed V)
       // alike, so the sum over k pairs each probability with its own V row.
-      typedef __attribute__((address_space(3))) short4_t lds_short4;
+      auto pv = [&](const unsigned char* vb) __attribute__((always_inline)) {
 #pragma unroll
-      for (int sp = 0; sp < SUB; sp += 2) {
-        const unsigned char* src0 =
-            &vlds[u][(sp * 16 + 4 * grp + (li >> 2)) * VROWB + 8 * (li & 3)];
-        const unsigned char* src1 = src0 + 16 * VROWB;
-        half8 pa8[NS];
+        for (int sp = 0; sp < SUB; sp += 2) {
+          half8 pa8[NS];
 #pragma unroll
-        for (int cs = 0; cs < NS; ++cs)
-          pa8[cs] = half8{pa[cs][sp][0], pa[cs][sp][1], pa[cs][sp][2], pa[cs][sp][3],
-                          pa[cs][sp + 1][0], pa[cs][sp + 1][1], pa[cs][sp + 1][2], pa[cs][sp + 1][3]};
+          for (int cs = 0; cs < NS; ++cs) {
+            pa8[cs] = half8{pa[cs][sp][0], pa[cs][sp][1], pa[cs][sp][2], pa[cs][sp][3],
+                            pa[cs][sp + 1][0], pa[cs][sp + 1][1], pa[cs][sp + 1][2], pa[cs][sp + 1][3]};
+            den[cs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], ones, den[cs], 0, 0, 0);
+          }
 #pragma unroll
-        for (int cs = 0; cs < NS; ++cs)
-          den[cs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], ones, den[cs], 0, 0, 0);
+          for (int db = 0; db < DBLK; ++db) {
+            const unsigned char* src = vb + sp * 16 * ROWB + vof[db];
+            const half4 v0 = __builtin_bit_cast(
+                half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)src));
+            const half4 v1 = __builtin_bit_cast(
+                half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src + 16 * ROWB)));
+            const half8 vf = half8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const half4 v0 = __builtin_bit_cast(
-              half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src0 + 32 * db)));
-          const half4 v1 = __builtin_bit_cast(
-              half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src1 + 32 * db)));
-          const half8 vf = half8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            for (int cs = 0; cs < NS; ++cs)
+              o[cs][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], vf, o[cs][db], 0, 0, 0);
+          }
+        }
+      };
+      // Softmax phase of tile jt: per set one maximum over the tile, then the
+      // probabilities relative to the running maximum, which moves only when the
+      // tile's maximum exceeds it by more than kSlack (log2 units); then o and
+      // den are rescaled once.
+      auto softmax = [&](int jt) __attribute__((always_inline)) {
+        const int tok0 = jt * KT;
+        if (tok0 + KT - 1 > wave_pos_min) {    // some column sees only part of the tile
 #pragma unroll
           for (int cs = 0; cs < NS; ++cs)
-            o[cs][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], vf, o[cs][db], 0, 0, 0);
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int t = tok0 + sub * 16 + 4 * grp + r;
+                s[cs][sub][r] = t <= pos[cs] ? s[cs][sub][r] : -INFINITY;
+              }
         }
+#pragma unroll
+        for (int cs = 0; cs < NS; ++cs) {
+          // Maximum of the raw scores (the scale is positive), then in log2 units.
+          float mt = -INFINITY;
+#pragma unroll
+          for (int sub = 0; sub < SUB; ++sub)
+            mt = fmaxf(mt, fmaxf(fmaxf(s[cs][sub][0], s[cs][sub][1]), fmaxf(s[cs][sub][2], s[cs][sub][3])));
+          mt = column_max(mt) * p.scale_log2;
+          const bool moved = mt > m[cs] + kSlack;
+          const float m_new = moved ? mt : m[cs];
+#pragma unroll
+          for (int sub = 0; sub < SUB; ++sub) {
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(s[cs][sub][r], p.scale_log2, -m_new));
+            pa[cs][sub] = half4{static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1]),
+                                static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])};
+          }
+          if (__builtin_amdgcn_ballot_w64(moved)) {
+            const float alpha = fast_exp2(m[cs] - m_new);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float ar = shfl(alpha, 4 * grp + r);
+              den[cs][r] *= ar;
+#pragma unroll
+              for (int db = 0; db < DBLK; ++db) o[cs][db][r] *= ar;
+            }
+          }
+          m[cs] = m_new;
+        }
+      };
+      // Matrix phase j: P.V of tile j - 1, then the scores of tile j.
+      auto matrix_phase = [&](int j, const unsigned char* kb, const unsigned char* vb_prev)
+          __attribute__((always_inline)) {
+        if (j >= 1 && j - 1 <= last) pv(vb_prev);
+        if (j < n && j <= last) scores(kb);
+      };
+      auto softmax_phase = [&](int j) __attribute__((always_inline)) {
+        if (j >= 0 && j <= last) softmax(j);
+      };
+      // Phases 2mm and 2mm + 1.  K(j) lives in buffer j % 2 of kt*, V(j) of vt*.
+      // entry_cur / entry_next: this wave's table entries for tiles mm and mm + 1.
+      int entry_cur = block_of(0), entry_next = block_of(1);
+      auto phase_pair = [&](int mm, unsigned char* kc, unsigned char* kn, unsigned char* vc,
+                            const unsigned char* vp) __attribute__((always_inline)) {
+        if (mm + 1 < n) load_tile(kmem, kn, mm + 1, entry_next);
+        if (mm < n) load_tile(vmem, vc, mm, entry_cur);
+        const int entry_after = block_of(mm + 2);   // lands by the wait that ends this pair
+        if constexpr (!XO) matrix_phase(mm, kc, vp); else softmax_phase(mm - 1);
+        __syncthreads();
+        if constexpr (XO) matrix_phase(mm, kc, vp); else softmax_phase(mm);
+        __builtin_amdgcn_s_waitcnt(kWaitVmem);   // this wave's tile loads have landed
+        __syncthreads();                          // and everyone's: K(mm+1), V(mm) readable
+        entry_cur = entry_next;
+        entry_next = entry_after;
+      };
+
+      load_tile(kmem, kt0, 0, entry_cur);
+      __builtin_amdgcn_s_waitcnt(kWaitVmem);
+      __syncthreads();
+      for (int mm = 0; mm <= n; mm += 2) {
+        phase_pair(mm, kt0, kt1, vt0, vt1);
+        if (mm + 1 > n) break;
+        phase_pair(mm + 1, kt1, kt0, vt1, vt0);
       }
-    };
-
-    // Tile jt is in register set ra (even jt) or rb (odd jt) and LDS buffer jt % 2.
-    auto step = [&](TileRegs& rg, int u, int jt) __attribute__((always_inline)) {
-      store(rg, u);
-      if (jt + 2 < ntiles) issue(rg, jt + 2);
-      __syncthreads();                       // tile jt visible; the other buffer free again
-      compute(u, jt);
-    };
-    issue(ra, 0);
-    if (ntiles > 1) issue(rb, 1);
-    int jt = 0;
-    for (; jt + 1 < ntiles; jt += 2) {
-      step(ra, 0, jt);
-      step(rb, 1, jt + 1);
     }
-    if (jt < ntiles) step(ra, 0, jt);
-  }
 
-  // Per set: each lane's output rows, columns 4*grp + r, over their denominators.
+    // Per set: each lane's output rows, columns 4*grp + r, over their denominators.
 #pragma unroll
-  for (int cs = 0; cs < NS; ++cs) {
+    for (int cs = 0; cs < NS; ++cs) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = 4 * grp + r;
-      const int qj = wj0 + cs * QB + c / HT;
-      if (qj >= nq) continue;
-      const float inv = den[cs][r] > 0.f ? 1.f / den[cs][r] : 0.f;   // a query with no token: zeros
-      float* dst = p.out + (static_cast<int64_t>(q_first + qj) * p.num_q_heads + h0 + c % HT) * D;
+      for (int r = 0; r < 4; ++r) {
+        const int c = 4 * grp + r;
+        const int qj = wj0 + cs * QB + c / HT;
+        if (qj >= nq) continue;
+        const float inv = den[cs][r] > 0.f ? 1.f / den[cs][r] : 0.f;   // a query with no token: zeros
+        float* dst = p.out + (static_cast<int64_t>(q_first + qj) * p.num_q_heads + h0 + c % HT) * D;
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) dst[db * 16 + li] = o[cs][db][r] * inv;
+        for (int db = 0; db < DBLK; ++db) dst[db * 16 + li] = o[cs][db][r] * inv;
+      }
     }
-  }
+  };
+  if (wave >= NW / 2)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 }
 
 using PrefillFn = void (*)(PrefillParams);

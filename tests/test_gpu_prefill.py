@@ -32,7 +32,7 @@ CASES = [
 ]
 
 
-def _setup(hq, hkv, d, bs, lens, qlens, seed):
+def _setup(hq, hkv, d, bs, lens, qlens, seed, poison=False):
     import torch
 
     from paged_kv_cache_244_amd.cache import PagedKVCache
@@ -43,6 +43,9 @@ def _setup(hq, hkv, d, bs, lens, qlens, seed):
     nb = sum(-(-L // bs) for L in lens) + 8
     c = PagedKVCache(nb, hkv, d, bs, initial_order=rng.permutation(nb).astype(np.int32),
                      num_q_heads=hq)
+    if poison:                         # every slot no token is written to holds NaN
+        c.k[0].fill_(float("nan"))
+        c.v[0].fill_(float("nan"))
     seqs = [c.new_sequence() for _ in lens]
     k = rng.standard_normal((sum(lens), hkv, d)).astype(np.float16)
     v = rng.standard_normal((sum(lens), hkv, d)).astype(np.float16)
@@ -80,6 +83,31 @@ def test_prefill_matches_oracle(name, hq, hkv, d, bs, lens, qlens):
     want = attention.attend_prefill_paged(q, c.k[0].cpu().numpy(), c.v[0].cpu().numpy(),
                                           tables.astype(np.int64), lens_h, starts, bs, scale)
     paths.assert_attention_close(got, want)
+
+
+POISON_CASES = [
+    ("gqa4_d128_b16", 32, 8, 128, 16),
+    ("gqa8_d64_b8", 16, 2, 64, 8),
+    ("mha_d128_b128", 8, 8, 128, 128),
+]
+
+
+@pytest.mark.parametrize("name,hq,hkv,d,bs", POISON_CASES, ids=[c[0] for c in POISON_CASES])
+def test_prefill_never_reads_past_the_context(name, hq, hkv, d, bs):
+    """The pool is NaN everywhere no token was written, so any slot past a request's
+    last token that entered a product (a score, or a value row times a zero weight)
+    would turn its rows NaN.  Lengths put the last token at every kind of place in a
+    tile and a block, including requests shorter than one 64-token tile."""
+    print(f"\n[case] prefill NaN-poisoned pool {name}", flush=True)
+    lens = [1, 7, 17, 63, 64, 65, 100, 129, 300]
+    c, tables, lens_h, starts, q = _setup(hq, hkv, d, bs, lens, None, seed=17, poison=True)
+    scale = 1.0 / np.sqrt(d)
+    got = _run(c, tables, lens_h, starts, q, scale)
+    assert np.isfinite(got).all()
+    want = attention.attend_prefill_paged(q, np.nan_to_num(c.k[0].cpu().numpy()),
+                                          np.nan_to_num(c.v[0].cpu().numpy()),
+                                          tables.astype(np.int64), lens_h, starts, bs, scale)
+    paths.assert_attention_close(got, want, label=f"prefill poisoned {name}")
 
 
 def test_prefill_plan_covers_blocks_largest_first():
