@@ -265,24 +265,34 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
         const int rl = i * RPI + lane / CPR;
         voff[i] = rl * ROWB + ((lane % CPR) ^ lds_swizzle<D>(wave * RPW + rl)) * 16;
       }
-      // Table entry of the block holding this wave's rows of tile jt (they lie in
-      // one block), or 0 for rows past t_end (tok < t_end <= cap: inside the
-      // table).  Read one phase pair before the tile's load needs it, so that its
-      // latency never stalls a phase.
-      auto block_of = [&](int jt) __attribute__((always_inline)) {
-        const int tok = jt * KT + wave * RPW;
+      // Tiles are loaded by the waves in their softmax phase: K tiles by waves
+      // 4-7, V tiles by waves 0-3.  Wave w moves row groups w mod 4 and
+      // w mod 4 + 4 (rows 8 g .. 8 g + 7 of a tile, inside one block), with the
+      // same lane offsets for both (the swizzle depends on the row mod 16 and
+      // the groups are 32 rows apart).
+      // Table entry of the block holding group g of tile jt, or 0 for rows past
+      // t_end (tok < t_end <= cap: inside the table).  Read one phase pair before
+      // the tile's load needs it, so that its latency never stalls a phase.
+      auto block_of = [&](int jt, int g) __attribute__((always_inline)) {
+        const int tok = jt * KT + g * RPW;
         return tok < t_end ? table[tok / B] : 0;
       };
-      auto load_tile = [&](const unsigned char* mem, unsigned char* dst, int jt, int entry)
+      auto load_group = [&](const unsigned char* mem, unsigned char* dst, int jt, int g, int entry)
           __attribute__((always_inline)) {
-        const int tok = jt * KT + wave * RPW;  // this wave's first row
+        const int tok = jt * KT + g * RPW;   // the group's first row
         const int rows = max(0, min(RPW, t_end - tok));
         // The same id in every lane: kept in a scalar register, so the buffer
         // resource is one too.
         const int raw = __builtin_amdgcn_readfirstlane(entry);
         const bool ok = rows > 0 && static_cast<unsigned>(raw) < static_cast<unsigned>(p.num_blocks);
         load_rows(mem + (ok ? raw : 0) * block_bytes + (tok % B) * ROWB, ok ? rows * ROWB : 0,
-                  dst + wave * RPW * ROWB, voff[0], voff[NI - 1], NI);
+                  dst + g * RPW * ROWB, voff[0], voff[NI - 1], NI);
+      };
+      const int g0 = wave % (NW / 2), g1 = g0 + NW / 2;   // this wave's row groups
+      auto load_tile = [&](const unsigned char* mem, unsigned char* dst, int jt, const int (&e)[2])
+          __attribute__((always_inline)) {
+        load_group(mem, dst, jt, g0, e[0]);
+        load_group(mem, dst, jt, g1, e[1]);
       };
 
       // Fragment addresses (bytes within a tile buffer).  K: row li of a 16-token
@@ -402,23 +412,43 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
         if (j >= 0 && j <= last) softmax(j);
       };
       // Phases 2mm and 2mm + 1.  K(j) lives in buffer j % 2 of kt*, V(j) of vt*.
-      // entry_cur / entry_next: this wave's table entries for tiles mm and mm + 1.
-      int entry_cur = block_of(0), entry_next = block_of(1);
+      // Pair mm loads K(mm+1) (waves 4-7, at the start of phase 2mm) and V(mm)
+      // (waves 0-3, at the start of phase 2mm + 1); both are waited for before
+      // the barrier that ends phase 2mm + 1.  entry: the loading wave's table
+      // entries (groups g0, g1) for the tile it loads in this pair, read one
+      // pair ahead.
+      constexpr int kAhead = XO ? 1 : 0;      // tile loaded in pair mm: mm + kAhead
+      int entry[2] = {block_of(kAhead, g0), block_of(kAhead, g1)};
       auto phase_pair = [&](int mm, unsigned char* kc, unsigned char* kn, unsigned char* vc,
                             const unsigned char* vp) __attribute__((always_inline)) {
-        if (mm + 1 < n) load_tile(kmem, kn, mm + 1, entry_next);
-        if (mm < n) load_tile(vmem, vc, mm, entry_cur);
-        const int entry_after = block_of(mm + 2);   // lands by the wait that ends this pair
-        if constexpr (!XO) matrix_phase(mm, kc, vp); else softmax_phase(mm - 1);
+        int entry_after[2] = {0, 0};
+        if constexpr (XO) {
+          if (mm + 1 < n) load_tile(kmem, kn, mm + 1, entry);
+          entry_after[0] = block_of(mm + 2, g0);   // lands by the wait that ends this pair
+          entry_after[1] = block_of(mm + 2, g1);
+          softmax_phase(mm - 1);
+        } else {
+          matrix_phase(mm, kc, vp);
+        }
         __syncthreads();
-        if constexpr (XO) matrix_phase(mm, kc, vp); else softmax_phase(mm);
+        if constexpr (XO) {
+          matrix_phase(mm, kc, vp);
+        } else {
+          if (mm < n) load_tile(vmem, vc, mm, entry);
+          entry_after[0] = block_of(mm + 1, g0);
+          entry_after[1] = block_of(mm + 1, g1);
+          softmax_phase(mm);
+        }
         __builtin_amdgcn_s_waitcnt(kWaitVmem);   // this wave's tile loads have landed
         __syncthreads();                          // and everyone's: K(mm+1), V(mm) readable
-        entry_cur = entry_next;
-        entry_next = entry_after;
+        entry[0] = entry_after[0];
+        entry[1] = entry_after[1];
       };
 
-      load_tile(kmem, kt0, 0, entry_cur);
+      if constexpr (XO) {
+        const int e0[2] = {block_of(0, g0), block_of(0, g1)};
+        load_tile(kmem, kt0, 0, e0);
+      }
       __builtin_amdgcn_s_waitcnt(kWaitVmem);
       __syncthreads();
       for (int mm = 0; mm <= n; mm += 2) {
