@@ -490,8 +490,8 @@ int pa_decode_contiguous(float* out, const void* q, int32_t q_dtype,
  *   block_tables, context_lens, k_cache, v_cache, num_blocks: as pa_decode.
  *   work_items: device uint32 [num_work_items] of (request << 16 | query
  *              block) entries, a block being pa_prefill_queries_per_item
- *              queries; pa_prefill_plan lists every block once, most tokens
- *              to read first.  Missing blocks leave their rows unwritten.
+ *              queries; pa_prefill_plan lists every block once, longest
+ *              requests first.  Missing blocks leave their rows unwritten.
  * Supported: head_dim 64/128, block_size 8..128, groups of 1, 2, 4, 8, 16 or a
  * multiple of 16 query heads per KV head.  Errors as pa_decode.
  */
@@ -508,9 +508,13 @@ int32_t pa_prefill_queries_per_item(int32_t num_q_heads, int32_t num_kv_heads);
 /*
  * pa_prefill_plan — host only: the work items of a pa_prefill launch from
  * host copies of each request's query count and context length, one per block
- * of pa_prefill_queries_per_item queries, ordered by the tokens the block
- * reads (its last query's position + 1), most first; ties by request, then
- * block.  items_capacity >= the total query count always suffices;
+ * of pa_prefill_queries_per_item queries.  A block's cost is the tokens it
+ * reads (its last query's position + 1).  Requests come in order of their
+ * costliest block, most first (ties: lower request index); each request's
+ * blocks are consecutive, costliest first (ties: lower block).  Keeping a
+ * request's blocks together keeps the workgroups that run at the same time on
+ * one request's keys and values, which then come from cache after the first
+ * read.  items_capacity >= the total query count always suffices;
  * *num_items_out is set even when the capacity is too small
  * (PKV_ERR_INVALID_ARG).
  */

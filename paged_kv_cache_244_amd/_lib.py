@@ -564,7 +564,8 @@ def pa_decode_contiguous(out, q, k_rows, v_rows, context_lens, scale, max_contex
 
 
 def prefill_plan(q_lens, context_lens, num_q_heads, num_kv_heads):
-    """Work items of a pa_prefill launch (host uint32, most tokens to read first)."""
+    """Work items of a pa_prefill launch (host uint32): requests by their costliest
+    block, each request's blocks together, costliest first."""
     ql = np.ascontiguousarray(q_lens, dtype=np.int32)
     cl = np.ascontiguousarray(context_lens, dtype=np.int32)
     if ql.shape != cl.shape or ql.ndim != 1:

@@ -540,29 +540,44 @@ extern "C" int pa_prefill_plan(const int32_t* q_lens, const int32_t* context_len
                 num_q_heads, num_kv_heads);
   if (num_seqs > 0 && (!q_lens || !context_lens))
     return fail(PKV_ERR_INVALID_ARG, "pa_prefill_plan: NULL lengths");
-  // Cost of a block = tokens its wave reads = position of its last query + 1.
-  std::vector<uint64_t> keys;
+  // Cost of a block = tokens its workgroup reads = position of its last query + 1.
+  // Requests in order of their largest block, most first; each request's blocks
+  // consecutive, most first.
+  struct Key {
+    int64_t req_cost, cost;
+    int32_t s, b;
+  };
+  std::vector<Key> keys;
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int64_t nq = q_lens[s] > 0 ? q_lens[s] : 0;
     const int64_t len = context_lens[s] > 0 ? context_lens[s] : 0;
     const int64_t nblocks = (nq + qb - 1) / qb;
     if (nblocks > 65536)
       return fail(PKV_ERR_INVALID_ARG, "pa_prefill_plan: request %d has too many query blocks", s);
+    const size_t first = keys.size();
+    int64_t req_cost = 0;
     for (int64_t b = 0; b < nblocks; ++b) {
       const int64_t last = std::min<int64_t>((b + 1) * qb, nq) - 1;
       int64_t cost = len - nq + last + 1;
       cost = cost < 0 ? 0 : (cost > len ? len : cost);
-      keys.push_back((static_cast<uint64_t>(UINT32_MAX - static_cast<uint32_t>(cost)) << 32) |
-                     (static_cast<uint64_t>(s) << 16) | static_cast<uint64_t>(b));
+      req_cost = std::max(req_cost, cost);
+      keys.push_back(Key{0, cost, s, static_cast<int32_t>(b)});
     }
+    for (size_t i = first; i < keys.size(); ++i) keys[i].req_cost = req_cost;
   }
   *num_items_out = static_cast<int32_t>(keys.size());
   if (static_cast<int64_t>(keys.size()) > items_capacity)
     return fail(PKV_ERR_INVALID_ARG, "pa_prefill_plan: %zu items do not fit in %d", keys.size(),
                 items_capacity);
   if (!keys.empty() && !items) return fail(PKV_ERR_INVALID_ARG, "pa_prefill_plan: NULL items");
-  std::sort(keys.begin(), keys.end());
-  for (size_t i = 0; i < keys.size(); ++i) items[i] = static_cast<uint32_t>(keys[i] & 0xFFFFFFFFu);
+  std::sort(keys.begin(), keys.end(), [](const Key& a, const Key& b) {
+    if (a.req_cost != b.req_cost) return a.req_cost > b.req_cost;
+    if (a.s != b.s) return a.s < b.s;
+    if (a.cost != b.cost) return a.cost > b.cost;
+    return a.b < b.b;
+  });
+  for (size_t i = 0; i < keys.size(); ++i)
+    items[i] = (static_cast<uint32_t>(keys[i].s) << 16) | static_cast<uint32_t>(keys[i].b);
   return PKV_OK;
 }
 

@@ -110,9 +110,9 @@ def test_prefill_never_reads_past_the_context(name, hq, hkv, d, bs):
     paths.assert_attention_close(got, want, label=f"prefill poisoned {name}")
 
 
-def test_prefill_plan_covers_blocks_largest_first():
+def test_prefill_plan_covers_blocks_request_by_request():
     print("\n[case] prefill plan", flush=True)
-    qlens, lens = [40, 0, 7, 33], [300, 5, 7, 33]
+    qlens, lens = [40, 0, 7, 33, 200], [300, 5, 7, 33, 200]
     qb = int(_lib.lib().pa_prefill_queries_per_item(32, 8))
     assert qb == 64                    # 8 waves x 2 sets x 16 columns / 4 heads per KV head
     items = _lib.prefill_plan(qlens, lens, 32, 8)
@@ -122,8 +122,16 @@ def test_prefill_plan_covers_blocks_largest_first():
 
     def cost(s, b):
         return lens[s] - qlens[s] + min((b + 1) * qb, qlens[s])
-    costs = [cost(s, b) for s, b in blocks]
-    assert costs == sorted(costs, reverse=True)
+    # Requests by their costliest block, most first; a request's blocks together,
+    # costliest first.
+    order = [s for s, _ in blocks]
+    runs = [s for i, s in enumerate(order) if i == 0 or order[i - 1] != s]
+    assert len(runs) == len(set(runs))
+    top = {s: max(cost(s, b) for b in range(-(-qlens[s] // qb))) for s in set(order)}
+    assert [top[s] for s in runs] == sorted((top[s] for s in runs), reverse=True)
+    for s in runs:
+        c = [cost(s, b) for t, b in blocks if t == s]
+        assert c == sorted(c, reverse=True)
     assert _lib.lib().pa_prefill_queries_per_item(24, 8) == 0        # 3 heads per KV head
 
 
