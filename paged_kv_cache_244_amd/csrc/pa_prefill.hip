@@ -32,23 +32,24 @@
 // weights.
 //
 // Keys and values move by 64-token tiles straight from memory into LDS
-// (buffer loads with an LDS destination: no registers, no vector-ALU work):
-// each wave loads 8 rows of a tile, which lie in one cache block, through a
-// buffer resource that spans only those rows of that block, so rows past the
-// last token the workgroup reads are out of range and arrive as zeros.  Rows
-// are unpadded; the 16-byte chunks of row r are stored XOR-permuted by a
-// function of r so that the 16 rows one K fragment read touches, and the 8
-// rows of a V transposed read, fall on distinct LDS banks.
+// (buffer loads with an LDS destination: no registers, no vector-ALU work).
+// A load group is 8 rows of a tile, which lie in one cache block; its buffer
+// resource spans only those rows of that block, so rows past the last token
+// the workgroup reads are out of range and arrive as zeros.  Rows are
+// unpadded; the 16-byte chunks of row r are stored XOR-permuted by a function
+// of r so that the 16 rows one K fragment read touches, and the rows of a V
+// transposed read, fall on distinct LDS banks.
 //
 // Waves 0-3 and 4-7 (one of each per SIMD) alternate between two phases per
 // tile, one phase apart: the matrix phase (P.V of the previous tile, then the
 // scores of this tile) and the softmax phase (mask, maximum, exponentials,
 // fp16 rounding, rare rescale) on the vector ALUs.  While one wave of a SIMD
 // keeps the matrix core busy the other runs its softmax, and every phase ends
-// at a workgroup barrier.  Two K and two V tile buffers: the loads of K(m+1)
-// and V(m) are issued at the start of phase 2m and waited for before the
-// barrier that ends phase 2m+1, so each has two phases in flight.
-//
+// at a workgroup barrier.  Two K and two V tile buffers.  The waves in their
+// softmax phase issue the loads, each two row groups: K(m+1) by waves 4-7 at
+// the start of phase 2m, V(m) by waves 0-3 at the start of phase 2m+1, both
+// waited for before the barrier that ends phase 2m+1.
+
 // Column c masks every token past its own position; tiles that every column of
 // a wave sees whole skip the masking, and a wave skips tiles that lie wholly
 // past its queries.  One pass, no split: the workgroup walks tokens [0, last
@@ -106,18 +107,22 @@ constexpr int kRawBufferWord3 = 0x00020000;
 constexpr int kWaitVmem = 0x0F70;
 
 // Logical 16-byte chunk c of tile row r sits at chunk c ^ lds_swizzle<D>(r) of
-// the row.  Rows are 2D bytes; a 256-byte line of LDS spans all 64 banks and
-// holds 128/D rows.  For line q (of the 16 rows of a K fragment) the swizzle
-// 2 (q mod D/16) + (q div D/16 mod 2) takes 16/(128/D) distinct values, which
-// puts the 16 rows' chunk of one K read on 16 distinct 16-byte bank groups, and
-// keeps the two chunks of a 32-byte V read together while moving it to a
-// different 32-byte bank group for each of 8 consecutive rows.
+// the row.  D = 128 (256-byte rows, one per 64-bank line): XOR with r mod 16
+// puts the 16 rows of a K fragment read on 16 distinct chunks, and the four
+// rows of a transposed V read (two chunks each) on distinct chunk pairs; of
+// the permutations tried it read fastest in a transposed-read probe on gfx950.
+// D = 64 (128-byte rows, two per line): XOR with 2 ((r/2) mod 4) + (r/8 mod 2)
+// gives the 16 rows of a K read 16 distinct (half-line, chunk) slots and the 8
+// rows of a V read distinct 32-byte slots.  Either way the swizzle depends on
+// r mod 16 only.
 template <int D>
 __device__ __forceinline__ int lds_swizzle(int r) {
-  constexpr int RPL = 128 / D;
-  constexpr int H = D / 16;
-  const int q = r / RPL;
-  return 2 * (q % H) + ((q / H) & 1);
+  if constexpr (D == 128) {
+    return r & 15;
+  } else {
+    const int q = r >> 1;
+    return 2 * (q & 3) + ((q >> 2) & 1);
+  }
 }
 
 // Maximum over the four lanes of a column (lanes l, l ^ 16, l ^ 32, l ^ 48).
