@@ -294,8 +294,8 @@ int32_t pa_decode_plan_capacity(int32_t num_seqs, int32_t max_context_len, int32
  *                    partition past the launch's partition count are skipped;
  *                    only the timing depends on the order.
  *   waves_per_cu   : 0 = as many waves per compute unit as the kernel's
- *                    registers allow; n > 0 reserves LDS so that at most about
- *                    n waves share a compute unit (values below 4 act as 4).
+ *                    registers allow; n > 0 reserves LDS so that at most n
+ *                    waves share a compute unit (values below 4 act as 4).
  *   Kernels: one query head per wave on the vector ALUs; when query heads come in
  *   groups of 4 or more per KV head and q is fp16, the group runs on the matrix
  *   cores (scores and P.V as MFMA, P rounded to fp16), unless the kernel policy

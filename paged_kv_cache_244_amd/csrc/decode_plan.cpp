@@ -80,7 +80,7 @@ int32_t auto_partition(const int32_t* lens, int32_t n, int tiles, int cus, int32
 }
 
 // Residency limit (waves per CU) for a launch, measured on MI355X: the MFMA
-// kernel runs best with 7 (of the 8 its registers allow; 4, 5, 6 and 8 were
+// kernel runs best with 6 (of the 8 its registers allow; 5, 7 and 8 were
 // slower on the GQA and long-context mixes); the VALU kernel gains from 4
 // only when requests run in one pass and their lengths are skewed (all pieces
 // are resident at once otherwise, so the dispatcher cannot balance them),

@@ -39,7 +39,7 @@ inline size_t workspace_bytes_for(int32_t S, int32_t Hq, int32_t D, int64_t part
 
 // Residency limits the planner sets (waves per CU): the MFMA kernel always,
 // the VALU kernel for one-pass launches over skewed lengths.
-constexpr int kMfmaWavesPerCu = 7;
+constexpr int kMfmaWavesPerCu = 6;
 constexpr int kValuSkewedWavesPerCu = 4;
 
 // Prefix groups (pa_decode_grouped): requests whose leading blocks are the

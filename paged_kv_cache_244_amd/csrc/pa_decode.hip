@@ -29,7 +29,7 @@
 namespace pkv_decode {
 namespace {
 
-// Dynamic LDS that limits a launch of fn to about waves_per_cu one-wave
+// Dynamic LDS that limits a launch of fn to waves_per_cu one-wave
 // workgroups per compute unit (0 = no limit).  Cached per kernel and device.
 struct LdsInfo {
   const void* fn = nullptr;
@@ -70,9 +70,11 @@ hipError_t reserve_lds_bytes(const void* fn, int waves_per_cu, unsigned* dyn) {
     g_lds_cache.push_back(info);
   }
   const int w = waves_per_cu < 4 ? 4 : waves_per_cu;
-  int bytes = info.per_cu / w - info.static_bytes;
+  // The workgroup's LDS total is rounded down to whole KiB: allocation is
+  // granular, and a total that rounds up past per_cu / w admits one wave fewer
+  // (measured: 23,296 bytes for w = 7 held 6 waves per compute unit).
+  int bytes = ((info.per_cu / w) & ~1023) - info.static_bytes;
   if (bytes > info.per_block - info.static_bytes) bytes = info.per_block - info.static_bytes;
-  bytes &= ~255;
   *dyn = bytes > 0 ? static_cast<unsigned>(bytes) : 0u;
   return hipSuccess;
 }

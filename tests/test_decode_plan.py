@@ -134,7 +134,7 @@ def test_residency_limit_follows_the_kernel():
     mfma = _lib.plan(lens, 32, 8, 128, 16, _lib.PKV_F16)[1]
     valu_f32 = _lib.plan(lens, 32, 8, 128, 16, _lib.PKV_F32)[1]
     mha = _lib.plan(lens, 8, 8, 128, 16, _lib.PKV_F16)[1]
-    assert mfma["waves_per_cu"] == 7
+    assert mfma["waves_per_cu"] == 6
     assert valu_f32["waves_per_cu"] == 0 and mha["waves_per_cu"] == 0
     # VALU, one pass, skewed: longest > 1.5 x mean of the non-empty lengths.
     def valu(lens, part=0):
