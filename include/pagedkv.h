@@ -754,6 +754,37 @@ int pkv_event_elapsed_ms(void* start, void* stop, float* ms);
 int pkv_read_probe(const void* src, int64_t num_tiles, const int32_t* tile_order, uint32_t* sink,
                    int32_t workgroups, void* stream);
 
+/*
+ * pkv_check_tables — debug check of device-resident block tables, off the
+ * decode path.  [C] "Shared prefixes need ownership rules": reviewing a paged
+ * cache means following each physical block from allocation to reuse, and a
+ * table that names ids outside the pool, or a length its table cannot hold,
+ * is how a lifecycle mistake reaches the GPU.  The attention kernels skip such
+ * ids so that they cannot fault (see "Device-resident indices" above); this
+ * call reports them.
+ *
+ *   block_tables : DEVICE int32 [num_seqs][max_blocks_per_seq] (may be NULL
+ *                  when max_blocks_per_seq is 0).
+ *   context_lens : DEVICE int32 [num_seqs].
+ *   result       : DEVICE int32 [4], overwritten (no need to clear it):
+ *                  [0] table entries that cover a request's context
+ *                      (entries 0 .. ceil(len / block_size) - 1, at most
+ *                      max_blocks_per_seq of them) and are outside
+ *                      [0, num_blocks);
+ *                  [1] requests whose length is negative or needs more than
+ *                      max_blocks_per_seq blocks;
+ *                  [2], [3] the first offender in (request, entry) order: its
+ *                      request and entry index, entry -1 for a length error
+ *                      (a request's length error comes before its entries);
+ *                      both -1 when nothing is wrong.
+ * One workgroup, enqueued on `stream`; read `result` after the stream has
+ * reached it.  Errors: PKV_ERR_INVALID_ARG for negative sizes, block_size
+ * <= 0 or NULL pointers; PKV_ERR_HIP for a failed launch.
+ */
+int pkv_check_tables(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                     int32_t num_blocks, int32_t* result, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,12 @@ block ``b`` holds, for every KV head, ``block_size`` token slots.
   section "Eviction and reuse can move costs elsewhere": evicted state moved
   to another memory tier).
 
+* A table check (a debug aid, not part of attention): a request's table row
+  must hold its context, and every entry covering the context must name a
+  block of the pool (rsw.lol, section "Shared prefixes need ownership rules":
+  a block is followed from allocation to reuse, and a table naming blocks
+  outside the pool betrays a lifecycle mistake).
+
 Every function copies bytes; nothing is rounded or converted.
 """
 
@@ -80,3 +86,36 @@ def gather_logical(pool, table_row, num_tokens, block_size):
     t = np.arange(num_tokens)
     phys = np.asarray(table_row)[t // block_size]
     return pool[phys, :, t % block_size, :]
+
+
+def check_tables(tables, lens, block_size, num_blocks):
+    """Count the faults of block tables against a pool of ``num_blocks`` blocks.
+
+    ``tables[s]`` is request s's row of ``max_blocks`` entries and ``lens[s]`` its
+    context length.  Request s needs ceil(len / block_size) blocks; a negative
+    length, or one needing more blocks than the row holds, is a length fault.
+    The entries covering the context (the first min(needed, max_blocks) of the
+    row; none for a negative length) must lie in [0, num_blocks); each one that
+    does not is an id fault.  Returns (id faults, length faults, first request,
+    first entry), the first offender taken in (request, entry) order with a
+    request's length fault (entry -1) before its entries, or (-1, -1) if none.
+    """
+    tables = np.asarray(tables)
+    max_blocks = tables.shape[1] if tables.ndim == 2 else 0
+    bad_ids = bad_lens = 0
+    first = None
+    for s, length in enumerate(int(x) for x in lens):
+        needed = 0 if length < 0 else -(-length // block_size)
+        if length < 0 or needed > max_blocks:
+            bad_lens += 1
+            if first is None:
+                first = (s, -1)
+        for j in range(min(needed, max_blocks)):
+            block = int(tables[s, j])
+            if block < 0 or block >= num_blocks:
+                bad_ids += 1
+                if first is None:
+                    first = (s, j)
+    if first is None:
+        first = (-1, -1)
+    return bad_ids, bad_lens, first[0], first[1]

@@ -103,6 +103,8 @@ _SIGNATURES = {
     "pkv_event_destroy": (c_int32, [c_void_p]),
     "pkv_event_elapsed_ms": (c_int32, [c_void_p, c_void_p, POINTER(c_float)]),
     "pkv_read_probe": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_void_p]),
+    "pkv_check_tables": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                   c_void_p]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "pa_decode_set_kernel_policy": (c_int32, [c_int32]),
     "pa_decode_plan": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
@@ -446,6 +448,24 @@ def time_next_call(timer=None):
         lib().pkv_time_next_call(None, None)
     else:
         lib().pkv_time_next_call(timer.start, timer.stop)
+
+
+def check_tables(block_tables, context_lens, block_size, num_blocks, stream=None):
+    """Debug check of device tables (int32 [S, max_blocks]) and lengths (int32 [S]):
+    returns {"bad_ids", "bad_lengths", "first_request", "first_entry"} (pkv_check_tables);
+    waits for the stream."""
+    torch = _torch()
+    if block_tables.dim() != 2 or tuple(context_lens.shape) != (block_tables.shape[0],):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    s, mb = (int(x) for x in block_tables.shape)
+    result = torch.empty(4, dtype=torch.int32, device=block_tables.device)
+    st = _stream(stream)
+    _check(lib().pkv_check_tables(_dev(block_tables, torch.int32, "block_tables"), mb,
+                                  _dev(context_lens, torch.int32, "context_lens"), s,
+                                  int(block_size), int(num_blocks), c_void_p(result.data_ptr()), st))
+    (stream if stream is not None else torch.cuda.current_stream()).synchronize()
+    r = [int(x) for x in result.cpu()]
+    return {"bad_ids": r[0], "bad_lengths": r[1], "first_request": r[2], "first_entry": r[3]}
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):

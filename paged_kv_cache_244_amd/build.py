@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 HIP_SOURCES = ["pa_decode.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip", "pa_decode_fused.hip",
                "pa_decode_reduce.hip",
-               "pa_prefill.hip", "kv_cache_ops.hip", "read_probe.hip"]
+               "pa_prefill.hip", "kv_cache_ops.hip", "read_probe.hip", "check_tables.hip"]
 HOST_SOURCES = ["allocator.cpp", "decode_plan.cpp", "errors.cpp"]
 
 # Device code: gfx950 only; packed-fp32 instructions disabled (the compiler

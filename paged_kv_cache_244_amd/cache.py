@@ -570,6 +570,13 @@ class PagedKVCache:
                         stream=self.stream)
         return out
 
+    def check_tables(self, batch: "DecodeBatch") -> dict:
+        """Debug check of a batch's device tables and lengths against this pool
+        (pkv_check_tables): ids outside the pool, lengths the tables cannot hold,
+        and the first offender.  Waits for the cache's stream."""
+        return _lib.check_tables(batch.tables, batch.lens, self.block_size, self.num_blocks,
+                                 stream=self.stream)
+
     def attend(self, q, batch: "DecodeBatch", scale, partition_size=None, layer=0, out=None,
                timing=None):
         """Decode attention for ``batch`` with the schedule planned for it.

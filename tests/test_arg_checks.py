@@ -82,3 +82,14 @@ def test_event_helpers_refuse_null():
     import ctypes
     ms = ctypes.c_float()
     assert lib.pkv_event_elapsed_ms(None, None, ctypes.byref(ms)) == _lib.PKV_ERR_INVALID_ARG
+
+
+def test_check_tables_arguments_checked_on_the_host():
+    lib = _lib.lib()
+    result = 4096   # never dereferenced: every call below fails its argument checks
+    assert lib.pkv_check_tables(None, 4, None, 2, 16, 10, None, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_check_tables(None, 4, None, -1, 16, 10, result, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_check_tables(None, 4, None, 2, 0, 10, result, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_check_tables(None, -1, None, 2, 16, 10, result, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_check_tables(None, 4, 64, 2, 16, 10, result, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_check_tables(64, 4, None, 2, 16, -3, result, None) == _lib.PKV_ERR_INVALID_ARG

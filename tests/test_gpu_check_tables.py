@@ -1,0 +1,51 @@
+"""pkv_check_tables against the oracle's definition (oracle.cache.check_tables)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import cache as oc
+from paged_kv_cache_244_amd import _lib
+from paged_kv_cache_244_amd.cache import PagedKVCache
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _run(tables, lens, block_size, num_blocks):
+    t = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).to(DEV)
+    n = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to(DEV)
+    r = _lib.check_tables(t, n, block_size, num_blocks)
+    return r["bad_ids"], r["bad_lengths"], r["first_request"], r["first_entry"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_planted_faults_match_the_oracle(seed):
+    rng = np.random.default_rng(seed)
+    s, mb, bs, nb = int(rng.integers(1, 300)), int(rng.integers(1, 3000)), 16, 5000
+    tables = rng.integers(0, nb, size=(s, mb)).astype(np.int32)
+    lens = rng.integers(0, mb * bs + 1, size=s).astype(np.int32)
+    # Faults: ids outside the pool (covered or not), negative and oversized lengths.
+    cells = rng.integers(0, s * mb, size=int(rng.integers(0, 40)))
+    tables.reshape(-1)[cells] = rng.choice([-1, nb, nb + 7, -(2 ** 31)], size=cells.size)
+    rows = rng.integers(0, s, size=int(rng.integers(0, 4)))
+    lens[rows] = rng.choice([-1, mb * bs + 1, 2 ** 31 - 1], size=rows.size)
+    assert _run(tables, lens, bs, nb) == oc.check_tables(tables, lens, bs, nb)
+
+
+def test_clean_and_edge_cases():
+    t = np.array([[3, 4, 99], [0, -1, 7]], np.int32)
+    assert _run(t, [20, 16], 16, 10) == (0, 0, -1, -1)
+    assert _run(t, [-5, 49], 16, 10) == oc.check_tables(t, [-5, 49], 16, 10) == (1, 2, 0, -1)
+    assert _run(np.zeros((0, 4), np.int32), [], 16, 10) == (0, 0, -1, -1)
+    assert _run(np.zeros((3, 0), np.int32), [0, 0, 5], 16, 10) == (0, 1, 2, -1)
+
+
+def test_a_live_cache_batch_is_clean():
+    cache = PagedKVCache(num_blocks=256, num_kv_heads=2, head_dim=64, block_size=16, device=DEV)
+    seqs = [cache.new_sequence() for _ in range(5)]
+    cache.reserve_many(seqs, [1, 17, 40, 100, 300])
+    child = cache.fork(seqs[3])
+    _, batch = cache.decode_step(seqs + [child])
+    torch.cuda.synchronize()
+    assert cache.check_tables(batch) == {"bad_ids": 0, "bad_lengths": 0, "first_request": -1,
+                                         "first_entry": -1}
