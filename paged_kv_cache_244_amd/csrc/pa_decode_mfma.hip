@@ -21,8 +21,8 @@
 //
 // Softmax: S^T is scaled into log2 units and masked (tokens past the context
 // get -inf; their V rows are zeroed in LDS).  The reference max of head i is
-// kept identical in its four lane groups (max exchanged with two shuffles per
-// tile).  Rescaling is lazy: the reference max moves only when a tile's max
+// kept identical in its four lane groups (the tile max crosses them with two
+// lane swaps, v_permlane32_swap and v_permlane16_swap, no LDS round trip).  Rescaling is lazy: the reference max moves only when a tile's max
 // exceeds it by more than kSlack = 8 (log2 units), so P = 2^(s - m) stays at
 // most 2^8, where fp16 still holds it to 2^-11 relative; O and the denominator
 // are rescaled only in tiles where some head's reference moved (a wave-uniform

@@ -192,9 +192,7 @@ __device__ __forceinline__ void mfma_piece(const DecodeParams& p, PieceSlot slot
       float sr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sr[r] = token_ok(4 * grp + r) ? s[r] * p.scale_log2 : -INFINITY;
-      float mt = fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3]));
-      mt = fmaxf(mt, shfl_xor(mt, 16));
-      mt = fmaxf(mt, shfl_xor(mt, 32));
+      float mt = column_max(fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3])));
       // Lazy rescaling: the reference max of a head moves only when a score
       // exceeds it by more than kSlack (log2 units), so P stays below 2^kSlack
       // (exact enough in fp16) and the accumulators are rescaled rarely.

@@ -125,26 +125,6 @@ __device__ __forceinline__ int lds_swizzle(int r) {
   }
 }
 
-// Maximum over the four lanes of a column (lanes l, l ^ 16, l ^ 32, l ^ 48).
-// v_permlane32_swap exchanges the upper half of its first operand with the
-// lower half of its second, v_permlane16_swap the odd rows of the first with
-// the even rows of the second; with both operands holding v, every lane finds
-// its partner's value in one of the two results.  The second operand is an
-// identity DPP move of v rather than v itself: given two identical operands the
-// compiler takes the two results to be equal and drops one.
-__device__ __forceinline__ float swap_max(float v, bool halves) {
-  const int b = __builtin_bit_cast(int, v);
-  const int c = __builtin_amdgcn_mov_dpp(b, 0xE4, 0xF, 0xF, false);   // quad_perm [0,1,2,3]
-  const auto x = halves ? __builtin_amdgcn_permlane32_swap(b, c, false, false)
-                        : __builtin_amdgcn_permlane16_swap(b, c, false, false);
-  return fmaxf(v, fmaxf(__builtin_bit_cast(float, static_cast<int>(x[0])),
-                        __builtin_bit_cast(float, static_cast<int>(x[1]))));
-}
-
-__device__ __forceinline__ float column_max(float v) {
-  return swap_max(swap_max(v, true), false);
-}
-
 // Wave-wide load of n (1 or 2) x 1 KiB from src straight into LDS at dst: load
 // i writes bytes [i * 1024, (i + 1) * 1024) of dst, lane l's 16 bytes at offset
 // l * 16 of them, read from src + voff_i.  Offsets at or past `bytes` are out of
