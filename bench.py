@@ -65,7 +65,8 @@ def parse_args():
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the read-ceiling measurement that the decode line reports")
     ap.add_argument("--time-every", type=int, default=5,
-                    help="decode workloads: the decode launches of every n-th timed step take "
+                    help="decode, beams and prefill workloads: the attention launches of every "
+                         "n-th timed step take "
                          "kernel-level timing events (first kernel's start to last kernel's "
                          "end); timed launches cost the GPU several microseconds more, so "
                          "timing every step would slow the steps being measured")
@@ -567,8 +568,9 @@ def prefill_bench(args):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    every = max(1, args.time_every)
     for i in range(args.steps):
-        step(i)
+        step(i if i % every == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = list(ring.results().values())
@@ -591,6 +593,7 @@ def prefill_bench(args):
                    "block_size": w.block_size, "prompt_tokens": int(w.lengths.sum()),
                    "flops_per_step": int(flops)},
         "prefill_us": round(float(np.mean(ms)) * 1e3, 2),
+        "prefill_timing": f"kernel-level HIP events on every {every}th timed step",
         "prefill_us_p10_p90": [round(float(np.percentile(ms, 10)) * 1e3, 2),
                                round(float(np.percentile(ms, 90)) * 1e3, 2)],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
@@ -826,13 +829,18 @@ def churn_bench(args):
         step(t)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    every = max(1, args.time_every)
     for i in range(args.steps):
-        step(args.warmup + i, ring.take(i))
+        step(args.warmup + i, ring.take(i) if i % every == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = list(ring.results().values())
+    by_step = ring.results()
+    sampled = sorted(by_step)
+    ms = [by_step[i] for i in sampled]
     timed = slice(args.warmup, total_steps)
-    uniq = float(np.mean(unique[timed])) * tok_bytes
+    # The roofline: unique bytes of the steps whose decode was timed over their mean time.
+    uniq = float(np.mean([unique[args.warmup + i] for i in sampled])) * tok_bytes
+    uniq_all = float(np.mean(unique[timed])) * tok_bytes
     logi = float(np.mean(logical[timed])) * tok_bytes
     dec_s = float(np.mean(ms)) / 1e3
     achieved = uniq / dec_s / 1e9
@@ -850,8 +858,9 @@ def churn_bench(args):
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "layers": layers, "cow_pairs_per_step": round(float(np.mean(pairs[timed])), 2),
                    "prefix_groups": not args.no_prefix_groups,
-                   "unique_kv_bytes_per_step": int(uniq), "logical_kv_bytes_per_step": int(logi)},
+                   "unique_kv_bytes_per_step": int(uniq_all), "logical_kv_bytes_per_step": int(logi)},
         "decode_us": round(dec_s * 1e6, 2),
+        "decode_timing": f"kernel-level HIP events on every {every}th timed step",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "pa_decode"},

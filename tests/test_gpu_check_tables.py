@@ -49,3 +49,24 @@ def test_a_live_cache_batch_is_clean():
     torch.cuda.synchronize()
     assert cache.check_tables(batch) == {"bad_ids": 0, "bad_lengths": 0, "first_request": -1,
                                          "first_entry": -1}
+
+
+def test_tables_stay_clean_through_churn():
+    """Admissions, forks, cancellations and immediate block reuse: every step's
+    device tables name only blocks of the pool and hold every context."""
+    rng = np.random.default_rng(11)
+    cache = PagedKVCache(num_blocks=512, num_kv_heads=2, head_dim=64, block_size=8, device=DEV,
+                         num_q_heads=4)
+    live = []
+    for step in range(40):
+        if rng.random() < 0.4 or not live:
+            s = cache.new_sequence()
+            cache.reserve(s, int(rng.integers(1, 60)))
+            live.append(s)
+        if live and rng.random() < 0.3:
+            live.append(cache.fork(live[int(rng.integers(len(live)))]))
+        if len(live) > 2 and rng.random() < 0.3:
+            cache.free(live.pop(int(rng.integers(len(live)))))
+        _, batch = cache.decode_step(live)
+        r = cache.check_tables(batch)
+        assert r == {"bad_ids": 0, "bad_lengths": 0, "first_request": -1, "first_entry": -1}, (step, r)
