@@ -118,6 +118,17 @@ __device__ __forceinline__ float shfl(float v, int src_lane) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Which head tile (or KV head) workgroup column x serves.  The dispatcher deals
+// workgroups to the 8 XCDs in turn, and the grid's x extent n is the fastest
+// index, so when n is a multiple of 8 column 8q + k always lands on XCD k.  With
+// the identity, XCD k would read only the heads of residue k mod 8, whose tiles
+// sit at a fixed offset in every block; on MI355X the XCDs that drew the odd
+// residues then ran ~20% slower per tile (OPT-13B, 40 heads).  Rotating the
+// residue by q gives every XCD heads of every residue.  A bijection of [0, n).
+__device__ __forceinline__ int spread_column(int x, int n) {
+  return n % 8 == 0 ? (x & ~7) | (((x & 7) + (x >> 3)) & 7) : x;
+}
+
 // Maximum over the four lanes of a column (lanes l, l ^ 16, l ^ 32, l ^ 48).
 // v_permlane32_swap exchanges the upper half of its first operand with the
 // lower half of its second, v_permlane16_swap the odd rows of the first with

@@ -51,14 +51,14 @@ __device__ __forceinline__ void mfma_piece(const DecodeParams& p, PieceSlot slot
   int h0, kvh, rows, rep;
   const int32_t* members = nullptr;
   if constexpr (kGroups) {
-    kvh = slot.x;
+    kvh = spread_column(slot.x, p.num_kv_heads);
     h0 = kvh * p.group;
     members = p.groups + static_cast<int64_t>(seq) * kGroupStride + 1;
     const int cap = GT / p.group;            // members that fit in the tile
     const int n = members[-1];
     rows = (n < 1 ? 1 : (n > cap ? cap : n)) * p.group;
   } else {
-    h0 = slot.x * GT;
+    h0 = spread_column(slot.x, p.num_head_tiles) * GT;
     kvh = h0 / p.group;
     rows = GT;
   }

@@ -78,7 +78,7 @@ __device__ __forceinline__ void valu_piece(const DecodeParams& p, PieceSlot slot
   static_assert(NLD >= 1 && NLD * TPL == TT && TPB * TT == B, "tile shape");
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int tile = slot.x;
+  const int tile = spread_column(slot.x, p.num_head_tiles);
   int seq, part;
   if (!scheduled_piece_at(p, slot.y, slot.z, slot.gdy, seq, part, p.num_seqs)) return;
   const int h0 = tile * GT;
