@@ -96,6 +96,7 @@ constexpr float kSlack = 8.f;
 constexpr int kPrefillWaves = 8;   // waves per workgroup, sharing K/V tiles
 constexpr int kPrefillSets = 2;    // 16-column sets per wave, sharing LDS reads
 constexpr int kPrefillTile = 64;   // tokens per K/V tile
+constexpr int kPvAhead = 3;        // P.V steps whose V operands are read ahead
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4_t lds_short4;
@@ -296,47 +297,70 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
       float4_t s[NS][SUB];                     // scores of the tile last scored
       half4 pa[NS][SUB];                       // its probabilities after the softmax phase
 
+      // Operand reads run ahead of the matrix instructions that use them: the
+      // next step's fragments are issued before this step's MFMAs, and
+      // scheduling barriers keep the compiler from pulling the reads back, so a
+      // step never waits for the full LDS latency of its own reads.
       auto scores = [&](const unsigned char* kb) __attribute__((always_inline)) {
+        half8 kf[2][KSTEPS];                   // K fragments of two 16-token steps
+        auto ldk = [&](int sub, half8 (&dst)[KSTEPS]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int kk = 0; kk < KSTEPS; ++kk)
+            dst[kk] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(kb + sub * 16 * ROWB + koff[kk]));
+        };
+        ldk(0, kf[0]);
 #pragma unroll
         for (int sub = 0; sub < SUB; ++sub) {
+          if (sub + 1 < SUB) ldk(sub + 1, kf[(sub + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int cs = 0; cs < NS; ++cs) s[cs][sub] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < KSTEPS; ++kk) {
-            const half8 kv =
-                __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(kb + sub * 16 * ROWB + koff[kk]));
+          for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
             for (int cs = 0; cs < NS; ++cs)
-              s[cs][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, qb[cs][kk], s[cs][sub], 0, 0, 0);
-          }
+              s[cs][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[sub & 1][kk], qb[cs][kk], s[cs][sub], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       };
       // P.V over 32 tokens per MFMA (the double-rate 16x16x32 form): slots 0-3 of a
       // lane's operand are tokens 4*grp..4*grp+3 of one 16-token step, slots 4-7
       // the same rows of the next step, in A (probabilities) and B (transposed V)
       // alike, so the sum over k pairs each probability with its own V row.
+      // The V operands of step i (32 tokens, 16 dimensions: two transposed reads)
+      // are read kPvAhead steps before step i's MFMAs, into a ring of
+      // kPvAhead + 1 operands.
       auto pv = [&](const unsigned char* vb) __attribute__((always_inline)) {
+        constexpr int NSTEP = (SUB / 2) * DBLK;
+        constexpr int AHEAD = kPvAhead;
+        half8 vr[AHEAD + 1];
+        auto ldv = [&](int i, half8& dst) __attribute__((always_inline)) {
+          const unsigned char* src = vb + 2 * (i / DBLK) * 16 * ROWB + vof[i % DBLK];
+          const half4 v0 = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)src));
+          const half4 v1 =
+              __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src + 16 * ROWB)));
+          dst = half8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        };
 #pragma unroll
-        for (int sp = 0; sp < SUB; sp += 2) {
-          half8 pa8[NS];
+        for (int i = 0; i < AHEAD; ++i) ldv(i, vr[i]);
+        half8 pa8[NS];
 #pragma unroll
-          for (int cs = 0; cs < NS; ++cs) {
-            pa8[cs] = half8{pa[cs][sp][0], pa[cs][sp][1], pa[cs][sp][2], pa[cs][sp][3],
-                            pa[cs][sp + 1][0], pa[cs][sp + 1][1], pa[cs][sp + 1][2], pa[cs][sp + 1][3]};
-            den[cs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], ones, den[cs], 0, 0, 0);
+        for (int i = 0; i < NSTEP; ++i) {
+          if (i + AHEAD < NSTEP) ldv(i + AHEAD, vr[(i + AHEAD) % (AHEAD + 1)]);
+          __builtin_amdgcn_sched_barrier(0);
+          const int sp = 2 * (i / DBLK), db = i % DBLK;
+          if (db == 0) {
+#pragma unroll
+            for (int cs = 0; cs < NS; ++cs) {
+              pa8[cs] = half8{pa[cs][sp][0], pa[cs][sp][1], pa[cs][sp][2], pa[cs][sp][3],
+                              pa[cs][sp + 1][0], pa[cs][sp + 1][1], pa[cs][sp + 1][2], pa[cs][sp + 1][3]};
+              den[cs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], ones, den[cs], 0, 0, 0);
+            }
           }
 #pragma unroll
-          for (int db = 0; db < DBLK; ++db) {
-            const unsigned char* src = vb + sp * 16 * ROWB + vof[db];
-            const half4 v0 = __builtin_bit_cast(
-                half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)src));
-            const half4 v1 = __builtin_bit_cast(
-                half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src + 16 * ROWB)));
-            const half8 vf = half8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-            for (int cs = 0; cs < NS; ++cs)
-              o[cs][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], vf, o[cs][db], 0, 0, 0);
-          }
+          for (int cs = 0; cs < NS; ++cs)
+            o[cs][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], vr[i % (AHEAD + 1)], o[cs][db], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       };
       // Softmax phase of tile jt: per set one maximum over the tile, then the
