@@ -43,7 +43,8 @@
 // Waves 0-3 and 4-7 (one of each per SIMD) alternate between two phases per
 // tile, one phase apart: the matrix phase (P.V of the previous tile, then the
 // scores of this tile) and the softmax phase (mask, maximum, exponentials,
-// fp16 rounding, rare rescale) on the vector ALUs.  While one wave of a SIMD
+// rare rescale) on the vector ALUs; the probabilities are rounded to fp16 in
+// the matrix phase that uses them, which is the shorter one.  While one wave of a SIMD
 // keeps the matrix core busy the other runs its softmax, and every phase ends
 // at a workgroup barrier.  Two K and two V tile buffers.  The waves in their
 // softmax phase issue the loads, each two row groups: K(m+1) by waves 4-7 at
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
         vof[db] = vrow * ROWB + ((2 * db + ((li >> 1) & 1)) ^ vswz) * 16 + 8 * (li & 1);
 
       float4_t s[NS][SUB];                     // scores of the tile last scored
-      half4 pa[NS][SUB];                       // its probabilities after the softmax phase
+      float4_t pa[NS][SUB];                    // its probabilities after the softmax phase (fp32)
 
       // Operand reads run ahead of the matrix instructions that use them: the
       // next step's fragments are issued before this step's MFMAs, and
@@ -352,8 +353,10 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
           if (db == 0) {
 #pragma unroll
             for (int cs = 0; cs < NS; ++cs) {
-              pa8[cs] = half8{pa[cs][sp][0], pa[cs][sp][1], pa[cs][sp][2], pa[cs][sp][3],
-                              pa[cs][sp + 1][0], pa[cs][sp + 1][1], pa[cs][sp + 1][2], pa[cs][sp + 1][3]};
+              pa8[cs] = half8{static_cast<_Float16>(pa[cs][sp][0]), static_cast<_Float16>(pa[cs][sp][1]),
+                              static_cast<_Float16>(pa[cs][sp][2]), static_cast<_Float16>(pa[cs][sp][3]),
+                              static_cast<_Float16>(pa[cs][sp + 1][0]), static_cast<_Float16>(pa[cs][sp + 1][1]),
+                              static_cast<_Float16>(pa[cs][sp + 1][2]), static_cast<_Float16>(pa[cs][sp + 1][3])};
               den[cs] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa8[cs], ones, den[cs], 0, 0, 0);
             }
           }
@@ -395,8 +398,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
             float pr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(s[cs][sub][r], p.scale_log2, -m_new));
-            pa[cs][sub] = half4{static_cast<_Float16>(pr[0]), static_cast<_Float16>(pr[1]),
-                                static_cast<_Float16>(pr[2]), static_cast<_Float16>(pr[3])};
+            pa[cs][sub] = float4_t{pr[0], pr[1], pr[2], pr[3]};
           }
           if (__builtin_amdgcn_ballot_w64(moved)) {
             const float alpha = fast_exp2(m[cs] - m_new);
