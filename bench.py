@@ -64,6 +64,11 @@ def parse_args():
                     help="only measure the HBM read ceiling (pkv_read_probe) and exit")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip the read-ceiling measurement that the decode line reports")
+    ap.add_argument("--timeline", action="store_true",
+                    help="opt13b, gqa, long_context, tiny: run on the instrumented "
+                         "libpagedkv_timeline.so (python -m paged_kv_cache_244_amd.build "
+                         "--timeline), record the per-wave timeline of the decode launch of "
+                         "one step after the warmup and print its summary (no JSON line)")
     ap.add_argument("--time-every", type=int, default=5,
                     help="decode, beams and prefill workloads: the attention launches of every "
                          "n-th timed step take "
@@ -935,8 +940,107 @@ def write_copy_times(marks, sc, w):
     return res
 
 
+def summarize_timeline(recs, w):
+    """Text summary of per-wave timeline records (pkv_wave_timeline_read layout)."""
+    recs = recs[recs[:, 0] > 0]
+    if len(recs) == 0:
+        return "no waves recorded"
+    rt0, rt1 = recs[:, 0].astype(np.int64), recs[:, 1].astype(np.int64)
+    t0 = rt0.min()
+    st, en = (rt0 - t0) / 100.0, (rt1 - t0) / 100.0          # 100 MHz real-time counter
+    dur = np.maximum(en - st, 1e-3)
+    c1 = (recs[:, 2] & 0xFFFFFFFF).astype(float)
+    c2 = (recs[:, 2] >> 32).astype(float)
+    c3 = (recs[:, 3] & 0xFFFFFFFF).astype(float)
+    c4 = (recs[:, 3] >> 32).astype(float)
+    xcc = (recs[:, 4] & 0xFFFFFFFF).astype(np.int64) % 8
+    tiles = (recs[:, 4] >> 32).astype(np.int64)
+    tokens = (recs[:, 5] >> 40).astype(np.int64)
+    clk = float(np.median(c4 / dur))                        # shader-clock ticks per us
+    span = float(en.max())
+    kv_bytes_tok = 2 * w.head_dim * 2                       # K and V of one token, one KV head
+    nbytes = float(np.sum(tokens)) * kv_bytes_tok
+    lines = [f"waves {len(recs)}, launch span {span:.1f} us (first start to last end), "
+             f"{nbytes / 1e6:.1f} MB of K/V streamed ({nbytes / span / 1e6:.2f} TB/s over the span), "
+             f"shader clock ~{clk / 1e3:.2f} GHz",
+             f"start-up, mean (median) us: work-list entry {np.mean(c1) / clk:.2f} ({np.median(c1) / clk:.2f}), "
+             f"then table row, query and length {np.mean(c2 - c1) / clk:.2f} ({np.median(c2 - c1) / clk:.2f}), "
+             f"then first tile {np.mean(c3 - c2) / clk:.2f} ({np.median(c3 - c2) / clk:.2f})",
+             f"tiles per wave p10/p50/p90/max: {np.percentile(tiles, [10, 50, 90, 100]).astype(int).tolist()}; "
+             f"wave time p10/p50/p90 {np.round(np.percentile(dur, [10, 50, 90]), 1).tolist()} us",
+             "by start time (5 us bins): waves, then mean us to entry / inputs / first tile, and us per "
+             "further tile of waves with >= 8 tiles:"]
+    for lo in range(0, int(st.max()) + 5, 5):
+        m = (st >= lo) & (st < lo + 5)
+        if not m.any():
+            continue
+        mm = m & (tiles >= 8)
+        per = (float(np.mean((c4[mm] - c3[mm]) / clk / (tiles[mm] - 1))) if mm.any() else float("nan"))
+        lines.append(f"  {lo:4d}-{lo + 5:<4d} {int(m.sum()):5d}  {np.mean(c1[m]) / clk:5.2f} "
+                     f"{np.mean(c2[m] - c1[m]) / clk:5.2f} {np.mean(c3[m] - c2[m]) / clk:5.2f}  {per:5.2f}")
+    grid = np.arange(0.0, span + 2.0, 2.0)
+    lines.append("resident waves every 2 us: " + " ".join(str(int(((st <= g) & (en > g)).sum())) for g in grid))
+    lines.append("by XCD: waves, wave time (ms), MB streamed, us per tile of waves with >= 8 tiles, last end (us):")
+    for x in range(8):
+        m = xcc == x
+        if not m.any():
+            continue
+        mm = m & (tiles >= 8)
+        per = float(np.mean((c4[mm] - c3[mm]) / clk / (tiles[mm] - 1))) if mm.any() else float("nan")
+        lines.append(f"  XCD {x}: {int(m.sum()):5d} {float(np.sum(dur[m])) / 1e3:7.2f} "
+                     f"{float(np.sum(tokens[m])) * kv_bytes_tok / 1e6:7.1f} {per:5.2f} {float(en[m].max()):7.1f}")
+    return "\n".join(lines)
+
+
+def wave_timeline(args):
+    """--timeline: the per-wave timeline of one decode launch, recorded by the
+    instrumented library after args.warmup steps; prints a text summary."""
+    import torch
+
+    from paged_kv_cache_244_amd import _lib, workloads
+
+    if args.workload not in ("opt13b", "gqa", "long_context", "tiny"):
+        raise SystemExit("--timeline records the decode workloads opt13b, gqa, long_context, tiny")
+    if not os.path.exists(_lib.TIMELINE_LIB_PATH):
+        raise SystemExit(f"{_lib.TIMELINE_LIB_PATH} is missing: "
+                         "python -m paged_kv_cache_244_amd.build --timeline")
+    _lib.LIB_PATH = _lib.TIMELINE_LIB_PATH                 # before the library is first loaded
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    _lib.set_kernel_policy(_lib.PKV_POLICY_VALU if args.kernel_policy == "valu"
+                           else _lib.PKV_POLICY_DEFAULT)
+    w = {"long_context": lambda: workloads.long_context(16),
+         "tiny": workloads.tiny}.get(args.workload, workloads.WORKLOADS.get(args.workload))()
+    total = args.warmup + 1
+    sc = decode_scenario(w, total, dev, args.replicas)
+    qd = _lib.PKV_F16 if w.q_dtype == np.float16 else _lib.PKV_F32
+    partition = (_lib.plan(sc.lengths + total, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                           w.block_size, qd)[1]["partition_size"]
+                 if args.partition == "auto" else int(args.partition))
+    sc.workspace(partition, int(sc.lengths.max()) + total)
+    plans = []
+    for t in range(args.warmup):
+        sc.step(t, partition, None, plans)
+    torch.cuda.synchronize()
+    kinds = (_lib.PKV_TIMELINE_VALU, _lib.PKV_TIMELINE_MFMA)
+    for k in kinds:
+        _lib.wave_timeline_read(k, clear=True)
+    sc.step(args.warmup, partition, None, plans)
+    torch.cuda.synchronize()
+    recs = np.concatenate([_lib.wave_timeline_read(k) for k in kinds])
+    plan = {k: v for k, v in plans[-1].items() if not hasattr(v, "__len__")}
+    print(f"per-wave timeline: workload {args.workload}, step {args.warmup} after {args.warmup} "
+          f"warmup steps, plan {plan}")
+    print(summarize_timeline(recs, w), flush=True)
+
+
 def main():
     args = parse_args()
+    if args.timeline:
+        wave_timeline(args)
+        return
     if args.copy_probe:
         copy_probe()
         return

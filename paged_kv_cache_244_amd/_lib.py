@@ -103,6 +103,7 @@ _SIGNATURES = {
     "pkv_event_destroy": (c_int32, [c_void_p]),
     "pkv_event_elapsed_ms": (c_int32, [c_void_p, c_void_p, POINTER(c_float)]),
     "pkv_read_probe": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p, c_int32, c_void_p]),
+    "pkv_wave_timeline_read": (c_int32, [c_int32, c_void_p, c_size_t, c_int32]),
     "pkv_check_tables": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32, c_void_p,
                                    c_void_p]),
     "pa_decode_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
@@ -466,6 +467,24 @@ def check_tables(block_tables, context_lens, block_size, num_blocks, stream=None
     (stream if stream is not None else torch.cuda.current_stream()).synchronize()
     r = [int(x) for x in result.cpu()]
     return {"bad_ids": r[0], "bad_lengths": r[1], "first_request": r[2], "first_entry": r[3]}
+
+
+PKV_TIMELINE_VALU = 0
+PKV_TIMELINE_MFMA = 1
+PKV_TIMELINE_RECORDS = 16384
+PKV_TIMELINE_WORDS = 6
+TIMELINE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv_timeline.so")
+
+
+def wave_timeline_read(kernel, clear=True):
+    """Per-wave records of the decode kernel family ``kernel`` (PKV_TIMELINE_VALU or
+    PKV_TIMELINE_MFMA) as uint64 [PKV_TIMELINE_RECORDS, PKV_TIMELINE_WORDS]
+    (pkv_wave_timeline_read; only the instrumented library records any)."""
+    import numpy as np
+    buf = np.zeros((PKV_TIMELINE_RECORDS, PKV_TIMELINE_WORDS), dtype=np.uint64)
+    _check(lib().pkv_wave_timeline_read(int(kernel), c_void_p(buf.ctypes.data), buf.nbytes,
+                                        1 if clear else 0))
+    return buf
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):

@@ -1,7 +1,9 @@
 """Build libpagedkv.so (HIP kernels for gfx950 + host allocator) in-tree.
 
-Usage: ``python -m paged_kv_cache_244_amd.build`` or ``build()`` from Python.
-Every call recompiles.  Only gfx950 code objects are produced.
+Usage: ``python -m paged_kv_cache_244_amd.build`` or ``build()`` from Python;
+``--timeline`` (``build(timeline=True)``) builds the instrumented
+libpagedkv_timeline.so instead.  Every call recompiles.  Only gfx950 code
+objects are produced.
 """
 
 from __future__ import annotations
@@ -17,6 +19,9 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+# The same sources with the decode kernels' per-wave timeline compiled in
+# (-DPKV_WAVE_TIMELINE): a measurement tool, never loaded by the product path.
+TIMELINE_LIB_PATH = os.path.join(PKG_DIR, "libpagedkv_timeline.so")
 
 HIP_SOURCES = ["pa_decode.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip", "pa_decode_fused.hip",
                "pa_decode_reduce.hip",
@@ -49,16 +54,18 @@ def _run(cmd):
     subprocess.run(cmd, check=True)
 
 
-def build(jobs: int = 4) -> str:
-    """Compile every source to an object, then link the shared library."""
-    obj_dir = os.path.join(ROOT, "_build")
+def build(jobs: int = 4, timeline: bool = False) -> str:
+    """Compile every source to an object, then link the shared library
+    (``timeline``: the instrumented libpagedkv_timeline.so instead)."""
+    obj_dir = os.path.join(ROOT, "_build", "timeline") if timeline else os.path.join(ROOT, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     cc = hipcc()
+    extra = ["-DPKV_WAVE_TIMELINE"] if timeline else []
     cmds, objs = [], []
     for src in HIP_SOURCES:
         obj = os.path.join(obj_dir, src + ".o")
         cmds.append([cc, "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj] + DEVICE_FLAGS + COMMON_FLAGS
-                    + SOURCE_FLAGS.get(src, []))
+                    + SOURCE_FLAGS.get(src, []) + extra)
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(obj_dir, src + ".o")
@@ -74,11 +81,13 @@ def build(jobs: int = 4) -> str:
     for p in procs:
         if p.wait() != 0:
             raise RuntimeError("compilation failed")
-    tmp = LIB_PATH + ".tmp"
+    out = TIMELINE_LIB_PATH if timeline else LIB_PATH
+    tmp = out + ".tmp"
     _run([cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs)
-    os.replace(tmp, LIB_PATH)
-    build_c_abi_test(cc)
-    return LIB_PATH
+    os.replace(tmp, out)
+    if not timeline:
+        build_c_abi_test(cc)
+    return out
 
 
 C_ABI_TEST_SRC = os.path.join(ROOT, "tests", "c_abi_decode.cpp")
@@ -98,5 +107,5 @@ def build_c_abi_test(cc: str) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(timeline="--timeline" in sys.argv[1:])
     sys.exit(0)

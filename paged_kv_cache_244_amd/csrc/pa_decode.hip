@@ -290,6 +290,21 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
 
 }  // namespace
 
+extern "C" int pkv_wave_timeline_read(int32_t kernel, void* dst, size_t bytes, int32_t clear) {
+  static_assert(PKV_TIMELINE_RECORDS == kTimelineWaves && PKV_TIMELINE_WORDS == kTimelineWords,
+                "timeline record layout");
+  if (kernel != PKV_TIMELINE_VALU && kernel != PKV_TIMELINE_MFMA)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_wave_timeline_read: unknown kernel %d", kernel);
+  if (!dst && bytes > 0) return fail(PKV_ERR_INVALID_ARG, "pkv_wave_timeline_read: NULL dst");
+  const hipError_t e = kernel == PKV_TIMELINE_VALU ? wave_timeline_read_valu(dst, bytes, clear != 0)
+                                                   : wave_timeline_read_mfma(dst, bytes, clear != 0);
+  if (e == hipErrorNotSupported)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "pkv_wave_timeline_read: this library records no timeline (build --timeline)");
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_wave_timeline_read: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 extern "C" int pa_decode(float* out, const void* q, int32_t q_dtype, const void* k_cache,
                          const void* v_cache, int32_t num_blocks, const int32_t* block_tables,
                          int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -198,6 +198,89 @@ __device__ __forceinline__ int partials_of(int nparts, int shared, int len) {
   return nparts + (shared > 0 && len > shared ? 1 : 0);
 }
 
+// Per-wave timeline of the decode kernels, for measurement only.  It is compiled
+// in with -DPKV_WAVE_TIMELINE (the instrumented library libpagedkv_timeline.so,
+// `python -m paged_kv_cache_244_amd.build --timeline`); in the product library
+// every member below is empty and the kernels are unchanged.  Each wave that
+// streams a piece writes one record of six 64-bit words into the array of its
+// translation unit, at its position in the launch (work-list entry * grid x +
+// column); pkv_wave_timeline_read copies the array to the host:
+//   0, 1  real-time counter (100 MHz) at the wave's start and at its end
+//   2     shader-clock cycles from the start to the work-list entry (bits 0-31)
+//         and to the table row, query and length (bits 32-63)
+//   3     cycles to the first tile consumed (bits 0-31) and to the end (32-63)
+//   4     XCC id (bits 0-31) and tiles of the piece (bits 32-63)
+//   5     request or group (bits 0-19), partition (20-39), tokens (40-63)
+// The two start-up marks wait for every load in flight, so the instrumented
+// start-up overlaps its loads at most as much as the product's.
+constexpr int kTimelineWaves = 16384;
+constexpr int kTimelineWords = 6;
+#ifdef PKV_WAVE_TIMELINE
+static __device__ uint64_t g_wave_timeline[kTimelineWaves * kTimelineWords];
+
+struct WaveTimeline {
+  uint64_t rt0, c0, c1 = 0, c2 = 0, c3 = 0;
+  __device__ __forceinline__ WaveTimeline()
+      : rt0(__builtin_amdgcn_s_memrealtime()), c0(__builtin_amdgcn_s_memtime()) {}
+  __device__ __forceinline__ void entry() {
+    __builtin_amdgcn_s_waitcnt(0);
+    c1 = __builtin_amdgcn_s_memtime();
+  }
+  __device__ __forceinline__ void inputs() {
+    __builtin_amdgcn_s_waitcnt(0);
+    c2 = __builtin_amdgcn_s_memtime();
+  }
+  __device__ __forceinline__ void first_tile() {
+    if (c3 == 0) c3 = __builtin_amdgcn_s_memtime();
+  }
+  __device__ __forceinline__ void finish(PieceSlot slot, int ntiles, int seq, int part,
+                                         int tokens) {
+    const uint64_t c4 = __builtin_amdgcn_s_memtime();
+    const uint64_t rt1 = __builtin_amdgcn_s_memrealtime();
+    const unsigned xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID, 32 bits
+    const unsigned idx = (slot.y + slot.z * slot.gdy) * gridDim.x + static_cast<unsigned>(slot.x);
+    if ((threadIdx.x & (kWave - 1)) != 0 || idx >= static_cast<unsigned>(kTimelineWaves)) return;
+    auto since = [&](uint64_t c) { return c ? (c - c0) & 0xFFFFFFFFull : 0ull; };
+    uint64_t* r = g_wave_timeline + static_cast<uint64_t>(idx) * kTimelineWords;
+    r[0] = rt0;
+    r[1] = rt1;
+    r[2] = since(c1) | (since(c2) << 32);
+    r[3] = since(c3) | (since(c4) << 32);
+    r[4] = static_cast<uint64_t>(xcc) | (static_cast<uint64_t>(ntiles) << 32);
+    r[5] = (static_cast<uint64_t>(seq) & 0xFFFFF) | ((static_cast<uint64_t>(part) & 0xFFFFF) << 20) |
+           (static_cast<uint64_t>(tokens) << 40);
+  }
+};
+
+// This translation unit's records to the host (at most the array's size), then,
+// with `clear`, zeroed.  Synchronous.
+static inline hipError_t wave_timeline_copy(void* dst, size_t bytes, bool clear) {
+  const size_t cap = sizeof(g_wave_timeline);
+  hipError_t e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_wave_timeline), bytes < cap ? bytes : cap, 0,
+                                     hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !clear) return e;
+  void* addr = nullptr;
+  e = hipGetSymbolAddress(&addr, HIP_SYMBOL(g_wave_timeline));
+  if (e != hipSuccess) return e;
+  return hipMemset(addr, 0, cap);
+}
+#else
+struct WaveTimeline {
+  __device__ __forceinline__ void entry() {}
+  __device__ __forceinline__ void inputs() {}
+  __device__ __forceinline__ void first_tile() {}
+  __device__ __forceinline__ void finish(PieceSlot, int, int, int, int) {}
+};
+
+static inline hipError_t wave_timeline_copy(void*, size_t, bool) { return hipErrorNotSupported; }
+#endif
+
+// Host side of the timeline: copy the records of the VALU (pa_decode_valu.hip)
+// or MFMA (pa_decode_mfma.hip) translation unit to dst and, with `clear`, zero
+// them.  hipErrorNotSupported in the product library.
+hipError_t wave_timeline_read_valu(void* dst, size_t bytes, bool clear);
+hipError_t wave_timeline_read_mfma(void* dst, size_t bytes, bool clear);
+
 // MFMA head-group kernel, defined in pa_decode_mfma.hip: 16-token tiles, scores
 // on v_mfma_f32_16x16x32_f16 and P.V on v_mfma_f32_16x16x16_f16, for head
 // groups of GT in {4, 8, 16} query heads and fp16 queries.

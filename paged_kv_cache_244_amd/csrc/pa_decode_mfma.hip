@@ -102,4 +102,8 @@ KernelFn pick_mfma_kernel(int head_dim, int block_size, int gt, bool contiguous)
   return nullptr;
 }
 
+hipError_t wave_timeline_read_mfma(void* dst, size_t bytes, bool clear) {
+  return wave_timeline_copy(dst, bytes, clear);
+}
+
 }  // namespace pkv_decode

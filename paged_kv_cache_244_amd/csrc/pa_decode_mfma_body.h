@@ -39,6 +39,7 @@ __device__ __forceinline__ void mfma_piece(const DecodeParams& p, PieceSlot slot
   static_assert(GT == 4 || GT == 8 || GT == 16, "head group");
   __shared__ __align__(16) unsigned char vlds[DEPTH][TT * ROWB];
 
+  WaveTimeline tl;                           // empty unless built with PKV_WAVE_TIMELINE
   const int lane = threadIdx.x;
   const int grp = lane >> 4;                 // lane group: tokens 4*grp..4*grp+3 of a tile
   const int li = lane & 15;                  // head index (scores) / column (outputs)
@@ -46,6 +47,7 @@ __device__ __forceinline__ void mfma_piece(const DecodeParams& p, PieceSlot slot
   if (!scheduled_piece_at(p, slot.y, slot.z, slot.gdy, seq, part,
                           kGroups ? p.num_groups : p.num_seqs))
     return;
+  tl.entry();
   // Tile row r: query head h0 + r of request seq; with groups, query head
   // h0 + r % G of member r / G.  Rows at or past `rows` are unused.
   int h0, kvh, rows, rep;
@@ -93,6 +95,7 @@ __device__ __forceinline__ void mfma_piece(const DecodeParams& p, PieceSlot slot
   }
   const int len = clamped_len(p, rep);
   const int shared = shared_len(p, rep);
+  tl.inputs();
   const int t_begin = part * p.part_tokens;
   if (t_begin >= len) {
     if (!kGroups && part == 0) {              // empty context: defined as zeros
@@ -169,6 +172,7 @@ __device__ __forceinline__ void mfma_piece(const DecodeParams& p, PieceSlot slot
     };
 
     auto consume = [&](uint4 (&kr)[KSTEPS], uint4 (&vr)[VLD], int jj, unsigned char* vl) {
+      tl.first_tile();
       const int tok0 = t_begin + (tile0 + jj) * TT;
       auto token_ok = [&](int r) {
         int raw, row;
@@ -252,6 +256,7 @@ __device__ __forceinline__ void mfma_piece(const DecodeParams& p, PieceSlot slot
       if (j + u + DEPTH < cn) consume(kbuf[u], vbuf[u], j + u + DEPTH, vlds[u]);
   }
 
+  tl.finish(slot, ntiles - skip_tiles, seq, part, t_end - t_first);
   // Denominator of head li: the four lane groups' shares.
   float l = lsum + shfl_xor(lsum, 16);
   l = l + shfl_xor(l, 32);

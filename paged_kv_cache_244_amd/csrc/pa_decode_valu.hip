@@ -94,4 +94,8 @@ KernelFn pick_valu_kernel(int head_dim, int block_size, int gt, bool qf32, bool 
   return nullptr;
 }
 
+hipError_t wave_timeline_read_valu(void* dst, size_t bytes, bool clear) {
+  return wave_timeline_copy(dst, bytes, clear);
+}
+
 }  // namespace pkv_decode

@@ -77,10 +77,12 @@ __device__ __forceinline__ void valu_piece(const DecodeParams& p, PieceSlot slot
   constexpr int CHUNKS = B * D / 8;        // 16-byte chunks per (block, KV head)
   static_assert(NLD >= 1 && NLD * TPL == TT && TPB * TT == B, "tile shape");
 
+  WaveTimeline tl;                         // empty unless built with PKV_WAVE_TIMELINE
   const int lane = threadIdx.x & (kWave - 1);
   const int tile = spread_column(slot.x, p.num_head_tiles);
   int seq, part;
   if (!scheduled_piece_at(p, slot.y, slot.z, slot.gdy, seq, part, p.num_seqs)) return;
+  tl.entry();
   const int h0 = tile * GT;
   const int kvh = h0 / p.group;
   const int row = lane / LPT;
@@ -96,6 +98,7 @@ __device__ __forceinline__ void valu_piece(const DecodeParams& p, PieceSlot slot
   qr.load(p.q, (static_cast<int64_t>(seq) * p.num_q_heads + h0) * D + dchunk * 8, D);
   const int len = clamped_len(p, seq);
   const int shared = shared_len(p, seq);
+  tl.inputs();
   const int t_begin = part * p.part_tokens;
   if (t_begin >= len) {
     if (part == 0 && row == 0) {             // empty context: defined as zeros
@@ -168,6 +171,7 @@ __device__ __forceinline__ void valu_piece(const DecodeParams& p, PieceSlot slot
     };
 
     auto consume = [&](uint4 (&kr)[NLD], uint4 (&vr)[NLD], int jj) {
+      tl.first_tile();
       const int ph = __builtin_amdgcn_readlane(staged, jj / TPB);
       const bool blk_ok = static_cast<unsigned>(ph) < static_cast<unsigned>(p.num_blocks);
       const int tok0 = t_begin + (tile0 + jj) * TT + row;
@@ -246,6 +250,7 @@ __device__ __forceinline__ void valu_piece(const DecodeParams& p, PieceSlot slot
     }
   }
 
+  tl.finish(slot, ntiles - skip_tiles, seq, part, t_end - t_begin - skip_tiles * TT);
   if (row != 0) return;
   if (np_eff == 1) {
 #pragma unroll

@@ -1,4 +1,5 @@
-"""kv_swap_blocks, pkv_upload_write and pkv_read_probe argument checks that need no GPU.
+"""kv_swap_blocks, pkv_upload_write, pkv_read_probe, pkv_check_tables and
+pkv_wave_timeline_read argument checks that need no GPU.
 
 Every call here is refused (or is a no-op) before the library touches the HIP
 runtime: bad sizes, geometry that is not built, nothing to copy, NULL pools and
@@ -7,6 +8,8 @@ too many pairs.  The copies themselves are checked on the GPU
 """
 
 import ctypes
+
+import numpy as np
 
 from paged_kv_cache_244_amd import _lib
 
@@ -93,3 +96,16 @@ def test_check_tables_arguments_checked_on_the_host():
     assert lib.pkv_check_tables(None, -1, None, 2, 16, 10, result, None) == _lib.PKV_ERR_INVALID_ARG
     assert lib.pkv_check_tables(None, 4, 64, 2, 16, 10, result, None) == _lib.PKV_ERR_INVALID_ARG
     assert lib.pkv_check_tables(64, 4, None, 2, 16, -3, result, None) == _lib.PKV_ERR_INVALID_ARG
+
+
+def test_wave_timeline_reader_in_the_product_library():
+    """libpagedkv.so records no per-wave timeline: the reader says so without a
+    device call; bad arguments are refused first."""
+    lib = _lib.lib()
+    buf = np.zeros(6, dtype=np.uint64)
+    ptr = buf.ctypes.data
+    assert lib.pkv_wave_timeline_read(2, ptr, buf.nbytes, 0) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_wave_timeline_read(_lib.PKV_TIMELINE_VALU, None, 48, 0) == _lib.PKV_ERR_INVALID_ARG
+    for kind in (_lib.PKV_TIMELINE_VALU, _lib.PKV_TIMELINE_MFMA):
+        assert lib.pkv_wave_timeline_read(kind, ptr, buf.nbytes, 1) == _lib.PKV_ERR_UNSUPPORTED
+        assert b"timeline" in lib.pkv_last_error()
