@@ -992,6 +992,61 @@ def summarize_timeline(recs, w):
     return "\n".join(lines)
 
 
+PAIR_STRETCHES = ("from the last pair (its end barrier)", "first-half load issue", "first-half work",
+                  "mid-pair barrier", "second-half load issue", "second-half work", "load wait")
+
+
+def prefill_timeline(args, dev):
+    """--timeline for prefill: args.warmup prefill steps, then one recorded launch;
+    prints each wave's mean shader-clock cycles per tile pair by stretch."""
+    import torch
+
+    from paged_kv_cache_244_amd import _lib, workloads
+    from paged_kv_cache_244_amd.cache import PagedKVCache
+
+    w = workloads.prefill()
+    cache = PagedKVCache(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size,
+                         initial_order=w.initial_order, device=dev, poison=False,
+                         num_q_heads=w.num_q_heads)
+    kd, vd, qd = _to_dev([w.k_tokens, w.v_tokens, w.q], dev)
+    out = torch.empty(qd.shape, dtype=torch.float32, device=dev)
+    lens = [int(L) for L in w.lengths]
+
+    def step():
+        seqs = [cache.new_sequence() for _ in lens]
+        cache.write(cache.reserve_many(seqs, lens), kd, vd)
+        cache.prefill(qd, seqs, lens, w.scale, out=out)
+        for sq in seqs:
+            cache.free(sq)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.wave_timeline_read(_lib.PKV_TIMELINE_PREFILL, clear=True)
+    step()
+    torch.cuda.synchronize()
+    recs = _lib.wave_timeline_read(_lib.PKV_TIMELINE_PREFILL)
+    recs = recs[(recs[:, 3] >> 32) > 0]                      # waves that summed some pairs
+    print(f"tile-pair timeline: workload prefill, launch after {args.warmup} warmup steps; "
+          f"{len(recs)} waves of {len(recs) // 8} full workgroups of head tile 0 with tile pairs 8-39")
+    if len(recs) == 0:
+        return
+    halves = np.stack([recs[:, 0] & 0xFFFFFFFF, recs[:, 0] >> 32, recs[:, 1] & 0xFFFFFFFF,
+                       recs[:, 1] >> 32, recs[:, 2] & 0xFFFFFFFF, recs[:, 2] >> 32,
+                       recs[:, 3] & 0xFFFFFFFF], axis=1).astype(float)
+    per_pair = halves / (recs[:, 3] >> 32).astype(float)[:, None]
+    wave = (recs[:, 4] >> 32).astype(int)
+    print("mean shader-clock cycles per tile pair, by wave (waves 0-3: matrix phase first; "
+          "4-7: softmax and K loads first):")
+    print("  wave  " + " | ".join(PAIR_STRETCHES) + " | pair")
+    for wv in range(8):
+        m = wave == wv
+        if m.any():
+            v = per_pair[m].mean(axis=0)
+            print(f"  {wv}     " + "  ".join(f"{x:6.0f}" for x in v) + f"  {v.sum():6.0f}")
+    print(f"pair: {per_pair.sum(axis=1).mean():.0f} cycles on average over the recorded waves", flush=True)
+
+
 def wave_timeline(args):
     """--timeline: the per-wave timeline of one decode launch, recorded by the
     instrumented library after args.warmup steps; prints a text summary."""
@@ -999,8 +1054,9 @@ def wave_timeline(args):
 
     from paged_kv_cache_244_amd import _lib, workloads
 
-    if args.workload not in ("opt13b", "gqa", "long_context", "tiny"):
-        raise SystemExit("--timeline records the decode workloads opt13b, gqa, long_context, tiny")
+    if args.workload not in ("opt13b", "gqa", "long_context", "tiny", "prefill"):
+        raise SystemExit("--timeline records the decode workloads opt13b, gqa, long_context, "
+                         "tiny and the prefill workload")
     if not os.path.exists(_lib.TIMELINE_LIB_PATH):
         raise SystemExit(f"{_lib.TIMELINE_LIB_PATH} is missing: "
                          "python -m paged_kv_cache_244_amd.build --timeline")
@@ -1009,6 +1065,9 @@ def wave_timeline(args):
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "prefill":
+        prefill_timeline(args, dev)
+        return
     _lib.set_kernel_policy(_lib.PKV_POLICY_VALU if args.kernel_policy == "valu"
                            else _lib.PKV_POLICY_DEFAULT)
     w = {"long_context": lambda: workloads.long_context(16),

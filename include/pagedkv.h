@@ -755,8 +755,8 @@ int pkv_read_probe(const void* src, int64_t num_tiles, const int32_t* tile_order
                    int32_t workgroups, void* stream);
 
 /*
- * pkv_wave_timeline_read — per-wave timeline of the decode kernels, a
- * measurement aid behind the decode rooflines: [B] "Why the KV cache is the
+ * pkv_wave_timeline_read — per-wave timeline of the decode kernels (and the
+ * tile-pair timeline of pa_prefill), a measurement aid behind the rooflines: [B] "Why the KV cache is the
  * thing that limits your batch" makes decode a matter of streaming every
  * cached byte, and this shows where a launch does not stream (start-up chains,
  * turnover, drain).  Only the instrumented library libpagedkv_timeline.so
@@ -773,8 +773,16 @@ int pkv_read_probe(const void* src, int64_t num_tiles, const int32_t* tile_order
  * the start to its work-list entry (bits 0-31) and to its table row, query and
  * length (32-63); [3] cycles to its first tile (0-31) and to its end (32-63);
  * [4] XCC id (0-31) and tiles streamed (32-63); [5] request or group (0-19),
- * partition (20-39) and tokens streamed (40-63).  Records of positions no
- * launch wrote since the last clear are zero.
+ * partition (20-39) and tokens streamed (40-63).  PKV_TIMELINE_PREFILL reads
+ * pa_prefill's tile-pair records instead: each wave of a full workgroup of
+ * head tile 0, at work item * 8 + wave, sums over tile pairs 8-39 the
+ * shader-clock cycles of seven stretches of a pair (0 from the previous
+ * pair's end, including the barrier that ended it; 1 first-half load issue;
+ * 2 first-half work; 3 the mid-pair barrier; 4 second-half load issue;
+ * 5 second-half work; 6 the wait for its loads): stretches 0-5 as 32-bit
+ * halves of words [0]-[2], stretch 6 and the number of pairs in [3], work
+ * item and wave in [4], XCC id in [5].  Records of positions no launch wrote
+ * since the last clear are zero.
  *
  *   dst   : HOST buffer of `bytes` bytes (at most
  *           PKV_TIMELINE_RECORDS * PKV_TIMELINE_WORDS * 8 are copied).
@@ -785,6 +793,7 @@ int pkv_read_probe(const void* src, int64_t num_tiles, const int32_t* tile_order
  */
 #define PKV_TIMELINE_VALU 0
 #define PKV_TIMELINE_MFMA 1
+#define PKV_TIMELINE_PREFILL 2
 #define PKV_TIMELINE_RECORDS 16384
 #define PKV_TIMELINE_WORDS 6
 int pkv_wave_timeline_read(int32_t kernel, void* dst, size_t bytes, int32_t clear);

@@ -471,14 +471,15 @@ def check_tables(block_tables, context_lens, block_size, num_blocks, stream=None
 
 PKV_TIMELINE_VALU = 0
 PKV_TIMELINE_MFMA = 1
+PKV_TIMELINE_PREFILL = 2
 PKV_TIMELINE_RECORDS = 16384
 PKV_TIMELINE_WORDS = 6
 TIMELINE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv_timeline.so")
 
 
 def wave_timeline_read(kernel, clear=True):
-    """Per-wave records of the decode kernel family ``kernel`` (PKV_TIMELINE_VALU or
-    PKV_TIMELINE_MFMA) as uint64 [PKV_TIMELINE_RECORDS, PKV_TIMELINE_WORDS]
+    """Per-wave records of the kernel family ``kernel`` (PKV_TIMELINE_VALU,
+    PKV_TIMELINE_MFMA or PKV_TIMELINE_PREFILL) as uint64 [PKV_TIMELINE_RECORDS, PKV_TIMELINE_WORDS]
     (pkv_wave_timeline_read; only the instrumented library records any)."""
     import numpy as np
     buf = np.zeros((PKV_TIMELINE_RECORDS, PKV_TIMELINE_WORDS), dtype=np.uint64)

@@ -290,14 +290,21 @@ int decode_impl(float* out, const void* q, int32_t q_dtype, const void* k_cache,
 
 }  // namespace
 
+namespace pkv_decode {
+// The prefill kernel's tile-pair records (pa_prefill.hip); hipErrorNotSupported
+// in the product library.
+hipError_t wave_timeline_read_prefill(void* dst, size_t bytes, bool clear);
+}  // namespace pkv_decode
+
 extern "C" int pkv_wave_timeline_read(int32_t kernel, void* dst, size_t bytes, int32_t clear) {
   static_assert(PKV_TIMELINE_RECORDS == kTimelineWaves && PKV_TIMELINE_WORDS == kTimelineWords,
                 "timeline record layout");
-  if (kernel != PKV_TIMELINE_VALU && kernel != PKV_TIMELINE_MFMA)
+  if (kernel != PKV_TIMELINE_VALU && kernel != PKV_TIMELINE_MFMA && kernel != PKV_TIMELINE_PREFILL)
     return fail(PKV_ERR_INVALID_ARG, "pkv_wave_timeline_read: unknown kernel %d", kernel);
   if (!dst && bytes > 0) return fail(PKV_ERR_INVALID_ARG, "pkv_wave_timeline_read: NULL dst");
-  const hipError_t e = kernel == PKV_TIMELINE_VALU ? wave_timeline_read_valu(dst, bytes, clear != 0)
-                                                   : wave_timeline_read_mfma(dst, bytes, clear != 0);
+  const hipError_t e = kernel == PKV_TIMELINE_VALU   ? wave_timeline_read_valu(dst, bytes, clear != 0)
+                       : kernel == PKV_TIMELINE_MFMA ? wave_timeline_read_mfma(dst, bytes, clear != 0)
+                                                     : wave_timeline_read_prefill(dst, bytes, clear != 0);
   if (e == hipErrorNotSupported)
     return fail(PKV_ERR_UNSUPPORTED,
                 "pkv_wave_timeline_read: this library records no timeline (build --timeline)");

@@ -148,6 +148,69 @@ __device__ __forceinline__ void load_rows(const unsigned char* src, int bytes, u
   if (n > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + 1024), 16, voff1, 0, 0, 0);
 }
 
+// Tile-pair timeline of the prefill kernel, for measurement only: compiled in
+// with -DPKV_WAVE_TIMELINE (libpagedkv_timeline.so), empty otherwise.  Each
+// wave of a full 64-query workgroup of head tile 0 sums, over tile pairs 8-39,
+// the shader-clock cycles of seven stretches of a pair: 0 from the end of the
+// previous pair to this one's start; 1 its first-half load issue; 2 its
+// first-half work; 3 the barrier ending the first half; 4 its second-half load
+// issue; 5 its second-half work; 6 its wait for its loads.  The barrier ending
+// the pair falls in stretch 0 of the next.  Record (pkv_wave_timeline_read,
+// PKV_TIMELINE_PREFILL), at work item * 8 + wave: stretches 0-5 as 32-bit
+// pairs in words 0-2, stretch 6 and the pairs summed in word 3, the work item
+// and the wave in word 4, the XCC id in word 5.
+#ifdef PKV_WAVE_TIMELINE
+static __device__ uint64_t g_prefill_timeline[kTimelineWaves * kTimelineWords];
+
+struct PairClock {
+  uint64_t ts[7], acc[7] = {0, 0, 0, 0, 0, 0, 0}, prev = 0;
+  uint32_t pairs = 0;
+  __device__ __forceinline__ void mark(int i) { ts[i] = __builtin_amdgcn_s_memtime(); }
+  __device__ __forceinline__ void end_pair(int mm) {
+    if (mm >= 8 && mm < 40) {
+      acc[0] += ts[0] - prev;
+#pragma unroll
+      for (int i = 1; i < 7; ++i) acc[i] += ts[i] - ts[i - 1];
+      ++pairs;
+    }
+    prev = ts[6];
+  }
+  __device__ __forceinline__ void finish(unsigned item, int wave, bool full) {
+    const unsigned idx = item * kPrefillWaves + static_cast<unsigned>(wave);
+    if (blockIdx.x != 0 || !full || (threadIdx.x & (kWave - 1)) != 0 ||
+        idx >= static_cast<unsigned>(kTimelineWaves))
+      return;
+    auto lo = [](uint64_t v) { return v & 0xFFFFFFFFull; };
+    uint64_t* r = g_prefill_timeline + static_cast<uint64_t>(idx) * kTimelineWords;
+    r[0] = lo(acc[0]) | (lo(acc[1]) << 32);
+    r[1] = lo(acc[2]) | (lo(acc[3]) << 32);
+    r[2] = lo(acc[4]) | (lo(acc[5]) << 32);
+    r[3] = lo(acc[6]) | (static_cast<uint64_t>(pairs) << 32);
+    r[4] = static_cast<uint64_t>(item) | (static_cast<uint64_t>(wave) << 32);
+    r[5] = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID
+  }
+};
+
+static hipError_t prefill_timeline_copy(void* dst, size_t bytes, bool clear) {
+  const size_t cap = sizeof(g_prefill_timeline);
+  hipError_t e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_prefill_timeline), bytes < cap ? bytes : cap,
+                                     0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !clear) return e;
+  void* addr = nullptr;
+  e = hipGetSymbolAddress(&addr, HIP_SYMBOL(g_prefill_timeline));
+  if (e != hipSuccess) return e;
+  return hipMemset(addr, 0, cap);
+}
+#else
+struct PairClock {
+  __device__ __forceinline__ void mark(int) {}
+  __device__ __forceinline__ void end_pair(int) {}
+  __device__ __forceinline__ void finish(unsigned, int, bool) {}
+};
+
+static hipError_t prefill_timeline_copy(void*, size_t, bool) { return hipErrorNotSupported; }
+#endif
+
 template <int D, int B, int HT>
 __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(PrefillParams p) {
   constexpr int NW = kPrefillWaves;
@@ -428,30 +491,41 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
       // the barrier that ends phase 2mm + 1.  entry: the loading wave's table
       // entries (groups g0, g1) for the tile it loads in this pair, read one
       // pair ahead.
+      PairClock pc;                            // empty unless built with PKV_WAVE_TIMELINE
       constexpr int kAhead = XO ? 1 : 0;      // tile loaded in pair mm: mm + kAhead
       int entry[2] = {block_of(kAhead, g0), block_of(kAhead, g1)};
       auto phase_pair = [&](int mm, unsigned char* kc, unsigned char* kn, unsigned char* vc,
                             const unsigned char* vp) __attribute__((always_inline)) {
         int entry_after[2] = {0, 0};
+        pc.mark(0);
         if constexpr (XO) {
           if (mm + 1 < n) load_tile(kmem, kn, mm + 1, entry);
+          pc.mark(1);
           entry_after[0] = block_of(mm + 2, g0);   // lands by the wait that ends this pair
           entry_after[1] = block_of(mm + 2, g1);
           softmax_phase(mm - 1);
         } else {
+          pc.mark(1);
           matrix_phase(mm, kc, vp);
         }
+        pc.mark(2);
         __syncthreads();
+        pc.mark(3);
         if constexpr (XO) {
+          pc.mark(4);
           matrix_phase(mm, kc, vp);
         } else {
           if (mm < n) load_tile(vmem, vc, mm, entry);
+          pc.mark(4);
           entry_after[0] = block_of(mm + 1, g0);
           entry_after[1] = block_of(mm + 1, g1);
           softmax_phase(mm);
         }
+        pc.mark(5);
         __builtin_amdgcn_s_waitcnt(kWaitVmem);   // this wave's tile loads have landed
+        pc.mark(6);
         __syncthreads();                          // and everyone's: K(mm+1), V(mm) readable
+        pc.end_pair(mm);
         entry[0] = entry_after[0];
         entry[1] = entry_after[1];
       };
@@ -467,6 +541,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
         if (mm + 1 > n) break;
         phase_pair(mm + 1, kt1, kt0, vt1, vt0);
       }
+      pc.finish(k, wave, j0 + NW * QW <= nq);
     }
 
     // Per set: each lane's output rows, columns 4*grp + r, over their denominators.
@@ -531,6 +606,12 @@ constexpr int kPrefillWavesPerCu = 0;
 
 using pkv::fail;
 using namespace pkv_decode;
+
+namespace pkv_decode {
+hipError_t wave_timeline_read_prefill(void* dst, size_t bytes, bool clear) {
+  return prefill_timeline_copy(dst, bytes, clear);
+}
+}  // namespace pkv_decode
 
 extern "C" int32_t pa_prefill_queries_per_item(int32_t num_q_heads, int32_t num_kv_heads) {
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;

@@ -104,8 +104,9 @@ def test_wave_timeline_reader_in_the_product_library():
     lib = _lib.lib()
     buf = np.zeros(6, dtype=np.uint64)
     ptr = buf.ctypes.data
-    assert lib.pkv_wave_timeline_read(2, ptr, buf.nbytes, 0) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_wave_timeline_read(3, ptr, buf.nbytes, 0) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_wave_timeline_read(-1, ptr, buf.nbytes, 0) == _lib.PKV_ERR_INVALID_ARG
     assert lib.pkv_wave_timeline_read(_lib.PKV_TIMELINE_VALU, None, 48, 0) == _lib.PKV_ERR_INVALID_ARG
-    for kind in (_lib.PKV_TIMELINE_VALU, _lib.PKV_TIMELINE_MFMA):
+    for kind in (_lib.PKV_TIMELINE_VALU, _lib.PKV_TIMELINE_MFMA, _lib.PKV_TIMELINE_PREFILL):
         assert lib.pkv_wave_timeline_read(kind, ptr, buf.nbytes, 1) == _lib.PKV_ERR_UNSUPPORTED
         assert b"timeline" in lib.pkv_last_error()

@@ -32,3 +32,18 @@ def test_timeline_records_every_wave_of_the_launch():
     assert waves == items * 8
     assert 0 < span < 10_000
     assert "resident waves every 2 us" in text and "XCD" in text
+
+
+def test_prefill_timeline_records_tile_pairs():
+    lib = os.path.join(ROOT, "paged_kv_cache_244_amd", "libpagedkv_timeline.so")
+    if not os.path.exists(lib):
+        pytest.fail("libpagedkv_timeline.so is not built (run __graft_entry__.build())")
+    print("timeline: bench.py --workload prefill --timeline --warmup 2", flush=True)
+    run = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "prefill",
+                          "--timeline", "--warmup", "2"], capture_output=True, text=True, timeout=300)
+    assert run.returncode == 0, run.stderr[-3000:]
+    text = run.stdout
+    waves, groups = (int(x) for x in re.search(r"(\d+) waves of (\d+) full workgroups", text).groups())
+    assert groups > 0 and waves == 8 * groups
+    pair = float(re.search(r"^pair: ([\d.]+) cycles", text, re.M).group(1))
+    assert 1000 < pair < 100_000
