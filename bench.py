@@ -993,7 +993,7 @@ def summarize_timeline(recs, w):
 
 
 PAIR_STRETCHES = ("from the last pair (its end barrier)", "first-half load issue", "first-half work",
-                  "mid-pair barrier", "second-half load issue", "second-half work", "load wait")
+                  "between the halves", "second-half load issue", "second-half work", "load wait")
 
 
 def prefill_timeline(args, dev):

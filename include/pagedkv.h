@@ -778,7 +778,7 @@ int pkv_read_probe(const void* src, int64_t num_tiles, const int32_t* tile_order
  * head tile 0, at work item * 8 + wave, sums over tile pairs 8-39 the
  * shader-clock cycles of seven stretches of a pair (0 from the previous
  * pair's end, including the barrier that ended it; 1 first-half load issue;
- * 2 first-half work; 3 the mid-pair barrier; 4 second-half load issue;
+ * 2 first-half work; 3 between the halves; 4 second-half load issue;
  * 5 second-half work; 6 the wait for its loads): stretches 0-5 as 32-bit
  * halves of words [0]-[2], stretch 6 and the number of pairs in [3], work
  * item and wave in [4], XCC id in [5].  Records of positions no launch wrote

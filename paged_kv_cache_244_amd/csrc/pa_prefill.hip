@@ -45,8 +45,8 @@
 // scores of this tile) and the softmax phase (mask, maximum, exponentials,
 // rare rescale) on the vector ALUs; the probabilities are rounded to fp16 in
 // the matrix phase that uses them, which is the shorter one.  While one wave of a SIMD
-// keeps the matrix core busy the other runs its softmax, and every phase ends
-// at a workgroup barrier.  Two K and two V tile buffers.  The waves in their
+// keeps the matrix core busy the other runs its softmax, and every tile pair
+// (two phases) ends at a workgroup barrier.  Two K and two V tile buffers.  The waves in their
 // softmax phase issue the loads, each two row groups: K(m+1) by waves 4-7 at
 // the start of phase 2m, V(m) by waves 0-3 at the start of phase 2m+1, both
 // waited for before the barrier that ends phase 2m+1.
@@ -153,8 +153,8 @@ __device__ __forceinline__ void load_rows(const unsigned char* src, int bytes, u
 // wave of a full 64-query workgroup of head tile 0 sums, over tile pairs 8-39,
 // the shader-clock cycles of seven stretches of a pair: 0 from the end of the
 // previous pair to this one's start; 1 its first-half load issue; 2 its
-// first-half work; 3 the barrier ending the first half; 4 its second-half load
-// issue; 5 its second-half work; 6 its wait for its loads.  The barrier ending
+// first-half work; 3 between the halves (no barrier there); 4 its second-half
+// load issue; 5 its second-half work; 6 its wait for its loads.  The barrier ending
 // the pair falls in stretch 0 of the next.  Record (pkv_wave_timeline_read,
 // PKV_TIMELINE_PREFILL), at work item * 8 + wave: stretches 0-5 as 32-bit
 // pairs in words 0-2, stretch 6 and the pairs summed in word 3, the work item
@@ -509,7 +509,9 @@ __global__ __launch_bounds__(kWave * kPrefillWaves) void pa_prefill_kernel(Prefi
           matrix_phase(mm, kc, vp);
         }
         pc.mark(2);
-        __syncthreads();
+        // No barrier between the halves: nothing one group writes in this pair is
+        // read by the other in it (the loads go to the buffers the previous pair
+        // finished with), and the barrier below starts every pair together.
         pc.mark(3);
         if constexpr (XO) {
           pc.mark(4);
