@@ -54,7 +54,7 @@ def _run(cmd):
     subprocess.run(cmd, check=True)
 
 
-def build(jobs: int = 4, timeline: bool = False) -> str:
+def build(jobs: int = min(8, os.cpu_count() or 4), timeline: bool = False) -> str:
     """Compile every source to an object, then link the shared library
     (``timeline``: the instrumented libpagedkv_timeline.so instead)."""
     obj_dir = os.path.join(ROOT, "_build", "timeline") if timeline else os.path.join(ROOT, "_build")
